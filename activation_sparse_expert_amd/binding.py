@@ -1,0 +1,224 @@
+"""ctypes binding of libmoe_sel.so: the C ABI of include/moe_sel.h, same names.
+
+Argument marshalling only. Host arrays are NumPy arrays; device arrays are any
+object with ``data_ptr()`` (torch tensors on the GPU) or a raw integer address.
+Streams are ``hipStream_t`` handles as integers (``torch.cuda.current_stream()
+.cuda_stream``); ``None`` means the current torch stream when torch is on a GPU,
+else the default stream.
+
+The library must have been built (``python -m activation_sparse_expert_amd.build``);
+importing this module without it raises immediately: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_sel.so")
+
+MOE_SEL_OK, MOE_SEL_EINVAL, MOE_SEL_EUNSUPPORTED, MOE_SEL_ENOMEM, MOE_SEL_EDEVICE = range(5)
+
+EXPORTED = (
+    "moe_sel_abi_version", "moe_sel_status_str", "moe_sel_last_error",
+    "moe_sel_prepare_expert_host", "moe_sel_prepare", "moe_sel_forward",
+    "moe_sel_forward_dense", "moe_sel_debug_selection", "moe_sel_export_expert",
+    "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy",
+)
+
+
+class moe_sel_config(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("d", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("m", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("max_top_e", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32),
+        ("tern_ratio", ctypes.c_double),
+    ]
+
+
+class MoeSelError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: {_status_name(status)} ({status}): {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m activation_sparse_expert_amd.build`")
+    # One HIP runtime per process: torch ships its own libamdhip64 (same soname).
+    # Loading torch first makes the library bind to that runtime, so torch's
+    # device pointers and stream handles are valid inside the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    sig = {
+        "moe_sel_abi_version": (i32, []),
+        "moe_sel_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_sel_last_error": (ctypes.c_char_p, []),
+        "moe_sel_prepare_expert_host": (ctypes.c_int, [ctypes.POINTER(moe_sel_config), vp, vp, vp,
+                                                       vp, vp, f32p, f32p, f32p, vp, vp, vp, vp]),
+        "moe_sel_prepare": (ctypes.c_int, [ctypes.POINTER(moe_sel_config), vp, vp, vp, vp,
+                                           ctypes.POINTER(vp)]),
+        "moe_sel_forward": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_sel_forward_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp]),
+        "moe_sel_debug_selection": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp]),
+        "moe_sel_export_expert": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_sel_get_config": (ctypes.c_int, [vp, ctypes.POINTER(moe_sel_config)]),
+        "moe_sel_device_bytes": (ctypes.c_uint64, [vp]),
+        "moe_sel_destroy": (None, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _status_name(status: int) -> str:
+    return _lib.moe_sel_status_str(int(status)).decode()
+
+
+def _check(status: int, func: str):
+    if status != MOE_SEL_OK:
+        raise MoeSelError(status, func, _lib.moe_sel_last_error().decode())
+
+
+def _host_ptr(a, dtype):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.dtype == dtype and a.flags.c_contiguous, (a.dtype, dtype)
+    return a.ctypes.data
+
+
+def _dev_ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream)
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+    except ImportError:
+        pass
+    return None
+
+
+def make_config(d, n_experts, m, rank, max_top_e, max_batch=1, tern_ratio=0.7) -> moe_sel_config:
+    return moe_sel_config(ctypes.sizeof(moe_sel_config), d, n_experts, m, rank, max_top_e, max_batch,
+                          float(tern_ratio))
+
+
+def moe_sel_abi_version() -> int:
+    return _lib.moe_sel_abi_version()
+
+
+def moe_sel_prepare_expert_host(cfg: moe_sel_config, w_gate, w_up, w_down, *, sketch=True, lowrank=True):
+    """Host-only preparation of one expert; returns a dict of NumPy arrays."""
+    m, d, r = cfg.m, cfg.d, cfg.rank
+    out = dict(alpha_gate=np.zeros(m, np.float32), alpha_up=np.zeros(m, np.float32),
+               down_norm=np.zeros(m, np.float32), nnz_gate=np.zeros(m, np.int32), nnz_up=np.zeros(m, np.int32))
+    if sketch:
+        out["tern_gate"] = np.zeros((m, d), np.int8)
+        out["tern_up"] = np.zeros((m, d), np.int8)
+    if lowrank and r > 0:
+        out["p_bf16"] = np.zeros((r, d), np.uint16)
+        out["q_bf16"] = np.zeros((m, r), np.uint16)
+    st = _lib.moe_sel_prepare_expert_host(
+        ctypes.byref(cfg), _host_ptr(w_gate, np.uint16), _host_ptr(w_up, np.uint16), _host_ptr(w_down, np.uint16),
+        _host_ptr(out.get("tern_gate"), np.int8), _host_ptr(out.get("tern_up"), np.int8),
+        _host_ptr(out["alpha_gate"], np.float32), _host_ptr(out["alpha_up"], np.float32),
+        _host_ptr(out["down_norm"], np.float32), _host_ptr(out["nnz_gate"], np.int32),
+        _host_ptr(out["nnz_up"], np.int32), _host_ptr(out.get("p_bf16"), np.uint16),
+        _host_ptr(out.get("q_bf16"), np.uint16))
+    _check(st, "moe_sel_prepare_expert_host")
+    return out
+
+
+def moe_sel_prepare(cfg: moe_sel_config, w_gate, w_up, w_down, stream=None) -> int:
+    """Build a context from host bf16 weights [E][m][d], [E][m][d], [E][d][m]; returns its handle."""
+    ctx = ctypes.c_void_p()
+    st = _lib.moe_sel_prepare(ctypes.byref(cfg), _host_ptr(w_gate, np.uint16), _host_ptr(w_up, np.uint16),
+                              _host_ptr(w_down, np.uint16), _stream(stream), ctypes.byref(ctx))
+    _check(st, "moe_sel_prepare")
+    return ctx.value
+
+
+def moe_sel_forward(ctx, x, logits, batch, top_e, k_budget, out, stream=None):
+    st = _lib.moe_sel_forward(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e), int(k_budget),
+                              _dev_ptr(out), _stream(stream))
+    _check(st, "moe_sel_forward")
+
+
+def moe_sel_forward_dense(ctx, x, logits, batch, top_e, out, stream=None):
+    st = _lib.moe_sel_forward_dense(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e), _dev_ptr(out),
+                                    _stream(stream))
+    _check(st, "moe_sel_forward_dense")
+
+
+def moe_sel_debug_selection(ctx, batch, top_e, k, m, with_scores=True):
+    out = dict(expert_ids=np.zeros((batch, top_e), np.int32), gate_w=np.zeros((batch, top_e), np.float32),
+               chan_idx=np.zeros((batch, top_e, k), np.int32), chan_count=np.zeros((batch, top_e), np.int32))
+    if with_scores:
+        out["h_hat"] = np.zeros((batch, top_e, m), np.float32)
+        out["score"] = np.zeros((batch, top_e, m), np.float32)
+    st = _lib.moe_sel_debug_selection(ctx, out["expert_ids"].ctypes.data, out["gate_w"].ctypes.data,
+                                      out["chan_idx"].ctypes.data, out["chan_count"].ctypes.data,
+                                      _host_ptr(out.get("h_hat"), np.float32), _host_ptr(out.get("score"), np.float32))
+    _check(st, "moe_sel_debug_selection")
+    return out
+
+
+def moe_sel_export_expert(ctx, expert, cfg: moe_sel_config):
+    m, d, r = cfg.m, cfg.d, cfg.rank
+    out = dict(tern_gate=np.zeros((m, d), np.int8), tern_up=np.zeros((m, d), np.int8),
+               alpha_gate=np.zeros(m, np.float32), alpha_up=np.zeros(m, np.float32),
+               down_norm=np.zeros(m, np.float32))
+    if r > 0:
+        out["p_bf16"] = np.zeros((r, d), np.uint16)
+        out["q_bf16"] = np.zeros((m, r), np.uint16)
+    st = _lib.moe_sel_export_expert(ctx, int(expert), out["tern_gate"].ctypes.data, out["tern_up"].ctypes.data,
+                                    out["alpha_gate"].ctypes.data, out["alpha_up"].ctypes.data,
+                                    out["down_norm"].ctypes.data, _host_ptr(out.get("p_bf16"), np.uint16),
+                                    _host_ptr(out.get("q_bf16"), np.uint16))
+    _check(st, "moe_sel_export_expert")
+    return out
+
+
+def moe_sel_get_config(ctx) -> moe_sel_config:
+    cfg = moe_sel_config()
+    _check(_lib.moe_sel_get_config(ctx, ctypes.byref(cfg)), "moe_sel_get_config")
+    return cfg
+
+
+def moe_sel_device_bytes(ctx) -> int:
+    return int(_lib.moe_sel_device_bytes(ctx))
+
+
+def moe_sel_destroy(ctx):
+    _lib.moe_sel_destroy(ctx)
+
+
+def moe_sel_status_str(status: int) -> str:
+    return _status_name(status)
+
+
+def moe_sel_last_error() -> str:
+    return _lib.moe_sel_last_error().decode()

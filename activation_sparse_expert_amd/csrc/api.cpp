@@ -1,0 +1,446 @@
+// C ABI of the library: validation, context lifecycle, preparation and the
+// enqueueing of forward calls. See include/moe_sel.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "kernels.h"
+#include "moe_sel.h"
+
+struct moe_sel_ctx {
+  moe_sel_config cfg{};
+  int device = 0;
+  // prepared layer
+  uint32_t* codes = nullptr;
+  float4* stats = nullptr;
+  uint16_t* wch = nullptr;
+  uint16_t* pmat = nullptr;
+  uint16_t* qmat = nullptr;
+  // workspace
+  int8_t* xq = nullptr;
+  int* xexp = nullptr;
+  int* pair_expert = nullptr;
+  float* pair_w = nullptr;
+  float* hhat = nullptr;
+  float* score = nullptr;
+  int* sel_idx = nullptr;
+  int* sel_count = nullptr;
+  float* zvec = nullptr;
+  float* hsel = nullptr;
+  float* ypart = nullptr;
+  std::vector<void*> allocations;
+  uint64_t device_bytes = 0;
+  // last sparse call (for moe_sel_debug_selection)
+  int last_batch = 0, last_top_e = 0, last_k = -1;
+  hipStream_t last_stream = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_sel_status fail(moe_sel_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+moe_sel_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_SEL_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+moe_sel_status dev_alloc(moe_sel_ctx* c, T** p, size_t count) {
+  const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+  void* q = nullptr;
+  const hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_SEL_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  c->allocations.push_back(q);
+  c->device_bytes += bytes;
+  *p = (T*)q;
+  return MOE_SEL_OK;
+}
+
+void free_ctx(moe_sel_ctx* c) {
+  if (!c) return;
+  for (void* p : c->allocations) (void)hipFree(p);
+  delete c;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct PrepJob {
+  const moe_sel_config* cfg;
+  const uint16_t *wg, *wu, *wd;
+  uint32_t* codes;
+  float* stats;
+  uint16_t* wch;
+  uint16_t* pmat;
+  uint16_t* qmat;
+  std::vector<std::string>* errors;
+};
+
+void prep_one(int e, void* arg) {
+  PrepJob* j = (PrepJob*)arg;
+  const moe_sel_config& c = *j->cfg;
+  const size_t md = (size_t)c.m * c.d;
+  moe_sel::ExpertPrep out;
+  out.codes = j->codes + (size_t)e * moe_sel::codes_dwords_per_expert(c.d, c.m);
+  out.stats = j->stats + (size_t)e * c.m * 4;
+  out.wch = j->wch + (size_t)e * 3 * md;
+  if (c.rank > 0) {
+    out.p_bf16 = j->pmat + (size_t)e * c.rank * c.d;
+    out.q_bf16 = j->qmat + (size_t)e * c.m * c.rank;
+  }
+  try {
+    (*j->errors)[e] = moe_sel::prepare_expert(c, j->wg + (size_t)e * md, j->wu + (size_t)e * md,
+                                              j->wd + (size_t)e * md, out);
+  } catch (const std::bad_alloc&) {
+    (*j->errors)[e] = "host allocation failed";
+  } catch (...) {
+    (*j->errors)[e] = "unexpected exception";
+  }
+}
+
+moe_sel_status check_forward(moe_sel_ctx* ctx, const void* x, const void* logits, int32_t batch, int32_t top_e,
+                             int32_t k, const void* out) {
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (!x || !logits || !out) return fail(MOE_SEL_EINVAL, "x, logits and out must be non-null");
+  if (!aligned16(x) || !aligned16(logits) || !aligned16(out))
+    return fail(MOE_SEL_EINVAL, "x, logits and out must be 16-byte aligned");
+  if (batch < 1 || batch > ctx->cfg.max_batch)
+    return fail(MOE_SEL_EINVAL, "batch " + std::to_string(batch) + " outside [1, " +
+                                    std::to_string(ctx->cfg.max_batch) + "]");
+  if (top_e < 1 || top_e > ctx->cfg.max_top_e)
+    return fail(MOE_SEL_EINVAL, "top_e " + std::to_string(top_e) + " outside [1, " +
+                                    std::to_string(ctx->cfg.max_top_e) + "]");
+  if (k < 0 || k > ctx->cfg.m)
+    return fail(MOE_SEL_EINVAL, "k_budget " + std::to_string(k) + " outside [0, " + std::to_string(ctx->cfg.m) + "]");
+  return MOE_SEL_OK;
+}
+
+moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logits, int32_t batch, int32_t top_e,
+                           int32_t k, uint16_t* out) {
+  moe_sel::FwdArgs a{};
+  a.codes = c->codes;
+  a.stats = c->stats;
+  a.wch = c->wch;
+  a.pmat = c->pmat;
+  a.qmat = c->qmat;
+  a.d = c->cfg.d;
+  a.m = c->cfg.m;
+  a.r = c->cfg.rank;
+  a.n_experts = c->cfg.n_experts;
+  a.x = x;
+  a.logits = logits;
+  a.out = out;
+  a.batch = batch;
+  a.top_e = top_e;
+  a.k = k;
+  a.xq = c->xq;
+  a.xexp = c->xexp;
+  a.pair_expert = c->pair_expert;
+  a.pair_w = c->pair_w;
+  a.hhat = c->hhat;
+  a.score = c->score;
+  a.sel_idx = c->sel_idx;
+  a.sel_count = c->sel_count;
+  a.zvec = c->zvec;
+  a.hsel = c->hsel;
+  a.ypart = c->ypart;
+  return a;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+    else prev = -1;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+namespace moe_sel {
+
+std::string validate_config(const moe_sel_config* c) {
+  if (!c) return "config is null";
+  if (c->struct_size != sizeof(moe_sel_config))
+    return "config.struct_size is " + std::to_string(c->struct_size) + ", expected " +
+           std::to_string(sizeof(moe_sel_config));
+  if (c->d < 64 || c->d > 16384 || c->d % 64) return "d must be a multiple of 64 in [64, 16384]";
+  if (c->m < 64 || c->m > 32768 || c->m % 64) return "m must be a multiple of 64 in [64, 32768]";
+  if (c->n_experts < 1 || c->n_experts > 1024) return "n_experts must be in [1, 1024]";
+  if (c->rank < 0 || c->rank > 128 || c->rank > c->d || c->rank > c->m) return "rank must be in [0, min(d, m, 128)]";
+  if (c->max_top_e < 1 || c->max_top_e > 64 || c->max_top_e > c->n_experts)
+    return "max_top_e must be in [1, min(n_experts, 64)]";
+  if (c->max_batch < 1 || c->max_batch > 4096) return "max_batch must be in [1, 4096]";
+  if (!(c->tern_ratio > 0.0 && c->tern_ratio < 1e3)) return "tern_ratio must be in (0, 1000)";
+  return std::string();
+}
+
+}  // namespace moe_sel
+
+extern "C" {
+
+int32_t moe_sel_abi_version(void) { return MOE_SEL_ABI_VERSION; }
+
+const char* moe_sel_status_str(moe_sel_status s) {
+  switch (s) {
+    case MOE_SEL_OK: return "ok";
+    case MOE_SEL_EINVAL: return "invalid argument";
+    case MOE_SEL_EUNSUPPORTED: return "unsupported";
+    case MOE_SEL_ENOMEM: return "out of memory";
+    case MOE_SEL_EDEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* moe_sel_last_error(void) { return g_last_error.c_str(); }
+
+moe_sel_status moe_sel_prepare_expert_host(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                                           const uint16_t* w_down, int8_t* tern_gate, int8_t* tern_up,
+                                           float* alpha_gate, float* alpha_up, float* down_norm, int32_t* nnz_gate,
+                                           int32_t* nnz_up, uint16_t* p_bf16, uint16_t* q_bf16) {
+  g_last_error.clear();
+  const std::string bad = moe_sel::validate_config(cfg);
+  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
+  if (!w_gate || !w_up || !w_down) return fail(MOE_SEL_EINVAL, "weights must be non-null");
+  moe_sel::ExpertPrep out;
+  out.tern_gate = tern_gate;
+  out.tern_up = tern_up;
+  out.alpha_gate = alpha_gate;
+  out.alpha_up = alpha_up;
+  out.down_norm = down_norm;
+  out.nnz_gate = nnz_gate;
+  out.nnz_up = nnz_up;
+  out.p_bf16 = p_bf16;
+  out.q_bf16 = q_bf16;
+  try {
+    const std::string err = moe_sel::prepare_expert(*cfg, w_gate, w_up, w_down, out);
+    if (!err.empty()) return fail(MOE_SEL_EINVAL, err);
+  } catch (const std::bad_alloc&) {
+    return fail(MOE_SEL_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(MOE_SEL_EINVAL, "unexpected exception");
+  }
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, void* stream, moe_sel_ctx** out) {
+  g_last_error.clear();
+  const std::string bad = moe_sel::validate_config(cfg);
+  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
+  if (!w_gate || !w_up || !w_down || !out) return fail(MOE_SEL_EINVAL, "weights and out must be non-null");
+  const moe_sel_config c = *cfg;
+  const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
+  const size_t pairs = (size_t)c.max_batch * c.max_top_e;
+  moe_sel_ctx* ctx = nullptr;
+  try {
+    ctx = new moe_sel_ctx();
+  } catch (...) {
+    return fail(MOE_SEL_ENOMEM, "host allocation failed");
+  }
+  ctx->cfg = c;
+  hipError_t he = hipGetDevice(&ctx->device);
+  if (he != hipSuccess) {
+    free_ctx(ctx);
+    return hip_fail(he, "hipGetDevice");
+  }
+  // host staging of the prepared layer
+  std::vector<uint32_t> h_codes;
+  std::vector<float> h_stats;
+  std::vector<uint16_t> h_wch, h_p, h_q;
+  try {
+    h_codes.resize(E * moe_sel::codes_dwords_per_expert(c.d, c.m));
+    h_stats.resize(E * m * 4);
+    h_wch.resize(E * m * 3 * d);
+    h_p.resize(std::max<size_t>(E * r * d, 1));
+    h_q.resize(std::max<size_t>(E * m * r, 1));
+  } catch (...) {
+    free_ctx(ctx);
+    return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
+  }
+  std::vector<std::string> errors(E);
+  PrepJob job{&c, w_gate, w_up, w_down, h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
+  moe_sel::parallel_for((int)E, 0, prep_one, &job);
+  for (size_t e = 0; e < E; ++e)
+    if (!errors[e].empty()) {
+      free_ctx(ctx);
+      return fail(MOE_SEL_EINVAL, "expert " + std::to_string(e) + ": " + errors[e]);
+    }
+  moe_sel_status st = MOE_SEL_OK;
+#define ALLOC(ptr, n) \
+  if (st == MOE_SEL_OK) st = dev_alloc(ctx, &ctx->ptr, (n))
+  ALLOC(codes, h_codes.size());
+  ALLOC(stats, E * m);
+  ALLOC(wch, h_wch.size());
+  ALLOC(pmat, h_p.size());
+  ALLOC(qmat, h_q.size());
+  ALLOC(xq, (size_t)c.max_batch * d);
+  ALLOC(xexp, (size_t)c.max_batch);
+  ALLOC(pair_expert, pairs);
+  ALLOC(pair_w, pairs);
+  ALLOC(hhat, pairs * m);
+  ALLOC(score, pairs * m);
+  ALLOC(sel_idx, pairs * m);
+  ALLOC(sel_count, pairs);
+  ALLOC(zvec, pairs * std::max<size_t>(r, 1));
+  ALLOC(hsel, pairs * m);
+  ALLOC(ypart, pairs * d);
+#undef ALLOC
+  if (st != MOE_SEL_OK) {
+    free_ctx(ctx);
+    return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  struct Up {
+    void* dst;
+    const void* src;
+    size_t bytes;
+  } ups[] = {{ctx->codes, h_codes.data(), h_codes.size() * 4},
+             {ctx->stats, h_stats.data(), h_stats.size() * 4},
+             {ctx->wch, h_wch.data(), h_wch.size() * 2},
+             {ctx->pmat, h_p.data(), h_p.size() * 2},
+             {ctx->qmat, h_q.data(), h_q.size() * 2}};
+  for (const Up& u : ups) {
+    he = hipMemcpyAsync(u.dst, u.src, u.bytes, hipMemcpyHostToDevice, s);
+    if (he != hipSuccess) {
+      free_ctx(ctx);
+      return hip_fail(he, "hipMemcpyAsync");
+    }
+  }
+  he = hipStreamSynchronize(s);
+  if (he != hipSuccess) {
+    free_ctx(ctx);
+    return hip_fail(he, "hipStreamSynchronize");
+  }
+  *out = ctx;
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float* logits, int32_t batch,
+                               int32_t top_e, int32_t k_budget, uint16_t* out, void* stream) {
+  g_last_error.clear();
+  moe_sel_status st = check_forward(ctx, x, logits, batch, top_e, k_budget, out);
+  if (st != MOE_SEL_OK) return st;
+  DeviceGuard guard(ctx->device);
+  const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, k_budget, out);
+  const hipError_t e = moe_sel::launch_forward(a, false, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  ctx->last_batch = batch;
+  ctx->last_top_e = top_e;
+  ctx->last_k = k_budget;
+  ctx->last_stream = (hipStream_t)stream;
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_forward_dense(moe_sel_ctx* ctx, const uint16_t* x, const float* logits, int32_t batch,
+                                     int32_t top_e, uint16_t* out, void* stream) {
+  g_last_error.clear();
+  moe_sel_status st = check_forward(ctx, x, logits, batch, top_e, 0, out);
+  if (st != MOE_SEL_OK) return st;
+  DeviceGuard guard(ctx->device);
+  const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, ctx->cfg.m, out);
+  const hipError_t e = moe_sel::launch_forward(a, true, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_debug_selection(moe_sel_ctx* ctx, int32_t* expert_ids, float* gate_w, int32_t* chan_idx,
+                                       int32_t* chan_count, float* h_hat, float* score) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (ctx->last_k < 0) return fail(MOE_SEL_EINVAL, "no sparse forward has run on this context");
+  DeviceGuard guard(ctx->device);
+  hipError_t e = hipStreamSynchronize(ctx->last_stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  const size_t pairs = (size_t)ctx->last_batch * ctx->last_top_e;
+  const size_t m = ctx->cfg.m, k = ctx->last_k;
+  if (expert_ids && (e = hipMemcpy(expert_ids, ctx->pair_expert, pairs * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (gate_w && (e = hipMemcpy(gate_w, ctx->pair_w, pairs * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (chan_count && (e = hipMemcpy(chan_count, ctx->sel_count, pairs * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (chan_idx && k > 0 &&
+      (e = hipMemcpy2D(chan_idx, k * 4, ctx->sel_idx, m * 4, k * 4, pairs, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy2D");
+  if (h_hat && (e = hipMemcpy(h_hat, ctx->hhat, pairs * m * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (score && (e = hipMemcpy(score, ctx->score, pairs * m * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert, int8_t* tern_gate, int8_t* tern_up,
+                                     float* alpha_gate, float* alpha_up, float* down_norm, uint16_t* p_bf16,
+                                     uint16_t* q_bf16) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (expert < 0 || expert >= ctx->cfg.n_experts) return fail(MOE_SEL_EINVAL, "expert out of range");
+  DeviceGuard guard(ctx->device);
+  const int d = ctx->cfg.d, m = ctx->cfg.m, r = ctx->cfg.rank;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  if (tern_gate || tern_up) {
+    const size_t nd = moe_sel::codes_dwords_per_expert(d, m);
+    std::vector<uint32_t> codes(nd);
+    if ((e = hipMemcpy(codes.data(), ctx->codes + (size_t)expert * nd, nd * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+    for (int j = 0; j < m; ++j)
+      for (int mat = 0; mat < 2; ++mat) {
+        int8_t* dst = mat == 0 ? tern_gate : tern_up;
+        if (!dst) continue;
+        for (int i = 0; i < d; ++i) {
+          const int b = i / moe_sel::kBlock, w = (i % moe_sel::kBlock) / 16, a = (i % 16) / 4, ii = i % 4;
+          const uint32_t word = codes[moe_sel::codes_dword_index(d, m, j / moe_sel::kGroup, mat, b,
+                                                                 j % moe_sel::kGroup, w)];
+          dst[(size_t)j * d + i] = (int8_t)((int)((word >> (8 * ii + 2 * a)) & 3u) - 1);
+        }
+      }
+  }
+  if (alpha_gate || alpha_up || down_norm) {
+    std::vector<float> st((size_t)m * 4);
+    if ((e = hipMemcpy(st.data(), ctx->stats + (size_t)expert * m, (size_t)m * 16, hipMemcpyDeviceToHost)) !=
+        hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+    for (int j = 0; j < m; ++j) {
+      if (alpha_gate) alpha_gate[j] = st[(size_t)j * 4];
+      if (alpha_up) alpha_up[j] = st[(size_t)j * 4 + 1];
+      if (down_norm) down_norm[j] = st[(size_t)j * 4 + 2];
+    }
+  }
+  if (p_bf16 && r > 0 &&
+      (e = hipMemcpy(p_bf16, ctx->pmat + (size_t)expert * r * d, (size_t)r * d * 2, hipMemcpyDeviceToHost)) !=
+          hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (q_bf16 && r > 0 &&
+      (e = hipMemcpy(q_bf16, ctx->qmat + (size_t)expert * m * r, (size_t)m * r * 2, hipMemcpyDeviceToHost)) !=
+          hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg) {
+  if (!ctx || !cfg) return fail(MOE_SEL_EINVAL, "ctx and cfg must be non-null");
+  *cfg = ctx->cfg;
+  return MOE_SEL_OK;
+}
+
+uint64_t moe_sel_device_bytes(const moe_sel_ctx* ctx) { return ctx ? ctx->device_bytes : 0; }
+
+void moe_sel_destroy(moe_sel_ctx* ctx) { free_ctx(ctx); }
+
+}  // extern "C"

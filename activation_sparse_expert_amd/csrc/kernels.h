@@ -1,0 +1,40 @@
+// Launch interface between the host runtime and the device kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe_sel {
+
+// Everything one forward call needs; all pointers are device pointers.
+struct FwdArgs {
+  // prepared layer (read-only)
+  const uint32_t* codes;   // packed 2-bit sketch codes
+  const float4* stats;     // [E][m] {alpha_gate, alpha_up, down_norm, 0}
+  const uint16_t* wch;     // [E][m][3][d] bf16
+  const uint16_t* pmat;    // [E][r][d] bf16
+  const uint16_t* qmat;    // [E][m][r] bf16
+  int d, m, r, n_experts;
+  // call
+  const uint16_t* x;       // [B][d] bf16
+  const float* logits;     // [B][E]
+  uint16_t* out;           // [B][d] bf16
+  int batch, top_e, k;
+  // workspace
+  int8_t* xq;              // [B][d]
+  int* xexp;               // [B]
+  int* pair_expert;        // [B*top_e]
+  float* pair_w;           // [B*top_e]
+  float* hhat;             // [P][m]
+  float* score;            // [P][m]
+  int* sel_idx;            // [P][m]
+  int* sel_count;          // [P]
+  float* zvec;             // [P][r]
+  float* hsel;             // [P][m]
+  float* ypart;            // [P][d]
+};
+
+hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
+
+}  // namespace moe_sel

@@ -1,0 +1,202 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Selections (routed experts, channel indices, counts) and the channel scores are
+compared bit for bit; outputs to max_t ||out - y||_inf / ||y||_inf <= 2e-2
+(bf16 output of an fp32 accumulation against the float64 oracle).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from activation_sparse_expert_amd import synth
+from gpu_common import TOL, Layer, out_to_f64, rel_err, to_dev_f32, to_dev_u16, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def b():
+    from activation_sparse_expert_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def tiny(b, torch):
+    lay = Layer(b, "tiny", max_batch=8)
+    yield lay
+    lay.close()
+
+
+def _run(b, torch, lay, x_bits, logits, k, top_e=None, dense=False):
+    top_e = top_e or lay.top_e
+    bsz = x_bits.shape[0]
+    x = to_dev_u16(torch, x_bits)
+    lg = to_dev_f32(torch, logits)
+    out = torch.zeros((bsz, lay.d), dtype=torch.int16, device="cuda")
+    if dense:
+        b.moe_sel_forward_dense(lay.ctx, x, lg, bsz, top_e, out)
+    else:
+        b.moe_sel_forward(lay.ctx, x, lg, bsz, top_e, k, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_selection(b, lay, ref, bsz, top_e, k, scores=True):
+    dbg = b.moe_sel_debug_selection(lay.ctx, bsz, top_e, k, lay.m, with_scores=scores)
+    assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+    assert np.all(dbg["chan_count"] == k)
+    for t in range(bsz):
+        for s in range(top_e):
+            assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (t, s)
+            if scores:
+                assert np.array_equal(dbg["score"][t, s].view(np.uint32), ref["score"][t][s].view(np.uint32)), (t, s)
+                assert np.array_equal(dbg["h_hat"][t, s].view(np.uint32), ref["h_hat"][t][s].view(np.uint32)), (t, s)
+    assert np.allclose(dbg["gate_w"], ref["gate_w"], rtol=1e-5, atol=1e-7)
+    return dbg
+
+
+def test_device_layout_round_trip(b, tiny):
+    for e in (0, 7):
+        dev = b.moe_sel_export_expert(tiny.ctx, e, tiny.cfg)
+        prep = tiny.oracle.expert(e)
+        assert np.array_equal(dev["tern_gate"], prep["tern_g"])
+        assert np.array_equal(dev["tern_up"], prep["tern_u"])
+        assert np.array_equal(dev["alpha_gate"].view(np.uint32), prep["alpha_g"].view(np.uint32))
+        assert np.array_equal(dev["down_norm"].view(np.uint32), prep["c"].view(np.uint32))
+
+
+def test_tiny_workload_parity(b, torch, tiny):
+    k = synth.WORKLOADS["tiny"]["ks"][0]
+    x = synth.tokens(0, 0, 1, tiny.d)
+    logits = synth.router_logits(0, 0, 1, tiny.E)
+    out = _run(b, torch, tiny, x, logits, k)
+    ref = tiny.oracle.forward(x, logits, tiny.top_e, k)
+    _check_selection(b, tiny, ref, 1, tiny.top_e, k)
+    err = rel_err(out_to_f64(torch, out), ref["y"])
+    print(f"tiny k={k}: max-rel-err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("k", [0, 1, 3, 91, 255, 511, 512])
+def test_budgets_including_edges(b, torch, tiny, k):
+    rng = np.random.default_rng(100 + k)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((2, tiny.E)).astype(np.float32)
+    out = _run(b, torch, tiny, x, logits, k)
+    ref = tiny.oracle.forward(x, logits, tiny.top_e, k)
+    _check_selection(b, tiny, ref, 2, tiny.top_e, k)
+    assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+
+
+def test_k_equals_m_equals_dense(b, torch, tiny):
+    rng = np.random.default_rng(7)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((3, tiny.E)).astype(np.float32)
+    full = out_to_f64(torch, _run(b, torch, tiny, x, logits, tiny.m))
+    dense = out_to_f64(torch, _run(b, torch, tiny, x, logits, 0, dense=True))
+    ref = tiny.oracle.forward_dense(x, logits, tiny.top_e)
+    assert rel_err(dense, ref) <= TOL and rel_err(full, ref) <= TOL
+    assert rel_err(full, dense) <= 1e-2
+
+
+def test_batch_rows_match_single_token_calls(b, torch, tiny):
+    rng = np.random.default_rng(8)
+    bsz, k = 8, 92
+    x = synth.f32_to_bf16_bits(rng.standard_normal((bsz, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((bsz, tiny.E)).astype(np.float32)
+    outb = _run(b, torch, tiny, x, logits, k).cpu().numpy()
+    selb = b.moe_sel_debug_selection(tiny.ctx, bsz, tiny.top_e, k, tiny.m, with_scores=False)
+    ref = tiny.oracle.forward(x, logits, tiny.top_e, k)
+    _check_selection(b, tiny, ref, bsz, tiny.top_e, k)
+    for t in (0, 5):
+        out1 = _run(b, torch, tiny, x[t:t + 1], logits[t:t + 1], k).cpu().numpy()
+        sel1 = b.moe_sel_debug_selection(tiny.ctx, 1, tiny.top_e, k, tiny.m, with_scores=False)
+        assert np.array_equal(sel1["chan_idx"][0], selb["chan_idx"][t])
+        assert np.array_equal(out1[0], outb[t])
+
+
+def test_fewer_experts_than_trained(b, torch, tiny):
+    rng = np.random.default_rng(9)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((1, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((1, tiny.E)).astype(np.float32)
+    out = _run(b, torch, tiny, x, logits, 40, top_e=1)
+    ref = tiny.oracle.forward(x, logits, 1, 40)
+    _check_selection(b, tiny, ref, 1, 1, 40)
+    assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+
+
+def test_degenerate_inputs(b, torch, tiny):
+    x = np.zeros((1, tiny.d), np.uint16)
+    logits = np.zeros((1, tiny.E), np.float32)
+    out = _run(b, torch, tiny, x, logits, 92).cpu().numpy()
+    assert not out.any()
+    dbg = b.moe_sel_debug_selection(tiny.ctx, 1, tiny.top_e, 92, tiny.m, with_scores=False)
+    assert dbg["expert_ids"][0].tolist() == [0, 1]
+    assert np.allclose(dbg["gate_w"], 0.5)
+    # all-zero scores: the k lowest channel indices
+    assert dbg["chan_idx"][0, 0].tolist() == list(range(92))
+
+
+def test_repeatable_bitwise(b, torch, tiny):
+    rng = np.random.default_rng(10)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((4, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((4, tiny.E)).astype(np.float32)
+    o1 = _run(b, torch, tiny, x, logits, 92).cpu().numpy()
+    o2 = _run(b, torch, tiny, x, logits, 92).cpu().numpy()
+    assert np.array_equal(o1, o2)
+
+
+def test_forward_argument_errors(b, torch, tiny):
+    x = torch.zeros((1, tiny.d), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((1, tiny.E), dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, tiny.d), dtype=torch.int16, device="cuda")
+    before = out.clone()
+    cases = [dict(batch=0), dict(batch=9), dict(top_e=0), dict(top_e=3), dict(k=-1), dict(k=513)]
+    for c in cases:
+        args = dict(batch=1, top_e=2, k=10)
+        args.update(c)
+        with pytest.raises(b.MoeSelError) as ei:
+            b.moe_sel_forward(tiny.ctx, x, lg, args["batch"], args["top_e"], args["k"], out)
+        assert ei.value.status == b.MOE_SEL_EINVAL
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_forward(tiny.ctx, x, lg, 1, 2, 10, 0)
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_forward(tiny.ctx, x.data_ptr() + 2, lg, 1, 2, 10, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, before)
+
+
+@pytest.fixture(scope="module")
+def qwen(b, torch):
+    lay = Layer(b, "qwen3", max_batch=4)
+    yield lay
+    lay.close()
+
+
+@pytest.mark.parametrize("k", [100, 138])
+def test_qwen3_shape_parity(b, torch, qwen, k):
+    w = synth.WORKLOADS["qwen3"]
+    x = synth.tokens(w["wid"], 0, 1, qwen.d)
+    logits = synth.router_logits(w["wid"], 0, 1, qwen.E)
+    out = _run(b, torch, qwen, x, logits, k)
+    ref = qwen.oracle.forward(x, logits, qwen.top_e, k)
+    _check_selection(b, qwen, ref, 1, qwen.top_e, k)
+    err = rel_err(out_to_f64(torch, out), ref["y"])
+    print(f"qwen3 k={k}: max-rel-err {err:.2e}")
+    assert err <= TOL
+    # the read budget is exactly k of m channels per routed expert
+    assert abs(k / qwen.m - {100: 0.13, 138: 0.18}[k]) <= 1 / (2 * qwen.m)
+
+
+def test_qwen3_shape_dense_parity(b, torch, qwen):
+    w = synth.WORKLOADS["qwen3"]
+    x = synth.tokens(w["wid"], 0, 1, qwen.d, index=1)
+    logits = synth.router_logits(w["wid"], 0, 1, qwen.E, index=1)
+    out = _run(b, torch, qwen, x, logits, 0, dense=True)
+    ref = qwen.oracle.forward_dense(x, logits, qwen.top_e)
+    assert rel_err(out_to_f64(torch, out), ref) <= TOL

@@ -1,0 +1,152 @@
+"""Host-side checks of the C-ABI library; none of these needs a GPU.
+
+* every function declared in include/moe_sel.h is exported by libmoe_sel.so;
+* config validation rejects what the header says it rejects;
+* the host preparation (ternary sketch, statistics, low-rank map) matches the
+  CPU oracle: sketch, scales, counts and norms bit for bit, the rank-r map to
+  the error of storing P and Q in bf16.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as om
+from activation_sparse_expert_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_sel.h")
+
+b = pytest.importorskip("activation_sparse_expert_amd.binding")
+
+
+def _bits(a):
+    return synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def test_header_declarations_are_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(moe_sel_[a-z_]+)\s*\(", text))
+    assert len(declared) >= 12
+    import ctypes
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared <= set(b.EXPORTED)
+    assert b.moe_sel_abi_version() == 1
+
+
+def test_config_validation():
+    good = dict(d=256, n_experts=8, m=512, rank=8, max_top_e=2, max_batch=4)
+    w = np.zeros((512, 256), np.uint16)
+    wd = np.zeros((256, 512), np.uint16)
+    b.moe_sel_prepare_expert_host(b.make_config(**good), w, w, wd, lowrank=False)
+    bad = [dict(d=100), dict(d=0), dict(m=96), dict(m=40000), dict(rank=-1), dict(rank=129),
+           dict(rank=300), dict(max_top_e=0), dict(max_top_e=9), dict(max_batch=0),
+           dict(n_experts=0), dict(tern_ratio=0.0)]
+    for change in bad:
+        cfg = dict(good)
+        cfg.update(change)
+        with pytest.raises(b.MoeSelError) as ei:
+            b.moe_sel_prepare_expert_host(b.make_config(**cfg), w, w, wd, lowrank=False)
+        assert ei.value.status == b.MOE_SEL_EINVAL, change
+        assert b.moe_sel_last_error()
+    cfg = b.make_config(**good)
+    cfg.struct_size = 8
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_prepare_expert_host(cfg, w, w, wd, lowrank=False)
+    inf = w.copy()
+    inf[3, 7] = 0x7F80
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_prepare_expert_host(b.make_config(**good), inf, w, wd, lowrank=False)
+    assert b.moe_sel_status_str(b.MOE_SEL_ENOMEM) == "out of memory"
+
+
+def _compare_sketch(lib_out, prep):
+    assert np.array_equal(lib_out["tern_gate"], prep["tern_g"])
+    assert np.array_equal(lib_out["tern_up"], prep["tern_u"])
+    assert np.array_equal(lib_out["alpha_gate"].view(np.uint32), prep["alpha_g"].view(np.uint32))
+    assert np.array_equal(lib_out["alpha_up"].view(np.uint32), prep["alpha_u"].view(np.uint32))
+    assert np.array_equal(lib_out["down_norm"].view(np.uint32), prep["c"].view(np.uint32))
+    assert np.array_equal(lib_out["nnz_gate"], prep["nnz_g"])
+    assert np.array_equal(lib_out["nnz_up"], prep["nnz_u"])
+
+
+def _product_err(lib_out, prep):
+    p = om.bf16_bits_to_f64(lib_out["p_bf16"]).T      # [d][r]
+    q = om.bf16_bits_to_f64(lib_out["q_bf16"])         # [m][r]
+    ref = prep["P"] @ prep["Q"].T
+    return np.linalg.norm(p @ q.T - ref) / np.linalg.norm(ref)
+
+
+def test_prepare_matches_oracle_tiny_workload():
+    w = synth.WORKLOADS["tiny"]
+    d, m, r = w["d"], w["m"], w["rank"]
+    cfg = b.make_config(d, w["n_experts"], m, r, w["top_e"])
+    for e in (0, 5):
+        wg, wu, wd = synth.expert_weights(w["wid"], 0, e, d, m)
+        lib_out = b.moe_sel_prepare_expert_host(cfg, wg, wu, wd)
+        prep = oracle.prepare_expert(wg, wu, wd, r)
+        _compare_sketch(lib_out, prep)
+        assert _product_err(lib_out, prep) < 6e-3
+
+
+def test_prepare_matches_oracle_extreme_magnitudes():
+    rng = np.random.default_rng(21)
+    d, m, r = 128, 64, 5
+    mags = 10.0 ** rng.uniform(-36, 36, size=(m, d))
+    wg = _bits(rng.standard_normal((m, d)) * mags)
+    wu = _bits(rng.standard_normal((m, d)) * 0.02)
+    wu[3] = 0                                    # an all-zero channel
+    wu[4] = _bits(np.full(d, 0.25))              # constant magnitude
+    wd = _bits(rng.standard_normal((d, m)) * 10.0 ** rng.uniform(-3, 3, size=(d, m)))
+    cfg = b.make_config(d, 1, m, r, 1, tern_ratio=0.7)
+    lib_out = b.moe_sel_prepare_expert_host(cfg, wg, wu, wd)
+    prep = oracle.prepare_expert(wg, wu, wd, r)
+    _compare_sketch(lib_out, prep)
+    assert lib_out["nnz_up"][3] == 0 and lib_out["alpha_up"][3] == 0
+    assert lib_out["nnz_up"][4] == d and lib_out["alpha_up"][4] == 0.25
+
+
+def test_prepare_other_threshold_ratio():
+    rng = np.random.default_rng(22)
+    d, m = 192, 64
+    wg = _bits(rng.standard_normal((m, d)) * 0.02)
+    wu = _bits(rng.laplace(size=(m, d)) * 0.02)
+    wd = _bits(rng.standard_normal((d, m)) * 0.02)
+    for ratio in (0.3, 0.7, 1.5):
+        cfg = b.make_config(d, 1, m, 0, 1, tern_ratio=ratio)
+        lib_out = b.moe_sel_prepare_expert_host(cfg, wg, wu, wd, lowrank=False)
+        prep = oracle.prepare_expert(wg, wu, wd, 0, tern_ratio=ratio)
+        _compare_sketch(lib_out, prep)
+
+
+@pytest.mark.parametrize("d,m,r", [(256, 128, 16), (64, 256, 8), (128, 128, 128), (64, 64, 1)])
+def test_lowrank_map_matches_truncated_svd(d, m, r):
+    """Both branches of the map (m <= d: Gram of the columns; m > d: Gram of the
+    rows), full rank, and rank one, against the oracle's truncated SVD."""
+    rng = np.random.default_rng(23 + d + m + r)
+    wg = _bits(rng.standard_normal((m, d)) * 0.02)
+    wd = _bits(rng.standard_normal((d, m)) * 0.02)
+    cfg = b.make_config(d, 1, m, r, 1)
+    lib_out = b.moe_sel_prepare_expert_host(cfg, wg, wg, wd, sketch=False)
+    prep = oracle.prepare_expert(wg, wg, wd, r)
+    assert _product_err(lib_out, prep) < 6e-3
+
+
+def test_lowrank_map_qwen_shape_flat_spectrum():
+    """A 2048 x 768 Gaussian down matrix has a nearly flat spectrum around the
+    32nd singular value; the library must still find the same subspace."""
+    w = synth.WORKLOADS["qwen3"]
+    d, m, r = w["d"], w["m"], w["rank"]
+    _, _, wd = synth.expert_weights(w["wid"], 0, 3, d, m)
+    wg = np.zeros((m, d), np.uint16)
+    cfg = b.make_config(d, 1, m, r, 1)
+    lib_out = b.moe_sel_prepare_expert_host(cfg, wg, wg, wd, sketch=False)
+    p, q, s = om.lowrank_factors(om.bf16_bits_to_f64(wd), r)
+    assert (s[r - 1] - s[r]) / s[r - 1] < 5e-3          # the gap is small
+    ref = p @ q.T
+    got = om.bf16_bits_to_f64(lib_out["p_bf16"]).T @ om.bf16_bits_to_f64(lib_out["q_bf16"]).T
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 6e-3
