@@ -24,8 +24,11 @@ EXPORTED = (
     "moe_sel_abi_version", "moe_sel_status_str", "moe_sel_last_error",
     "moe_sel_prepare_expert_host", "moe_sel_prepare", "moe_sel_forward",
     "moe_sel_forward_dense", "moe_sel_debug_selection", "moe_sel_export_expert",
-    "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy",
+    "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
+    "moe_sel_set_path", "moe_sel_last_path",
 )
+
+MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
 
 
 class moe_sel_config(ctypes.Structure):
@@ -74,6 +77,9 @@ def _load():
         "moe_sel_get_config": (ctypes.c_int, [vp, ctypes.POINTER(moe_sel_config)]),
         "moe_sel_device_bytes": (ctypes.c_uint64, [vp]),
         "moe_sel_destroy": (None, [vp]),
+        "moe_sel_check_device": (ctypes.c_int, [vp]),
+        "moe_sel_set_path": (ctypes.c_int, [vp, ctypes.c_int]),
+        "moe_sel_last_path": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +216,18 @@ def moe_sel_get_config(ctx) -> moe_sel_config:
 
 def moe_sel_device_bytes(ctx) -> int:
     return int(_lib.moe_sel_device_bytes(ctx))
+
+
+def moe_sel_check_device(ctx):
+    _check(_lib.moe_sel_check_device(ctx), "moe_sel_check_device")
+
+
+def moe_sel_set_path(ctx, path: int):
+    _check(_lib.moe_sel_set_path(ctx, int(path)), "moe_sel_set_path")
+
+
+def moe_sel_last_path(ctx) -> int:
+    return int(_lib.moe_sel_last_path(ctx))
 
 
 def moe_sel_destroy(ctx):

@@ -2,7 +2,9 @@
 // enqueueing of forward calls. See include/moe_sel.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -33,6 +35,18 @@ struct moe_sel_ctx {
   float* zvec = nullptr;
   float* hsel = nullptr;
   float* ypart = nullptr;
+  // single-launch path
+  uint64_t* xscore = nullptr;
+  float* zpart = nullptr;
+  float* partial = nullptr;
+  float* zcopy = nullptr;
+  int* err = nullptr;
+  size_t xscore_count = 0, zpart_count = 0, partial_count = 0, zcopy_count = 0;
+  int fused_max_batch = 0;
+  int num_cus = 0;
+  int fused_bpc_sparse = 0, fused_bpc_dense = 0;
+  moe_sel_path path = MOE_SEL_PATH_AUTO;
+  int last_path = -1;
   std::vector<void*> allocations;
   uint64_t device_bytes = 0;
   // last sparse call (for moe_sel_debug_selection)
@@ -41,6 +55,10 @@ struct moe_sel_ctx {
 };
 
 namespace {
+
+constexpr int kFusedMaxBatch = 8;   // single-launch path: up to this many tokens
+constexpr int kMinChunk = 8;        // fewest channels per gather block
+constexpr int kTargetGather = 512;  // aim for about this many gather blocks
 
 thread_local std::string g_last_error;
 
@@ -126,6 +144,14 @@ moe_sel_status check_forward(moe_sel_ctx* ctx, const void* x, const void* logits
   return MOE_SEL_OK;
 }
 
+bool force_multi_kernel() {
+  static const bool v = [] {
+    const char* e = std::getenv("MOE_SEL_MULTI_KERNEL");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
 moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logits, int32_t batch, int32_t top_e,
                            int32_t k, uint16_t* out) {
   moe_sel::FwdArgs a{};
@@ -156,6 +182,58 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.hsel = c->hsel;
   a.ypart = c->ypart;
   return a;
+}
+
+// The single-launch path when its blocks all fit on the device at once, else
+// the one-kernel-per-phase path.
+// Returns hipErrorNotSupported when the single-launch path is required but cannot be used.
+hipError_t launch_any(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, hipStream_t stream) {
+  const int pairs = base.batch * base.top_e;
+  const bool want_fused = c->path != MOE_SEL_PATH_MULTI_KERNEL && !force_multi_kernel();
+  if (want_fused && c->xscore && base.batch <= c->fused_max_batch &&
+      moe_sel::fused_supported(base.d, base.m, base.r, base.top_e)) {
+    const int count = dense ? base.m : base.k;
+    int chunk = kMinChunk;
+    while (chunk < moe_sel::fused_max_chunk(dense) && (size_t)pairs * ((count + chunk - 1) / chunk) > (size_t)kTargetGather)
+      chunk *= 2;
+    moe_sel::FusedArgs f;
+    static_cast<moe_sel::FwdArgs&>(f) = base;
+    f.xscore = c->xscore;
+    f.zpart = c->zpart;
+    f.partial = c->partial;
+    f.zcopy = c->zcopy;
+    f.err = c->err;
+    f.chunk = chunk;
+    f.nc = std::max(1, (count + chunk - 1) / chunk);
+    f.n_score = dense ? 0 : pairs * (base.m / moe_sel::kGroup);
+    f.n_gather = pairs * f.nc;
+    f.n_combine = base.batch * (base.d / 32);
+    const long total = (long)f.n_score + f.n_gather + f.n_combine;
+    const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
+    if (total <= (long)bpc * c->num_cus) {
+      c->last_path = MOE_SEL_PATH_SINGLE_LAUNCH;
+      return moe_sel::launch_fused(f, dense, stream);
+    }
+  }
+  if (c->path == MOE_SEL_PATH_SINGLE_LAUNCH) return hipErrorNotSupported;
+  c->last_path = MOE_SEL_PATH_MULTI_KERNEL;
+  return moe_sel::launch_forward(base, dense, stream);
+}
+
+// every hand-off slot empty (0xFF bytes), error bits clear
+hipError_t reset_handoff(moe_sel_ctx* c, hipStream_t s) {
+  hipError_t he = hipSuccess;
+  const struct {
+    void* p;
+    size_t bytes;
+  } slots[] = {{c->xscore, c->xscore_count * 8},
+               {c->zpart, c->zpart_count * 4},
+               {c->partial, c->partial_count * 4},
+               {c->zcopy, c->zcopy_count * 4}};
+  for (const auto& sl : slots)
+    if (he == hipSuccess) he = hipMemsetAsync(sl.p, 0xFF, sl.bytes, s);
+  if (he == hipSuccess) he = hipMemsetAsync(c->err, 0, 4, s);
+  return he;
 }
 
 struct DeviceGuard {
@@ -299,6 +377,23 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   ALLOC(zvec, pairs * std::max<size_t>(r, 1));
   ALLOC(hsel, pairs * m);
   ALLOC(ypart, pairs * d);
+  // single-launch path: sized for up to kFusedMaxBatch tokens and the smallest chunk
+  const bool fusable = moe_sel::fused_supported(c.d, c.m, c.rank, c.max_top_e);
+  if (fusable) {
+    ctx->fused_max_batch = std::min(c.max_batch, kFusedMaxBatch);
+    const size_t fp = (size_t)ctx->fused_max_batch * c.max_top_e;
+    const size_t nc_max = (m + kMinChunk - 1) / kMinChunk;
+    const size_t groups = m / moe_sel::kGroup, slices = d / 64;
+    ctx->xscore_count = fp * nc_max * m;
+    ctx->zpart_count = fp * groups * std::max<size_t>(r, 1);
+    ctx->partial_count = (size_t)ctx->fused_max_batch * slices * c.max_top_e * nc_max * 64;
+    ctx->zcopy_count = (size_t)ctx->fused_max_batch * 2 * slices * c.max_top_e * std::max<size_t>(r, 1);
+    ALLOC(xscore, ctx->xscore_count);
+    ALLOC(zpart, ctx->zpart_count);
+    ALLOC(partial, ctx->partial_count);
+    ALLOC(zcopy, ctx->zcopy_count);
+    ALLOC(err, 1);
+  }
 #undef ALLOC
   if (st != MOE_SEL_OK) {
     free_ctx(ctx);
@@ -321,6 +416,18 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
       return hip_fail(he, "hipMemcpyAsync");
     }
   }
+  if (ctx->xscore) {
+    he = reset_handoff(ctx, s);
+    if (he == hipSuccess) {
+      he = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, ctx->device);
+      ctx->fused_bpc_sparse = moe_sel::fused_blocks_per_cu(false, c.d, c.m, c.rank);
+      ctx->fused_bpc_dense = moe_sel::fused_blocks_per_cu(true, c.d, c.m, c.rank);
+    }
+    if (he != hipSuccess) {
+      free_ctx(ctx);
+      return hip_fail(he, "fused path set-up");
+    }
+  }
   he = hipStreamSynchronize(s);
   if (he != hipSuccess) {
     free_ctx(ctx);
@@ -337,7 +444,8 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
   if (st != MOE_SEL_OK) return st;
   DeviceGuard guard(ctx->device);
   const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, k_budget, out);
-  const hipError_t e = moe_sel::launch_forward(a, false, (hipStream_t)stream);
+  const hipError_t e = launch_any(ctx, a, false, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, "single-launch path cannot run this call");
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   ctx->last_batch = batch;
   ctx->last_top_e = top_e;
@@ -353,7 +461,8 @@ moe_sel_status moe_sel_forward_dense(moe_sel_ctx* ctx, const uint16_t* x, const 
   if (st != MOE_SEL_OK) return st;
   DeviceGuard guard(ctx->device);
   const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, ctx->cfg.m, out);
-  const hipError_t e = moe_sel::launch_forward(a, true, (hipStream_t)stream);
+  const hipError_t e = launch_any(ctx, a, true, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, "single-launch path cannot run this call");
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return MOE_SEL_OK;
 }
@@ -432,6 +541,34 @@ moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert, int8_t* t
     return hip_fail(e, "hipMemcpy");
   return MOE_SEL_OK;
 }
+
+moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  DeviceGuard guard(ctx->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  if (!ctx->err) return MOE_SEL_OK;
+  int bits = 0;
+  if ((e = hipMemcpy(&bits, ctx->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
+  if (bits == 0) return MOE_SEL_OK;
+  // a bounded wait expired: reset the hand-off state so the next call starts clean
+  (void)reset_handoff(ctx, nullptr);
+  (void)hipDeviceSynchronize();
+  return fail(MOE_SEL_EDEVICE, "a cross-block wait timed out (bits " + std::to_string(bits) +
+                                   "); outputs of the affected calls are invalid");
+}
+
+moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (path != MOE_SEL_PATH_AUTO && path != MOE_SEL_PATH_MULTI_KERNEL && path != MOE_SEL_PATH_SINGLE_LAUNCH)
+    return fail(MOE_SEL_EINVAL, "unknown path");
+  ctx->path = path;
+  return MOE_SEL_OK;
+}
+
+int32_t moe_sel_last_path(const moe_sel_ctx* ctx) { return ctx ? ctx->last_path : -1; }
 
 moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg) {
   if (!ctx || !cfg) return fail(MOE_SEL_EINVAL, "ctx and cfg must be non-null");

@@ -1,0 +1,679 @@
+// Device helpers shared by the multi-kernel and the fused forward paths.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe_sel {
+namespace dev {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// ---------------------------------------------------------------------------
+// binary32 silu with every operation separately rounded (no contraction):
+// Cody & Waite reduction with ln 2 split as 2839/4096 plus the binary32 nearest
+// to the remainder, degree-7 Taylor series of e^r, then z / (1 + e^-z); the
+// argument is cut at |z| > 87 (z itself above, +0 below).
+// ---------------------------------------------------------------------------
+constexpr float kL2E = 1.44269504088896340736f;
+constexpr float kLn2Hi = 2839.0f / 4096.0f;
+constexpr float kLn2Lo = (float)(0.693147180559945309417232121458 - 2839.0 / 4096.0);
+constexpr float kF2 = (float)(1.0 / 2.0);
+constexpr float kF3 = (float)(1.0 / 6.0);
+constexpr float kF4 = (float)(1.0 / 24.0);
+constexpr float kF5 = (float)(1.0 / 120.0);
+constexpr float kF6 = (float)(1.0 / 720.0);
+constexpr float kF7 = (float)(1.0 / 5040.0);
+
+__device__ __forceinline__ float silu_pinned(float z) {
+#pragma clang fp contract(off)
+  if (z > 87.0f) return z;
+  if (z < -87.0f) return 0.0f;
+  const float t = -z;
+  const float n = __builtin_rintf(t * kL2E);
+  const float r = (t - n * kLn2Hi) - n * kLn2Lo;
+  float p = kF7;
+  p = p * r + kF6;
+  p = p * r + kF5;
+  p = p * r + kF4;
+  p = p * r + kF3;
+  p = p * r + kF2;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const float et = __builtin_ldexpf(p, (int)n);
+  return z / (1.0f + et);
+}
+
+// Channel score from the exact integer sketch dots: G = alpha_g * Dg * 2^xexp,
+// U = alpha_u * Du * 2^xexp, h = silu_pinned(G) * U, score = |h| * ||down||.
+__device__ __forceinline__ void pinned_score(int dg, int du, int xexp, float4 st, float& h, float& score) {
+#pragma clang fp contract(off)
+  const float g = __builtin_ldexpf(st.x * (float)dg, xexp);
+  const float u = __builtin_ldexpf(st.y * (float)du, xexp);
+  h = silu_pinned(g) * u;
+  score = __builtin_fabsf(h) * st.z;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__device__ __forceinline__ void unpack8(uint4 w, float* x) {
+  x[0] = bf16lo(w.x); x[1] = bf16hi(w.x);
+  x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
+  x[4] = bf16lo(w.z); x[5] = bf16hi(w.z);
+  x[6] = bf16lo(w.w); x[7] = bf16hi(w.w);
+}
+
+__device__ __forceinline__ float dot8_bf16(uint4 w, const float* x) {
+  float s = bf16lo(w.x) * x[0];
+  s += bf16hi(w.x) * x[1];
+  s += bf16lo(w.y) * x[2];
+  s += bf16hi(w.y) * x[3];
+  s += bf16lo(w.z) * x[4];
+  s += bf16hi(w.z) * x[5];
+  s += bf16lo(w.w) * x[6];
+  s += bf16hi(w.w) * x[7];
+  return s;
+}
+
+__device__ __forceinline__ void axpy8_bf16(float a, uint4 w, float* y) {
+  y[0] += a * bf16lo(w.x); y[1] += a * bf16hi(w.x);
+  y[2] += a * bf16lo(w.y); y[3] += a * bf16hi(w.y);
+  y[4] += a * bf16lo(w.z); y[5] += a * bf16hi(w.z);
+  y[6] += a * bf16lo(w.w); y[7] += a * bf16hi(w.w);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_dev(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions and scans on DPP row operations (VALU data movement:
+// quad permutes, row mirrors and the gfx9 row broadcasts), not LDS shuffles.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = false>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, BOUND);
+}
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = false>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, BOUND));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// sum over the 64 lanes, returned to every lane
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kQuadXor1>(v);
+  v += dpp_f<kQuadXor2>(v);
+  v += dpp_f<kRowHalfMirror>(v);
+  v += dpp_f<kRowMirror>(v);
+  v += dpp_f<kRowBcast15, 0xA>(v);
+  v += dpp_f<kRowBcast31, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kQuadXor1>(v);
+  v += dpp_i<kQuadXor2>(v);
+  v += dpp_i<kRowHalfMirror>(v);
+  v += dpp_i<kRowMirror>(v);
+  v += dpp_i<kRowBcast15, 0xA>(v);
+  v += dpp_i<kRowBcast31, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kQuadXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kQuadXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowHalfMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowBcast15, 0xA>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowBcast31, 0xC>((int)v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<kRowShr1, 0xF, true>(v);
+  v += dpp_i<kRowShr2, 0xF, true>(v);
+  v += dpp_i<kRowShr4, 0xF, true>(v);
+  v += dpp_i<kRowShr8, 0xF, true>(v);
+  v += dpp_i<kRowBcast15, 0xA>(v);
+  v += dpp_i<kRowBcast31, 0xC>(v);
+  return v;
+}
+
+// exclusive prefix sum over the block in thread order; *total = block sum.
+// s_tmp[kWaves]; two barriers (all threads call).
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = s_tmp[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// 2-bit offset-binary codes (t + 1) of 16 hidden elements against 16 int8
+// activations: the four byte-aligned 2-bit fields of each shift line up with
+// four consecutive activations.
+__device__ __forceinline__ int dot_codes16(uint32_t cw, int4 x, int acc) {
+  acc = __builtin_amdgcn_sdot4((int)(cw & 0x03030303u), x.x, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)((cw >> 2) & 0x03030303u), x.y, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)((cw >> 4) & 0x03030303u), x.z, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)((cw >> 6) & 0x03030303u), x.w, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ int byte_sum4(int4 x, int acc) {
+  acc = __builtin_amdgcn_sdot4(x.x, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4(x.y, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4(x.z, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4(x.w, 0x01010101, acc, false);
+  return acc;
+}
+
+// exclusive count of `flag` over the block in thread order; *total = block count.
+// Uses s_tmp[kWaves]; contains barriers (all threads must call).
+__device__ __forceinline__ int block_excl_count(bool flag, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t mask = __ballot(flag);
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+  if (lane == 0) s_tmp[wave] = __popcll(mask);
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = s_tmp[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + below;
+}
+
+// ---------------------------------------------------------------------------
+// Routing of one token by a single wave: the top_e largest logits (lower
+// expert index first on equal logits), best first, and the softmax over them.
+// n_experts <= 1024, top_e <= 64. Results in s_ids / s_w (LDS), written by lane 0..top_e-1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kPer = 16;
+  float v[kPer];
+  bool live[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = lane + 64 * u;
+    live[u] = idx < n_experts;
+    v[u] = live[u] ? logits[idx] : 0.0f;
+  }
+  float top = 0.0f, mine = 0.0f;
+  int mine_id = 0;
+  for (int s = 0; s < top_e; ++s) {
+    float bv = 0.0f;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (live[u] && (bi == 0x7FFFFFFF || v[u] > bv)) {
+        bv = v[u];
+        bi = lane + 64 * u;
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (lane + 64 * u == bi) live[u] = false;
+    if (s == 0) top = bv;
+    if (lane == s) {
+      mine = bv;
+      mine_id = bi;
+    }
+  }
+  const float ex = lane < top_e ? __expf(mine - top) : 0.0f;
+  const float den = wave_sum(ex);
+  if (lane < top_e) {
+    s_ids[lane] = mine_id;
+    s_w[lane] = ex / den;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k threshold over m non-negative binary32 scores held as bit patterns in
+// LDS (their integer order is their value order): four 8-bit most-significant
+// digit passes. Returns the k-th largest key T and krem = how many keys equal
+// to T are selected (the lowest-index ones). 1 <= k < m. All threads call.
+// s_hist[256], s_tmp[kWaves], s_misc[2] are LDS scratch.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void block_topk_threshold(const uint32_t* s_keys, int m, int k, int* s_hist, int* s_tmp,
+                                                     int* s_misc, uint32_t& T, int& krem_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  int krem = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    s_hist[tid] = 0;
+    __syncthreads();
+    for (int base = 0; base < m; base += kThreads) {
+      const int j = base + tid;
+      const uint32_t key = j < m ? s_keys[j] : 0u;
+      const bool act = j < m && (key & pmask) == prefix;
+      const int dg = (int)((key >> shift) & 255u);
+      if (pass == 0) {
+        // few distinct top digits: one LDS atomic per distinct digit per wave
+        uint64_t todo = __ballot(act);
+        while (todo) {
+          const int leader = __builtin_ctzll(todo);
+          const int ldg = __shfl(dg, leader, 64);
+          const uint64_t same = __ballot(act && dg == ldg);
+          if (lane == leader) atomicAdd(&s_hist[ldg], __popcll(same));
+          todo &= ~same;
+        }
+      } else if (act) {
+        atomicAdd(&s_hist[dg], 1);
+      }
+    }
+    __syncthreads();
+    // thread tid owns bin 255 - tid: an inclusive scan over threads is a suffix scan over bins
+    const int c = s_hist[255 - tid];
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_tmp[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) incl += s_tmp[w];
+    if (incl - c < krem && krem <= incl) {
+      s_misc[0] = 255 - tid;
+      s_misc[1] = incl - c;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_misc[0] << shift;
+    pmask |= 255u << shift;
+    krem -= s_misc[1];
+    __syncthreads();
+  }
+  T = prefix;
+  krem_out = krem;
+}
+
+// Writes the selected channel indices (all keys > T, then the krem lowest-index
+// keys == T), ascending, to out[0..k). Returns k. All threads call.
+__device__ __forceinline__ int block_compact(const uint32_t* s_keys, int m, uint32_t T, int krem, int* out,
+                                             int* s_tmp) {
+  int run_eq = 0, run_sel = 0;
+  for (int base = 0; base < m; base += kThreads) {
+    const int j = base + threadIdx.x;
+    const uint32_t key = j < m ? s_keys[j] : 0u;
+    const bool gt = j < m && key > T;
+    const bool eq = j < m && key == T;
+    int eq_tot, sel_tot;
+    const int eq_before = block_excl_count(eq, s_tmp, &eq_tot);
+    const bool take = gt || (eq && run_eq + eq_before < krem);
+    const int sel_before = block_excl_count(take, s_tmp, &sel_tot);
+    if (take) out[run_sel + sel_before] = j;
+    run_eq += eq_tot;
+    run_sel += sel_tot;
+  }
+  return run_sel;
+}
+
+// ---------------------------------------------------------------------------
+// Order keys: a 64-bit integer per (value, index) whose unsigned order is
+// "larger value first, lower index first", so a rank is a count of larger keys
+// (one compare each, no branches).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_order_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t order_key(uint32_t ordered_value, int index) {
+  return ((uint64_t)ordered_value << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)index);
+}
+
+// ---------------------------------------------------------------------------
+// Routing of one token by the whole block (n_experts <= 1024): the rank of every
+// logit (larger first, lower index first) is the count of larger order keys,
+// computed by all threads in parallel over parts of the expert range; ranks
+// below top_e are the routed experts, and the gate weights are the softmax over
+// their logits. s_scr: 2 * n_experts uint64 + n_experts ints of LDS scratch.
+// Barriers inside; s_ids / s_w valid when it returns.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void block_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
+                                            void* s_scr) {
+  const int tid = threadIdx.x;
+  uint64_t* s_key = (uint64_t*)s_scr;
+  int* s_rank = (int*)(s_key + n_experts);
+  float* s_val = (float*)(s_rank + n_experts);
+  for (int i = tid; i < n_experts; i += kThreads) {
+    const float v = logits[i];
+    s_key[i] = order_key(float_order_bits(v), i);
+    s_val[i] = v;
+    s_rank[i] = 0;
+  }
+  __syncthreads();
+  // thread -> (expert i, part of the comparison range)
+  const int span = n_experts < kThreads ? n_experts : kThreads;
+  const int parts = kThreads / span;
+  const int len = (n_experts + parts - 1) / parts;
+  for (int i0 = 0; i0 < n_experts; i0 += span) {
+    const int i = i0 + tid % span, part = tid / span;
+    if (i < n_experts && part < parts) {
+      const uint64_t ki = s_key[i];
+      const int j0 = part * len, j1 = min(n_experts, j0 + len);
+      int rank = 0;
+#pragma unroll 8
+      for (int j = j0; j < j1; ++j) rank += s_key[j] > ki;
+      if (parts > 1) atomicAdd(&s_rank[i], rank);
+      else s_rank[i] = rank;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_experts; i += kThreads)
+    if (s_rank[i] < top_e) s_ids[s_rank[i]] = i;
+  __syncthreads();
+  if (tid < top_e) {
+    const float top = s_val[s_ids[0]];
+    float den = 0.0f;
+    for (int s = 0; s < top_e; ++s) den += __expf(s_val[s_ids[s]] - top);
+    s_w[tid] = __expf(s_val[s_ids[tid]] - top) / den;
+  }
+  __syncthreads();
+}
+
+// Compiler-level ordering of LDS accesses inside one wavefront (a wave's LDS
+// operations execute in order, so wave-synchronous code needs no s_barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int incl = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(incl, 63);
+  return incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of m <= kThreads * KPT non-negative binary32 scores (bit patterns keep
+// their order), k in [1, m): three most-significant-digit radix passes over bits
+// 30..20, 19..9 and 8..0, each a 2048-bin LDS histogram and a block suffix scan,
+// give the k-th largest key T and krem = how many keys equal to T are taken
+// (the lowest-index ones). Thread t owns the consecutive keys [t*KPT, t*KPT+KPT).
+// s_hist: 2048 ints; s_tmp: kWaves + 2 ints. Barriers inside (all threads call).
+// ---------------------------------------------------------------------------
+template <int KPT>
+__device__ __forceinline__ void block_topk_radix(const uint32_t (&key)[KPT], int per, int m, int k, int* s_hist,
+                                                 int* s_tmp, uint32_t& T, int& krem_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int krem = k;
+  constexpr int kShift[3] = {20, 9, 0};
+  constexpr uint32_t kDigitMask[3] = {0x7FFu, 0x7FFu, 0x1FFu};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass];
+    const uint32_t dmask = kDigitMask[pass];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = tid * per + u;
+      if (u < per && j < m && (key[u] & pmask) == prefix) atomicAdd(&s_hist[(key[u] >> shift) & dmask], 1);
+    }
+    __syncthreads();
+    int h[8], c = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      h[b] = s_hist[tid * 8 + b];
+      c += h[b];
+    }
+    int total;
+    const int before = block_excl_scan(c, s_tmp, &total);
+    int above = total - before - c;  // keys whose digit is above this thread's 8 bins
+#pragma unroll
+    for (int b = 7; b >= 0; --b) {
+      if (above < krem && krem <= above + h[b]) {
+        s_tmp[kWaves] = tid * 8 + b;
+        s_tmp[kWaves + 1] = above;
+      }
+      above += h[b];
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_tmp[kWaves] << shift;
+    pmask |= dmask << shift;
+    krem -= s_tmp[kWaves + 1];
+    __syncthreads();
+  }
+  T = prefix;
+  krem_out = krem;
+}
+
+// Top-k selection flags for the keys a thread owns (consecutive [t*KPT, t*KPT+KPT)):
+// one radix pass on bits 30..20 finds the 2048-bin bucket holding the k-th
+// largest key; keys above it are taken, and the bucket's keys are ranked exactly
+// by pairwise comparison in the order (larger key first, lower index first). A
+// bucket of more than kThreads keys falls back to the three-pass threshold.
+// Returns per-key ascending output ranks in sel[] (-1 if not selected) and the
+// count. 1 <= k < m. s_hist: 2048 ints; s_cand: 2 * kThreads ints; s_take: m
+// bytes; s_tmp: kWaves + 2 ints. Barriers inside (all threads call).
+// Callers that pass PREZEROED have cleared s_hist and s_tmp[kWaves + 1] and
+// passed a block barrier since.
+__device__ __forceinline__ void block_topk_prezero(int* s_hist, int* s_tmp) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) s_hist[threadIdx.x * 8 + b] = 0;
+  if (threadIdx.x == 0) s_tmp[kWaves + 1] = 0;
+}
+
+template <int KPT, bool PREZEROED = false>
+__device__ __forceinline__ int block_topk_select_strided(const uint32_t (&key)[KPT], int per, int m, int k, int* s_hist, int* s_cand,
+                                                 unsigned char* s_take, int* s_tmp, int (&sel)[KPT]) {
+  const int tid = threadIdx.x;
+  if (!PREZEROED) {
+    block_topk_prezero(s_hist, s_tmp);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if ((u < per && tid * per + u < m)) atomicAdd(&s_hist[key[u] >> 20], 1);
+  __syncthreads();
+  int h[8], c = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    h[b] = s_hist[tid * 8 + b];
+    c += h[b];
+  }
+  int total;
+  const int before = block_excl_scan(c, s_tmp, &total);
+  int above = total - before - c;
+#pragma unroll
+  for (int b = 7; b >= 0; --b) {
+    if (above < k && k <= above + h[b]) {
+      s_hist[0] = tid * 8 + b;  // bucket (bin 0's count is no longer needed)
+      s_hist[1] = above;
+      s_hist[2] = h[b];
+    }
+    above += h[b];
+  }
+  __syncthreads();
+  const uint32_t D = (uint32_t)s_hist[0];
+  const int krem = k - s_hist[1];
+  const int ncand = s_hist[2];
+  bool take[KPT];
+  if (ncand <= kThreads) {
+    int* ckey = s_cand;
+    int* cidx = s_cand + kThreads;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = tid * per + u;
+      if (u < per && j < m && (key[u] >> 20) == D) {
+        const int slot = atomicAdd(&s_tmp[kWaves + 1], 1);
+        ckey[slot] = (int)key[u];
+        cidx[slot] = j;
+      }
+    }
+    __syncthreads();
+    if (tid < ncand) {
+      const int ic = cidx[tid];
+      const uint64_t kc = order_key((uint32_t)ckey[tid], ic);
+      int rank = 0;
+#pragma unroll 8
+      for (int o = 0; o < ncand; ++o) rank += order_key((uint32_t)ckey[o], cidx[o]) > kc;
+      s_take[ic] = rank < krem;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = tid * per + u;
+      const uint32_t dg = key[u] >> 20;
+      take[u] = u < per && j < m && (dg > D || (dg == D && s_take[j]));
+    }
+  } else {
+    uint32_t T;
+    int kr;
+    block_topk_radix<KPT>(key, per, m, k, s_hist, s_tmp, T, kr);
+    int n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) n_eq += ((u < per && tid * per + u < m) && key[u] == T);
+    int eq_total;
+    int eq_before = block_excl_scan(n_eq, s_tmp, &eq_total);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool valid = (u < per && tid * per + u < m);
+      const bool eq = valid && key[u] == T;
+      take[u] = valid && (key[u] > T || (eq && eq_before < kr));
+      eq_before += eq;
+    }
+  }
+  int n_sel = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) n_sel += take[u];
+  int sel_total;
+  int r = block_excl_scan(n_sel, s_tmp, &sel_total);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    sel[u] = take[u] ? r : -1;
+    r += take[u];
+  }
+  return sel_total;
+}
+
+// Ascending ranks of the selected keys (all keys > T, then the krem lowest-index
+// keys == T): sel[u] = rank of key u of this thread, or -1. Returns the count.
+template <int KPT>
+__device__ __forceinline__ int block_select_ranks(const uint32_t (&key)[KPT], int per, int m, uint32_t T, int krem,
+                                                  int* s_tmp, int (&sel)[KPT]) {
+  const int tid = threadIdx.x;
+  int n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) n_eq += (u < per && tid * per + u < m && key[u] == T);
+  int eq_total;
+  int eq_before = block_excl_scan(n_eq, s_tmp, &eq_total);
+  int n_sel = 0;
+  bool take[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool valid = u < per && tid * per + u < m;
+    const bool eq = valid && key[u] == T;
+    take[u] = valid && (key[u] > T || (eq && eq_before < krem));
+    eq_before += eq;
+    n_sel += take[u];
+  }
+  int sel_total;
+  int r = block_excl_scan(n_sel, s_tmp, &sel_total);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    sel[u] = take[u] ? r : -1;
+    r += take[u];
+  }
+  return sel_total;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off without cache maintenance. Data that crosses
+// workgroups is written and read with device-coherent accesses (agent-scope
+// relaxed atomics: stores write through to the device coherence point, loads
+// read from it, on every XCD), so no L2 write-back or invalidate is needed.
+// Producer: coherent stores, wait_stores() (every wave waits until its stores
+// are acknowledged), barrier, then one coherent flag store per consumer.
+// Consumer: one wave polls its flags with coherent loads, the block syncs, then
+// reads the data with coherent loads; it clears the flags it consumed (each
+// flag has exactly one consumer, so every call starts from zeroed flags and
+// HIP-graph replays stay valid). Waits are bounded: on time-out an error bit is
+// set and the block proceeds.
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 21;
+
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_coh2(const float* p) {
+  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+// every outstanding vector memory access of this wave (loads and stores) done
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void set_flag(int* flag) { st_coh(flag, 1); }
+
+// One wave polls n flags, then clears them. Returns false on time-out.
+__device__ __forceinline__ bool wave_wait_flags(int* flags, int n) {
+  const int lane = threadIdx.x & 63;
+  int spins = 0;
+  bool ok = true;
+  while (true) {
+    bool all = true;
+    for (int i = lane; i < n; i += 64)
+      all &= __hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    if (__all(all)) break;
+    if (++spins > kSpinLimit) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  for (int i = lane; i < n; i += 64) st_coh(&flags[i], 0);
+  return ok;
+}
+
+}  // namespace dev
+}  // namespace moe_sel

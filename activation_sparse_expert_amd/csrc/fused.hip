@@ -1,0 +1,682 @@
+// Fused single-launch forward for small batches on gfx950.
+//
+// One kernel runs the whole block; its workgroups take one of three roles by
+// block index, producers always below their consumers:
+//
+//   [0, n_score)            score    one (token, expert) pair x 64 channels:
+//                                    route + quantise (redundant per block), the
+//                                    2-bit sketch GEMV, pinned channel scores,
+//                                    h_hat, and this group's share of Q^T h_hat;
+//   [.., + n_gather)        gather   one pair x C selected channels: repeats the
+//                                    pair's top-k selection on the m published
+//                                    scores, reads its C channels' bf16 gate/up/
+//                                    down vectors (one 12*d-byte run each), SwiGLU
+//                                    and the gate-weighted down partial over all
+//                                    of d; chunk 0 also forms z = Q^T h_hat over
+//                                    the skipped channels;
+//   [.., + n_combine)       combine  one token x 64 output elements: prefetches
+//                                    its slice of P for the routed experts, sums
+//                                    the token's partials and P z, writes bf16.
+//
+// "Top-k instead of a threshold" and "A reader built from weights alone" (page
+// "KAIST drops calibration from MoE decoding, speeds up blocks by up to 2.69x
+// over vLLM") give the selection and the compensation; the dense variant reads
+// every channel and has no score blocks.
+//
+// Hand-off: every value that crosses workgroups has exactly one consumer and a
+// slot of its own, holding the sentinel 0xFFFFFFFF when empty (a NaN pattern
+// that no arithmetic here produces). Producers write their slots with
+// device-coherent stores and move on; consumers poll the data itself with
+// device-coherent loads until no sentinel is left, then write the sentinel back,
+// so every call starts from empty slots and HIP-graph replays stay valid. Waits
+// are bounded; on time-out an error bit is set and the block proceeds.
+//
+// Decode-time work is latency bound, so every role issues all of its global
+// loads before consuming any (fixed unrolled counts, clamped addresses, masked
+// contributions).
+//
+// The launch requires every block to be resident at once (checked on the host
+// with the occupancy API).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "device_common.h"
+#include "internal.h"
+#include "kernels.h"
+
+namespace moe_sel {
+namespace {
+
+using namespace dev;
+
+constexpr int kMaxChunkSparse = 8;   // channels per gather block, all loaded at once
+constexpr int kMaxChunkDense = 16;
+constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
+constexpr int kScoreBlk = 16;        // sketch blocks loaded together per wave
+constexpr int kZPass = 4;            // compensation row passes loaded together
+constexpr int kMaxZPart = 4;         // zpart values per thread (groups * r <= 1024)
+constexpr int kMaxP = 4;             // 16-byte P pieces per combine thread (top_e * r <= 256)
+constexpr int kCombPer = 24;         // partial values per combine thread per poll batch
+constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+constexpr uint64_t kEmpty64 = 0xFFFFFFFFFFFFFFFFull;
+
+struct Smem {
+  int ids[64];
+  float w[64];
+  union {
+    int hist[2048];                // radix select
+    uint64_t route[3 * kThreads];  // routing scratch
+  };
+  int cand[2 * kThreads];          // boundary-bucket candidates of the select
+  int tmp[kWaves + 2];
+  float red[kWaves][2 * kMaxChunkDense];
+  uint32_t amax[kWaves];
+};
+
+__device__ __forceinline__ bool empty(float v) { return __float_as_uint(v) == kEmpty; }
+
+__device__ __forceinline__ uint64_t ld_coh64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_coh(float* p) { st_coh(p, __uint_as_float(kEmpty)); }
+
+// one bounded wait step; returns false once the spin budget is exhausted
+__device__ __forceinline__ bool keep_polling(int& spins, int* err, int bit) {
+  if (++spins > kSpinLimit) {
+    if (threadIdx.x == 0) atomicOr(err, bit);
+    return false;
+  }
+  __builtin_amdgcn_s_sleep(2);
+  return true;
+}
+
+template <int SLOTS>
+__device__ __forceinline__ void load_x(const uint16_t* x, int d, uint4 (&xv)[SLOTS]) {
+  const int nslots = d / 8;
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int s = threadIdx.x + u * kThreads;
+    xv[u] = s < nslots ? *(const uint4*)(x + 8 * s) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// int8 activations with a power-of-two scale into LDS; returns the exponent
+template <int SLOTS>
+__device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, int8_t* xq, Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nslots = d / 8;
+  uint32_t amax = 0;
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const uint32_t w4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) amax = max(amax, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
+  }
+  amax = wave_max_u(amax);
+  if (lane == 0) sm.amax[wave] = amax;
+  __syncthreads();
+  amax = sm.amax[0];
+  for (int w = 1; w < kWaves; ++w) amax = max(amax, sm.amax[w]);
+  int e_t = 0;
+  if (amax != 0) {
+    const float av = __uint_as_float(amax << 16);
+    int ex;
+    (void)__builtin_frexpf(av, &ex);  // av = f * 2^ex, f in [0.5, 1)
+    e_t = ex - 7;
+    if (__builtin_ldexpf(av, -e_t) > 127.0f) e_t += 1;
+  }
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int s = tid + u * kThreads;
+    if (s < nslots) {
+      float f[8];
+      unpack8(xv[u], f);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo |= ((uint32_t)(int)__builtin_rintf(__builtin_ldexpf(f[q], -e_t)) & 0xFFu) << (8 * q);
+        hi |= ((uint32_t)(int)__builtin_rintf(__builtin_ldexpf(f[q + 4], -e_t)) & 0xFFu) << (8 * q);
+      }
+      *(uint2*)(xq + 8 * s) = make_uint2(lo, hi);
+    }
+  }
+  return e_t;
+}
+
+__device__ __forceinline__ void route(const FusedArgs& a, int t, Smem& sm) {
+  block_route(a.logits + (size_t)t * a.n_experts, a.n_experts, a.top_e, sm.ids, sm.w, sm.route);
+}
+
+// ---------------------------------------------------------------------------
+// score role
+// ---------------------------------------------------------------------------
+template <int SLOTS>
+__device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
+  const int groups = a.m / kGroup;
+  const int p = bid / groups, g = bid % groups;
+  const int t = p / a.top_e, slot = p % a.top_e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = a.r;
+  int8_t* s_xq = (int8_t*)dyn;                               // d bytes
+  uint16_t* s_q = (uint16_t*)(dyn + a.d);                    // 64 x r bf16
+  float* s_h = (float*)(dyn + a.d + 64 * r * 2);             // 64
+  float* s_sc = s_h + 64;                                    // 64
+  int* s_part = (int*)(s_sc + 64);                           // kWaves x 64
+
+  uint4 xv[SLOTS];
+  load_x<SLOTS>(a.x + (size_t)t * a.d, a.d, xv);  // in flight during the routing
+  route(a, t, sm);
+  const int e = sm.ids[slot];
+  // every global load of this block: the sketch codes, the group's Q rows, its statistics
+  const int mat = wave >> 1, half = wave & 1;
+  const int nb = a.d / kBlock;
+  const int b0 = half ? nb / 2 : 0, b1 = half ? nb : nb / 2;
+  const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
+                                   codes_dword_index(a.d, a.m, g, mat, 0, lane, 0));
+  uint4 cb[kScoreBlk];
+#pragma unroll
+  for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)min(b0 + i, b1 - 1) * 64];
+  const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * a.m + (size_t)g * kGroup) * r);
+  const int qpieces = 8 * r;  // 64 rows x r bf16 / 8
+  uint4 qv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qv[u] = qpieces ? qsrc[min(tid + u * kThreads, qpieces - 1)] : make_uint4(0, 0, 0, 0);
+  const float4 st = a.stats[(size_t)e * a.m + g * kGroup + lane];
+  const int e_t = quantise_to_lds<SLOTS>(xv, a.d, s_xq, sm);
+  __syncthreads();  // x_q in LDS
+  int acc = 0, qs = 0;
+  for (int c0 = b0; c0 < b1; c0 += kScoreBlk) {
+    if (c0 != b0) {
+#pragma unroll
+      for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)min(c0 + i, b1 - 1) * 64];
+    }
+#pragma unroll
+    for (int i = 0; i < kScoreBlk; ++i) {
+      if (c0 + i < b1) {
+        const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
+        const int4 x0 = xb[0], x1 = xb[1], x2 = xb[2], x3 = xb[3];
+        acc = dot_codes16(cb[i].x, x0, acc);
+        acc = dot_codes16(cb[i].y, x1, acc);
+        acc = dot_codes16(cb[i].z, x2, acc);
+        acc = dot_codes16(cb[i].w, x3, acc);
+        qs = byte_sum4(x0, qs);
+        qs = byte_sum4(x1, qs);
+        qs = byte_sum4(x2, qs);
+        qs = byte_sum4(x3, qs);
+      }
+    }
+  }
+  s_part[wave * 64 + lane] = acc - qs;  // sum (code - 1) * q = sum t * q
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < qpieces) ((uint4*)s_q)[i] = qv[u];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int dg = s_part[lane] + s_part[64 + lane];
+    const int du = s_part[128 + lane] + s_part[192 + lane];
+    float h, sc;
+    pinned_score(dg, du, e_t, st, h, sc);
+    s_h[lane] = h;
+    s_sc[lane] = sc;
+  }
+  __syncthreads();
+  // publish (score, h_hat) of the 64 channels to each gather block of the pair
+  const int j0 = g * kGroup;
+  for (int i = tid; i < a.nc * 64; i += kThreads) {
+    const int c = i >> 6, l = i & 63;
+    const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
+    st_coh64(&a.xscore[((size_t)p * a.nc + c) * a.m + j0 + l], v);
+  }
+  // this group's share of Q^T h_hat over all of its channels, for chunk 0
+  if (tid < r) {
+    float z = 0.0f;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j) z += s_h[j] * bf16f(s_q[j * r + tid]);
+    st_coh(&a.zpart[((size_t)p * groups + g) * r + tid], z);
+  }
+  if (tid < 64) {  // for inspection only
+    st_coh(&a.hhat[(size_t)p * a.m + j0 + tid], s_h[tid]);
+    st_coh(&a.score[(size_t)p * a.m + j0 + tid], s_sc[tid]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gather role
+// ---------------------------------------------------------------------------
+// Waits for the pair's m (score, h_hat) values in this block's own slots (and,
+// for chunk 0, the pair's zpart slots), then selects the pair's top-k: the
+// selected channels ascending in s_sel[0..k), the sketch activations in s_hh,
+// the zpart values in s_zp. Chunk 0 also records the selection for inspection.
+__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, Smem& sm, float* s_hh,
+                                              uint32_t* s_keys, int* s_sel, unsigned char* s_take, float* s_zp) {
+  const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
+  const int groups = m / kGroup;
+  uint64_t* slots = a.xscore + ((size_t)p * a.nc + c) * m;
+  const int nzp = (c == 0) ? groups * r : 0;
+  float* zslots = a.zpart + (size_t)p * groups * r;
+  block_topk_prezero(sm.hist, sm.tmp);  // ordered before the select by the polling barrier
+  uint64_t v[kMaxKeysPer];
+  float zv[kMaxZPart];
+  uint32_t pending = 0;  // bit u: key slot u; bit 16 + u: zpart slot u
+#pragma unroll
+  for (int u = 0; u < kMaxKeysPer; ++u) {
+    v[u] = 0ull;
+    if (tid + u * kThreads < m) pending |= 1u << u;
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxZPart; ++u) {
+    zv[u] = 0.0f;
+    if (tid + u * kThreads < nzp) pending |= 1u << (16 + u);
+  }
+  int spins = 0;
+  while (true) {
+#pragma unroll
+    for (int u = 0; u < kMaxKeysPer; ++u)
+      if ((pending >> u) & 1) v[u] = ld_coh64(slots + tid + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kMaxZPart; ++u)
+      if ((pending >> (16 + u)) & 1) zv[u] = ld_coh(zslots + tid + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kMaxKeysPer; ++u)
+      if ((uint32_t)v[u] != kEmpty) pending &= ~(1u << u);
+#pragma unroll
+    for (int u = 0; u < kMaxZPart; ++u)
+      if (!empty(zv[u])) pending &= ~(1u << (16 + u));
+    if (__syncthreads_and(pending == 0)) break;
+    if (!keep_polling(spins, a.err, 1)) break;
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxKeysPer; ++u) {
+    const int j = tid + u * kThreads;
+    if (j < m) {
+      s_keys[j] = (uint32_t)v[u];
+      s_hh[j] = __uint_as_float((uint32_t)(v[u] >> 32));
+      st_coh64(slots + j, kEmpty64);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxZPart; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < nzp) {
+      s_zp[i] = zv[u];
+      clear_coh(zslots + i);
+    }
+  }
+  __syncthreads();
+  if (k >= m || k <= 0) {
+    for (int j = tid; j < k; j += kThreads) s_sel[j] = j;
+    __syncthreads();
+  } else {
+    constexpr int KPT = kMaxKeysPer;
+    uint32_t key[KPT];
+    const int per = (m + kThreads - 1) / kThreads;  // consecutive keys per thread
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = tid * per + u;
+      key[u] = (u < per && j < m) ? s_keys[j] : 0u;
+    }
+    int sel[KPT];
+    if (per <= 4) {
+      uint32_t k4[4] = {key[0], key[1], key[2], key[3]};
+      int s4[4];
+      block_topk_select_strided<4, true>(k4, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, s4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s4[u] >= 0) s_sel[s4[u]] = tid * per + u;
+    } else {
+      block_topk_select_strided<KPT, true>(key, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, sel);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (sel[u] >= 0) s_sel[sel[u]] = tid * per + u;
+    }
+    __syncthreads();
+  }
+  if (c == 0)
+    for (int i = tid; i < k; i += kThreads) a.sel_idx[(size_t)p * m + i] = s_sel[i];  // for inspection only
+}
+
+template <bool DENSE, int SLOTS>
+__device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
+  constexpr int kMaxChunk = DENSE ? kMaxChunkDense : kMaxChunkSparse;
+  const int C = a.chunk;
+  const int d = a.d, m = a.m, r = a.r;
+  const int p = bid / a.nc, c = bid % a.nc;
+  const int t = p / a.top_e, slot = p % a.top_e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int groups = m / kGroup;
+  const int nslots = d / 8;  // 16-byte pieces of a hidden vector
+  float* s_hh = (float*)dyn;                            // m
+  uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
+  int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m: the selection, ascending
+  unsigned char* s_take = dyn + 12 * (size_t)m;         // m
+  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // groups * r (chunk 0)
+  float* s_zr = s_zp + groups * (r > 0 ? r : 1);        // kThreads x 8 (chunk 0)
+
+  float xv[SLOTS][8];
+  const uint16_t* xrow = a.x + (size_t)t * d;
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int s = tid + u * kThreads;
+    if (s < nslots) {
+      unpack8(*(const uint4*)(xrow + 8 * s), xv[u]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xv[u][q] = 0.0f;
+    }
+  }
+  route(a, t, sm);
+  const int count = DENSE ? m : a.k;
+  const int first = c * C;
+  int mine = count - first;
+  mine = mine < 0 ? 0 : (mine > C ? C : mine);
+  if (!DENSE) gather_select(a, p, c, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const int e = sm.ids[slot];
+  const float wp = sm.w[slot];
+  if (!DENSE && c == 0 && tid == 0) {  // routing and selection of the pair, for inspection
+    a.pair_expert[p] = e;
+    a.pair_w[p] = wp;
+    a.sel_count[p] = count;
+  }
+  // ---- every load of this block's channels at once (clamped; masked below)
+  const uint16_t* wbase = a.wch + (size_t)e * m * 3 * d;
+  uint4 gv[kMaxChunk][SLOTS], uv[kMaxChunk][SLOTS], dv[kMaxChunk][SLOTS];
+  int jj[kMaxChunk];
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    const int ii = mine > 0 ? min(i, mine - 1) : 0;
+    jj[i] = DENSE ? min(first + ii, m - 1) : (mine > 0 ? s_sel[first + ii] : 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    if (i < C) {
+      const uint16_t* row = wbase + (size_t)jj[i] * 3 * d;
+#pragma unroll
+      for (int u = 0; u < SLOTS; ++u) {
+        const int s = min(tid + u * kThreads, nslots - 1);
+        gv[i][u] = *(const uint4*)(row + 8 * s);
+        uv[i][u] = *(const uint4*)(row + d + 8 * s);
+        dv[i][u] = *(const uint4*)(row + 2 * d + 8 * s);
+      }
+    }
+  }
+  // chunk 0: z = sum_g zpart[g] - sum_{j selected} h_hat_j Q[j, :]. Thread t owns
+  // 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass;
+  // its row loads go out together with the weight loads above.
+  float zacc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) zacc[q] = 0.0f;
+  const bool zwork = !DENSE && r > 0 && c == 0;
+  if (zwork) {
+    const int cgs = r >> 3, cg = tid % cgs, row = tid / cgs, rows_per_pass = kThreads / cgs;
+    const uint16_t* Q = a.qmat + (size_t)e * m * r + 8 * cg;
+    for (int i0 = 0; i0 < count || i0 < groups; i0 += rows_per_pass * kZPass) {
+      uint4 qv[kZPass];
+#pragma unroll
+      for (int u = 0; u < kZPass; ++u) {
+        const int i = i0 + u * rows_per_pass + row;
+        qv[u] = i < count ? *(const uint4*)(Q + (size_t)s_sel[i] * r) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kZPass; ++u) {
+        const int i = i0 + u * rows_per_pass + row;
+        if (i < count) axpy8_bf16(-s_hh[s_sel[i]], qv[u], zacc);
+        if (i < groups)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zacc[q] += s_zp[i * r + 8 * cg + q];
+      }
+    }
+  }
+  // ---- SwiGLU of the C channels
+  float gs[kMaxChunk], us[kMaxChunk];
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    gs[i] = 0.0f;
+    us[i] = 0.0f;
+    if (i < C) {
+#pragma unroll
+      for (int u = 0; u < SLOTS; ++u) {
+        gs[i] += dot8_bf16(gv[i][u], xv[u]);
+        us[i] += dot8_bf16(uv[i][u], xv[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    if (i < C) {
+      const float gw = wave_sum(gs[i]);
+      const float uw = wave_sum(us[i]);
+      if (lane == 0) {
+        sm.red[wave][2 * i] = gw;
+        sm.red[wave][2 * i + 1] = uw;
+      }
+    }
+  }
+  __syncthreads();
+  float yacc[SLOTS][8];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) yacc[u][q] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    if (i < C && i < mine) {
+      float g = 0.0f, u = 0.0f;
+      for (int w = 0; w < kWaves; ++w) {
+        g += sm.red[w][2 * i];
+        u += sm.red[w][2 * i + 1];
+      }
+      const float h = wp * (silu_f32(g) * u);
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) axpy8_bf16(h, dv[i][s], yacc[s]);
+    }
+  }
+  // ---- results: down partial (slice-major [t][slice][producer][64]); chunk 0
+  // also hands z to every combine block of the token
+  const int slices = d / 64;
+  const int qt = a.top_e * a.nc;
+  const int q = slot * a.nc + c;
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int s = tid + u * kThreads;
+    if (s < nslots) {
+      const int sl = s >> 3, off = (s & 7) * 8;
+      float* dst = a.partial + (((size_t)t * slices + sl) * qt + q) * 64 + off;
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) st_coh2(dst + 2 * h2, yacc[u][2 * h2], yacc[u][2 * h2 + 1]);
+    }
+  }
+  if (zwork) {
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) s_zr[tid * 8 + qq] = zacc[qq];
+    __syncthreads();
+    // column sums over the threads sharing a column group (once), then one copy
+    // per combine block of the token
+    const int cgs = r >> 3;
+    float* s_zc = s_zr + kThreads * 8;  // r
+    if (tid < r) {
+      float z = 0.0f;
+#pragma unroll 8
+      for (int th = tid >> 3; th < kThreads; th += cgs) z += s_zr[th * 8 + (tid & 7)];
+      s_zc[tid] = z;
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * slices * r; i += kThreads) {
+      const int col = i % r, half_slice = i / r;
+      st_coh(&a.zcopy[(((size_t)t * 2 * slices + half_slice) * a.top_e + slot) * r + col], s_zc[col]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine role: one token x 32 output elements (half of a 64-wide slice)
+// ---------------------------------------------------------------------------
+template <bool DENSE>
+__device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
+  const int d = a.d;
+  const int slices = d / 64;
+  const int t = bid / (2 * slices), hs = bid % (2 * slices);  // hs: half-slice index
+  const int sl = hs >> 1, hf = hs & 1;
+  const int tid = threadIdx.x;
+  const int el = tid & 31, pg = tid >> 5;  // element, producer lane group (8)
+  const int qt = a.top_e * a.nc;
+  const int r = DENSE ? 0 : a.r;
+  const int rdiv = r > 0 ? r : 1;
+  float* s_red = (float*)dyn;                 // kThreads x 8
+  float* s_z = s_red + kThreads * 8;          // top_e x r
+  float* s_y = s_z + 256;                     // 8 x 32
+
+  route(a, t, sm);
+  // prefetch P[e][c][32 elements] for the token's experts: top_e * r rows of 64 bytes
+  const int npieces = a.top_e * r * 4;
+  uint4 pv[kMaxP];
+#pragma unroll
+  for (int u = 0; u < kMaxP; ++u) {
+    const int i = min(tid + u * kThreads, max(npieces - 1, 0));
+    const int part = i & 3, row = i >> 2;
+    const int s = row / rdiv, cc = row % rdiv;
+    pv[u] = npieces ? *(const uint4*)(a.pmat + ((size_t)sm.ids[s] * r + cc) * d + 64 * sl + 32 * hf + 8 * part)
+                    : make_uint4(0, 0, 0, 0);
+  }
+  // every wave polls its own slots: partial values of producers pg + 8 u, and (threads
+  // below top_e * r) one z value
+  const float* src = a.partial + ((size_t)t * slices + sl) * qt * 64 + 32 * hf + el;
+  float* zsrc = a.zcopy + ((size_t)t * 2 * slices + hs) * a.top_e * rdiv;
+  const bool zthread = r > 0 && tid < a.top_e * r;
+  float z = 0.0f;
+  bool zpend = zthread;
+  float y = 0.0f;
+  int spins = 0;
+  // producers in batches of 8 * kCombPer; values are summed in producer order
+  for (int base = 0; base < qt; base += 8 * kCombPer) {
+    const float* bsrc = src + (size_t)(base + pg) * 64;
+    float v[kCombPer];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int u = 0; u < kCombPer; ++u) {
+      v[u] = 0.0f;
+      if (base + pg + 8 * u < qt) pending |= 1u << u;
+    }
+    while (true) {
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u)
+        if ((pending >> u) & 1) v[u] = ld_coh(bsrc + (size_t)u * 512);
+      if (zpend) z = ld_coh(zsrc + tid);
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u)
+        if (!empty(v[u])) pending &= ~(1u << u);
+      if (zpend && !empty(z)) zpend = false;
+      if (__all(pending == 0 && !zpend)) break;
+      if (!keep_polling(spins, a.err, 2)) break;
+    }
+#pragma unroll
+    for (int u = 0; u < kCombPer; ++u) {
+      if (base + pg + 8 * u < qt) {
+        y += v[u];
+        clear_coh(const_cast<float*>(bsrc) + (size_t)u * 512);
+      }
+    }
+  }
+  if (zthread) {
+    s_z[tid] = z;
+    clear_coh(zsrc + tid);
+  }
+  __syncthreads();
+  // P z for these elements: every thread's pieces share part (tid & 3): elements 8*part..+7
+  float pz[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) pz[q] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kMaxP; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < npieces) {
+      const int row = i >> 2;
+      const int s = row / rdiv, cc = row % rdiv;
+      axpy8_bf16(sm.w[s] * s_z[s * r + cc], pv[u], pz);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s_red[tid * 8 + q] = pz[q];
+  __syncthreads();
+  {
+    // element el = 8 * part + qq: threads th == part (mod 4); this thread takes th = part + 4 (pg + 8 n)
+    const int part = el >> 3, qq = el & 7;
+    float yz = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) yz += s_red[(part + 4 * (pg + 8 * n)) * 8 + qq];
+    s_y[pg * 32 + el] = y + yz;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float o = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) o += s_y[g * 32 + tid];
+    a.out[(size_t)t * d + 64 * sl + 32 * hf + tid] = f32_to_bf16_dev(o);
+  }
+}
+
+template <bool DENSE, int SLOTS>
+__global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ Smem sm;
+  int bid = blockIdx.x;
+  if (!DENSE) {
+    if (bid < a.n_score) {
+      score_role<SLOTS>(a, bid, sm, s_dyn);
+      return;
+    }
+    bid -= a.n_score;
+  }
+  if (bid < a.n_gather) {
+    gather_role<DENSE, SLOTS>(a, bid, sm, s_dyn);
+    return;
+  }
+  bid -= a.n_gather;
+  combine_role<DENSE>(a, bid, sm, s_dyn);
+}
+
+}  // namespace
+
+bool fused_supported(int d, int m, int r, int top_e) {
+  return d <= 4096 && m <= kMaxKeysPer * kThreads && top_e * r <= 256 && top_e <= 64 &&
+         (m / kGroup) * r <= kMaxZPart * kThreads && (r == 0 || (kThreads % r == 0 && r % 8 == 0));
+}
+
+int fused_max_chunk(bool dense) { return dense ? kMaxChunkDense : kMaxChunkSparse; }
+
+size_t fused_lds_bytes(int d, int m, int r) {
+  const size_t score = (size_t)d + 128 * (size_t)r + 512 + 1024;
+  const size_t gather = 13 * (size_t)m + 4 * (size_t)(m / kGroup) * (size_t)std::max(r, 1) + (size_t)kThreads * 8 * 4 +
+                        4 * (size_t)std::max(r, 1);
+  const size_t combine = (size_t)kThreads * 8 * 4 + 256 * 4 + 8 * 32 * 4;
+  return std::max(score, std::max(gather, combine));
+}
+
+static const void* fused_kernel(bool dense, int d) {
+  const int slots = (d / 8 + kThreads - 1) / kThreads;
+  if (dense) return slots <= 1 ? (const void*)k_fused<true, 1> : (const void*)k_fused<true, 2>;
+  return slots <= 1 ? (const void*)k_fused<false, 1> : (const void*)k_fused<false, 2>;
+}
+
+int fused_blocks_per_cu(bool dense, int d, int m, int r) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel(dense, d), kThreads, fused_lds_bytes(d, m, r)) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream) {
+  const int total = (dense ? 0 : a.n_score) + a.n_gather + a.n_combine;
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(fused_kernel(dense, a.d), dim3(total), dim3(kThreads), args, fused_lds_bytes(a.d, a.m, a.r),
+                         stream);
+}
+
+}  // namespace moe_sel

@@ -37,4 +37,23 @@ struct FwdArgs {
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 
+// Single-launch forward (fused.hip): block roles score / gather / combine.
+struct FusedArgs : FwdArgs {
+  // hand-off slots, each with one consumer, empty = 0xFFFFFFFF
+  uint64_t* xscore;  // [P][nc][m]        (score, h_hat) for gather block (pair, c)
+  float* zpart;      // [P][m/64][r]      per-group share of Q^T h_hat, for chunk 0
+  float* partial;    // [B][d/64][top_e*nc][64] gate-weighted down partials, for combine
+  float* zcopy;      // [B][d/32][top_e][r] z of each routed pair, for each combine block
+  int* err;          // error bits (1: gather wait timed out, 2: combine wait timed out)
+  int n_score, n_gather, n_combine;
+  int nc;            // gather blocks per pair
+  int chunk;         // channels per gather block
+};
+
+bool fused_supported(int d, int m, int r, int top_e);
+int fused_max_chunk(bool dense);
+size_t fused_lds_bytes(int d, int m, int r);
+int fused_blocks_per_cu(bool dense, int d, int m, int r);
+hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream);
+
 }  // namespace moe_sel

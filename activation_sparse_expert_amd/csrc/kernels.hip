@@ -20,104 +20,14 @@
 
 #include <cstdint>
 
+#include "device_common.h"
 #include "internal.h"
 #include "kernels.h"
 
 namespace moe_sel {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
-// ---------------------------------------------------------------------------
-// binary32 silu with every operation separately rounded (no contraction):
-// Cody & Waite reduction with ln 2 split as 2839/4096 plus the binary32 nearest
-// to the remainder, degree-7 Taylor series of e^r, then z / (1 + e^-z).
-// ---------------------------------------------------------------------------
-constexpr float kL2E = 1.44269504088896340736f;
-constexpr float kLn2Hi = 2839.0f / 4096.0f;
-constexpr float kLn2Lo = (float)(0.693147180559945309417232121458 - 2839.0 / 4096.0);
-constexpr float kF2 = (float)(1.0 / 2.0);
-constexpr float kF3 = (float)(1.0 / 6.0);
-constexpr float kF4 = (float)(1.0 / 24.0);
-constexpr float kF5 = (float)(1.0 / 120.0);
-constexpr float kF6 = (float)(1.0 / 720.0);
-constexpr float kF7 = (float)(1.0 / 5040.0);
-
-__device__ __noinline__ float silu_pinned(float z) {
-#pragma clang fp contract(off)
-  if (z > 87.0f) return z;
-  if (z < -87.0f) return 0.0f;
-  const float t = -z;
-  const float n = __builtin_rintf(t * kL2E);
-  const float r = (t - n * kLn2Hi) - n * kLn2Lo;
-  float p = kF7;
-  p = p * r + kF6;
-  p = p * r + kF5;
-  p = p * r + kF4;
-  p = p * r + kF3;
-  p = p * r + kF2;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  const float et = __builtin_ldexpf(p, (int)n);
-  return z / (1.0f + et);
-}
-
-// channel score from the exact integer sketch dots (see silu_pinned)
-__device__ __forceinline__ void pinned_score(int dg, int du, int xexp, float4 st, float& h, float& score) {
-#pragma clang fp contract(off)
-  const float g = __builtin_ldexpf(st.x * (float)dg, xexp);
-  const float u = __builtin_ldexpf(st.y * (float)du, xexp);
-  h = silu_pinned(g) * u;
-  score = __builtin_fabsf(h) * st.z;
-}
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-
-__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-__device__ __forceinline__ float dot8_bf16(uint4 w, const float* x) {
-  float s = bf16lo(w.x) * x[0];
-  s += bf16hi(w.x) * x[1];
-  s += bf16lo(w.y) * x[2];
-  s += bf16hi(w.y) * x[3];
-  s += bf16lo(w.z) * x[4];
-  s += bf16hi(w.z) * x[5];
-  s += bf16lo(w.w) * x[6];
-  s += bf16hi(w.w) * x[7];
-  return s;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_dev(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// exclusive count of `flag` over the block in thread order; *total = block count.
-// Uses s_tmp[kWaves + 1]; contains barriers (all threads must call).
-__device__ __forceinline__ int block_excl_count(bool flag, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t mask = __ballot(flag);
-  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-  if (lane == 0) s_tmp[wave] = __popcll(mask);
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = s_tmp[w];
-    before += w < wave ? c : 0;
-    all += c;
-  }
-  __syncthreads();
-  *total = all;
-  return before + below;
-}
+using namespace dev;
 
 // ===========================================================================
 // Phase 1: routing and activation quantisation, one block per token.
@@ -222,22 +132,6 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
 // Phase 2: sketch scores. One block per (pair, 64-channel group): wave w scores
 // matrix w/2 (gate, up) over half w%2 of the hidden dimension; lane = channel.
 // ===========================================================================
-__device__ __forceinline__ int dot_codes16(uint32_t cw, int4 x, int acc) {
-  acc = __builtin_amdgcn_sdot4((int)(cw & 0x03030303u), x.x, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 2) & 0x03030303u), x.y, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 4) & 0x03030303u), x.z, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 6) & 0x03030303u), x.w, acc, false);
-  return acc;
-}
-
-__device__ __forceinline__ int byte_sum4(int4 x, int acc) {
-  acc = __builtin_amdgcn_sdot4(x.x, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.y, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.z, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.w, 0x01010101, acc, false);
-  return acc;
-}
-
 __global__ __launch_bounds__(kThreads) void k_score(FwdArgs a) {
   extern __shared__ int4 s_xq4[];  // d bytes of int8 activations
   __shared__ int s_part[kWaves][64];

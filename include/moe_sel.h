@@ -67,6 +67,13 @@ typedef enum moe_sel_status {
   MOE_SEL_EDEVICE = 4        /* the HIP runtime reported an error */
 } moe_sel_status;
 
+/* How a forward call is executed on the GPU (same results either way). */
+typedef enum moe_sel_path {
+  MOE_SEL_PATH_AUTO = 0,          /* single launch when it fits, else one kernel per phase */
+  MOE_SEL_PATH_MULTI_KERNEL = 1,  /* one kernel per phase (any batch and shape) */
+  MOE_SEL_PATH_SINGLE_LAUNCH = 2  /* one fused kernel; EUNSUPPORTED when it cannot be used */
+} moe_sel_path;
+
 /* Shape of one MoE layer. */
 typedef struct moe_sel_config {
   uint32_t struct_size;  /* must be sizeof(moe_sel_config) */
@@ -184,6 +191,27 @@ moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert,
                                      int8_t* tern_gate, int8_t* tern_up,
                                      float* alpha_gate, float* alpha_up, float* down_norm,
                                      uint16_t* p_bf16, uint16_t* q_bf16);
+
+/*
+ * Synchronise the device and report whether any enqueued call on this context
+ * hit a bounded cross-workgroup wait that expired (single-launch path). Such a
+ * call's output is invalid; the context's hand-off state is reset so later
+ * calls are unaffected. Errors: EINVAL (null ctx), EDEVICE (time-out or HIP error).
+ */
+moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx);
+
+/*
+ * Choose the execution path of later forward calls on this context (default
+ * MOE_SEL_PATH_AUTO). The single-launch path needs d <= 4096, m <= 4096,
+ * top_e * rank <= 256, rank dividing 256 and a multiple of 8, batch <= 8, and all of its workgroups
+ * resident at once.
+ * Errors: EINVAL (null ctx or unknown path).
+ */
+moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path);
+
+/* Path taken by the last forward call on this context (MOE_SEL_PATH_MULTI_KERNEL
+ * or MOE_SEL_PATH_SINGLE_LAUNCH), or -1 if none ran yet or ctx is null. */
+int32_t moe_sel_last_path(const moe_sel_ctx* ctx);
 
 /* Shape the context was prepared with (copied into *cfg). EINVAL on null. */
 moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg);
