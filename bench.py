@@ -3,22 +3,27 @@
 
 One step = one forward of the whole block (route, quantise, sketch scores, top-k
 selection, gathered SwiGLU over the selected channels, down projection with the
-low-rank compensation, combine) for one batch of decode tokens of the
-Qwen3-30B-A3B-shaped block (d=2048, 128 experts, top-8, m=768, r=32), batch 1,
-k=138 (18% budget) by default. Inputs are synthetic and already resident in HBM.
+low-rank compensation, combine) for one batch of decode tokens. The default
+workload is the Qwen3-30B-A3B-shaped block (d=2048, 128 experts, top-8, m=768,
+r=32) at batch 1 with k=138 (the 18% budget); the 13% budget (k=100) and the
+dense-read block over the same inputs are timed in the same run. Inputs are
+synthetic (seeded bf16 N(0, 0.02) weights, N(0, 1) tokens and logits) and
+already resident in HBM when the timed region starts.
 
 Cold-cache protocol: `--copies` distinct prepared layers (different weights) and
 `--tokens` distinct tokens per layer are visited round-robin, so no weight,
-sketch or map byte is reused within ~copies*tokens calls (> 1 GB of traffic,
+sketch or map byte is reused within copies*tokens calls (over 1 GB of traffic,
 several times the 256 MB last-level cache). The sequence of forwards is captured
 once in a HIP graph and replayed; the timed region is bracketed by
-torch.cuda.synchronize() and HIP events on the launch stream.
+torch.cuda.synchronize() and HIP events recorded on the launch stream.
+`--eager` launches every forward directly instead (for profilers).
 
-Prints ONE JSON line (rank 0, N=1).
+Prints ONE JSON line. Only one GPU is supported (`--gpus 1`).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,14 +36,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose change invalidates stored counter readings of the single-launch kernel
+FUSED_SOURCES = ("activation_sparse_expert_amd/csrc/fused.hip",
+                 "activation_sparse_expert_amd/csrc/device_common.h",
+                 "activation_sparse_expert_amd/csrc/kernels.h")
 
 
 def algorithmic_bytes(d, m, n_exp, top_e, r, k, batch, dense=False):
-    """Bytes the method must move per forward call (batch-1 form: every routed pair
-    reads its own k channels). Sparse: per routed expert the 2-bit gate+up sketch
-    (m*d/2), the channel statistics (12*m), the selected channels' bf16 gate, up and
-    down vectors (6*d*k) and the rank-r map (2*(m+d)*r). Dense: 6*d*m per routed
-    expert. Plus x (2d), out (2d) and the logits (4E) per token."""
+    """Bytes the method must move per forward call when every routed pair reads its
+    own k channels. Sparse: per routed expert the 2-bit gate+up sketch (m*d/2), the
+    channel statistics (12*m), the selected channels' bf16 gate, up and down vectors
+    (6*d*k) and the rank-r map (2*(m+d)*r). Dense: 6*d*m per routed expert. Plus x
+    (2d), out (2d) and the logits (4E) per token."""
     pairs = batch * top_e
     per_tok = batch * (4 * d + 4 * n_exp)
     if dense:
@@ -46,24 +56,160 @@ def algorithmic_bytes(d, m, n_exp, top_e, r, k, batch, dense=False):
     return pairs * (m * d // 2 + 12 * m + 6 * d * k + 2 * (m + d) * r) + per_tok
 
 
+def sources_digest(paths=FUSED_SOURCES):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None, None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("sources_digest") != sources_digest():
+        return None, vals.get("sources_digest")
+    try:
+        return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])), vals["sources_digest"]
+    except (KeyError, ValueError):
+        return None, None
+
+
+class Block:
+    """`copies` prepared layers of one workload plus `ntok` distinct input batches each."""
+
+    def __init__(self, b, synth, torch, w, copies, ntok, stream):
+        self.b, self.w, self.copies, self.ntok, self.stream = b, w, copies, ntok, stream
+        d, m, n_exp, top_e, r, batch = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"], w["batch"]
+        self.ctxs, self.xs, self.lgs, self.outs = [], [], [], []
+        self.host_layer0 = None
+        routing = w["routing"] if w["routing"] != "router" else "normal"
+        for l in range(copies):
+            wg, wu, wd = synth.layer_weights(w["wid"], l, n_exp, d, m, w["channel_scale"])
+            cfg = b.make_config(d, n_exp, m, r, top_e, batch)
+            self.ctxs.append(b.moe_sel_prepare(cfg, wg, wu, wd, stream=stream.cuda_stream))
+            if l == 0:
+                self.host_layer0 = (wg, wu, wd)
+            del wg, wu, wd
+            xb = np.stack([synth.tokens(w["wid"], l, batch, d, index=i) for i in range(ntok)])
+            lb = np.stack([synth.router_logits(w["wid"], l, batch, n_exp, routing, index=i) for i in range(ntok)])
+            self.xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda"))
+            self.lgs.append(torch.from_numpy(lb).to("cuda"))
+            self.outs.append(torch.zeros((batch, d), dtype=torch.int16, device="cuda"))
+
+    def launch(self, n, k):
+        """Enqueue n forwards (k=None: the dense-read block) on the stream."""
+        b, w, s = self.b, self.w, self.stream.cuda_stream
+        for i in range(n):
+            l, t = i % self.copies, (i // self.copies) % self.ntok
+            if k is None:
+                b.moe_sel_forward_dense(self.ctxs[l], self.xs[l][t], self.lgs[l][t], w["batch"], w["top_e"],
+                                        self.outs[l], s)
+            else:
+                b.moe_sel_forward(self.ctxs[l], self.xs[l][t], self.lgs[l][t], w["batch"], w["top_e"], k,
+                                  self.outs[l], s)
+
+    def destroy(self):
+        for c in self.ctxs:
+            self.b.moe_sel_destroy(c)
+
+
+def time_block(torch, blk, k, steps, warmup, eager):
+    """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones."""
+    R = blk.copies * blk.ntok
+    stream = blk.stream
+    with torch.cuda.stream(stream):
+        blk.launch(R, k)  # eager pass over every (layer, token)
+    torch.cuda.synchronize()
+    for c in blk.ctxs:
+        blk.b.moe_sel_check_device(c)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if eager:
+        with torch.cuda.stream(stream):
+            blk.launch(warmup, k)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            blk.launch(steps, k)
+            ev1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            blk.launch(R, k)
+        rem = steps % R
+        g_rem = None
+        if rem:
+            g_rem = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rem, stream=stream):
+                blk.launch(rem, k)
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, math.ceil(warmup / R))):
+                g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(steps // R):
+                g.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+    for c in blk.ctxs:
+        blk.b.moe_sel_check_device(c)  # raises if a bounded wait gave up
+    return ev0.elapsed_time(ev1) / steps
+
+
+def copy_ceiling(torch, stream, nbytes=1 << 30, reps=8):
+    """Measured HBM ceiling: torch's device copy of `nbytes` (read + write bytes / time)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    s = ev0.elapsed_time(ev1) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / s / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--workload", default="qwen3")
+    ap.add_argument("--workload", default="qwen3", choices=("qwen3",))
     ap.add_argument("--k", type=int, default=None, help="channel budget (default: the 18%% budget)")
     ap.add_argument("--copies", type=int, default=4, help="distinct prepared layers rotated")
-    ap.add_argument("--tokens", type=int, default=16, help="distinct tokens per layer")
+    ap.add_argument("--tokens", type=int, default=16, help="distinct token batches per layer")
+    ap.add_argument("--eager", action="store_true", help="launch every forward directly (no graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--no-extra-budgets", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run plain 256 MiB copies (known bytes) for counter scaling")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "bench.py runs on exactly one GPU: the path is a single-GPU "
-                                   "kernel pipeline and no multi-GPU figure is produced (use --gpus 1)"}))
+        print(json.dumps({"error": "bench.py runs on exactly one GPU: the block is a single-GPU kernel "
+                                   "pipeline and no multi-GPU figure is produced; run it with --gpus 1"}))
         sys.exit(2)
 
     import torch
@@ -73,77 +219,47 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
-    d, m, n_exp, top_e, r = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"]
-    batch = w["batch"]
+    d, m, n_exp, top_e, r, batch = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"], w["batch"]
     k = args.k if args.k is not None else w["ks"][-1]
-    copies, ntok = args.copies, args.tokens
-    R = copies * ntok
 
     t0 = time.time()
     stream = torch.cuda.Stream()
-    ctxs, xs, lgs, outs = [], [], [], []
-    host_layer0 = None
-    for l in range(copies):
-        wg, wu, wd = synth.layer_weights(w["wid"], l, n_exp, d, m, w["channel_scale"])
-        cfg = b.make_config(d, n_exp, m, r, top_e, batch)
-        ctxs.append(b.moe_sel_prepare(cfg, wg, wu, wd, stream=stream.cuda_stream))
-        if l == 0:
-            host_layer0 = (wg, wu, wd)
-        del wg, wu, wd
-        xb = np.stack([synth.tokens(w["wid"], l, batch, d, index=i) for i in range(ntok)])
-        lb = np.stack([synth.router_logits(w["wid"], l, batch, n_exp, w["routing"] if w["routing"] != "router"
-                                           else "normal", index=i) for i in range(ntok)])
-        xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda"))
-        lgs.append(torch.from_numpy(lb).to("cuda"))
-        outs.append(torch.zeros((batch, d), dtype=torch.int16, device="cuda"))
+    blk = Block(b, synth, torch, w, args.copies, args.tokens, stream)
     setup_s = time.time() - t0
 
-    def launch_seq(n, dense):
-        for i in range(n):
-            l, t = i % copies, (i // copies) % ntok
-            if dense:
-                b.moe_sel_forward_dense(ctxs[l], xs[l][t], lgs[l][t], batch, top_e, outs[l], stream.cuda_stream)
-            else:
-                b.moe_sel_forward(ctxs[l], xs[l][t], lgs[l][t], batch, top_e, k, outs[l], stream.cuda_stream)
-
-    def timed(dense):
+    ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager)
+    path = b.moe_sel_last_path(blk.ctxs[0])
+    single = path == b.MOE_SEL_PATH_SINGLE_LAUNCH
+    extra_k = {}
+    if not args.no_extra_budgets:
+        for k2 in w["ks"]:
+            if k2 != k:
+                ms2 = time_block(torch, blk, k2, args.steps, args.warmup, args.eager)
+                extra_k[str(k2)] = {"tokens_per_s": round(batch / (ms2 * 1e-3), 1), "ms_per_step": round(ms2, 6),
+                                    "budget": round(k2 / m, 4),
+                                    "achieved_GBs": round(algorithmic_bytes(d, m, n_exp, top_e, r, k2, batch)
+                                                          / (ms2 * 1e-3) / 1e9, 1)}
+    ms_dense = None if args.no_dense else time_block(torch, blk, None, args.steps, args.warmup, args.eager)
+    ceiling = copy_ceiling(torch, stream)
+    if args.traffic_probe:
+        src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(2.0)
+        dst = torch.empty_like(src)
         with torch.cuda.stream(stream):
-            launch_seq(R, dense)                     # eager warm-up of every (layer, token)
+            for _ in range(4):
+                dst.copy_(src)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            launch_seq(R, dense)
-        rem = args.steps % R
-        g_rem = None
-        if rem:
-            g_rem = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_rem, stream=stream):
-                launch_seq(rem, dense)
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, math.ceil(args.warmup / R))):
-                g.replay()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            for _ in range(args.steps // R):
-                g.replay()
-            if g_rem is not None:
-                g_rem.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / args.steps  # ms per step
-
-    ms = timed(False)
-    ms_dense = None if args.no_dense else timed(True)
+        del src, dst
 
     tok_s = batch / (ms * 1e-3)
     bytes_sparse = algorithmic_bytes(d, m, n_exp, top_e, r, k, batch)
     bytes_dense = algorithmic_bytes(d, m, n_exp, top_e, r, k, batch, dense=True)
-    achieved = bytes_sparse / (ms * 1e-3) / 1e9
+    # The single-launch path runs the whole block as one kernel per forward, so the
+    # kernel's average launch duration is the timed region over the forwards in it.
+    kernel_s = ms * 1e-3
+    achieved = bytes_sparse / kernel_s / 1e9
+    traffic, digest = stored_traffic(f"traffic_k_fused_{args.workload}_b{batch}_k{k}.txt") if single else (None, None)
     result = {
-        "metric": "MoE-block tokens/s at batch 1 (achieved HBM GB/s on bytes read in roofline)",
+        "metric": "MoE-block tokens/s at batch 1; achieved HBM GB/s vs peak on bytes read",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -156,36 +272,44 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: Qwen3-30B-A3B-shaped MoE block d={d} E={n_exp} top-{top_e} m={m}"
-                        if args.workload == "qwen3" else f"{args.workload}: d={d} E={n_exp} top-{top_e} m={m}",
-            "batch": batch, "k": k, "budget": round(k / m, 4), "rank": r,
-            "cold_rotation": {"layers": copies, "tokens_per_layer": ntok},
-            "timing": "HIP graph of consecutive block calls; events on the launch stream",
+            "workload": f"Qwen3-30B-A3B-shaped MoE block, d={d}, {n_exp} experts, top-{top_e}, m={m}, "
+                        f"batch {batch}, k={k} ({k / m:.1%} budget), r={r}",
+            "batch": batch, "k": k, "rank": r,
+            "cold_rotation": {"layers": args.copies, "token_batches_per_layer": args.tokens},
+            "timing": "eager launches" if args.eager else "HIP graph of consecutive block calls",
+            "path": "single-launch" if single else "multi-kernel",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "whole block (all phases)", "algorithmic_bytes_per_launch": bytes_sparse,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "k_fused<sparse> (whole block in one launch)" if single else "multi-kernel block",
+            "algorithmic_bytes_per_launch": bytes_sparse,
+            "kernel_avg_us": round(kernel_s * 1e6, 3),
+            "traffic_sources_digest": digest,
+            "measured_copy_ceiling_GBs": round(ceiling, 1),
+            "frac_of_measured_ceiling": round(achieved / ceiling, 4),
         },
         "setup_s": round(setup_s, 1),
     }
+    if extra_k:
+        result["other_budgets"] = extra_k
     if ms_dense is not None:
+        dense_gbs = bytes_dense / (ms_dense * 1e-3) / 1e9
         result["dense"] = {
             "tokens_per_s": round(batch / (ms_dense * 1e-3), 1), "ms_per_step": round(ms_dense, 6),
-            "algorithmic_bytes": bytes_dense,
-            "achieved_GBs": round(bytes_dense / (ms_dense * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": bytes_dense, "achieved_GBs": round(dense_gbs, 1),
+            "frac": round(dense_gbs / HBM_PEAK_GBS, 4),
         }
         result["speedup_vs_dense"] = round(ms_dense / ms, 3)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(host_layer0, w, k, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(blk.host_layer0, w, k, args.cpu_seconds)
 
-    for c in ctxs:
-        b.moe_sel_destroy(c)
+    blk.destroy()
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(weights, w, k, ntok):
+def cpu_baseline(weights, w, k, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the same workload."""
     import oracle
     from activation_sparse_expert_amd import synth
@@ -197,10 +321,11 @@ def cpu_baseline(weights, w, k, ntok):
     wg, wu, wd = weights
     d, m, n_exp, top_e, r = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"]
     lay = oracle.OracleLayer(lambda e: (wg[e], wu[e], wd[e]), n_exp, d, m, r)
+    ntok = 4
     xs = [synth.tokens(w["wid"], 0, 1, d, index=i) for i in range(ntok)]
     lgs = [synth.router_logits(w["wid"], 0, 1, n_exp, "normal", index=i) for i in range(ntok)]
     t0 = time.time()
-    for x, lg in zip(xs, lgs):
+    for lg in lgs:
         for e in oracle.route(lg[0], top_e)[0]:
             lay.expert(e)
     prep_s = time.time() - t0
@@ -210,12 +335,13 @@ def cpu_baseline(weights, w, k, ntok):
             lay.forward(x, lg, top_e, k)
             n += 1
         reps += 1
-        if time.time() - t0 > 8.0 or reps >= 50:
+        if time.time() - t0 > seconds or reps >= 200:
             break
     el = time.time() - t0
-    return {"value": round(n / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{ntok} distinct batch-1 tokens of layer 0 x {reps} repetitions ({n} block forwards, "
-                      f"k={k}); preparation of the {len(lay._prep)} routed experts excluded ({prep_s:.1f} s)"}
+                      f"k={k}, {el:.1f} s); preparation of the {len(lay._prep)} routed experts excluded "
+                      f"({prep_s:.1f} s)"}
 
 
 if __name__ == "__main__":
