@@ -33,8 +33,23 @@ struct moe_sel_ctx {
   int* sel_idx = nullptr;
   int* sel_count = nullptr;
   float* zvec = nullptr;
-  float* hsel = nullptr;
   float* ypart = nullptr;
+  // expert-grouped path
+  int* xqsum = nullptr;
+  int* tile_expert = nullptr;
+  int* tile_first = nullptr;
+  int* tile_n = nullptr;
+  int* n_tiles = nullptr;
+  int* tpair = nullptr;
+  uint32_t* selbits = nullptr;
+  float* gzpart = nullptr;
+  int* ulist = nullptr;
+  uint64_t* umask = nullptr;
+  int* ucount = nullptr;
+  uint16_t* hbuf = nullptr;
+  float* zsel = nullptr;
+  int* tile_cnt = nullptr;
+  int max_tiles = 0;
   // single-launch path
   uint64_t* xscore = nullptr;
   float* zpart = nullptr;
@@ -179,8 +194,23 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.sel_idx = c->sel_idx;
   a.sel_count = c->sel_count;
   a.zvec = c->zvec;
-  a.hsel = c->hsel;
   a.ypart = c->ypart;
+  a.xqsum = c->xqsum;
+  a.tile_expert = c->tile_expert;
+  a.tile_first = c->tile_first;
+  a.tile_n = c->tile_n;
+  a.n_tiles = c->n_tiles;
+  a.tpair = c->tpair;
+  a.selbits = c->selbits;
+  a.gzpart = c->gzpart;
+  a.ulist = c->ulist;
+  a.umask = c->umask;
+  a.ucount = c->ucount;
+  a.hbuf = c->hbuf;
+  a.zsel = c->zsel;
+  a.tile_cnt = c->tile_cnt;
+  a.max_tiles = moe_sel::grouped_max_tiles(batch * top_e, c->cfg.n_experts);
+  a.kpad = moe_sel::grouped_kpad(c->cfg.m, c->cfg.rank);
   return a;
 }
 
@@ -321,6 +351,8 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   const std::string bad = moe_sel::validate_config(cfg);
   if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
   if (!w_gate || !w_up || !w_down || !out) return fail(MOE_SEL_EINVAL, "weights and out must be non-null");
+  if (!moe_sel::grouped_supported(cfg->d, cfg->m))
+    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(cfg->m) + " is above the per-pair selection limit (15360)");
   const moe_sel_config c = *cfg;
   const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
   const size_t pairs = (size_t)c.max_batch * c.max_top_e;
@@ -375,8 +407,23 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   ALLOC(sel_idx, pairs * m);
   ALLOC(sel_count, pairs);
   ALLOC(zvec, pairs * std::max<size_t>(r, 1));
-  ALLOC(hsel, pairs * m);
   ALLOC(ypart, pairs * d);
+  ctx->max_tiles = moe_sel::grouped_max_tiles((int)pairs, c.n_experts);
+  const size_t mt = ctx->max_tiles;
+  ALLOC(xqsum, (size_t)c.max_batch);
+  ALLOC(tile_expert, mt);
+  ALLOC(tile_first, mt);
+  ALLOC(tile_n, mt);
+  ALLOC(n_tiles, 1);
+  ALLOC(tpair, pairs);
+  ALLOC(selbits, pairs * (m / 32));
+  ALLOC(gzpart, pairs * (m / moe_sel::kGroup) * std::max<size_t>(r, 1));
+  ALLOC(ulist, mt * m);
+  ALLOC(umask, mt * m);
+  ALLOC(ucount, mt);
+  ALLOC(hbuf, pairs * moe_sel::grouped_kpad(c.m, c.rank));
+  ALLOC(zsel, pairs * (m / 16) * std::max<size_t>(r, 1));
+  ALLOC(tile_cnt, mt);
   // single-launch path: sized for up to kFusedMaxBatch tokens and the smallest chunk
   const bool fusable = moe_sel::fused_supported(c.d, c.m, c.rank, c.max_top_e);
   if (fusable) {
@@ -415,6 +462,11 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
       free_ctx(ctx);
       return hip_fail(he, "hipMemcpyAsync");
     }
+  }
+  he = hipMemsetAsync(ctx->tile_cnt, 0, mt * sizeof(int), s);
+  if (he != hipSuccess) {
+    free_ctx(ctx);
+    return hip_fail(he, "hipMemsetAsync");
   }
   if (ctx->xscore) {
     he = reset_handoff(ctx, s);

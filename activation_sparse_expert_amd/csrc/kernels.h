@@ -30,10 +30,34 @@ struct FwdArgs {
   float* score;            // [P][m]
   int* sel_idx;            // [P][m]
   int* sel_count;          // [P]
-  float* zvec;             // [P][r]
-  float* hsel;             // [P][m]
+  float* zvec;             // [P][r]  sum over all channels of h_hat_j Q[j, :]
   float* ypart;            // [P][d]
+  // expert-grouped multi-kernel path
+  int* xqsum;              // [B] sum of the int8 activations
+  int* tile_expert;        // [max_tiles]
+  int* tile_first;         // [max_tiles] offset into tpair
+  int* tile_n;             // [max_tiles] tokens in the tile (1..64)
+  int* n_tiles;            // [1]
+  int* tpair;              // [P] pair indices sorted by (expert, token)
+  uint32_t* selbits;       // [P][m/32] selected channels of each pair
+  float* gzpart;           // [P][m/64][r] per-group share of Q^T h_hat
+  int* ulist;              // [max_tiles][m] union channels of a tile, ascending
+  uint64_t* umask;         // [max_tiles][m] which tile tokens selected each union channel
+  int* ucount;             // [max_tiles]
+  uint16_t* hbuf;          // [P][kpad] bf16 activations by union position, then z
+  float* zsel;             // [P][m/16][r] Q^T h_hat over one gate/up block's selected channels
+  int* tile_cnt;           // [max_tiles] arrival counters (zero between calls)
+  int max_tiles, kpad;
 };
+
+// expert tiles hold up to this many tokens
+constexpr int kTileTokens = 64;
+inline int grouped_max_tiles(int pairs, int n_experts) {
+  const int bound = pairs / kTileTokens + (pairs < n_experts ? pairs : n_experts);
+  return pairs < bound ? pairs : bound;
+}
+inline int grouped_kpad(int m, int r) { return (m + r + 31) / 32 * 32; }
+bool grouped_supported(int d, int m);
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 

@@ -1,21 +1,36 @@
-// Device kernels of the routed-MoE block with sketch-based top-k channel
-// selection, written for gfx950 (CDNA4, 64-wide wavefronts).
+// Expert-grouped multi-kernel forward of the routed-MoE block with sketch-based
+// top-k channel selection, for gfx950 (CDNA4, 64-wide wavefronts, MFMA).
 //
-// Phases of one forward call, in order (pages cited by title and section):
-//   route+quantise  top_e experts per token, gate weights, int8 activations
+// Used for batches above the single-launch limit and for shapes the single
+// launch does not cover (large m). The (token, expert) pairs of a call are
+// grouped by expert into tiles of up to 64 tokens, so every weight byte an
+// expert needs is read once per tile, not once per token: the sketch codes once
+// per tile, and each channel row once per tile when at least one of the tile's
+// tokens selected it (the union of the tokens' selections). Each token still
+// uses only its own k channels: the others are masked out of its activations.
+//
+// Phases (pages cited by title and section):
+//   route+quantise  per token: top_e experts, gate weights, int8 activations
 //                   ("KAIST drops calibration from MoE decoding...", opening
-//                   paragraph: each token reads its routed experts);
-//   score           ternary-sketch GEMV over packed 2-bit codes, pinned binary32
-//                   channel scores (same page, "A reader built from weights alone");
-//   select          per (token, expert) top-k by radix passes over the score bits,
-//                   lowest index on ties, output ascending (same page, "Top-k
-//                   instead of a threshold"); also the compensation coordinates
-//                   z = Q^T h_hat over the skipped channels;
-//   gate/up         SwiGLU activations of the selected channels only, from the
-//                   channel-major bf16 layout (fp32 accumulation);
-//   down            per output slice, sum of h_j * down_j over the selected
-//                   channels plus the low-rank term P z;
-//   combine         gate-weighted sum over a token's experts, bf16 output.
+//                   paragraph: every token reads its routed experts' weights);
+//   plan            pairs sorted by (expert, token), cut into expert tiles;
+//   score           per (tile, 64-channel group): ternary-sketch scores of every
+//                   channel for every token of the tile, an int8 MFMA contraction
+//                   of the 2-bit codes with the activations, then the pinned
+//                   binary32 score (same page, "A reader built from weights
+//                   alone"); also the group's share of Q^T h_hat;
+//   select          per pair: the k largest scores, lower index on ties (same
+//                   page, "Top-k instead of a threshold");
+//   union           per tile: union of the tokens' selections, with per-channel
+//                   token masks;
+//   gate/up         per (tile, 16 union channels): bf16 MFMA of the channel rows
+//                   with the tile's activations, SwiGLU, masked per token; the
+//                   tile's last block finishes the compensation coordinates
+//                   z = Q^T h_hat over each token's skipped channels;
+//   down            per (tile, 64 outputs): bf16 MFMA of the activations with the
+//                   down columns of the union channels and, as r extra columns,
+//                   the low-rank map P applied to z;
+//   combine         per token: gate-weighted sum over its experts, bf16 output.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -29,8 +44,36 @@ namespace {
 
 using namespace dev;
 
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+constexpr int kT = kTileTokens;  // tokens per tile (4 MFMA subtiles of 16)
+constexpr int kCh = 16;          // union channels per gate/up block
+constexpr int kPlanThreads = 1024;
+constexpr int kDownPitch = 40;   // halfwords per LDS row of the transposed down tile (80 bytes)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// four byte-wide codes (t + 1) per dword, in hidden-element order (see the code layout)
+__device__ __forceinline__ i32x4 expand_codes(uint32_t w) {
+  return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+               (int)((w >> 6) & 0x03030303u)};
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= (uint32_t)dpp_i<kQuadXor1>((int)v);
+  v |= (uint32_t)dpp_i<kQuadXor2>((int)v);
+  v |= (uint32_t)dpp_i<kRowHalfMirror>((int)v);
+  v |= (uint32_t)dpp_i<kRowMirror>((int)v);
+  v |= (uint32_t)dpp_i<kRowBcast15, 0xA>((int)v);
+  v |= (uint32_t)dpp_i<kRowBcast31, 0xC>((int)v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // ===========================================================================
-// Phase 1: routing and activation quantisation, one block per token.
+// Routing and activation quantisation, one block per token.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   const int t = blockIdx.x;
@@ -40,8 +83,9 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   __shared__ int s_sel[64];
   __shared__ float s_selv[64];
   __shared__ uint32_t s_amax[kWaves];
+  __shared__ int s_qs[kWaves];
 
-  // --- top_e experts: repeated block arg-max, larger logit first, lower index on ties
+  // top_e experts: repeated block arg-max, larger logit first, lower index on ties
   const float* L = a.logits + (size_t)t * a.n_experts;
   constexpr int kMaxPer = 4;  // n_experts <= 1024
   float v[kMaxPer];
@@ -103,11 +147,11 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
     a.pair_w[p] = __expf(s_selv[tid] - top) / denom;
   }
 
-  // --- int8 activations with a power-of-two scale
+  // int8 activations with a power-of-two scale, and their sum
   const uint16_t* x = a.x + (size_t)t * a.d;
   uint32_t amax = 0;
   for (int i = tid; i < a.d; i += kThreads) amax = max(amax, (uint32_t)(x[i] & 0x7FFFu));
-  for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+  amax = wave_max_u(amax);
   if (lane == 0) s_amax[wave] = amax;
   __syncthreads();
   amax = s_amax[0];
@@ -122,72 +166,196 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   }
   if (tid == 0) a.xexp[t] = e;
   int8_t* q = a.xq + (size_t)t * a.d;
+  int qs = 0;
   for (int i = tid; i < a.d; i += kThreads) {
     const float xv = __uint_as_float((uint32_t)x[i] << 16);
-    q[i] = amax ? (int8_t)(int)__builtin_rintf(__builtin_ldexpf(xv, -e)) : (int8_t)0;
+    const int qi = amax ? (int)__builtin_rintf(__builtin_ldexpf(xv, -e)) : 0;
+    q[i] = (int8_t)qi;
+    qs += qi;
   }
+  qs = wave_sum_i(qs);
+  if (lane == 0) s_qs[wave] = qs;
+  __syncthreads();
+  if (tid == 0) a.xqsum[t] = s_qs[0] + s_qs[1] + s_qs[2] + s_qs[3];
 }
 
 // ===========================================================================
-// Phase 2: sketch scores. One block per (pair, 64-channel group): wave w scores
-// matrix w/2 (gate, up) over half w%2 of the hidden dimension; lane = channel.
+// Plan: pairs sorted by (expert, token) and cut into tiles of up to kT tokens.
+// One block. Pairs of a token have distinct experts, so within an expert the
+// order by token is the order by pair index, and a token's rank among an
+// expert's tokens is a popcount over per-expert token bitmaps of a chunk.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_score(FwdArgs a) {
-  extern __shared__ int4 s_xq4[];  // d bytes of int8 activations
-  __shared__ int s_part[kWaves][64];
-  const int groups = a.m / kGroup;
-  const int p = blockIdx.x / groups, g = blockIdx.x % groups;
-  const int t = p / a.top_e;
-  const int e = a.pair_expert[p];
+__global__ __launch_bounds__(kPlanThreads) void k_plan(FwdArgs a) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_run[1024];
+  __shared__ uint32_t s_bm[1024 * 4];  // per expert: bitmap of the chunk's tokens (<= 128)
+  __shared__ int s_wc[16], s_wt[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int4* xsrc = (const int4*)(a.xq + (size_t)t * a.d);
-  for (int i = tid; i < a.d / 16; i += kThreads) s_xq4[i] = xsrc[i];
-  __syncthreads();
-  const int mat = wave >> 1, half = wave & 1;
-  const int nb = a.d / kBlock;
-  const int b0 = half ? nb / 2 : 0, b1 = half ? nb : nb / 2;
-  const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
-                                   codes_dword_index(a.d, a.m, g, mat, 0, lane, 0));
-  int acc = 0, qs = 0;
-  for (int b = b0; b < b1; ++b) {
-    const uint4 c = cp[(size_t)b * 64];
-    const int4* xb = s_xq4 + b * 4;
-    const int4 x0 = xb[0], x1 = xb[1], x2 = xb[2], x3 = xb[3];
-    acc = dot_codes16(c.x, x0, acc);
-    acc = dot_codes16(c.y, x1, acc);
-    acc = dot_codes16(c.z, x2, acc);
-    acc = dot_codes16(c.w, x3, acc);
-    qs = byte_sum4(x0, qs);
-    qs = byte_sum4(x1, qs);
-    qs = byte_sum4(x2, qs);
-    qs = byte_sum4(x3, qs);
+  const int E = a.n_experts, P = a.batch * a.top_e;
+  if (tid < E) {
+    s_cnt[tid] = 0;
+    s_run[tid] = 0;
   }
-  s_part[wave][lane] = acc - qs;  // sum (code - 1) * q = sum t * q
   __syncthreads();
-  if (wave == 0) {
-    const int dg = s_part[0][lane] + s_part[1][lane];
-    const int du = s_part[2][lane] + s_part[3][lane];
-    const int j = g * kGroup + lane;
-    const float4 st = a.stats[(size_t)e * a.m + j];
-    float h, sc;
-    pinned_score(dg, du, a.xexp[t], st, h, sc);
-    a.hhat[(size_t)p * a.m + j] = h;
-    a.score[(size_t)p * a.m + j] = sc;
+  for (int p = tid; p < P; p += kPlanThreads) atomicAdd(&s_cnt[a.pair_expert[p]], 1);
+  __syncthreads();
+  // exclusive scans over experts of the pair counts and of the tile counts
+  const int c = tid < E ? s_cnt[tid] : 0;
+  const int nt = (c + kT - 1) / kT;
+  const int ic = wave_incl_scan(c), it = wave_incl_scan(nt);
+  if (lane == 63) {
+    s_wc[wave] = ic;
+    s_wt[wave] = it;
+  }
+  __syncthreads();
+  int bc = 0, bt = 0, tot_t = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    bc += w < wave ? s_wc[w] : 0;
+    bt += w < wave ? s_wt[w] : 0;
+    tot_t += s_wt[w];
+  }
+  const int off = bc + ic - c, toff = bt + it - nt;
+  if (tid < E) {
+    s_off[tid] = off;
+    for (int i = 0; i < nt; ++i) {
+      a.tile_expert[toff + i] = tid;
+      a.tile_first[toff + i] = off + i * kT;
+      a.tile_n[toff + i] = min(kT, c - i * kT);
+    }
+  }
+  if (tid == 0) *a.n_tiles = tot_t;
+  // stable placement, chunks of ct tokens (ct * top_e <= 1024 pairs, ct <= 128)
+  const int ct = max(1, min(128, kPlanThreads / a.top_e));
+  for (int t0 = 0; t0 < a.batch; t0 += ct) {
+    for (int i = tid; i < E * 4; i += kPlanThreads) s_bm[i] = 0u;
+    __syncthreads();
+    const int tl = tid / a.top_e;
+    const int t = t0 + tl;
+    const bool live = tl < ct && t < a.batch;
+    const int p = t * a.top_e + tid % a.top_e;
+    const int e = live ? a.pair_expert[p] : 0;
+    if (live) atomicOr(&s_bm[e * 4 + (tl >> 5)], 1u << (tl & 31));
+    __syncthreads();
+    if (live) {
+      int rank = s_run[e];
+      for (int w = 0; w < (tl >> 5); ++w) rank += __popc(s_bm[e * 4 + w]);
+      rank += __popc(s_bm[e * 4 + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
+      a.tpair[s_off[e] + rank] = p;
+    }
+    __syncthreads();
+    if (tid < E)
+      s_run[tid] += __popc(s_bm[tid * 4]) + __popc(s_bm[tid * 4 + 1]) + __popc(s_bm[tid * 4 + 2]) +
+                    __popc(s_bm[tid * 4 + 3]);
+    __syncthreads();
   }
 }
 
 // ===========================================================================
-// Phase 3: top-k per pair by four 8-bit radix passes over the score bits
-// (non-negative binary32 scores order like their bit patterns), then an
-// index-order compaction with wave ballots. One block per pair.
-// Also z = sum over skipped channels of h_hat_j * Q[j, :].
+// Sketch scores of one tile for one 64-channel group: int8 MFMA 16x16x64.
+// Wave w owns channels 16w..16w+15 of the group for both matrices; N = tokens
+// in subtiles of 16. C = sum (code) * q = D + sum q, so D = C - sum q.
+// ===========================================================================
+__global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
+  extern __shared__ float s_dyn_score[];  // h [kT][64], then Q rows [64][r]
+  const int d = a.d, m = a.m, r = a.r;
+  const int groups = m / kGroup;
+  const int tile = blockIdx.x / groups, grp = blockIdx.x % groups;
+  if (tile >= *a.n_tiles) return;
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  const int nsub = (n + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  float* s_h = s_dyn_score;
+  float* s_q = s_dyn_score + kT * 64;
+
+  const int8_t* xr[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int j = 16 * ns + li;
+    const int pp = a.tpair[first + (j < n ? j : 0)];
+    xr[ns] = a.xq + (size_t)(pp / a.top_e) * d + 16 * lg;
+  }
+  const size_t ebase = (size_t)e * codes_dwords_per_expert(d, m);
+  const uint32_t* cg = a.codes + ebase + codes_dword_index(d, m, grp, 0, 0, 16 * wave + li, lg);
+  const uint32_t* cu = a.codes + ebase + codes_dword_index(d, m, grp, 1, 0, 16 * wave + li, lg);
+  // Q rows of the group, staged while the codes stream
+  if (r > 0)
+    for (int i = tid; i < 64 * r; i += kThreads)
+      s_q[i] = __uint_as_float((uint32_t)a.qmat[((size_t)e * m + 64 * grp) * r + i] << 16);
+
+  // lane holds C[channel 4 lg + v][token li] of each subtile
+  const int ch0 = 64 * grp + 16 * wave + 4 * lg;
+  float4 st[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) st[v] = a.stats[(size_t)e * m + ch0 + v];
+  const int nb = d / kBlock;
+  constexpr int U = 4;
+  // token subtiles one after another: the codes stream from HBM once and are
+  // re-read from L2 for the later subtiles of a large tile
+  for (int ns = 0; ns < nsub; ++ns) {
+    i32x4 accg = i32x4{0, 0, 0, 0}, accu = i32x4{0, 0, 0, 0};
+    int b = 0;
+    for (; b + U <= nb; b += U) {
+      uint32_t wg[U], wu[U];
+      i32x4 xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        wg[u] = cg[(size_t)(b + u) * 256];
+        wu[u] = cu[(size_t)(b + u) * 256];
+        xv[u] = *(const i32x4*)(xr[ns] + 64 * (b + u));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[u]), xv[u], accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[u]), xv[u], accu, 0, 0, 0);
+      }
+    }
+    for (; b < nb; ++b) {
+      const i32x4 xv = *(const i32x4*)(xr[ns] + 64 * b);
+      accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(cg[(size_t)b * 256]), xv, accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(cu[(size_t)b * 256]), xv, accu, 0, 0, 0);
+    }
+    const int j = 16 * ns + li;
+    if (j < n) {
+      const int pp = a.tpair[first + j];
+      const int t = pp / a.top_e;
+      const int xe = a.xexp[t], qs = a.xqsum[t];
+      float h[4], sc[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pinned_score(accg[v] - qs, accu[v] - qs, xe, st[v], h[v], sc[v]);
+      *(float4*)(a.hhat + (size_t)pp * m + ch0) = make_float4(h[0], h[1], h[2], h[3]);
+      *(float4*)(a.score + (size_t)pp * m + ch0) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+      if (r > 0)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_h[j * 64 + 16 * wave + 4 * lg + v] = h[v];
+    }
+  }
+  if (r == 0) return;
+  __syncthreads();
+  // this group's share of Q^T h_hat for every token of the tile
+  const int groups_r = groups * r;
+  for (int i = tid; i < n * r; i += kThreads) {
+    const int j = i / r, c = i % r;
+    float z = 0.0f;
+#pragma unroll 8
+    for (int ch = 0; ch < 64; ++ch) z += s_h[j * 64 + ch] * s_q[ch * r + c];
+    const int pp = a.tpair[first + j];
+    a.gzpart[(size_t)pp * groups_r + grp * r + c] = z;
+  }
+}
+
+// ===========================================================================
+// Top-k per pair by four 8-bit radix passes over the score bits (non-negative
+// binary32 scores order like their bit patterns), then an index-order
+// compaction with wave ballots. One block per pair. Writes the ascending list,
+// its length and a bitmap of the selection.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
   extern __shared__ uint32_t s_dyn[];  // keys [m], then selection bits [m/32]
   __shared__ int s_hist[256];
   __shared__ int s_tmp[kWaves + 1];
   __shared__ int s_digit, s_gt;
-  __shared__ float s_z[kWaves][128];
   const int p = blockIdx.x;
   const int m = a.m, k = a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -217,11 +385,7 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
       __syncthreads();
       // thread tid owns bin 255 - tid: an inclusive scan over threads is a suffix scan over bins
       const int c = s_hist[255 - tid];
-      int incl = c;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
+      int incl = wave_incl_scan(c);
       if (lane == 63) s_tmp[wave] = incl;
       __syncthreads();
       for (int w = 0; w < wave; ++w) incl += s_tmp[w];
@@ -257,143 +421,313 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
   }
   __syncthreads();
   if (tid == 0) a.sel_count[p] = count;
-  // compensation coordinates over the skipped channels
-  const int r = a.r;
-  if (r > 0) {
-    const int e = a.pair_expert[p];
-    const uint16_t* Q = a.qmat + (size_t)e * m * r;
-    const float* hh = a.hhat + (size_t)p * m;
-    float z0 = 0.0f, z1 = 0.0f;
-    for (int j = wave; j < m; j += kWaves) {
-      if ((s_bits[j >> 5] >> (j & 31)) & 1u) continue;
-      const float hj = hh[j];
-      const uint16_t* row = Q + (size_t)j * r;
-      if (lane < r) z0 += hj * __uint_as_float((uint32_t)row[lane] << 16);
-      if (lane + 64 < r) z1 += hj * __uint_as_float((uint32_t)row[lane + 64] << 16);
-    }
-    s_z[wave][lane] = z0;
-    s_z[wave][lane + 64] = z1;
-    __syncthreads();
-    if (tid < r) {
-      float z = 0.0f;
-      for (int w = 0; w < kWaves; ++w) z += s_z[w][tid];
-      a.zvec[(size_t)p * r + tid] = z;
-    }
-  }
+  for (int w = tid; w < m / 32; w += kThreads) a.selbits[(size_t)p * (m / 32) + w] = s_bits[w];
 }
 
 // ===========================================================================
-// Phase 4: SwiGLU activations of the selected channels (or all, dense).
-// One block per (pair, chunk of kChunk channels); thread t owns 16-byte slots
-// t, t+256, ... of the hidden dimension.
+// Union of a tile's selections: ascending channel list and, per listed
+// channel, the mask of the tile's tokens that selected it. Also the sum over
+// groups of Q^T h_hat per token (z over all channels). One block per tile.
 // ===========================================================================
-constexpr int kChunk = 4;
-constexpr int kMaxSlots = 8;  // d <= 16384
-
-__global__ __launch_bounds__(kThreads) void k_gate_up(FwdArgs a, int dense) {
-  __shared__ float s_red[kWaves][2 * kChunk];
-  const int m = a.m, d = a.d;
-  const int count = dense ? m : a.k;
-  const int chunks = (count + kChunk - 1) / kChunk;
-  const int p = blockIdx.x / chunks, ch = blockIdx.x % chunks;
-  const int t = p / a.top_e;
-  const int e = a.pair_expert[p];
+__global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
+  extern __shared__ uint32_t s_dyn_u[];  // union words [m/32], their exclusive popcount offsets [m/32]
+  __shared__ int s_tmp[kWaves];
+  const int tile = blockIdx.x;
+  if (tile >= *a.n_tiles) return;
+  const int m = a.m, words = m / 32;
+  const int first = a.tile_first[tile], n = a.tile_n[tile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nslots = d / 8;
-  const uint16_t* xrow = a.x + (size_t)t * d;
-  float xv[kMaxSlots][8];
-  for (int u = 0; u < kMaxSlots; ++u) {
-    const int s = tid + u * kThreads;
-    if (s < nslots) {
-      const uint4 w = *(const uint4*)(xrow + 8 * s);
-      xv[u][0] = bf16lo(w.x); xv[u][1] = bf16hi(w.x);
-      xv[u][2] = bf16lo(w.y); xv[u][3] = bf16hi(w.y);
-      xv[u][4] = bf16lo(w.z); xv[u][5] = bf16hi(w.z);
-      xv[u][6] = bf16lo(w.w); xv[u][7] = bf16hi(w.w);
+  int* ul = a.ulist + (size_t)tile * m;
+  uint64_t* um = a.umask + (size_t)tile * m;
+  if (dense) {
+    const uint64_t all = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    for (int j = tid; j < m; j += kThreads) {
+      ul[j] = j;
+      um[j] = all;
     }
+    if (tid == 0) a.ucount[tile] = m;
+    return;
   }
-  const int* idx = a.sel_idx + (size_t)p * m;
-  float gs[kChunk], us[kChunk];
-  for (int c = 0; c < kChunk; ++c) {
-    gs[c] = 0.0f;
-    us[c] = 0.0f;
-    const int i = ch * kChunk + c;
-    if (i >= count) continue;
-    const int j = dense ? i : idx[i];
-    const uint16_t* base = a.wch + ((size_t)e * m + j) * 3 * d;
-    for (int u = 0; u < kMaxSlots; ++u) {
-      const int s = tid + u * kThreads;
-      if (s < nslots) {
-        gs[c] += dot8_bf16(*(const uint4*)(base + 8 * s), xv[u]);
-        us[c] += dot8_bf16(*(const uint4*)(base + d + 8 * s), xv[u]);
-      }
-    }
-  }
-  for (int c = 0; c < kChunk; ++c) {
-    const float g = wave_sum(gs[c]);
-    const float u = wave_sum(us[c]);
-    if (lane == 0) {
-      s_red[wave][2 * c] = g;
-      s_red[wave][2 * c + 1] = u;
-    }
+  uint32_t* s_u = s_dyn_u;
+  int* s_pos = (int*)(s_dyn_u + words);
+  // lane i < n holds token i's word of the selection bitmap
+  const uint32_t* sb = a.selbits + (size_t)a.tpair[first + (lane < n ? lane : 0)] * words;
+  for (int w = wave; w < words; w += kWaves) {
+    const uint32_t v = lane < n ? sb[w] : 0u;
+    const uint32_t u = wave_or(v);
+    if (lane == 0) s_u[w] = u;
   }
   __syncthreads();
-  if (tid < kChunk) {
-    const int i = ch * kChunk + tid;
-    if (i < count) {
-      float g = 0.0f, u = 0.0f;
-      for (int w = 0; w < kWaves; ++w) {
-        g += s_red[w][2 * tid];
-        u += s_red[w][2 * tid + 1];
-      }
-      a.hsel[(size_t)p * m + i] = silu_f32(g) * u;
+  int run = 0;
+  for (int base = 0; base < words; base += kThreads) {
+    const int w = base + tid;
+    const int c = w < words ? __popc(s_u[w]) : 0;
+    int tot;
+    const int ex = block_excl_scan(c, s_tmp, &tot);
+    if (w < words) s_pos[w] = run + ex;
+    run += tot;
+  }
+  __syncthreads();
+  for (int w = wave; w < words; w += kWaves) {
+    const uint32_t v = lane < n ? sb[w] : 0u;
+    const uint32_t u = s_u[w];
+    uint64_t mine = 0;
+    for (int bit = 0; bit < 32; ++bit) {
+      const uint64_t mk = __ballot((v >> bit) & 1u);
+      if (lane == bit) mine = mk;
+    }
+    if (lane < 32 && ((u >> lane) & 1u)) {
+      const int pos = s_pos[w] + __popc(u & ((1u << lane) - 1u));
+      ul[pos] = 32 * w + lane;
+      um[pos] = mine;
     }
   }
+  if (tid == 0) a.ucount[tile] = run;
+  const int r = a.r, groups = m / kGroup;
+  if (r > 0)
+    for (int i = tid; i < n * r; i += kThreads) {
+      const int j = i / r, c = i % r;
+      const int pp = a.tpair[first + j];
+      const float* zp = a.gzpart + (size_t)pp * groups * r + c;
+      float z = 0.0f;
+      for (int g = 0; g < groups; ++g) z += zp[(size_t)g * r];
+      a.zvec[(size_t)pp * r + c] = z;
+    }
 }
 
 // ===========================================================================
-// Phase 5: one block per (pair, 64-element output slice): sum over the pair's
-// selected channels of h_i * down_j[slice] (128-byte pieces), plus P z.
+// SwiGLU of 16 union channels for every token of a tile: bf16 MFMA 16x16x32
+// (M = channels, N = tokens, K = hidden), the hidden dimension split over the
+// four waves. Activations of tokens that did not select a channel are zero.
+// The tile's last block to finish writes z = Q^T h_hat over each token's
+// skipped channels after the union activations, as r more columns.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_down(FwdArgs a, int dense) {
-  __shared__ float s_red[32][65];
-  const int m = a.m, d = a.d;
+__global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
+  __shared__ f32x4 s_acc[kWaves][2][64];  // 8 KiB
+  __shared__ float s_hz[kCh][kT];
+  __shared__ float s_qr[kCh * 128];
+  __shared__ int s_last;
+  const int d = a.d, m = a.m;
+  const int maxch = m / kCh;
+  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
+  if (tile >= *a.n_tiles) return;
+  const int uc = a.ucount[tile];
+  const int nch = max(1, (uc + kCh - 1) / kCh);
+  if (chunk >= nch) return;
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  const int nsub = (n + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int r = dense ? 0 : a.r;
+  const int* ul = a.ulist + (size_t)tile * m;
+  const uint64_t* um = a.umask + (size_t)tile * m;
+
+  // A rows: union channel 16 chunk + li (clamped); B columns: token 16 ns + li (clamped)
+  const int pos_a = min(kCh * chunk + li, max(uc - 1, 0));
+  const int ja = uc > 0 ? ul[pos_a] : 0;
+  const uint16_t* grow = a.wch + ((size_t)e * m + ja) * 3 * d + 8 * lg;
+  const uint16_t* urow = grow + d;
+  const uint16_t* xr[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int j = 16 * ns + li;
+    const int pp = a.tpair[first + (j < n ? j : 0)];
+    xr[ns] = a.x + (size_t)(pp / a.top_e) * d + 8 * lg;
+  }
+  const int nsteps = d / 32;
+  const int kpad = a.kpad;
+  constexpr int U = 4;
+  // token subtiles one after another (weights re-read from L2 after the first)
+  for (int ns = 0; ns < nsub; ++ns) {
+    f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
+    int s = wave;
+    for (; s + kWaves * (U - 1) < nsteps; s += kWaves * U) {
+      u32x4 gv[U], uv[U], xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k0 = 32 * (s + kWaves * u);
+        gv[u] = *(const u32x4*)(grow + k0);
+        uv[u] = *(const u32x4*)(urow + k0);
+        xv[u] = *(const u32x4*)(xr[ns] + k0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv[u]), as_bf16x8(xv[u]), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv[u]), as_bf16x8(xv[u]), accu, 0, 0, 0);
+      }
+    }
+    for (; s < nsteps; s += kWaves) {
+      const int k0 = 32 * s;
+      const u32x4 gv = *(const u32x4*)(grow + k0), uv = *(const u32x4*)(urow + k0);
+      const u32x4 xv = *(const u32x4*)(xr[ns] + k0);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv), as_bf16x8(xv), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv), as_bf16x8(xv), accu, 0, 0, 0);
+    }
+    s_acc[wave][0][lane] = accg;
+    s_acc[wave][1][lane] = accu;
+    __syncthreads();
+    // wave 0 finishes the subtile: lane holds channels 4 lg + v, token 16 ns + li
+    if (wave == 0) {
+      const int j = 16 * ns + li;
+      f32x4 g = s_acc[0][0][lane], u = s_acc[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        g += s_acc[w][0][lane];
+        u += s_acc[w][1][lane];
+      }
+      uint16_t hb[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int pos = kCh * chunk + 4 * lg + v;
+        const bool member = pos < uc && j < n && ((um[pos] >> j) & 1ull);
+        const float h = member ? silu_f32(g[v]) * u[v] : 0.0f;
+        hb[v] = f32_to_bf16_dev(h);
+      }
+      if (j < n) {
+        const int pp = a.tpair[first + j];
+        uint2 w2;
+        w2.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+        w2.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+        *(uint2*)(a.hbuf + (size_t)pp * kpad + kCh * chunk + 4 * lg) = w2;
+      }
+    }
+    __syncthreads();
+  }
+  if (r == 0) {
+    // only the K padding after the union is left: zero it once per tile (chunk 0)
+    if (chunk == 0 && !dense) {
+      const int kend = (uc + 31) / 32 * 32;
+      for (int i = tid; i < n * (kend - uc); i += kThreads) {
+        const int j = i / (kend - uc), c = uc + i % (kend - uc);
+        a.hbuf[(size_t)a.tpair[first + j] * kpad + c] = 0;
+      }
+    }
+    return;
+  }
+  // Q^T h_hat over this block's selected channels, per token
+  for (int i = tid; i < kCh * r; i += kThreads) {
+    const int ci = i / r, c = i % r;
+    const int pos = kCh * chunk + ci;
+    s_qr[i] = pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16) : 0.0f;
+  }
+  for (int i = tid; i < kCh * n; i += kThreads) {
+    const int ci = i / n, j = i % n;
+    const int pos = kCh * chunk + ci;
+    float hz = 0.0f;
+    if (pos < uc && ((um[pos] >> j) & 1ull)) hz = a.hhat[(size_t)a.tpair[first + j] * m + ul[pos]];
+    s_hz[ci][j] = hz;
+  }
+  __syncthreads();
+  for (int i = tid; i < n * r; i += kThreads) {
+    const int j = i / r, c = i % r;
+    float z = 0.0f;
+#pragma unroll
+    for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci][j] * s_qr[ci * r + c];
+    st_coh(&a.zsel[((size_t)a.tpair[first + j] * maxch + chunk) * r + c], z);
+  }
+  // the tile's last block: z over the skipped channels into the columns after the union
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.tile_cnt[tile], 1) == nch - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int kend = (uc + r + 31) / 32 * 32;
+  const bool all_kept = a.k >= m;
+  for (int i = tid; i < n * (kend - uc); i += kThreads) {
+    const int j = i / (kend - uc), c = i % (kend - uc);
+    const int pp = a.tpair[first + j];
+    float z = 0.0f;
+    if (c < r && !all_kept) {
+      z = a.zvec[(size_t)pp * r + c];
+      for (int q = 0; q < nch; ++q) z -= ld_coh(&a.zsel[((size_t)pp * maxch + q) * r + c]);
+    }
+    a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(z);
+  }
+  if (tid == 0) a.tile_cnt[tile] = 0;
+}
+
+// ===========================================================================
+// Down projection of a tile for 64 outputs: bf16 MFMA 16x16x32 with M = tokens,
+// N = outputs (16 per wave), K = the union channels' down columns followed by
+// the r rows of P^T (whose activations are z). The 32 x 64 weight tile of each
+// K step is staged through LDS transposed, double-buffered.
+// ===========================================================================
+__global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense) {
+  __shared__ __align__(16) uint16_t s_b[2][64 * kDownPitch];
+  const int d = a.d, m = a.m;
   const int slices = d / 64;
-  const int p = blockIdx.x / slices, sl = blockIdx.x % slices;
-  const int e = a.pair_expert[p];
-  const int count = dense ? m : a.sel_count[p];
-  const int tid = threadIdx.x;
-  const int part = tid & 7, row = tid >> 3;  // 32 rows x 8 parts of 16 bytes
-  const int* idx = a.sel_idx + (size_t)p * m;
-  const float* hs = a.hsel + (size_t)p * m;
-  float acc[8];
-  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int i = row; i < count; i += 32) {
-    const int j = dense ? i : idx[i];
-    const uint4 w = *(const uint4*)(a.wch + (((size_t)e * m + j) * 3 + 2) * d + 64 * sl + 8 * part);
-    const float h = hs[i];
-    acc[0] += h * bf16lo(w.x); acc[1] += h * bf16hi(w.x);
-    acc[2] += h * bf16lo(w.y); acc[3] += h * bf16hi(w.y);
-    acc[4] += h * bf16lo(w.z); acc[5] += h * bf16hi(w.z);
-    acc[6] += h * bf16lo(w.w); acc[7] += h * bf16hi(w.w);
+  const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
+  if (tile >= *a.n_tiles) return;
+  const int uc = a.ucount[tile];
+  const int r = dense ? 0 : a.r;
+  const int K = uc + r;
+  const int steps = (K + 31) / 32;
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  const int msub = (n + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int* ul = a.ulist + (size_t)tile * m;
+  const int kpad = a.kpad;
+  // staging: thread loads row kr (of 32) and 8 outputs at 8 part of the slice
+  const int kr = tid >> 3, part = tid & 7;
+  auto brow = [&](int s) -> const uint16_t* {
+    int k = 32 * s + kr;
+    k = min(k, K - 1);
+    if (k < uc) return a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d + 64 * sl + 8 * part;
+    return a.pmat + ((size_t)e * a.r + (k - uc)) * d + 64 * sl + 8 * part;
+  };
+  const uint16_t* hrow[4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    const int j = 16 * ms + li;
+    hrow[ms] = a.hbuf + (size_t)a.tpair[first + (j < n ? j : 0)] * kpad + 8 * lg;
   }
-  for (int q = 0; q < 8; ++q) s_red[row][part * 8 + q] = acc[q];
-  __syncthreads();
-  if (tid < 64) {
-    float y = 0.0f;
-    for (int rr = 0; rr < 32; ++rr) y += s_red[rr][tid];
-    const int r = a.r;
-    if (!dense && r > 0) {
-      const uint16_t* P = a.pmat + (size_t)e * r * d;
-      const float* z = a.zvec + (size_t)p * r;
-      for (int c = 0; c < r; ++c) y += z[c] * __uint_as_float((uint32_t)P[(size_t)c * d + 64 * sl + tid] << 16);
+  f32x4 acc[4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (steps > 0) {
+    u32x4 vb = *(const u32x4*)brow(0);
+    u32x4 va[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+      if (ms < msub) va[ms] = *(const u32x4*)(hrow[ms]);
+    for (int s = 0; s < steps; ++s) {
+      uint16_t* sb = s_b[s & 1];
+      const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        sb[(8 * part + q) * kDownPitch + kr] = (uint16_t)(wv[q >> 1] >> (16 * (q & 1)));
+      __syncthreads();
+      const int sn = s + 1 < steps ? s + 1 : s;
+      const u32x4 vb_next = *(const u32x4*)brow(sn);
+      u32x4 va_next[4];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+        if (ms < msub) va_next[ms] = *(const u32x4*)(hrow[ms] + 32 * sn);
+      const u32x4 bv = *(const u32x4*)(sb + (16 * wave + li) * kDownPitch + 8 * lg);
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+        if (ms < msub) acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ms]), as_bf16x8(bv), acc[ms], 0, 0, 0);
+      vb = vb_next;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+        if (ms < msub) va[ms] = va_next[ms];
     }
-    a.ypart[(size_t)p * d + 64 * sl + tid] = y;
   }
+  // lane holds C[token 16 ms + 4 lg + v][output 16 wave + li]
+  const int o = 64 * sl + 16 * wave + li;
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * ms + 4 * lg + v;
+      if (ms < msub && j < n) a.ypart[(size_t)a.tpair[first + j] * d + o] = acc[ms][v];
+    }
 }
 
 // ===========================================================================
-// Phase 6: gate-weighted sum over a token's experts, bf16 output.
+// Gate-weighted sum over a token's experts, bf16 output.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a) {
   const int per_tok = (a.d + kThreads - 1) / kThreads;
@@ -410,19 +744,22 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a) {
 
 }  // namespace
 
+// k_select keeps m keys and m/32 bitmap words in LDS (64 KiB)
+bool grouped_supported(int d, int m) { return d >= 64 && (size_t)m * 4 + (size_t)m / 8 + 2048 <= 65536; }
+
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int pairs = a.batch * a.top_e;
+  const int groups = a.m / kGroup;
   hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
-    hipLaunchKernelGGL(k_score, dim3(pairs * (a.m / kGroup)), dim3(kThreads), (size_t)a.d, stream, a);
+    const size_t score_lds = ((size_t)kT * 64 + (size_t)64 * a.r) * 4;
+    hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads), score_lds, stream, a);
     hipLaunchKernelGGL(k_select, dim3(pairs), dim3(kThreads), (size_t)(a.m + a.m / 32) * 4, stream, a);
   }
-  const int count = dense ? a.m : a.k;
-  if (count > 0) {
-    const int chunks = (count + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL(k_gate_up, dim3(pairs * chunks), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  }
-  hipLaunchKernelGGL(k_down, dim3(pairs * (a.d / 64)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), (size_t)(a.m / 32) * 8, stream, a, dense ? 1 : 0);
+  hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  hipLaunchKernelGGL(k_down_g, dim3(a.max_tiles * (a.d / 64)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   const int per_tok = (a.d + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -293,3 +293,85 @@ def test_graph_replay_matches_eager(b, torch, tiny_layer):
         b.moe_sel_check_device(lay.ctx)
         for i in range(n):
             assert torch.equal(outs[i], eager[i]), (rep, i)
+
+
+def test_graph_replay_matches_eager_multi_kernel(b, torch, tiny_layer):
+    """The expert-grouped path under graph capture: per-tile arrival counters and
+    all workspace state are left clean by every call, so replays reproduce the
+    eager outputs."""
+    lay = tiny_layer
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_MULTI_KERNEL)
+    lay.path = None
+    rng = np.random.default_rng(12)
+    bsz = 12
+    x = to_dev_u16(torch, synth.f32_to_bf16_bits(rng.standard_normal((bsz, lay.d)).astype(np.float32)))
+    lg = to_dev_f32(torch, rng.standard_normal((bsz, lay.E)).astype(np.float32))
+    outs = [torch.zeros((bsz, lay.d), dtype=torch.int16, device="cuda") for _ in range(2)]
+    stream = torch.cuda.Stream()
+    def calls():
+        b.moe_sel_forward(lay.ctx, x, lg, bsz, lay.top_e, 60, outs[0], stream.cuda_stream)
+        b.moe_sel_forward_dense(lay.ctx, x, lg, bsz, lay.top_e, outs[1], stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        junk = torch.zeros((bsz, lay.d), dtype=torch.int16, device="cuda")
+        b.moe_sel_forward(lay.ctx, x, lg, bsz, lay.top_e, 5, junk)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
+
+
+def test_tiles_split_beyond_64_tokens_per_expert(b, torch):
+    """200 tokens over 8 experts (top-2): experts receive more than 64 tokens, so
+    their pairs span several tiles; every token still matches the oracle."""
+    lay = Layer(b, "tiny", max_batch=200)
+    try:
+        rng = np.random.default_rng(13)
+        bsz, k = 200, 92
+        x = synth.f32_to_bf16_bits(rng.standard_normal((bsz, lay.d)).astype(np.float32))
+        logits = rng.standard_normal((bsz, lay.E)).astype(np.float32)
+        logits[:, 3] += 2.0  # expert 3 takes most tokens
+        lay.path = "multi_kernel"
+        out = _run(b, torch, lay, x, logits, k)
+        ref = lay.oracle.forward(x, logits, lay.top_e, k)
+        assert (ref["expert_ids"] == 3).sum() > 128
+        _check_selection(b, lay, ref, bsz, lay.top_e, k)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+        dense = _run(b, torch, lay, x, logits, 0, dense=True)
+        assert rel_err(out_to_f64(torch, dense), lay.oracle.forward_dense(x, logits, lay.top_e)) <= TOL
+    finally:
+        lay.close()
+
+
+def test_qwen3_batch64_zipf_parity(b, torch):
+    """Qwen3-shaped block at 64 decode tokens with Zipf(1.1)-skewed routing: the
+    per-expert union path selects each token's own channels bit for bit and every
+    token's output is within tolerance."""
+    w = synth.WORKLOADS["qwen3_b64"]
+    lay = Layer(b, "qwen3_b64", max_batch=64)
+    try:
+        bsz, k = 64, w["ks"][0]
+        x = synth.tokens(w["wid"], 0, bsz, lay.d)
+        logits = synth.router_logits(w["wid"], 0, bsz, lay.E, "zipf")
+        lay.path = None
+        out = _run(b, torch, lay, x, logits, k)
+        assert b.moe_sel_last_path(lay.ctx) == b.MOE_SEL_PATH_MULTI_KERNEL
+        ref = lay.oracle.forward(x, logits, lay.top_e, k)
+        counts = np.bincount(ref["expert_ids"].ravel(), minlength=lay.E)
+        print(f"experts used {np.count_nonzero(counts)}, hottest {counts.max()} tokens")
+        _check_selection(b, lay, ref, bsz, lay.top_e, k)
+        err = rel_err(out_to_f64(torch, out), ref["y"])
+        print(f"qwen3 batch 64 zipf k={k}: max-rel-err {err:.2e}")
+        assert err <= TOL
+    finally:
+        lay.close()
