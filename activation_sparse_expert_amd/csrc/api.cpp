@@ -48,7 +48,6 @@ struct moe_sel_ctx {
   int* ucount = nullptr;
   uint16_t* hbuf = nullptr;
   float* zsel = nullptr;
-  int* tile_cnt = nullptr;
   int max_tiles = 0;
   // single-launch path
   uint64_t* xscore = nullptr;
@@ -208,7 +207,6 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.ucount = c->ucount;
   a.hbuf = c->hbuf;
   a.zsel = c->zsel;
-  a.tile_cnt = c->tile_cnt;
   a.max_tiles = moe_sel::grouped_max_tiles(batch * top_e, c->cfg.n_experts);
   a.kpad = moe_sel::grouped_kpad(c->cfg.m, c->cfg.rank);
   return a;
@@ -407,7 +405,13 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   ALLOC(sel_idx, pairs * m);
   ALLOC(sel_count, pairs);
   ALLOC(zvec, pairs * std::max<size_t>(r, 1));
-  ALLOC(ypart, pairs * d);
+  // partial outputs: the largest split times the pairs of any call size
+  size_t ypart_count = 0;
+  for (int pp = 1; pp <= c.max_batch * c.max_top_e; ++pp) {
+    const size_t need = (size_t)moe_sel::grouped_down_split(moe_sel::grouped_max_tiles(pp, c.n_experts), c.d) * pp * d;
+    ypart_count = std::max(ypart_count, need);
+  }
+  ALLOC(ypart, ypart_count);
   ctx->max_tiles = moe_sel::grouped_max_tiles((int)pairs, c.n_experts);
   const size_t mt = ctx->max_tiles;
   ALLOC(xqsum, (size_t)c.max_batch);
@@ -423,7 +427,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   ALLOC(ucount, mt);
   ALLOC(hbuf, pairs * moe_sel::grouped_kpad(c.m, c.rank));
   ALLOC(zsel, pairs * (m / 16) * std::max<size_t>(r, 1));
-  ALLOC(tile_cnt, mt);
+
   // single-launch path: sized for up to kFusedMaxBatch tokens and the smallest chunk
   const bool fusable = moe_sel::fused_supported(c.d, c.m, c.rank, c.max_top_e);
   if (fusable) {
@@ -462,11 +466,6 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
       free_ctx(ctx);
       return hip_fail(he, "hipMemcpyAsync");
     }
-  }
-  he = hipMemsetAsync(ctx->tile_cnt, 0, mt * sizeof(int), s);
-  if (he != hipSuccess) {
-    free_ctx(ctx);
-    return hip_fail(he, "hipMemsetAsync");
   }
   if (ctx->xscore) {
     he = reset_handoff(ctx, s);

@@ -31,7 +31,7 @@ struct FwdArgs {
   int* sel_idx;            // [P][m]
   int* sel_count;          // [P]
   float* zvec;             // [P][r]  sum over all channels of h_hat_j Q[j, :]
-  float* ypart;            // [P][d]
+  float* ypart;            // [kc][P][d] partial outputs of each K split of the down projection
   // expert-grouped multi-kernel path
   int* xqsum;              // [B] sum of the int8 activations
   int* tile_expert;        // [max_tiles]
@@ -46,7 +46,6 @@ struct FwdArgs {
   int* ucount;             // [max_tiles]
   uint16_t* hbuf;          // [P][kpad] bf16 activations by union position, then z
   float* zsel;             // [P][m/16][r] Q^T h_hat over one gate/up block's selected channels
-  int* tile_cnt;           // [max_tiles] arrival counters (zero between calls)
   int max_tiles, kpad;
 };
 
@@ -58,6 +57,11 @@ inline int grouped_max_tiles(int pairs, int n_experts) {
 }
 inline int grouped_kpad(int m, int r) { return (m + r + 31) / 32 * 32; }
 bool grouped_supported(int d, int m);
+// down projection: outputs per block, and the split of its K range over blocks
+constexpr int kDownTargetBlocks = 1024;
+constexpr int kMaxDownSplit = 16;
+int grouped_down_width(int d);
+int grouped_down_split(int max_tiles, int d);
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 

@@ -290,27 +290,47 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) st[v] = a.stats[(size_t)e * m + ch0 + v];
   const int nb = d / kBlock;
-  constexpr int U = 4;
+  // Main loop over groups of 4 code blocks: lane (i + 16 g) loads channel i's
+  // 16-byte piece of block b + g and feeds its dword q to MFMA q, whose B operand
+  // is the matching 16 activations; the contraction order over the hidden
+  // dimension is permuted, which leaves the exact integer sums unchanged.
+  const size_t blk4 = (size_t)64;  // u32x4 per (group, matrix, block)
+  const u32x4* cg4 = (const u32x4*)(a.codes + ebase + codes_dword_index(d, m, grp, 0, lg, 16 * wave + li, 0));
+  const u32x4* cu4 = (const u32x4*)(a.codes + ebase + codes_dword_index(d, m, grp, 1, lg, 16 * wave + li, 0));
   // token subtiles one after another: the codes stream from HBM once and are
   // re-read from L2 for the later subtiles of a large tile
   for (int ns = 0; ns < nsub; ++ns) {
     i32x4 accg = i32x4{0, 0, 0, 0}, accu = i32x4{0, 0, 0, 0};
+    const int8_t* x4 = xr[ns] - 16 * lg + 64 * lg;  // token row + block offset lg
     int b = 0;
-    for (; b + U <= nb; b += U) {
-      uint32_t wg[U], wu[U];
-      i32x4 xv[U];
+    for (; b + 8 <= nb; b += 8) {
+      u32x4 wg[2], wu[2];
+      i32x4 xv[2][4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        wg[u] = cg[(size_t)(b + u) * 256];
-        wu[u] = cu[(size_t)(b + u) * 256];
-        xv[u] = *(const i32x4*)(xr[ns] + 64 * (b + u));
+      for (int u = 0; u < 2; ++u) {
+        wg[u] = cg4[(size_t)(b + 4 * u) * blk4];
+        wu[u] = cu4[(size_t)(b + 4 * u) * blk4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[u][q] = *(const i32x4*)(x4 + 64 * (b + 4 * u) + 16 * q);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[u]), xv[u], accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[u]), xv[u], accu, 0, 0, 0);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[u][q]), xv[u][q], accg, 0, 0, 0);
+          accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[u][q]), xv[u][q], accu, 0, 0, 0);
+        }
+    }
+    for (; b + 4 <= nb; b += 4) {
+      const u32x4 wg = cg4[(size_t)b * blk4], wu = cu4[(size_t)b * blk4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x4 xv = *(const i32x4*)(x4 + 64 * b + 16 * q);
+        accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[q]), xv, accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[q]), xv, accu, 0, 0, 0);
       }
     }
+    // remaining blocks one at a time: lane (i + 16 g) takes dword g of block b
     for (; b < nb; ++b) {
       const i32x4 xv = *(const i32x4*)(xr[ns] + 64 * b);
       accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(cg[(size_t)b * 256]), xv, accg, 0, 0, 0);
@@ -499,14 +519,13 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
 // SwiGLU of 16 union channels for every token of a tile: bf16 MFMA 16x16x32
 // (M = channels, N = tokens, K = hidden), the hidden dimension split over the
 // four waves. Activations of tokens that did not select a channel are zero.
-// The tile's last block to finish writes z = Q^T h_hat over each token's
-// skipped channels after the union activations, as r more columns.
+// Blocks of a sparse call also leave their channels' share of Q^T h_hat per
+// token, from which k_zfin finishes the compensation coordinates.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   __shared__ f32x4 s_acc[kWaves][2][64];  // 8 KiB
   __shared__ float s_hz[kCh][kT];
   __shared__ float s_qr[kCh * 128];
-  __shared__ int s_last;
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
   const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
@@ -593,17 +612,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     }
     __syncthreads();
   }
-  if (r == 0) {
-    // only the K padding after the union is left: zero it once per tile (chunk 0)
-    if (chunk == 0 && !dense) {
-      const int kend = (uc + 31) / 32 * 32;
-      for (int i = tid; i < n * (kend - uc); i += kThreads) {
-        const int j = i / (kend - uc), c = uc + i % (kend - uc);
-        a.hbuf[(size_t)a.tpair[first + j] * kpad + c] = 0;
-      }
-    }
-    return;
-  }
+  if (r == 0) return;
   // Q^T h_hat over this block's selected channels, per token
   for (int i = tid; i < kCh * r; i += kThreads) {
     const int ci = i / r, c = i % r;
@@ -623,59 +632,89 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     float z = 0.0f;
 #pragma unroll
     for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci][j] * s_qr[ci * r + c];
-    st_coh(&a.zsel[((size_t)a.tpair[first + j] * maxch + chunk) * r + c], z);
+    a.zsel[((size_t)a.tpair[first + j] * maxch + chunk) * r + c] = z;
   }
-  // the tile's last block: z over the skipped channels into the columns after the union
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.tile_cnt[tile], 1) == nch - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
+
+// ===========================================================================
+// Per tile, after gate/up: z = Q^T h_hat over each token's skipped channels
+// (the all-channel sum minus the gate/up blocks' selected-channel shares, in
+// block order) into the activation columns after the union, then zeros up to
+// the next multiple of 32 columns.
+// ===========================================================================
+__global__ __launch_bounds__(kThreads) void k_zfin(FwdArgs a) {
+  const int tile = blockIdx.x;
+  if (tile >= *a.n_tiles) return;
+  const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad;
+  const int uc = a.ucount[tile];
+  const int nch = max(1, (uc + kCh - 1) / kCh);
+  const int first = a.tile_first[tile], n = a.tile_n[tile];
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
-  for (int i = tid; i < n * (kend - uc); i += kThreads) {
+  for (int i = threadIdx.x; i < n * (kend - uc); i += kThreads) {
     const int j = i / (kend - uc), c = i % (kend - uc);
     const int pp = a.tpair[first + j];
     float z = 0.0f;
     if (c < r && !all_kept) {
+      const float* zs = a.zsel + (size_t)pp * maxch * r + c;
       z = a.zvec[(size_t)pp * r + c];
-      for (int q = 0; q < nch; ++q) z -= ld_coh(&a.zsel[((size_t)pp * maxch + q) * r + c]);
+      int q = 0;
+      for (; q + 8 <= nch; q += 8) {
+        float part[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) part[u] = zs[(size_t)(q + u) * r];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z -= part[u];
+      }
+      for (; q < nch; ++q) z -= zs[(size_t)q * r];
     }
     a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(z);
   }
-  if (tid == 0) a.tile_cnt[tile] = 0;
 }
 
 // ===========================================================================
-// Down projection of a tile for 64 outputs: bf16 MFMA 16x16x32 with M = tokens,
-// N = outputs (16 per wave), K = the union channels' down columns followed by
-// the r rows of P^T (whose activations are z). The 32 x 64 weight tile of each
-// K step is staged through LDS transposed, double-buffered.
+// Down projection of a tile for SW = 64 NW outputs: bf16 MFMA 16x16x32 with
+// M = tokens, N = outputs (16 NW per wave), K = the union channels' down columns
+// followed by the r rows of P^T (whose activations are z). Each stage stages
+// KS channels x SW outputs through LDS: a thread loads 4 channel rows x 8
+// outputs (16 bytes each, so a row is read in SW * 2-byte runs), transposes the
+// 4 x 8 block in registers and writes one 8-byte LDS row piece per output.
+// With few tiles the K range is split over kc blocks, each writing its own
+// partial output, which the combine adds in a fixed order.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense) {
-  __shared__ __align__(16) uint16_t s_b[2][64 * kDownPitch];
+template <int NW>
+__global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int kc) {
+  constexpr int SW = 64 * NW;      // outputs per block
+  constexpr int OG = SW / 8;       // 8-output groups
+  constexpr int CG = kThreads / OG;
+  constexpr int RPT = 4;           // channel rows per thread per stage
+  constexpr int KS = RPT * CG;     // channels per stage
+  constexpr int PITCH = KS + 8;    // halfwords per LDS row (one output)
+  __shared__ __align__(16) uint16_t s_b[SW * PITCH];
   const int d = a.d, m = a.m;
-  const int slices = d / 64;
-  const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
+  const int slices = d / SW;
+  const int per_tile = slices * kc;
+  const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
+  const int sl = rem % slices, kci = rem / slices;
   if (tile >= *a.n_tiles) return;
   const int uc = a.ucount[tile];
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
-  const int steps = (K + 31) / 32;
+  const int nst = (K + KS - 1) / KS;
+  const int spc = (nst + kc - 1) / kc;
+  const int st0 = kci * spc, st1 = min(nst, st0 + spc);
   const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   const int msub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int* ul = a.ulist + (size_t)tile * m;
   const int kpad = a.kpad;
-  // staging: thread loads row kr (of 32) and 8 outputs at 8 part of the slice
-  const int kr = tid >> 3, part = tid & 7;
-  auto brow = [&](int s) -> const uint16_t* {
-    int k = 32 * s + kr;
+  const int og = tid % OG, cg = tid / OG;
+  const size_t col = (size_t)SW * sl + 8 * og;
+  auto brow = [&](int k) -> const uint16_t* {
     k = min(k, K - 1);
-    if (k < uc) return a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d + 64 * sl + 8 * part;
-    return a.pmat + ((size_t)e * a.r + (k - uc)) * d + 64 * sl + 8 * part;
+    if (k < uc) return a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d + col;
+    return a.pmat + ((size_t)e * a.r + (k - uc)) * d + col;
   };
   const uint16_t* hrow[4];
 #pragma unroll
@@ -683,61 +722,84 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense) {
     const int j = 16 * ms + li;
     hrow[ms] = a.hbuf + (size_t)a.tpair[first + (j < n ? j : 0)] * kpad + 8 * lg;
   }
-  f32x4 acc[4];
+  f32x4 acc[4][NW];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (steps > 0) {
-    u32x4 vb = *(const u32x4*)brow(0);
-    u32x4 va[4];
+  for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
-      if (ms < msub) va[ms] = *(const u32x4*)(hrow[ms]);
-    for (int s = 0; s < steps; ++s) {
-      uint16_t* sb = s_b[s & 1];
-      const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+    for (int nw = 0; nw < NW; ++nw) acc[ms][nw] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 cur[RPT];
+  if (st0 < st1) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        sb[(8 * part + q) * kDownPitch + kr] = (uint16_t)(wv[q >> 1] >> (16 * (q & 1)));
-      __syncthreads();
-      const int sn = s + 1 < steps ? s + 1 : s;
-      const u32x4 vb_next = *(const u32x4*)brow(sn);
-      u32x4 va_next[4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        if (ms < msub) va_next[ms] = *(const u32x4*)(hrow[ms] + 32 * sn);
-      const u32x4 bv = *(const u32x4*)(sb + (16 * wave + li) * kDownPitch + 8 * lg);
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        if (ms < msub) acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ms]), as_bf16x8(bv), acc[ms], 0, 0, 0);
-      vb = vb_next;
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        if (ms < msub) va[ms] = va_next[ms];
-    }
+    for (int i = 0; i < RPT; ++i) cur[i] = *(const u32x4*)brow(KS * st0 + RPT * cg + i);
   }
-  // lane holds C[token 16 ms + 4 lg + v][output 16 wave + li]
-  const int o = 64 * sl + 16 * wave + li;
+  for (int st = st0; st < st1; ++st) {
+    u32x4 nxt[RPT];
+    const int stn = st + 1 < st1 ? st + 1 : st;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) nxt[i] = *(const u32x4*)brow(KS * stn + RPT * cg + i);
+    // 4 x 8 transpose: output o gets channels RPT cg .. RPT cg + 3
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+      uint2 w;
+      const uint32_t x0 = cur[0][o >> 1], y0 = cur[1][o >> 1], x1 = cur[2][o >> 1], y1 = cur[3][o >> 1];
+      w.x = (o & 1) ? ((x0 >> 16) | (y0 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (y0 << 16));
+      w.y = (o & 1) ? ((x1 >> 16) | (y1 & 0xFFFF0000u)) : ((x1 & 0xFFFFu) | (y1 << 16));
+      *(uint2*)(s_b + (8 * og + o) * PITCH + RPT * cg) = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS / 32; ++ks) {
+      const int k0 = KS * st + 32 * ks;
+      if (k0 < K) {
+        u32x4 va[4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+          if (ms < msub) va[ms] = *(const u32x4*)(hrow[ms] + k0);
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw) {
+          const u32x4 bv = *(const u32x4*)(s_b + (16 * NW * wave + 16 * nw + li) * PITCH + 32 * ks + 8 * lg);
+#pragma unroll
+          for (int ms = 0; ms < 4; ++ms)
+            if (ms < msub)
+              acc[ms][nw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ms]), as_bf16x8(bv), acc[ms][nw], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) cur[i] = nxt[i];
+  }
+  // lane holds C[token 16 ms + 4 lg + v][output 16 NW wave + 16 nw + li]
+  float* yp = a.ypart + (size_t)kci * a.batch * a.top_e * d;
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = 16 * ms + 4 * lg + v;
-      if (ms < msub && j < n) a.ypart[(size_t)a.tpair[first + j] * d + o] = acc[ms][v];
+      if (ms < msub && j < n) {
+        float* yrow = yp + (size_t)a.tpair[first + j] * d + (size_t)SW * sl + 16 * NW * wave + li;
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw) yrow[16 * nw] = acc[ms][nw][v];
+      }
     }
 }
 
 // ===========================================================================
 // Gate-weighted sum over a token's experts, bf16 output.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   const int per_tok = (a.d + kThreads - 1) / kThreads;
   const int t = blockIdx.x / per_tok, blk = blockIdx.x % per_tok;
   const int i = blk * kThreads + threadIdx.x;
   if (i >= a.d) return;
+  const size_t kstride = (size_t)a.batch * a.top_e * a.d;
   float y = 0.0f;
   for (int s = 0; s < a.top_e; ++s) {
     const int p = t * a.top_e + s;
-    y += a.pair_w[p] * a.ypart[(size_t)p * a.d + i];
+    const float* yp = a.ypart + (size_t)p * a.d + i;
+    float v = 0.0f;
+    for (int q = 0; q < kc; ++q) v += yp[q * kstride];
+    y += a.pair_w[p] * v;
   }
   a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(y);
 }
@@ -746,6 +808,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a) {
 
 // k_select keeps m keys and m/32 bitmap words in LDS (64 KiB)
 bool grouped_supported(int d, int m) { return d >= 64 && (size_t)m * 4 + (size_t)m / 8 + 2048 <= 65536; }
+
+int grouped_down_width(int d) { return d % 256 == 0 ? 256 : 64; }
+
+int grouped_down_split(int max_tiles, int d) {
+  const int blocks = max_tiles * (d / grouped_down_width(d));
+  const int kc = (kDownTargetBlocks + blocks - 1) / blocks;
+  return kc < 1 ? 1 : (kc > kMaxDownSplit ? kMaxDownSplit : kc);
+}
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int pairs = a.batch * a.top_e;
@@ -759,9 +829,15 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   }
   hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), (size_t)(a.m / 32) * 8, stream, a, dense ? 1 : 0);
   hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  hipLaunchKernelGGL(k_down_g, dim3(a.max_tiles * (a.d / 64)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles), dim3(kThreads), 0, stream, a);
+  const int sw = grouped_down_width(a.d);
+  const int kc = grouped_down_split(a.max_tiles, a.d);
+  if (sw == 256)
+    hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
+  else
+    hipLaunchKernelGGL(k_down_g<1>, dim3(a.max_tiles * (a.d / 64) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
   const int per_tok = (a.d + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok), dim3(kThreads), 0, stream, a, kc);
   return hipGetLastError();
 }
 

@@ -85,73 +85,77 @@ def stored_traffic(name):
 
 
 class Block:
-    """`copies` prepared layers of one workload plus `ntok` distinct input batches each."""
+    """`copies` prepared layers of one workload plus `ntok` distinct input batches
+    each, at batch 1 (logits N(0, 1)) and at batch 64 (Zipf-skewed logits)."""
 
-    def __init__(self, b, synth, torch, w, copies, ntok, stream):
+    def __init__(self, b, synth, torch, w, copies, ntok, stream, big_batch=0):
         self.b, self.w, self.copies, self.ntok, self.stream = b, w, copies, ntok, stream
-        d, m, n_exp, top_e, r, batch = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"], w["batch"]
-        self.ctxs, self.xs, self.lgs, self.outs = [], [], [], []
-        self.host_layer0 = None
-        routing = w["routing"] if w["routing"] != "router" else "normal"
+        d, m, n_exp, top_e, r = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"]
+        self.ctxs, self.host_layer0 = [], None
+        self.inputs = {}  # batch -> (xs, lgs, outs) per layer copy
+        batches = [w["batch"]] + ([big_batch] if big_batch else [])
         for l in range(copies):
             wg, wu, wd = synth.layer_weights(w["wid"], l, n_exp, d, m, w["channel_scale"])
-            cfg = b.make_config(d, n_exp, m, r, top_e, batch)
+            cfg = b.make_config(d, n_exp, m, r, top_e, max(batches))
             self.ctxs.append(b.moe_sel_prepare(cfg, wg, wu, wd, stream=stream.cuda_stream))
             if l == 0:
                 self.host_layer0 = (wg, wu, wd)
             del wg, wu, wd
-            xb = np.stack([synth.tokens(w["wid"], l, batch, d, index=i) for i in range(ntok)])
-            lb = np.stack([synth.router_logits(w["wid"], l, batch, n_exp, routing, index=i) for i in range(ntok)])
-            self.xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda"))
-            self.lgs.append(torch.from_numpy(lb).to("cuda"))
-            self.outs.append(torch.zeros((batch, d), dtype=torch.int16, device="cuda"))
+            for bsz in batches:
+                wid = w["wid"] if bsz == w["batch"] else synth.WORKLOADS["qwen3_b64"]["wid"]
+                routing = "normal" if bsz == w["batch"] else "zipf"
+                xb = np.stack([synth.tokens(wid, l, bsz, d, index=i) for i in range(ntok)])
+                lb = np.stack([synth.router_logits(wid, l, bsz, n_exp, routing, index=i) for i in range(ntok)])
+                xs, lgs, outs = self.inputs.setdefault(bsz, ([], [], []))
+                xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda"))
+                lgs.append(torch.from_numpy(lb).to("cuda"))
+                outs.append(torch.zeros((bsz, d), dtype=torch.int16, device="cuda"))
 
-    def launch(self, n, k):
-        """Enqueue n forwards (k=None: the dense-read block) on the stream."""
+    def launch(self, n, k, bsz):
+        """Enqueue n forwards of `bsz` tokens (k=None: the dense-read block) on the stream."""
         b, w, s = self.b, self.w, self.stream.cuda_stream
+        xs, lgs, outs = self.inputs[bsz]
         for i in range(n):
             l, t = i % self.copies, (i // self.copies) % self.ntok
             if k is None:
-                b.moe_sel_forward_dense(self.ctxs[l], self.xs[l][t], self.lgs[l][t], w["batch"], w["top_e"],
-                                        self.outs[l], s)
+                b.moe_sel_forward_dense(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], outs[l], s)
             else:
-                b.moe_sel_forward(self.ctxs[l], self.xs[l][t], self.lgs[l][t], w["batch"], w["top_e"], k,
-                                  self.outs[l], s)
+                b.moe_sel_forward(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], k, outs[l], s)
 
     def destroy(self):
         for c in self.ctxs:
             self.b.moe_sel_destroy(c)
 
 
-def time_block(torch, blk, k, steps, warmup, eager):
+def time_block(torch, blk, k, steps, warmup, eager, bsz):
     """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones."""
     R = blk.copies * blk.ntok
     stream = blk.stream
     with torch.cuda.stream(stream):
-        blk.launch(R, k)  # eager pass over every (layer, token)
+        blk.launch(R, k, bsz)  # eager pass over every (layer, token batch)
     torch.cuda.synchronize()
     for c in blk.ctxs:
         blk.b.moe_sel_check_device(c)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if eager:
         with torch.cuda.stream(stream):
-            blk.launch(warmup, k)
+            blk.launch(warmup, k, bsz)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            blk.launch(steps, k)
+            blk.launch(steps, k, bsz)
             ev1.record(stream)
         torch.cuda.synchronize()
     else:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            blk.launch(R, k)
+            blk.launch(R, k, bsz)
         rem = steps % R
         g_rem = None
         if rem:
             g_rem = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_rem, stream=stream):
-                blk.launch(rem, k)
+                blk.launch(rem, k, bsz)
         with torch.cuda.stream(stream):
             for _ in range(max(1, math.ceil(warmup / R))):
                 g.replay()
@@ -204,6 +208,9 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run plain 256 MiB copies (known bytes) for counter scaling")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--big-batch", type=int, default=64,
+                    help="also time this many Zipf-routed tokens per call (0: skip)")
+    ap.add_argument("--big-steps", type=int, default=512)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -224,22 +231,35 @@ def main():
 
     t0 = time.time()
     stream = torch.cuda.Stream()
-    blk = Block(b, synth, torch, w, args.copies, args.tokens, stream)
+    blk = Block(b, synth, torch, w, args.copies, args.tokens, stream, args.big_batch)
     setup_s = time.time() - t0
 
-    ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager)
+    ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager, batch)
     path = b.moe_sel_last_path(blk.ctxs[0])
     single = path == b.MOE_SEL_PATH_SINGLE_LAUNCH
     extra_k = {}
     if not args.no_extra_budgets:
         for k2 in w["ks"]:
             if k2 != k:
-                ms2 = time_block(torch, blk, k2, args.steps, args.warmup, args.eager)
+                ms2 = time_block(torch, blk, k2, args.steps, args.warmup, args.eager, batch)
                 extra_k[str(k2)] = {"tokens_per_s": round(batch / (ms2 * 1e-3), 1), "ms_per_step": round(ms2, 6),
                                     "budget": round(k2 / m, 4),
                                     "achieved_GBs": round(algorithmic_bytes(d, m, n_exp, top_e, r, k2, batch)
                                                           / (ms2 * 1e-3) / 1e9, 1)}
-    ms_dense = None if args.no_dense else time_block(torch, blk, None, args.steps, args.warmup, args.eager)
+    ms_dense = None if args.no_dense else time_block(torch, blk, None, args.steps, args.warmup, args.eager, batch)
+    big = None
+    if args.big_batch:
+        bb = args.big_batch
+        ws = args.big_steps // 8
+        ms_b = time_block(torch, blk, k, args.big_steps, ws, args.eager, bb)
+        ms_bd = None if args.no_dense else time_block(torch, blk, None, args.big_steps, ws, args.eager, bb)
+        big = {"batch": bb, "routing": "Zipf(1.1)", "k": k, "steps": args.big_steps,
+               "tokens_per_s": round(bb / (ms_b * 1e-3), 1), "ms_per_step": round(ms_b, 6),
+               "path": "expert-grouped multi-kernel"}
+        if ms_bd is not None:
+            big["dense_tokens_per_s"] = round(bb / (ms_bd * 1e-3), 1)
+            big["dense_ms_per_step"] = round(ms_bd, 6)
+            big["speedup_vs_dense"] = round(ms_bd / ms_b, 3)
     ceiling = copy_ceiling(torch, stream)
     if args.traffic_probe:
         src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(2.0)
@@ -293,6 +313,8 @@ def main():
     }
     if extra_k:
         result["other_budgets"] = extra_k
+    if big is not None:
+        result["batch64" if big["batch"] == 64 else f"batch{big['batch']}"] = big
     if ms_dense is not None:
         dense_gbs = bytes_dense / (ms_dense * 1e-3) / 1e9
         result["dense"] = {

@@ -133,12 +133,14 @@ def test_batch_rows_match_single_token_calls(b, torch, tiny, bsz):
     selb = b.moe_sel_debug_selection(tiny.ctx, bsz, tiny.top_e, k, tiny.m, with_scores=False)
     ref = tiny.oracle.forward(x, logits, tiny.top_e, k)
     _check_selection(b, tiny, ref, bsz, tiny.top_e, k)
+    assert rel_err(oracle.bf16_bits_to_f64(outb.view(np.uint16)), ref["y"]) <= TOL
     for t in (0, 5):
         out1 = _run(b, torch, tiny, x[t:t + 1], logits[t:t + 1], k).cpu().numpy()
         sel1 = b.moe_sel_debug_selection(tiny.ctx, 1, tiny.top_e, k, tiny.m, with_scores=False)
         assert np.array_equal(sel1["chan_idx"][0], selb["chan_idx"][t])
-        if b.moe_sel_last_path(tiny.ctx) == path_b:
-            assert np.array_equal(out1[0], outb[t])      # same path: same summation order
+        if b.moe_sel_last_path(tiny.ctx) == path_b == b.MOE_SEL_PATH_SINGLE_LAUNCH:
+            # one block sums a token's terms in the same order at every batch size
+            assert np.array_equal(out1[0], outb[t])
         else:
             o1 = oracle.bf16_bits_to_f64(out1[0].view(np.uint16))
             ob = oracle.bf16_bits_to_f64(outb[t].view(np.uint16))
