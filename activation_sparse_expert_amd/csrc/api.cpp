@@ -408,7 +408,8 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   // partial outputs: the largest split times the pairs of any call size
   size_t ypart_count = 0;
   for (int pp = 1; pp <= c.max_batch * c.max_top_e; ++pp) {
-    const size_t need = (size_t)moe_sel::grouped_down_split(moe_sel::grouped_max_tiles(pp, c.n_experts), c.d) * pp * d;
+    const size_t need =
+        (size_t)moe_sel::grouped_down_split(moe_sel::grouped_max_tiles(pp, c.n_experts), c.d, c.m, c.rank) * pp * d;
     ypart_count = std::max(ypart_count, need);
   }
   ALLOC(ypart, ypart_count);

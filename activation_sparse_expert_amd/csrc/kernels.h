@@ -36,7 +36,7 @@ struct FwdArgs {
   int* xqsum;              // [B] sum of the int8 activations
   int* tile_expert;        // [max_tiles]
   int* tile_first;         // [max_tiles] offset into tpair
-  int* tile_n;             // [max_tiles] tokens in the tile (1..64)
+  int* tile_n;             // [max_tiles] tokens in the tile (1..kTileTokens)
   int* n_tiles;            // [1]
   int* tpair;              // [P] pair indices sorted by (expert, token)
   uint32_t* selbits;       // [P][m/32] selected channels of each pair
@@ -50,7 +50,7 @@ struct FwdArgs {
 };
 
 // expert tiles hold up to this many tokens
-constexpr int kTileTokens = 64;
+constexpr int kTileTokens = 32;
 inline int grouped_max_tiles(int pairs, int n_experts) {
   const int bound = pairs / kTileTokens + (pairs < n_experts ? pairs : n_experts);
   return pairs < bound ? pairs : bound;
@@ -59,9 +59,10 @@ inline int grouped_kpad(int m, int r) { return (m + r + 31) / 32 * 32; }
 bool grouped_supported(int d, int m);
 // down projection: outputs per block, and the split of its K range over blocks
 constexpr int kDownTargetBlocks = 1024;
-constexpr int kMaxDownSplit = 16;
+constexpr int kDownMaxStages = 8;
+constexpr int kMaxDownSplit = 64;
 int grouped_down_width(int d);
-int grouped_down_split(int max_tiles, int d);
+int grouped_down_split(int max_tiles, int d, int m, int r);
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 

@@ -3,7 +3,7 @@
 //
 // Used for batches above the single-launch limit and for shapes the single
 // launch does not cover (large m). The (token, expert) pairs of a call are
-// grouped by expert into tiles of up to 64 tokens, so every weight byte an
+// grouped by expert into tiles of up to 32 tokens, so every weight byte an
 // expert needs is read once per tile, not once per token: the sketch codes once
 // per tile, and each channel row once per tile when at least one of the tile's
 // tokens selected it (the union of the tokens' selections). Each token still
@@ -33,6 +33,7 @@
 //   combine         per token: gate-weighted sum over its experts, bf16 output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "device_common.h"
@@ -49,7 +50,8 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-constexpr int kT = kTileTokens;  // tokens per tile (4 MFMA subtiles of 16)
+constexpr int kT = kTileTokens;  // tokens per tile
+constexpr int kMSub = kT / 16;   // MFMA subtiles of 16 tokens
 constexpr int kCh = 16;          // union channels per gate/up block
 constexpr int kPlanThreads = 1024;
 constexpr int kDownPitch = 40;   // halfwords per LDS row of the transposed down tile (80 bytes)
@@ -269,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
   float* s_h = s_dyn_score;
   float* s_q = s_dyn_score + kT * 64;
 
-  const int8_t* xr[4];
+  const int8_t* xr[kMSub];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
+  for (int ns = 0; ns < kMSub; ++ns) {
     const int j = 16 * ns + li;
     const int pp = a.tpair[first + (j < n ? j : 0)];
     xr[ns] = a.xq + (size_t)(pp / a.top_e) * d + 16 * lg;
@@ -446,8 +448,7 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
 
 // ===========================================================================
 // Union of a tile's selections: ascending channel list and, per listed
-// channel, the mask of the tile's tokens that selected it. Also the sum over
-// groups of Q^T h_hat per token (z over all channels). One block per tile.
+// channel, the mask of the tile's tokens that selected it. One block per tile.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
   extern __shared__ uint32_t s_dyn_u[];  // union words [m/32], their exclusive popcount offsets [m/32]
@@ -503,16 +504,6 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     }
   }
   if (tid == 0) a.ucount[tile] = run;
-  const int r = a.r, groups = m / kGroup;
-  if (r > 0)
-    for (int i = tid; i < n * r; i += kThreads) {
-      const int j = i / r, c = i % r;
-      const int pp = a.tpair[first + j];
-      const float* zp = a.gzpart + (size_t)pp * groups * r + c;
-      float z = 0.0f;
-      for (int g = 0; g < groups; ++g) z += zp[(size_t)g * r];
-      a.zvec[(size_t)pp * r + c] = z;
-    }
 }
 
 // ===========================================================================
@@ -546,9 +537,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   const int ja = uc > 0 ? ul[pos_a] : 0;
   const uint16_t* grow = a.wch + ((size_t)e * m + ja) * 3 * d + 8 * lg;
   const uint16_t* urow = grow + d;
-  const uint16_t* xr[4];
+  const uint16_t* xr[kMSub];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
+  for (int ns = 0; ns < kMSub; ++ns) {
     const int j = 16 * ns + li;
     const int pp = a.tpair[first + (j < n ? j : 0)];
     xr[ns] = a.x + (size_t)(pp / a.top_e) * d + 8 * lg;
@@ -637,36 +628,41 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
 }
 
 // ===========================================================================
-// Per tile, after gate/up: z = Q^T h_hat over each token's skipped channels
-// (the all-channel sum minus the gate/up blocks' selected-channel shares, in
-// block order) into the activation columns after the union, then zeros up to
-// the next multiple of 32 columns.
+// After gate/up, one 64-thread block per (tile, token): z = Q^T h_hat over the
+// token's skipped channels, i.e. the score blocks' per-group shares (all
+// channels) minus the gate/up blocks' selected-channel shares, each summed in
+// block order, written to the activation columns after the union; then zeros
+// up to the next multiple of 32 columns.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_zfin(FwdArgs a) {
-  const int tile = blockIdx.x;
-  if (tile >= *a.n_tiles) return;
-  const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad;
+template <int N>
+__device__ __forceinline__ float sum_strided(const float* p, size_t stride, int count) {
+  float s = 0.0f;
+  int q = 0;
+  for (; q + N <= count; q += N) {
+    float part[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) part[u] = p[(size_t)(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < N; ++u) s += part[u];
+  }
+  for (; q < count; ++q) s += p[(size_t)q * stride];
+  return s;
+}
+
+__global__ __launch_bounds__(64) void k_zfin(FwdArgs a) {
+  const int tile = blockIdx.x / kT, j = blockIdx.x % kT;
+  if (tile >= *a.n_tiles || j >= a.tile_n[tile]) return;
+  const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad, groups = m / kGroup;
   const int uc = a.ucount[tile];
   const int nch = max(1, (uc + kCh - 1) / kCh);
-  const int first = a.tile_first[tile], n = a.tile_n[tile];
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
-  for (int i = threadIdx.x; i < n * (kend - uc); i += kThreads) {
-    const int j = i / (kend - uc), c = i % (kend - uc);
-    const int pp = a.tpair[first + j];
+  const int pp = a.tpair[a.tile_first[tile] + j];
+  for (int c = threadIdx.x; c < kend - uc; c += 64) {
     float z = 0.0f;
     if (c < r && !all_kept) {
-      const float* zs = a.zsel + (size_t)pp * maxch * r + c;
-      z = a.zvec[(size_t)pp * r + c];
-      int q = 0;
-      for (; q + 8 <= nch; q += 8) {
-        float part[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) part[u] = zs[(size_t)(q + u) * r];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) z -= part[u];
-      }
-      for (; q < nch; ++q) z -= zs[(size_t)q * r];
+      z = sum_strided<12>(a.gzpart + (size_t)pp * groups * r + c, r, groups);
+      z -= sum_strided<16>(a.zsel + (size_t)pp * maxch * r + c, r, nch);
     }
     a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(z);
   }
@@ -716,15 +712,15 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     if (k < uc) return a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d + col;
     return a.pmat + ((size_t)e * a.r + (k - uc)) * d + col;
   };
-  const uint16_t* hrow[4];
+  const uint16_t* hrow[kMSub];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
+  for (int ms = 0; ms < kMSub; ++ms) {
     const int j = 16 * ms + li;
     hrow[ms] = a.hbuf + (size_t)a.tpair[first + (j < n ? j : 0)] * kpad + 8 * lg;
   }
-  f32x4 acc[4][NW];
+  f32x4 acc[kMSub][NW];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms)
+  for (int ms = 0; ms < kMSub; ++ms)
 #pragma unroll
     for (int nw = 0; nw < NW; ++nw) acc[ms][nw] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 cur[RPT];
@@ -751,15 +747,15 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     for (int ks = 0; ks < KS / 32; ++ks) {
       const int k0 = KS * st + 32 * ks;
       if (k0 < K) {
-        u32x4 va[4];
+        u32x4 va[kMSub];
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+        for (int ms = 0; ms < kMSub; ++ms)
           if (ms < msub) va[ms] = *(const u32x4*)(hrow[ms] + k0);
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
           const u32x4 bv = *(const u32x4*)(s_b + (16 * NW * wave + 16 * nw + li) * PITCH + 32 * ks + 8 * lg);
 #pragma unroll
-          for (int ms = 0; ms < 4; ++ms)
+          for (int ms = 0; ms < kMSub; ++ms)
             if (ms < msub)
               acc[ms][nw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ms]), as_bf16x8(bv), acc[ms][nw], 0, 0, 0);
         }
@@ -772,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   // lane holds C[token 16 ms + 4 lg + v][output 16 NW wave + 16 nw + li]
   float* yp = a.ypart + (size_t)kci * a.batch * a.top_e * d;
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms)
+  for (int ms = 0; ms < kMSub; ++ms)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = 16 * ms + 4 * lg + v;
@@ -811,9 +807,14 @@ bool grouped_supported(int d, int m) { return d >= 64 && (size_t)m * 4 + (size_t
 
 int grouped_down_width(int d) { return d % 256 == 0 ? 256 : 64; }
 
-int grouped_down_split(int max_tiles, int d) {
-  const int blocks = max_tiles * (d / grouped_down_width(d));
-  const int kc = (kDownTargetBlocks + blocks - 1) / blocks;
+int grouped_down_split(int max_tiles, int d, int m, int r) {
+  const int sw = grouped_down_width(d);
+  const int blocks = max_tiles * (d / sw);
+  int kc = (kDownTargetBlocks + blocks - 1) / blocks;
+  // no block takes more than kDownMaxStages stages of the longest tile
+  const int ks = sw == 256 ? 32 : 128;
+  const int nst_max = (m + r + ks - 1) / ks;
+  kc = std::max(kc, (nst_max + kDownMaxStages - 1) / kDownMaxStages);
   return kc < 1 ? 1 : (kc > kMaxDownSplit ? kMaxDownSplit : kc);
 }
 
@@ -829,9 +830,9 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   }
   hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), (size_t)(a.m / 32) * 8, stream, a, dense ? 1 : 0);
   hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles), dim3(kThreads), 0, stream, a);
+  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(64), 0, stream, a);
   const int sw = grouped_down_width(a.d);
-  const int kc = grouped_down_split(a.max_tiles, a.d);
+  const int kc = grouped_down_split(a.max_tiles, a.d, a.m, dense ? 0 : a.r);
   if (sw == 256)
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
   else

@@ -333,9 +333,10 @@ def test_graph_replay_matches_eager_multi_kernel(b, torch, tiny_layer):
     b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
 
 
-def test_tiles_split_beyond_64_tokens_per_expert(b, torch):
-    """200 tokens over 8 experts (top-2): experts receive more than 64 tokens, so
-    their pairs span several tiles; every token still matches the oracle."""
+def test_tiles_split_across_many_tokens_per_expert(b, torch):
+    """200 tokens over 8 experts (top-2): experts receive more tokens than one
+    expert tile holds, so their pairs span several tiles; every token still
+    matches the oracle."""
     lay = Layer(b, "tiny", max_batch=200)
     try:
         rng = np.random.default_rng(13)
