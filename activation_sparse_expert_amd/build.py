@@ -30,6 +30,7 @@ HOST_EXACT = ["-ffp-contract=off", "-fno-fast-math", "-march=x86-64-v3"]
 SOURCES = [
     ("kernels.hip", DEVICE),
     ("fused.hip", DEVICE),
+    ("lowrank_device.hip", DEVICE),
     ("api.cpp", DEVICE),
     ("prepare_host.cpp", HOST_EXACT),
 ]

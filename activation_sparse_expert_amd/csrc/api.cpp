@@ -108,8 +108,19 @@ void free_ctx(moe_sel_ctx* c) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The rank-r maps of large experts are built on the device (fp64), small ones
+// on the host; MOE_SEL_LOWRANK=host or =device forces one of the two.
+bool lowrank_on_device(const moe_sel_config& c) {
+  if (c.rank <= 0) return false;
+  const char* env = std::getenv("MOE_SEL_LOWRANK");
+  if (env && std::strcmp(env, "host") == 0) return false;
+  if (env && std::strcmp(env, "device") == 0) return true;
+  return std::min(c.d, c.m) > 1024;
+}
+
 struct PrepJob {
   const moe_sel_config* cfg;
+  bool host_lowrank;
   const uint16_t *wg, *wu, *wd;
   uint32_t* codes;
   float* stats;
@@ -127,7 +138,7 @@ void prep_one(int e, void* arg) {
   out.codes = j->codes + (size_t)e * moe_sel::codes_dwords_per_expert(c.d, c.m);
   out.stats = j->stats + (size_t)e * c.m * 4;
   out.wch = j->wch + (size_t)e * 3 * md;
-  if (c.rank > 0) {
+  if (c.rank > 0 && j->host_lowrank) {
     out.p_bf16 = j->pmat + (size_t)e * c.rank * c.d;
     out.q_bf16 = j->qmat + (size_t)e * c.m * c.rank;
   }
@@ -381,7 +392,9 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
   }
   std::vector<std::string> errors(E);
-  PrepJob job{&c, w_gate, w_up, w_down, h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
+  const bool dev_lowrank = lowrank_on_device(c);
+  PrepJob job{&c, !dev_lowrank, w_gate, w_up, w_down, h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(),
+              h_q.data(), &errors};
   moe_sel::parallel_for((int)E, 0, prep_one, &job);
   for (size_t e = 0; e < E; ++e)
     if (!errors[e].empty()) {
@@ -461,7 +474,19 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
              {ctx->wch, h_wch.data(), h_wch.size() * 2},
              {ctx->pmat, h_p.data(), h_p.size() * 2},
              {ctx->qmat, h_q.data(), h_q.size() * 2}};
-  for (const Up& u : ups) {
+  for (int ui = 0; ui < 5; ++ui) {
+    const Up& u = ups[ui];
+    if (ui == 3 && dev_lowrank) {
+      // maps from the channel rows now on the device, one expert at a time
+      for (size_t ex = 0; ex < E; ++ex) {
+        const std::string err = moe_sel::lowrank_map_device(ctx->wch + ex * m * 3 * d, c.d, c.m, c.rank,
+                                                            h_p.data() + ex * r * d, h_q.data() + ex * m * r, s);
+        if (!err.empty()) {
+          free_ctx(ctx);
+          return fail(MOE_SEL_EDEVICE, "expert " + std::to_string(ex) + ": " + err);
+        }
+      }
+    }
     he = hipMemcpyAsync(u.dst, u.src, u.bytes, hipMemcpyHostToDevice, s);
     if (he != hipSuccess) {
       free_ctx(ctx);

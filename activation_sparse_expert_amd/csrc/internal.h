@@ -5,6 +5,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "moe_sel.h"
 
@@ -59,6 +60,22 @@ struct ExpertPrep {
   uint16_t* p_bf16 = nullptr;    // [r][d]
   uint16_t* q_bf16 = nullptr;    // [m][r]
 };
+
+// Symmetric eigen-solver pieces (Golub & Van Loan): the Householder
+// tridiagonal form of an n x n matrix, and the top-r eigenpairs from it.
+struct Tridiag {
+  std::vector<double> diag, off;  // off[i] couples i and i+1
+  std::vector<double> beta;       // reflector k acts on indices k+1..n-1
+};
+void eigvecs_from_tridiag(const double* refl, int n, int r, const Tridiag& T, std::vector<double>& vecs,
+                          std::vector<double>& vals);
+
+// Rank-r map of one expert built on the device in fp64 (Gram matrix,
+// tridiagonalisation and projection on the GPU; the tridiagonal eigen-solve on
+// the host). wch_dev: the expert's channel-major rows on the device. Outputs are
+// host arrays P^T [r][d] and Q [m][r] in bf16. Empty string on success.
+std::string lowrank_map_device(const uint16_t* wch_dev, int d, int m, int r, uint16_t* p_out, uint16_t* q_out,
+                               void* stream);
 
 // Returns an empty string on success, else the failure message.
 std::string prepare_expert(const moe_sel_config& cfg, const uint16_t* w_gate, const uint16_t* w_up,

@@ -175,11 +175,6 @@ float column_norm(const uint16_t* wd, int d, int m, int j) {
 // tridiagonalisation, bisection on Sturm counts, inverse iteration with full
 // re-orthogonalisation, back-transformation).
 // ---------------------------------------------------------------------------
-struct Tridiag {
-  std::vector<double> diag, off;     // off[i] couples i and i+1
-  std::vector<double> beta;          // reflector k acts on indices k+1..n-1
-};
-
 // A (n x n, row-major, symmetric, overwritten with reflectors in rows k: A[k][k+1..]).
 void tridiagonalize(std::vector<double>& A, int n, Tridiag& T) {
   T.diag.assign(n, 0.0);
@@ -278,10 +273,14 @@ void tridiag_solve(const Tridiag& T, double lam, double tiny, std::vector<double
   for (int i = n - 3; i >= 0; --i) b[i] = (b[i] - du[i] * b[i + 1] - du2[i] * b[i + 2]) / dd[i];
 }
 
-// Top-r eigenvectors (columns of vecs, n x r row-major) of the symmetric matrix A.
-void top_eigvecs(std::vector<double>& A, int n, int r, std::vector<double>& vecs, std::vector<double>& vals) {
-  Tridiag T;
-  tridiagonalize(A, n, T);
+}  // namespace
+
+// Top-r eigenpairs from the tridiagonal form T and the reflectors stored in the
+// rows of refl (row k, columns k+1..n-1): bisection on Sturm counts, inverse
+// iteration with full re-orthogonalisation, then back-transformation of all r
+// vectors together.
+void eigvecs_from_tridiag(const double* refl, int n, int r, const Tridiag& T, std::vector<double>& vecs,
+                          std::vector<double>& vals) {
   double tnorm = 0.0;
   for (int i = 0; i < n; ++i) {
     double s = std::fabs(T.diag[i]);
@@ -333,22 +332,38 @@ void top_eigvecs(std::vector<double>& A, int n, int r, std::vector<double>& vecs
       for (int j = 0; j < n; ++j) y[j] /= nrm;
     }
   }
-  // back-transform: x = H_0 H_1 ... H_{n-3} y
+  // back-transform all vectors: Y = H_0 H_1 ... H_{n-3} Y, with Y n x r row-major
   vecs.assign((size_t)n * r, 0.0);
-  for (int i = 0; i < r; ++i) {
-    std::vector<double>& y = ys[i];
-    for (int k = n - 3; k >= 0; --k) {
-      const double beta = T.beta[k];
-      if (beta == 0.0) continue;
-      const double* v = &A[(size_t)k * n + k + 1];
-      const int len = n - k - 1;
-      double dot = 0.0;
-      for (int j = 0; j < len; ++j) dot += v[j] * y[k + 1 + j];
-      dot *= beta;
-      for (int j = 0; j < len; ++j) y[k + 1 + j] -= dot * v[j];
+  for (int i = 0; i < r; ++i)
+    for (int j = 0; j < n; ++j) vecs[(size_t)j * r + i] = ys[i][j];
+  std::vector<double> dots(r);
+  for (int k = n - 3; k >= 0; --k) {
+    const double beta = T.beta[k];
+    if (beta == 0.0) continue;
+    const double* v = refl + (size_t)k * n + k + 1;
+    const int len = n - k - 1;
+    std::fill(dots.begin(), dots.end(), 0.0);
+    for (int j = 0; j < len; ++j) {
+      const double vj = v[j];
+      const double* yrow = &vecs[(size_t)(k + 1 + j) * r];
+      for (int c = 0; c < r; ++c) dots[c] += vj * yrow[c];
     }
-    for (int j = 0; j < n; ++j) vecs[(size_t)j * r + i] = y[j];
+    for (int c = 0; c < r; ++c) dots[c] *= beta;
+    for (int j = 0; j < len; ++j) {
+      const double vj = v[j];
+      double* yrow = &vecs[(size_t)(k + 1 + j) * r];
+      for (int c = 0; c < r; ++c) yrow[c] -= vj * dots[c];
+    }
   }
+}
+
+namespace {
+
+// Top-r eigenvectors (columns of vecs, n x r row-major) of the symmetric matrix A.
+void top_eigvecs(std::vector<double>& A, int n, int r, std::vector<double>& vecs, std::vector<double>& vals) {
+  Tridiag T;
+  tridiagonalize(A, n, T);
+  eigvecs_from_tridiag(A.data(), n, r, T, vecs, vals);
 }
 
 // P^T [r][d] and Q [m][r] with P Q^T = best rank-r approximation of W [d][m].

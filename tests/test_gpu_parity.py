@@ -378,3 +378,29 @@ def test_qwen3_batch64_zipf_parity(b, torch):
         assert err <= TOL
     finally:
         lay.close()
+
+
+@pytest.fixture(scope="module")
+def mixtral(b, torch):
+    """Two Mixtral-8x7B-shaped experts (d=4096, m=14336, r=64, per-channel
+    LogNormal scales); with top-2 routing both are routed for every token."""
+    lay = Layer(b, "mixtral", max_batch=1, n_experts=2)
+    yield lay
+    lay.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", [1864, 2580])
+def test_mixtral_shape_parity(b, torch, mixtral, k):
+    w = synth.WORKLOADS["mixtral"]
+    x = synth.tokens(w["wid"], 0, 1, mixtral.d)
+    logits = synth.router_logits(w["wid"], 0, 1, mixtral.E)
+    mixtral.path = None
+    out = _run(b, torch, mixtral, x, logits, k)
+    assert b.moe_sel_last_path(mixtral.ctx) == b.MOE_SEL_PATH_MULTI_KERNEL
+    ref = mixtral.oracle.forward(x, logits, mixtral.top_e, k)
+    _check_selection(b, mixtral, ref, 1, mixtral.top_e, k)
+    err = rel_err(out_to_f64(torch, out), ref["y"])
+    print(f"mixtral k={k}: max-rel-err {err:.2e}")
+    assert err <= TOL
+    assert abs(k / mixtral.m - {1864: 0.13, 2580: 0.18}[k]) <= 1 / (2 * mixtral.m)
