@@ -62,7 +62,8 @@ constexpr int kDownTargetBlocks = 1024;
 constexpr int kDownMaxStages = 8;
 constexpr int kMaxDownSplit = 64;
 int grouped_down_width(int d);
-int grouped_down_split(int max_tiles, int d, int m, int r);
+// kmax: the largest union of channels a tile of the call can hold
+int grouped_down_split(int max_tiles, int d, int kmax, int r);
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 

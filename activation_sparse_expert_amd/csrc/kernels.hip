@@ -87,6 +87,18 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   __shared__ uint32_t s_amax[kWaves];
   __shared__ int s_qs[kWaves];
 
+  // the token's activations, 16-byte pieces in registers (d <= 16384), in flight
+  // while the experts are chosen
+  constexpr int kXP = 8;
+  const int npc = a.d / 8;
+  const uint16_t* x = a.x + (size_t)t * a.d;
+  uint4 xv[kXP];
+#pragma unroll
+  for (int u = 0; u < kXP; ++u) {
+    const int pc = tid + u * kThreads;
+    xv[u] = pc < npc ? *(const uint4*)(x + 8 * pc) : make_uint4(0, 0, 0, 0);
+  }
+
   // top_e experts: repeated block arg-max, larger logit first, lower index on ties
   const float* L = a.logits + (size_t)t * a.n_experts;
   constexpr int kMaxPer = 4;  // n_experts <= 1024
@@ -150,9 +162,13 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   }
 
   // int8 activations with a power-of-two scale, and their sum
-  const uint16_t* x = a.x + (size_t)t * a.d;
   uint32_t amax = 0;
-  for (int i = tid; i < a.d; i += kThreads) amax = max(amax, (uint32_t)(x[i] & 0x7FFFu));
+#pragma unroll
+  for (int u = 0; u < kXP; ++u) {
+    const uint32_t w4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) amax = max(amax, max(w4[h] & 0x7FFFu, (w4[h] >> 16) & 0x7FFFu));
+  }
   amax = wave_max_u(amax);
   if (lane == 0) s_amax[wave] = amax;
   __syncthreads();
@@ -169,11 +185,22 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
   if (tid == 0) a.xexp[t] = e;
   int8_t* q = a.xq + (size_t)t * a.d;
   int qs = 0;
-  for (int i = tid; i < a.d; i += kThreads) {
-    const float xv = __uint_as_float((uint32_t)x[i] << 16);
-    const int qi = amax ? (int)__builtin_rintf(__builtin_ldexpf(xv, -e)) : 0;
-    q[i] = (int8_t)qi;
-    qs += qi;
+#pragma unroll
+  for (int u = 0; u < kXP; ++u) {
+    const int pc = tid + u * kThreads;
+    if (pc < npc) {
+      const uint32_t w4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t bits = (w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+        const float xf = __uint_as_float(bits << 16);
+        const int qi = amax ? (int)__builtin_rintf(__builtin_ldexpf(xf, -e)) : 0;
+        qs += qi;
+        packed[h >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (h & 3));
+      }
+      *(uint2*)(q + 8 * pc) = make_uint2(packed[0], packed[1]);
+    }
   }
   qs = wave_sum_i(qs);
   if (lane == 0) s_qs[wave] = qs;
@@ -421,25 +448,32 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
       krem -= s_gt;
       __syncthreads();
     }
-    // prefix is the k-th largest key; take every larger key and the krem lowest-index equal keys
-    int run_eq = 0, run_sel = 0;
-    for (int base = 0; base < m; base += kThreads) {
-      const int j = base + tid;
-      const uint32_t key = j < m ? s_keys[j] : 0u;
-      const bool gt = j < m && key > prefix;
-      const bool eq = j < m && key == prefix;
-      int eq_tot, sel_tot;
-      const int eq_before = block_excl_count(eq, s_tmp, &eq_tot);
-      const bool take = gt || (eq && run_eq + eq_before < krem);
-      const int sel_before = block_excl_count(take, s_tmp, &sel_tot);
+    // prefix is the k-th largest key; take every larger key and the krem lowest-index
+    // equal keys. Thread t owns keys [t per, (t + 1) per), so one scan of the equal
+    // counts and one of the taken counts place every index in ascending order.
+    const int per = (m + kThreads - 1) / kThreads;
+    const int j0 = min(m, tid * per), j1 = min(m, j0 + per);
+    int ngt = 0, neq = 0;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = s_keys[j];
+      ngt += key > prefix;
+      neq += key == prefix;
+    }
+    int eq_tot, sel_tot;
+    const int eq_before = block_excl_scan(neq, s_tmp, &eq_tot);
+    const int take_eq = max(0, min(neq, krem - eq_before));
+    int pos = block_excl_scan(ngt + take_eq, s_tmp, &sel_tot);
+    int eq_seen = 0;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = s_keys[j];
+      bool take = key > prefix;
+      if (key == prefix) take = eq_seen++ < take_eq;
       if (take) {
-        idx_out[run_sel + sel_before] = j;
+        idx_out[pos++] = j;
         atomicOr(&s_bits[j >> 5], 1u << (j & 31));
       }
-      run_eq += eq_tot;
-      run_sel += sel_tot;
     }
-    count = run_sel;
+    count = sel_tot;
   }
   __syncthreads();
   if (tid == 0) a.sel_count[p] = count;
@@ -451,7 +485,6 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
 // channel, the mask of the tile's tokens that selected it. One block per tile.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
-  extern __shared__ uint32_t s_dyn_u[];  // union words [m/32], their exclusive popcount offsets [m/32]
   __shared__ int s_tmp[kWaves];
   const int tile = blockIdx.x;
   if (tile >= *a.n_tiles) return;
@@ -469,39 +502,35 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     if (tid == 0) a.ucount[tile] = m;
     return;
   }
-  uint32_t* s_u = s_dyn_u;
-  int* s_pos = (int*)(s_dyn_u + words);
-  // lane i < n holds token i's word of the selection bitmap
-  const uint32_t* sb = a.selbits + (size_t)a.tpair[first + (lane < n ? lane : 0)] * words;
-  for (int w = wave; w < words; w += kWaves) {
-    const uint32_t v = lane < n ? sb[w] : 0u;
-    const uint32_t u = wave_or(v);
-    if (lane == 0) s_u[w] = u;
-  }
+  // one thread per bitmap word: the tokens' words, their union, then the listed
+  // channels of the word with their token masks at exclusive-scan positions
+  __shared__ int s_p[kT];
+  if (tid < n) s_p[tid] = a.tpair[first + tid];
   __syncthreads();
   int run = 0;
   for (int base = 0; base < words; base += kThreads) {
     const int w = base + tid;
-    const int c = w < words ? __popc(s_u[w]) : 0;
+    uint32_t v[kT];
+    uint32_t u = 0;
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      v[i] = (i < n && w < words) ? a.selbits[(size_t)s_p[i] * words + w] : 0u;
+      u |= v[i];
+    }
     int tot;
-    const int ex = block_excl_scan(c, s_tmp, &tot);
-    if (w < words) s_pos[w] = run + ex;
+    int pos = run + block_excl_scan(__popc(u), s_tmp, &tot);
+    uint32_t rest = u;
+    while (rest) {
+      const int bit = __ffs(rest) - 1;
+      rest &= rest - 1u;
+      uint64_t mk = 0;
+#pragma unroll
+      for (int i = 0; i < kT; ++i) mk |= (uint64_t)((v[i] >> bit) & 1u) << i;
+      ul[pos] = 32 * w + bit;
+      um[pos] = mk;
+      ++pos;
+    }
     run += tot;
-  }
-  __syncthreads();
-  for (int w = wave; w < words; w += kWaves) {
-    const uint32_t v = lane < n ? sb[w] : 0u;
-    const uint32_t u = s_u[w];
-    uint64_t mine = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const uint64_t mk = __ballot((v >> bit) & 1u);
-      if (lane == bit) mine = mk;
-    }
-    if (lane < 32 && ((u >> lane) & 1u)) {
-      const int pos = s_pos[w] + __popc(u & ((1u << lane) - 1u));
-      ul[pos] = 32 * w + lane;
-      um[pos] = mine;
-    }
   }
   if (tid == 0) a.ucount[tile] = run;
 }
@@ -628,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
 }
 
 // ===========================================================================
-// After gate/up, one 64-thread block per (tile, token): z = Q^T h_hat over the
+// After gate/up, one block per (tile, token): z = Q^T h_hat over the
 // token's skipped channels, i.e. the score blocks' per-group shares (all
 // channels) minus the gate/up blocks' selected-channel shares, each summed in
 // block order, written to the activation columns after the union; then zeros
@@ -649,7 +678,8 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
   return s;
 }
 
-__global__ __launch_bounds__(64) void k_zfin(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_zfin(FwdArgs a) {
+  __shared__ float s_part[kWaves][64];
   const int tile = blockIdx.x / kT, j = blockIdx.x % kT;
   if (tile >= *a.n_tiles || j >= a.tile_n[tile]) return;
   const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad, groups = m / kGroup;
@@ -658,13 +688,23 @@ __global__ __launch_bounds__(64) void k_zfin(FwdArgs a) {
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
   const int pp = a.tpair[a.tile_first[tile] + j];
-  for (int c = threadIdx.x; c < kend - uc; c += 64) {
+  // wave q sums its quarter of the groups and of the gate/up blocks
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g0 = groups * q / kWaves, g1 = groups * (q + 1) / kWaves;
+  const int c0 = nch * q / kWaves, c1 = nch * (q + 1) / kWaves;
+  const float* gz = a.gzpart + (size_t)pp * groups * r;
+  const float* zs = a.zsel + (size_t)pp * maxch * r;
+  for (int cb = 0; cb < kend - uc; cb += 64) {
+    const int c = cb + lane;
     float z = 0.0f;
-    if (c < r && !all_kept) {
-      z = sum_strided<12>(a.gzpart + (size_t)pp * groups * r + c, r, groups);
-      z -= sum_strided<16>(a.zsel + (size_t)pp * maxch * r + c, r, nch);
-    }
-    a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(z);
+    if (c < r && !all_kept)
+      z = sum_strided<12>(gz + (size_t)g0 * r + c, r, g1 - g0) - sum_strided<16>(zs + (size_t)c0 * r + c, r, c1 - c0);
+    s_part[q][lane] = z;
+    __syncthreads();
+    if (q == 0 && c < kend - uc)
+      a.hbuf[(size_t)pp * kpad + uc + c] =
+          f32_to_bf16_dev((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]));
+    __syncthreads();
   }
 }
 
@@ -792,10 +832,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   float y = 0.0f;
   for (int s = 0; s < a.top_e; ++s) {
     const int p = t * a.top_e + s;
-    const float* yp = a.ypart + (size_t)p * a.d + i;
-    float v = 0.0f;
-    for (int q = 0; q < kc; ++q) v += yp[q * kstride];
-    y += a.pair_w[p] * v;
+    y += a.pair_w[p] * sum_strided<16>(a.ypart + (size_t)p * a.d + i, kstride, kc);
   }
   a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(y);
 }
@@ -807,13 +844,13 @@ bool grouped_supported(int d, int m) { return d >= 64 && (size_t)m * 4 + (size_t
 
 int grouped_down_width(int d) { return d % 256 == 0 ? 256 : 64; }
 
-int grouped_down_split(int max_tiles, int d, int m, int r) {
+int grouped_down_split(int max_tiles, int d, int kmax, int r) {
   const int sw = grouped_down_width(d);
   const int blocks = max_tiles * (d / sw);
   int kc = (kDownTargetBlocks + blocks - 1) / blocks;
   // no block takes more than kDownMaxStages stages of the longest tile
   const int ks = sw == 256 ? 32 : 128;
-  const int nst_max = (m + r + ks - 1) / ks;
+  const int nst_max = (kmax + r + ks - 1) / ks;
   kc = std::max(kc, (nst_max + kDownMaxStages - 1) / kDownMaxStages);
   return kc < 1 ? 1 : (kc > kMaxDownSplit ? kMaxDownSplit : kc);
 }
@@ -828,11 +865,13 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads), score_lds, stream, a);
     hipLaunchKernelGGL(k_select, dim3(pairs), dim3(kThreads), (size_t)(a.m + a.m / 32) * 4, stream, a);
   }
-  hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), (size_t)(a.m / 32) * 8, stream, a, dense ? 1 : 0);
+  hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(64), 0, stream, a);
+  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
-  const int kc = grouped_down_split(a.max_tiles, a.d, a.m, dense ? 0 : a.r);
+  // the largest union a tile can have: k channels per token, at most m
+  const int kmax = dense ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
+  const int kc = grouped_down_split(a.max_tiles, a.d, kmax, dense ? 0 : a.r);
   if (sw == 256)
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
   else

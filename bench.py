@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--big-batch", type=int, default=64,
                     help="also time this many Zipf-routed tokens per call (0: skip)")
     ap.add_argument("--big-steps", type=int, default=512)
+    ap.add_argument("--mixtral", type=int, default=1,
+                    help="also time the Mixtral-shaped block at batch 1 (0: skip)")
+    ap.add_argument("--mixtral-steps", type=int, default=256)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -326,9 +329,40 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(blk.host_layer0, w, k, args.cpu_seconds)
-
     blk.destroy()
+    del blk
+    if args.mixtral:
+        result["mixtral"] = time_mixtral(b, synth, torch, stream, args.mixtral_steps, args.eager)
+
     print(json.dumps(result), flush=True)
+
+
+def time_mixtral(b, synth, torch, stream, steps, eager):
+    """Mixtral-8x7B-shaped block (d=4096, 8 experts, top-2, m=14336, r=64, LogNormal
+    channel scales) at batch 1: both budgets and the dense-read block, over two
+    rotated layer copies and eight tokens each (16 calls, about 3 GB of weights)."""
+    w = synth.WORKLOADS["mixtral"]
+    d, m, n_exp, top_e, r = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"]
+    t0 = time.time()
+    blk = Block(b, synth, torch, w, 2, 8, stream)
+    setup = time.time() - t0
+    out = {"workload": f"Mixtral-8x7B-shaped MoE block, d={d}, {n_exp} experts, top-{top_e}, m={m}, batch 1, "
+                       f"r={r}", "setup_s": round(setup, 1), "steps": steps,
+           "path": "expert-grouped multi-kernel"}
+    for k in w["ks"]:
+        ms = time_block(torch, blk, k, steps, steps // 8, eager, 1)
+        byt = algorithmic_bytes(d, m, n_exp, top_e, r, k, 1)
+        out[f"k{k}"] = {"tokens_per_s": round(1 / (ms * 1e-3), 1), "ms_per_step": round(ms, 6),
+                        "budget": round(k / m, 4), "algorithmic_bytes": byt,
+                        "achieved_GBs": round(byt / (ms * 1e-3) / 1e9, 1)}
+    ms_d = time_block(torch, blk, None, steps, steps // 8, eager, 1)
+    byt = algorithmic_bytes(d, m, n_exp, top_e, r, 0, 1, dense=True)
+    out["dense"] = {"tokens_per_s": round(1 / (ms_d * 1e-3), 1), "ms_per_step": round(ms_d, 6),
+                    "algorithmic_bytes": byt, "achieved_GBs": round(byt / (ms_d * 1e-3) / 1e9, 1)}
+    for k in w["ks"]:
+        out[f"k{k}"]["speedup_vs_dense"] = round(ms_d / out[f"k{k}"]["ms_per_step"], 3)
+    blk.destroy()
+    return out
 
 
 def cpu_baseline(weights, w, k, seconds):
