@@ -361,7 +361,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
   if (!w_gate || !w_up || !w_down || !out) return fail(MOE_SEL_EINVAL, "weights and out must be non-null");
   if (!moe_sel::grouped_supported(cfg->d, cfg->m))
-    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(cfg->m) + " is above the per-pair selection limit (15360)");
+    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(cfg->m) + " is above the per-pair selection limit (16384)");
   const moe_sel_config c = *cfg;
   const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
   const size_t pairs = (size_t)c.max_batch * c.max_top_e;

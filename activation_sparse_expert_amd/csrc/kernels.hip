@@ -395,89 +395,155 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 }
 
 // ===========================================================================
-// Top-k per pair by four 8-bit radix passes over the score bits (non-negative
-// binary32 scores order like their bit patterns), then an index-order
-// compaction with wave ballots. One block per pair. Writes the ascending list,
-// its length and a bitmap of the selection.
+// Top-k per pair, one block per pair, each thread holding its keys in registers.
+// Non-negative binary32 scores order like their bit patterns. Radix passes over
+// the bits 31..20, 19..9 and 8..0 narrow down the bin holding the k-th largest
+// key: after each pass, keys in higher bins are taken and only keys in the
+// boundary bin stay candidates. As soon as the boundary bin holds at most
+// kSelCand keys they are ranked exactly by (score desc, index asc); if all
+// three passes run, the k-th key itself is known and equal keys are taken
+// lowest index first. Selections are gathered in a bitmap, which then yields
+// the ascending index list by a word-level scan.
 // ===========================================================================
+constexpr int kSelCand = 256;
+constexpr int kSelMaxWords = 512;  // m <= 16384
+
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
-  extern __shared__ uint32_t s_dyn[];  // keys [m], then selection bits [m/32]
-  __shared__ int s_hist[256];
-  __shared__ int s_tmp[kWaves + 1];
-  __shared__ int s_digit, s_gt;
+  __shared__ int s_hist[2048];  // histogram of a pass, then candidate keys and indices
+  __shared__ uint32_t s_bits[kSelMaxWords];
+  __shared__ int s_tmp[kWaves + 2];
+  __shared__ int s_sc[4];
   const int p = blockIdx.x;
-  const int m = a.m, k = a.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t* s_keys = s_dyn;
-  uint32_t* s_bits = s_dyn + m;
-  const float* sc = a.score + (size_t)p * m;
-  for (int j = tid; j < m; j += kThreads) s_keys[j] = __float_as_uint(sc[j]);
-  for (int w = tid; w < m / 32; w += kThreads) s_bits[w] = 0u;
-  __syncthreads();
-  int* idx_out = a.sel_idx + (size_t)p * m;
-  int count = 0;
-  if (k >= m) {
-    for (int j = tid; j < m; j += kThreads) idx_out[j] = j;
-    for (int w = tid; w < m / 32; w += kThreads) s_bits[w] = 0xFFFFFFFFu;
-    count = m;
-  } else if (k > 0) {
-    uint32_t prefix = 0, pmask = 0;
-    int krem = k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      s_hist[tid] = 0;
+  const int m = a.m, k = a.k, words = m / 32;
+  const int tid = threadIdx.x;
+  const uint32_t* keys = (const uint32_t*)(a.score + (size_t)p * m);
+  for (int w = tid; w < words; w += kThreads) s_bits[w] = k >= m ? 0xFFFFFFFFu : 0u;
+  // this thread's keys j = tid + 256 u, in registers for every pass
+  uint32_t key[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int j = tid + u * kThreads;
+    key[u] = j < m ? keys[j] : 0u;
+  }
+  if (k > 0 && k < m) {
+    constexpr int kShift[3] = {20, 9, 0};
+    constexpr int kBins[3] = {2048, 2048, 512};
+    uint32_t prefix = 0;  // boundary bits above the current pass
+    int krem = k, level = 0, ncand = m;
+    for (; level < 3; ++level) {
+      const int sh = kShift[level], hi = level == 0 ? 32 : kShift[level - 1];
+      const uint32_t dmask = (uint32_t)kBins[level] - 1u;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
       __syncthreads();
-      for (int j = tid; j < m; j += kThreads) {
-        const uint32_t key = s_keys[j];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (tid + u * kThreads < m && (level == 0 || (key[u] >> hi) == prefix))
+          atomicAdd(&s_hist[(key[u] >> sh) & dmask], 1);
+      __syncthreads();
+      int h[8], c = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        h[b] = s_hist[tid * 8 + b];
+        c += h[b];
+      }
+      int total;
+      const int before = block_excl_scan(c, s_tmp, &total);
+      int above = total - before - c;  // keys of this pass in bins above this thread's 8
+#pragma unroll
+      for (int b = 7; b >= 0; --b) {
+        if (above < krem && krem <= above + h[b]) {
+          s_sc[0] = tid * 8 + b;
+          s_sc[1] = above;
+          s_sc[2] = h[b];
+        }
+        above += h[b];
       }
       __syncthreads();
-      // thread tid owns bin 255 - tid: an inclusive scan over threads is a suffix scan over bins
-      const int c = s_hist[255 - tid];
-      int incl = wave_incl_scan(c);
-      if (lane == 63) s_tmp[wave] = incl;
-      __syncthreads();
-      for (int w = 0; w < wave; ++w) incl += s_tmp[w];
-      if (incl - c < krem && krem <= incl) {
-        s_digit = 255 - tid;
-        s_gt = incl - c;
+      // keys of this pass in bins above the boundary bin are taken
+      const uint32_t dsel = (uint32_t)s_sc[0];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int j = tid + u * kThreads;
+        if (j < m && (level == 0 || (key[u] >> hi) == prefix) && ((key[u] >> sh) & dmask) > dsel)
+          atomicOr(&s_bits[j >> 5], 1u << (j & 31));
       }
-      __syncthreads();
-      prefix |= (uint32_t)s_digit << shift;
-      pmask |= 255u << shift;
-      krem -= s_gt;
-      __syncthreads();
-    }
-    // prefix is the k-th largest key; take every larger key and the krem lowest-index
-    // equal keys. Thread t owns keys [t per, (t + 1) per), so one scan of the equal
-    // counts and one of the taken counts place every index in ascending order.
-    const int per = (m + kThreads - 1) / kThreads;
-    const int j0 = min(m, tid * per), j1 = min(m, j0 + per);
-    int ngt = 0, neq = 0;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t key = s_keys[j];
-      ngt += key > prefix;
-      neq += key == prefix;
-    }
-    int eq_tot, sel_tot;
-    const int eq_before = block_excl_scan(neq, s_tmp, &eq_tot);
-    const int take_eq = max(0, min(neq, krem - eq_before));
-    int pos = block_excl_scan(ngt + take_eq, s_tmp, &sel_tot);
-    int eq_seen = 0;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t key = s_keys[j];
-      bool take = key > prefix;
-      if (key == prefix) take = eq_seen++ < take_eq;
-      if (take) {
-        idx_out[pos++] = j;
-        atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+      krem -= s_sc[1];
+      ncand = s_sc[2];
+      prefix = (prefix << (hi - sh)) | dsel;
+      if (ncand <= kSelCand) {
+        ++level;
+        break;
       }
     }
-    count = sel_tot;
+    const int sh = kShift[level - 1];
+    if (ncand <= kSelCand) {
+      // rank the boundary bin's keys exactly
+      int* ckey = s_hist;
+      int* cidx = s_hist + kSelCand;
+      if (tid == 0) s_tmp[kWaves + 1] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int j = tid + u * kThreads;
+        if (j < m && (key[u] >> sh) == prefix) {
+          const int slot = atomicAdd(&s_tmp[kWaves + 1], 1);
+          ckey[slot] = (int)key[u];
+          cidx[slot] = j;
+        }
+      }
+      __syncthreads();
+      if (tid < ncand) {
+        const int ic = cidx[tid];
+        const uint64_t kc = order_key((uint32_t)ckey[tid], ic);
+        int rank = 0;
+#pragma unroll 8
+        for (int o = 0; o < ncand; ++o) rank += order_key((uint32_t)ckey[o], cidx[o]) > kc;
+        if (rank < krem) atomicOr(&s_bits[ic >> 5], 1u << (ic & 31));
+      }
+    } else {
+      // prefix is the k-th largest key itself: its krem lowest-index copies, word by word
+      __syncthreads();
+      int run_eq = 0;
+      for (int base = 0; base < words; base += kThreads) {
+        const int w = base + tid;
+        uint32_t eq = 0;
+        if (w < words)
+#pragma unroll 8
+          for (int b = 0; b < 32; ++b) eq |= (uint32_t)(keys[32 * w + b] == prefix) << b;
+        int eq_tot;
+        const int eq_before = run_eq + block_excl_scan(__popc(eq), s_tmp, &eq_tot);
+        int want = max(0, min(__popc(eq), krem - eq_before));
+        uint32_t takeq = 0, rest = eq;
+        while (want-- > 0) {
+          const uint32_t low = rest & (0u - rest);
+          takeq |= low;
+          rest ^= low;
+        }
+        if (w < words) s_bits[w] |= takeq;
+        run_eq += eq_tot;
+      }
+    }
   }
   __syncthreads();
-  if (tid == 0) a.sel_count[p] = count;
-  for (int w = tid; w < m / 32; w += kThreads) a.selbits[(size_t)p * (m / 32) + w] = s_bits[w];
+  // ascending index list from the bitmap
+  int* idx_out = a.sel_idx + (size_t)p * m;
+  int run = 0;
+  for (int base = 0; base < words; base += kThreads) {
+    const int w = base + tid;
+    const uint32_t u = w < words ? s_bits[w] : 0u;
+    int tot;
+    int pos = run + block_excl_scan(__popc(u), s_tmp, &tot);
+    uint32_t rest = u;
+    while (rest) {
+      idx_out[pos++] = 32 * w + __ffs(rest) - 1;
+      rest &= rest - 1u;
+    }
+    if (w < words) a.selbits[(size_t)p * words + w] = u;
+    run += tot;
+  }
+  if (tid == 0) a.sel_count[p] = run;
 }
 
 // ===========================================================================
@@ -839,8 +905,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
 
 }  // namespace
 
-// k_select keeps m keys and m/32 bitmap words in LDS (64 KiB)
-bool grouped_supported(int d, int m) { return d >= 64 && (size_t)m * 4 + (size_t)m / 8 + 2048 <= 65536; }
+// k_select keeps the selection bitmap (m/32 words) in LDS
+bool grouped_supported(int d, int m) { return d >= 64 && m / 32 <= kSelMaxWords; }
 
 int grouped_down_width(int d) { return d % 256 == 0 ? 256 : 64; }
 
@@ -863,7 +929,12 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   if (!dense) {
     const size_t score_lds = ((size_t)kT * 64 + (size_t)64 * a.r) * 4;
     hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads), score_lds, stream, a);
-    hipLaunchKernelGGL(k_select, dim3(pairs), dim3(kThreads), (size_t)(a.m + a.m / 32) * 4, stream, a);
+    if (a.m <= 4 * kThreads)
+      hipLaunchKernelGGL(k_select<4>, dim3(pairs), dim3(kThreads), 0, stream, a);
+    else if (a.m <= 16 * kThreads)
+      hipLaunchKernelGGL(k_select<16>, dim3(pairs), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_select<64>, dim3(pairs), dim3(kThreads), 0, stream, a);
   }
   hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
