@@ -332,18 +332,19 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
     i32x4 accg = i32x4{0, 0, 0, 0}, accu = i32x4{0, 0, 0, 0};
     const int8_t* x4 = xr[ns] - 16 * lg + 64 * lg;  // token row + block offset lg
     int b = 0;
-    for (; b + 8 <= nb; b += 8) {
-      u32x4 wg[2], wu[2];
-      i32x4 xv[2][4];
+    constexpr int SB = 4;  // groups of four code blocks per iteration
+    for (; b + 4 * SB <= nb; b += 4 * SB) {
+      u32x4 wg[SB], wu[SB];
+      i32x4 xv[SB][4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < SB; ++u) {
         wg[u] = cg4[(size_t)(b + 4 * u) * blk4];
         wu[u] = cu4[(size_t)(b + 4 * u) * blk4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[u][q] = *(const i32x4*)(x4 + 64 * (b + 4 * u) + 16 * q);
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < SB; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[u][q]), xv[u][q], accg, 0, 0, 0);
@@ -568,6 +569,16 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     if (tid == 0) a.ucount[tile] = m;
     return;
   }
+  if (n == 1) {
+    const int pp = a.tpair[first];
+    const int cnt = a.sel_count[pp];
+    for (int j = tid; j < cnt; j += kThreads) {
+      ul[j] = a.sel_idx[(size_t)pp * m + j];
+      um[j] = 1ull;
+    }
+    if (tid == 0) a.ucount[tile] = cnt;
+    return;
+  }
   // one thread per bitmap word: the tokens' words, their union, then the listed
   // channels of the word with their token masks at exclusive-scan positions
   __shared__ int s_p[kT];
@@ -641,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   }
   const int nsteps = d / 32;
   const int kpad = a.kpad;
-  constexpr int U = 4;
+  constexpr int U = 8;
   // token subtiles one after another (weights re-read from L2 after the first)
   for (int ns = 0; ns < nsub; ++ns) {
     f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
