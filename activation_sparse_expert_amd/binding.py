@@ -25,7 +25,7 @@ EXPORTED = (
     "moe_sel_prepare_expert_host", "moe_sel_prepare", "moe_sel_forward",
     "moe_sel_forward_dense", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
-    "moe_sel_set_path", "moe_sel_last_path",
+    "moe_sel_set_path", "moe_sel_last_path", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
@@ -80,6 +80,8 @@ def _load():
         "moe_sel_check_device": (ctypes.c_int, [vp]),
         "moe_sel_set_path": (ctypes.c_int, [vp, ctypes.c_int]),
         "moe_sel_last_path": (i32, [vp]),
+        "moe_sel_router_logits": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
+        "moe_sel_residual_rmsnorm": (ctypes.c_int, [vp, vp, i32, i32, ctypes.c_float, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -240,3 +242,13 @@ def moe_sel_status_str(status: int) -> str:
 
 def moe_sel_last_error() -> str:
     return _lib.moe_sel_last_error().decode()
+
+
+def moe_sel_router_logits(x, w_router, batch, d, n_experts, logits, stream=None):
+    _check(_lib.moe_sel_router_logits(_dev_ptr(x), _dev_ptr(w_router), int(batch), int(d), int(n_experts),
+                                      _dev_ptr(logits), _stream(stream)), "moe_sel_router_logits")
+
+
+def moe_sel_residual_rmsnorm(x, y, batch, d, eps, out, stream=None):
+    _check(_lib.moe_sel_residual_rmsnorm(_dev_ptr(x), _dev_ptr(y), int(batch), int(d), float(eps),
+                                         _dev_ptr(out), _stream(stream)), "moe_sel_residual_rmsnorm")

@@ -108,14 +108,12 @@ void free_ctx(moe_sel_ctx* c) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The rank-r maps of large experts are built on the device (fp64), small ones
-// on the host; MOE_SEL_LOWRANK=host or =device forces one of the two.
+// The rank-r maps are built on the device (fp64, batched over experts);
+// MOE_SEL_LOWRANK=host builds them on the host instead (the same eigen-solver).
 bool lowrank_on_device(const moe_sel_config& c) {
   if (c.rank <= 0) return false;
   const char* env = std::getenv("MOE_SEL_LOWRANK");
-  if (env && std::strcmp(env, "host") == 0) return false;
-  if (env && std::strcmp(env, "device") == 0) return true;
-  return std::min(c.d, c.m) > 1024;
+  return !(env && std::strcmp(env, "host") == 0);
 }
 
 struct PrepJob {
@@ -477,14 +475,12 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   for (int ui = 0; ui < 5; ++ui) {
     const Up& u = ups[ui];
     if (ui == 3 && dev_lowrank) {
-      // maps from the channel rows now on the device, one expert at a time
-      for (size_t ex = 0; ex < E; ++ex) {
-        const std::string err = moe_sel::lowrank_map_device(ctx->wch + ex * m * 3 * d, c.d, c.m, c.rank,
-                                                            h_p.data() + ex * r * d, h_q.data() + ex * m * r, s);
-        if (!err.empty()) {
-          free_ctx(ctx);
-          return fail(MOE_SEL_EDEVICE, "expert " + std::to_string(ex) + ": " + err);
-        }
+      // maps from the channel rows now on the device
+      const std::string err = moe_sel::lowrank_maps_device(ctx->wch, c.n_experts, c.d, c.m, c.rank, h_p.data(),
+                                                           h_q.data(), s);
+      if (!err.empty()) {
+        free_ctx(ctx);
+        return fail(MOE_SEL_EDEVICE, err);
       }
     }
     he = hipMemcpyAsync(u.dst, u.src, u.bytes, hipMemcpyHostToDevice, s);
@@ -656,5 +652,31 @@ moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg) {
 uint64_t moe_sel_device_bytes(const moe_sel_ctx* ctx) { return ctx ? ctx->device_bytes : 0; }
 
 void moe_sel_destroy(moe_sel_ctx* ctx) { free_ctx(ctx); }
+
+moe_sel_status moe_sel_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t batch, int32_t d,
+                                     int32_t n_experts, float* logits, void* stream) {
+  g_last_error.clear();
+  if (!x || !w_router || !logits) return fail(MOE_SEL_EINVAL, "x, w_router and logits must be non-null");
+  if (!aligned16(x) || !aligned16(w_router) || ((uintptr_t)logits & 3u))
+    return fail(MOE_SEL_EINVAL, "x and w_router must be 16-byte aligned, logits 4-byte aligned");
+  if (batch < 1 || batch > 65535) return fail(MOE_SEL_EINVAL, "batch must be in [1, 65535]");
+  if (d < 64 || d > 16384 || d % 64) return fail(MOE_SEL_EINVAL, "d must be a multiple of 64 in [64, 16384]");
+  if (n_experts < 1 || n_experts > 1024) return fail(MOE_SEL_EINVAL, "n_experts must be in [1, 1024]");
+  const hipError_t e = moe_sel::launch_router(x, w_router, batch, d, n_experts, logits, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
+moe_sel_status moe_sel_residual_rmsnorm(const uint16_t* x, const uint16_t* y, int32_t batch, int32_t d, float eps,
+                                        uint16_t* out, void* stream) {
+  g_last_error.clear();
+  if (!x || !y || !out) return fail(MOE_SEL_EINVAL, "x, y and out must be non-null");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(out))
+    return fail(MOE_SEL_EINVAL, "x, y and out must be 16-byte aligned");
+  if (batch < 1 || batch > 65535) return fail(MOE_SEL_EINVAL, "batch must be in [1, 65535]");
+  if (d < 64 || d > 16384 || d % 64) return fail(MOE_SEL_EINVAL, "d must be a multiple of 64 in [64, 16384]");
+  if (!(eps > 0.0f) || !(eps < 1.0f)) return fail(MOE_SEL_EINVAL, "eps must be in (0, 1)");
+  const hipError_t e = moe_sel::launch_resnorm(x, y, batch, d, eps, out, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
 
 }  // extern "C"

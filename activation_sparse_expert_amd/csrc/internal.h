@@ -70,12 +70,13 @@ struct Tridiag {
 void eigvecs_from_tridiag(const double* refl, int n, int r, const Tridiag& T, std::vector<double>& vecs,
                           std::vector<double>& vals);
 
-// Rank-r map of one expert built on the device in fp64 (Gram matrix,
-// tridiagonalisation and projection on the GPU; the tridiagonal eigen-solve on
-// the host). wch_dev: the expert's channel-major rows on the device. Outputs are
-// host arrays P^T [r][d] and Q [m][r] in bf16. Empty string on success.
-std::string lowrank_map_device(const uint16_t* wch_dev, int d, int m, int r, uint16_t* p_out, uint16_t* q_out,
-                               void* stream);
+// Rank-r maps of all experts built on the device in fp64 (Gram matrices,
+// tridiagonalisation and projection on the GPU, batched over experts; the
+// tridiagonal eigen-solves on host threads). wch_dev: the experts' channel-major
+// rows on the device ([E][m][3][d]). Outputs are host arrays P^T [E][r][d] and
+// Q [E][m][r] in bf16. Empty string on success.
+std::string lowrank_maps_device(const uint16_t* wch_dev, int n_experts, int d, int m, int r, uint16_t* p_out,
+                                uint16_t* q_out, void* stream);
 
 // Returns an empty string on success, else the failure message.
 std::string prepare_expert(const moe_sel_config& cfg, const uint16_t* w_gate, const uint16_t* w_up,

@@ -86,4 +86,10 @@ size_t fused_lds_bytes(int d, int m, int r);
 int fused_blocks_per_cu(bool dense, int d, int m, int r);
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream);
 
+// Decode-step glue (decode_glue.hip)
+hipError_t launch_router(const uint16_t* x, const uint16_t* w, int batch, int d, int n_experts, float* logits,
+                         hipStream_t stream);
+hipError_t launch_resnorm(const uint16_t* x, const uint16_t* y, int batch, int d, float eps, uint16_t* out,
+                          hipStream_t stream);
+
 }  // namespace moe_sel

@@ -199,12 +199,15 @@ void tridiagonalize(std::vector<double>& A, int n, Tridiag& T) {
     const double beta = 2.0 / vnorm2;
     T.off[k] = alpha;
     T.beta[k] = beta;
-    // p = beta * A22 v
+    // p = beta * A22 v (eight interleaved partial sums per row, added pairwise)
     for (int i = 0; i < len; ++i) {
       const double* row = &A[(size_t)(k + 1 + i) * n + k + 1];
-      double s = 0.0;
-      for (int j = 0; j < len; ++j) s += row[j] * v[j];
-      p[i] = beta * s;
+      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int j = 0;
+      for (; j + 8 <= len; j += 8)
+        for (int q = 0; q < 8; ++q) acc[q] += row[j + q] * v[j + q];
+      for (; j < len; ++j) acc[0] += row[j] * v[j];
+      p[i] = beta * (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
     }
     double pv = 0.0;
     for (int i = 0; i < len; ++i) pv += p[i] * v[i];
@@ -366,6 +369,27 @@ void top_eigvecs(std::vector<double>& A, int n, int r, std::vector<double>& vecs
   eigvecs_from_tridiag(A.data(), n, r, T, vecs, vals);
 }
 
+// G (n x n) = sum over the rows x of X [rows][n] of x^T x. Rows of G are
+// accumulated in blocks of 32 so a block stays in cache while X streams; each
+// entry sums over the rows in order. Only the lower triangle is formed, then
+// mirrored.
+void gram_lower(const double* X, int rows, int n, double* G) {
+  constexpr int kB = 32;
+  for (int a0 = 0; a0 < n; a0 += kB) {
+    const int a1 = std::min(n, a0 + kB);
+    for (int i = 0; i < rows; ++i) {
+      const double* x = X + (size_t)i * n;
+      for (int a = a0; a < a1; ++a) {
+        const double xa = x[a];
+        double* g = G + (size_t)a * n;
+        for (int b = 0; b <= a; ++b) g[b] += xa * x[b];
+      }
+    }
+  }
+  for (int a = 0; a < n; ++a)
+    for (int b = 0; b < a; ++b) G[(size_t)b * n + a] = G[(size_t)a * n + b];
+}
+
 // P^T [r][d] and Q [m][r] with P Q^T = best rank-r approximation of W [d][m].
 void lowrank_map(const uint16_t* wd_bits, int d, int m, int r, uint16_t* p_out, uint16_t* q_out) {
   if (r == 0) return;
@@ -373,27 +397,10 @@ void lowrank_map(const uint16_t* wd_bits, int d, int m, int r, uint16_t* p_out, 
   for (size_t i = 0; i < W.size(); ++i) W[i] = (double)bf16_to_f32(wd_bits[i]);
   std::vector<double> vecs, vals;
   if (m <= d) {
-    // G = W^T W (m x m); rows of Wt are columns of W
-    std::vector<double> Wt((size_t)m * d);
-    for (int i = 0; i < d; ++i)
-      for (int j = 0; j < m; ++j) Wt[(size_t)j * d + i] = W[(size_t)i * m + j];
-    std::vector<double> G((size_t)m * m);
-    for (int a = 0; a < m; ++a) {
-      const double* ra = &Wt[(size_t)a * d];
-      for (int b = 0; b <= a; ++b) {
-        const double* rb = &Wt[(size_t)b * d];
-        double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        int i = 0;
-        for (; i + 4 <= d; i += 4) {
-          s0 += ra[i] * rb[i];
-          s1 += ra[i + 1] * rb[i + 1];
-          s2 += ra[i + 2] * rb[i + 2];
-          s3 += ra[i + 3] * rb[i + 3];
-        }
-        for (; i < d; ++i) s0 += ra[i] * rb[i];
-        G[(size_t)a * m + b] = G[(size_t)b * m + a] = (s0 + s1) + (s2 + s3);
-      }
-    }
+    // G = W^T W (m x m) = sum over rows i of W[i]^T W[i]: lower triangle, one
+    // row of W at a time (contiguous inner loops), mirrored at the end
+    std::vector<double> G((size_t)m * m, 0.0);
+    gram_lower(W.data(), d, m, G.data());
     top_eigvecs(G, m, r, vecs, vals);  // V_r: m x r
     for (int j = 0; j < m; ++j)
       for (int c = 0; c < r; ++c) q_out[(size_t)j * r + c] = f32_to_bf16((float)vecs[(size_t)j * r + c]);
@@ -405,24 +412,12 @@ void lowrank_map(const uint16_t* wd_bits, int d, int m, int r, uint16_t* p_out, 
         p_out[(size_t)c * d + i] = f32_to_bf16((float)s);
       }
   } else {
-    // G = W W^T (d x d)
-    std::vector<double> G((size_t)d * d);
-    for (int a = 0; a < d; ++a) {
-      const double* ra = &W[(size_t)a * m];
-      for (int b = 0; b <= a; ++b) {
-        const double* rb = &W[(size_t)b * m];
-        double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        int j = 0;
-        for (; j + 4 <= m; j += 4) {
-          s0 += ra[j] * rb[j];
-          s1 += ra[j + 1] * rb[j + 1];
-          s2 += ra[j + 2] * rb[j + 2];
-          s3 += ra[j + 3] * rb[j + 3];
-        }
-        for (; j < m; ++j) s0 += ra[j] * rb[j];
-        G[(size_t)a * d + b] = G[(size_t)b * d + a] = (s0 + s1) + (s2 + s3);
-      }
-    }
+    // G = W W^T (d x d) = sum over channels j of W[:, j] W[:, j]^T
+    std::vector<double> Wt((size_t)m * d);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < m; ++j) Wt[(size_t)j * d + i] = W[(size_t)i * m + j];
+    std::vector<double> G((size_t)d * d, 0.0);
+    gram_lower(Wt.data(), m, d, G.data());
     top_eigvecs(G, d, r, vecs, vals);  // U_r: d x r
     for (int c = 0; c < r; ++c)
       for (int i = 0; i < d; ++i) p_out[(size_t)c * d + i] = f32_to_bf16((float)vecs[(size_t)i * r + c]);

@@ -21,6 +21,8 @@ intermediate channels per expert m, channel budgets k, compensation rank r):
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 # tensor ids inside a spawn key
@@ -90,8 +92,19 @@ def layer_weights(wid: int, layer: int, n_experts: int, d: int, m: int,
     wg = np.zeros((n_experts, m, d), np.uint16)
     wu = np.zeros((n_experts, m, d), np.uint16)
     wd = np.zeros((n_experts, d, m), np.uint16)
-    for e in (range(n_experts) if experts is None else experts):
+
+    def one(e):
         wg[e], wu[e], wd[e] = expert_weights(wid, layer, e, d, m, channel_scale)
+
+    todo = list(range(n_experts) if experts is None else experts)
+    if len(todo) > 1:
+        # every expert has its own seeded stream, so threads change no value
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, len(todo), os.cpu_count() or 1)) as pool:
+            list(pool.map(one, todo))
+    else:
+        for e in todo:
+            one(e)
     return wg, wu, wd
 
 

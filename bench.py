@@ -214,6 +214,10 @@ def main():
     ap.add_argument("--mixtral", type=int, default=1,
                     help="also time the Mixtral-shaped block at batch 1 (0: skip)")
     ap.add_argument("--mixtral-steps", type=int, default=256)
+    ap.add_argument("--decode48", type=int, default=1,
+                    help="also time a 48-layer decode step at batch 1, 8 and 32 (0: skip)")
+    ap.add_argument("--decode-layers", type=int, default=12, help="distinct prepared layers in the 48-layer stack")
+    ap.add_argument("--decode-steps", type=int, default=30)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -333,6 +337,8 @@ def main():
     del blk
     if args.mixtral:
         result["mixtral"] = time_mixtral(b, synth, torch, stream, args.mixtral_steps, args.eager)
+    if args.decode48:
+        result["decode48"] = time_decode48(b, synth, torch, stream, args.decode_layers, args.decode_steps)
 
     print(json.dumps(result), flush=True)
 
@@ -362,6 +368,76 @@ def time_mixtral(b, synth, torch, stream, steps, eager):
     for k in w["ks"]:
         out[f"k{k}"]["speedup_vs_dense"] = round(ms_d / out[f"k{k}"]["ms_per_step"], 3)
     blk.destroy()
+    return out
+
+
+def time_decode48(b, synth, torch, stream, distinct, steps, batches=(1, 8, 32), n_layers=48, eps=1e-6):
+    """Decode step over 48 stacked Qwen3-shaped layers (k=137, r=32): per layer the
+    router logits, the block and the residual renormalisation, all on the GPU. The
+    stack cycles `distinct` prepared layers (each with its own router); a step
+    touches more weight bytes per cycle than the last-level cache holds."""
+    w = synth.WORKLOADS["qwen3_48l"]
+    d, m, n_exp, top_e, r, k = w["d"], w["m"], w["n_experts"], w["top_e"], w["rank"], w["ks"][0]
+    t0 = time.time()
+    ctxs, wrs = [], []
+    for l in range(distinct):
+        wg, wu, wd = synth.layer_weights(w["wid"], l, n_exp, d, m)
+        ctxs.append(b.moe_sel_prepare(b.make_config(d, n_exp, m, r, top_e, max(batches)), wg, wu, wd,
+                                      stream=stream.cuda_stream))
+        del wg, wu, wd
+        wrs.append(torch.from_numpy(synth.router_weights(w["wid"], l, n_exp, d).view(np.int16)).to("cuda"))
+    out = {"workload": f"{n_layers} stacked Qwen3-shaped layers (d={d}, {n_exp} experts, top-{top_e}, m={m}), "
+                       f"k={k} ({k / m:.1%}), r={r}; router and residual RMS renormalisation per layer",
+           "distinct_layers": distinct, "setup_s": round(time.time() - t0, 1), "steps": steps}
+    s = stream.cuda_stream
+    for bsz in batches:
+        x0 = torch.from_numpy(synth.tokens(w["wid"], 0, bsz, d).view(np.int16)).to("cuda")
+        x = x0.clone()
+        lg = torch.empty((bsz, n_exp), dtype=torch.float32, device="cuda")
+        y = torch.empty((bsz, d), dtype=torch.int16, device="cuda")
+
+        def step(dense):
+            for l in range(n_layers):
+                c = ctxs[l % distinct]
+                b.moe_sel_router_logits(x, wrs[l % distinct], bsz, d, n_exp, lg, s)
+                if dense:
+                    b.moe_sel_forward_dense(c, x, lg, bsz, top_e, y, s)
+                else:
+                    b.moe_sel_forward(c, x, lg, bsz, top_e, k, y, s)
+                b.moe_sel_residual_rmsnorm(x, y, bsz, d, eps, x, s)
+
+        res = {}
+        for dense in (False, True):
+            with torch.cuda.stream(stream):
+                x.copy_(x0)
+                step(dense)
+            torch.cuda.synchronize()
+            for c in ctxs:
+                b.moe_sel_check_device(c)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(dense)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                x.copy_(x0)
+                g.replay()
+                ev0.record(stream)
+                for _ in range(steps):
+                    g.replay()
+                ev1.record(stream)
+            torch.cuda.synchronize()
+            for c in ctxs:
+                b.moe_sel_check_device(c)
+            ms = ev0.elapsed_time(ev1) / steps
+            res["dense" if dense else "sparse"] = ms
+            del g
+        out[f"batch{bsz}"] = {"tokens_per_s": round(bsz / (res["sparse"] * 1e-3), 1),
+                              "ms_per_step": round(res["sparse"], 4),
+                              "dense_tokens_per_s": round(bsz / (res["dense"] * 1e-3), 1),
+                              "dense_ms_per_step": round(res["dense"], 4),
+                              "speedup_vs_dense": round(res["dense"] / res["sparse"], 3)}
+    for c in ctxs:
+        b.moe_sel_destroy(c)
     return out
 
 

@@ -223,6 +223,34 @@ uint64_t moe_sel_device_bytes(const moe_sel_ctx* ctx);
  * must make sure no enqueued call on it is still running. */
 void moe_sel_destroy(moe_sel_ctx* ctx);
 
+/*
+ * Decode-step glue for stacking blocks over layers. The pages measure MoE
+ * blocks inside decoding ("KAIST drops calibration from MoE decoding, speeds
+ * up blocks by up to 2.69x over vLLM", opening paragraph); these two calls
+ * chain blocks into a many-layer decode step with a router per layer and the
+ * residual stream renormalised between layers.
+ *
+ * moe_sel_router_logits: logits[t][e] = sum_i x[t][i] * w_router[e][i], fp32
+ * accumulation of the bf16 products.
+ *   x        [batch][d] bf16 bits, device, 16-byte aligned
+ *   w_router [n_experts][d] bf16 bits, device, 16-byte aligned (caller-owned)
+ *   logits   [batch][n_experts] fp32, device, written
+ *   batch 1..65535, d a multiple of 64 in [64, 16384], n_experts 1..1024.
+ * Asynchronous on stream. Errors: EINVAL (checked before enqueueing), EDEVICE.
+ */
+moe_sel_status moe_sel_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t batch, int32_t d,
+                                     int32_t n_experts, float* logits, void* stream);
+
+/*
+ * moe_sel_residual_rmsnorm: out[t] = bf16(v / sqrt(mean_i v_i^2 + eps)) with
+ * v = x[t] + y[t] in fp32 (round to nearest even into bf16). out may alias x.
+ *   x, y, out [batch][d] bf16 bits, device, 16-byte aligned
+ *   batch 1..65535, d a multiple of 64 in [64, 16384], eps in (0, 1).
+ * Asynchronous on stream. Errors: EINVAL (checked before enqueueing), EDEVICE.
+ */
+moe_sel_status moe_sel_residual_rmsnorm(const uint16_t* x, const uint16_t* y, int32_t batch, int32_t d, float eps,
+                                        uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,9 +13,12 @@ from .moe_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     compensation,
     expert_swiglu_selected,
+    f64_to_bf16_bits,
     prepare_expert,
     quantize_token,
+    residual_rmsnorm,
     route,
+    router_logits,
     score_channels,
     select_topk,
     silu_pinned,

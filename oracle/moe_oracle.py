@@ -354,3 +354,52 @@ class OracleLayer:
             for slot, ex in enumerate(ids):
                 y[t] += gw[slot] * expert_swiglu_selected(self.expert(ex), x, np.arange(self.m))
         return y
+
+
+# ---------------------------------------------------------------------------
+# Stacked decode step (glue between blocks). The pages measure MoE blocks inside
+# decoding ([KAIST] opening paragraph); chaining blocks over layers needs a
+# router per layer and a residual stream between layers. Readings: the router is
+# a plain linear map of the hidden state to one logit per expert; the residual
+# adds the block output and renormalises to unit root-mean-square.
+# ---------------------------------------------------------------------------
+def router_logits(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """logits[t][e] = sum_i x[t][i] * W[e][i] in float64, rounded once to binary32."""
+    x = bf16_bits_to_f64(np.atleast_2d(x_bits))
+    w = bf16_bits_to_f64(w_router_bits)
+    return (x @ w.T).astype(np.float32)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16, nearest with ties to even, returning raw bits.
+
+    Exact: the value is split into sign, exponent and a 53-bit significand with
+    math.frexp, and the significand is rounded to 8 bits by integer arithmetic.
+    Subnormal bfloat16 results are not needed here (|v| >= 2^-126 or v == 0)."""
+    flat = np.asarray(v, dtype=np.float64).ravel()
+    out = np.empty(flat.shape, np.uint16)
+    for i, val in enumerate(flat):
+        if val == 0.0:
+            out[i] = 0x8000 if math.copysign(1.0, val) < 0 else 0
+            continue
+        sign = 0x8000 if val < 0 else 0
+        mant, exp = math.frexp(abs(val))          # abs(val) = mant * 2^exp, mant in [0.5, 1)
+        sig = int(mant * (1 << 53))               # exact 53-bit integer significand
+        keep, rest = divmod(sig, 1 << 45)         # 8 significant bits kept, 45 dropped
+        half = 1 << 44
+        if rest > half or (rest == half and (keep & 1)):
+            keep += 1
+        if keep == (1 << 8):                      # rounding carried into the next binade
+            keep >>= 1
+            exp += 1
+        biased = exp - 1 + 127                    # value = (keep / 2^7) * 2^(exp - 1)
+        assert 1 <= biased <= 254, "outside the normal bfloat16 range"
+        out[i] = sign | (biased << 7) | (keep & 0x7F)
+    return out.reshape(np.shape(v))
+
+
+def residual_rmsnorm(x_bits: np.ndarray, y_bits: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """x_next = bf16(v / sqrt(mean(v^2) + eps)) with v = x + y, all in float64."""
+    v = bf16_bits_to_f64(np.atleast_2d(x_bits)) + bf16_bits_to_f64(np.atleast_2d(y_bits))
+    scale = 1.0 / np.sqrt((v * v).mean(axis=1, keepdims=True) + eps)
+    return f64_to_bf16_bits(v * scale)

@@ -1,0 +1,144 @@
+"""Stacked decode step over Qwen3-shaped layers (router -> block -> residual
+renormalisation per layer): the glue kernels against the oracle, every layer of
+a short stack against the oracle fed with the oracle's own hidden states, and
+properties of a longer chain run on the GPU alone."""
+import numpy as np
+import pytest
+
+import oracle
+from activation_sparse_expert_amd import synth
+from gpu_common import TOL, Layer, out_to_f64, rel_err, to_dev_u16, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS["qwen3_48l"]
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def b():
+    torch_cuda()
+    from activation_sparse_expert_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+def _router(b, torch, x_bits, wr_bits):
+    bsz, d = x_bits.shape
+    E = wr_bits.shape[0]
+    lg = torch.empty((bsz, E), dtype=torch.float32, device="cuda")
+    b.moe_sel_router_logits(to_dev_u16(torch, x_bits), to_dev_u16(torch, wr_bits), bsz, d, E, lg)
+    torch.cuda.synchronize()
+    return lg
+
+
+def test_router_logits_match_oracle(b, torch):
+    d, E = W["d"], W["n_experts"]
+    x = synth.tokens(W["wid"], 0, 8, d)
+    wr = synth.router_weights(W["wid"], 0, E, d)
+    got = _router(b, torch, x, wr).cpu().numpy()
+    ref = oracle.router_logits(x, wr)
+    assert np.allclose(got, ref, rtol=1e-5, atol=1e-5), np.abs(got - ref).max()
+
+
+def test_residual_rmsnorm_matches_oracle_within_one_bf16_step(b, torch):
+    d = W["d"]
+    x = synth.tokens(W["wid"], 1, 8, d)
+    y = synth.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((8, d)).astype(np.float32) * 0.3)
+    out = torch.empty((8, d), dtype=torch.int16, device="cuda")
+    b.moe_sel_residual_rmsnorm(to_dev_u16(torch, x), to_dev_u16(torch, y), 8, d, EPS, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).astype(np.int64)
+    ref = oracle.residual_rmsnorm(x, y, EPS).astype(np.int64)
+    # same sign everywhere (no zeros here), magnitudes within one bf16 step
+    assert np.all((got >> 15) == (ref >> 15))
+    assert np.abs((got & 0x7FFF) - (ref & 0x7FFF)).max() <= 1
+
+
+def test_glue_argument_errors(b, torch):
+    x = torch.zeros((1, 64), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((1, 4), dtype=torch.float32, device="cuda")
+    for args in [(x, x, 0, 64, 4, lg), (x, x, 1, 96, 4, lg), (x, x, 1, 64, 0, lg), (x, None, 1, 64, 4, lg)]:
+        with pytest.raises(b.MoeSelError):
+            b.moe_sel_router_logits(*args)
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_residual_rmsnorm(x, x, 1, 64, 0.0, x)
+
+
+@pytest.mark.timeout(600)
+def test_stacked_layers_against_oracle_fed_with_its_own_states(b, torch):
+    """Three stacked layers, batch 4, k = 137 (17.8% of 768): the oracle runs the
+    stack on the CPU; at every layer the GPU is given the oracle's hidden state
+    and logits and must reproduce that layer's selections bit for bit and its
+    output within tolerance; the GPU's router and renormalisation are checked
+    against the oracle's at the same layer."""
+    d, E, top_e, k = W["d"], W["n_experts"], W["top_e"], W["ks"][0]
+    bsz, n_layers = 4, 3
+    x = synth.tokens(W["wid"], 0, bsz, d)
+    for l in range(n_layers):
+        lay = Layer(b, "qwen3_48l", max_batch=bsz, layer=l)
+        try:
+            wr = synth.router_weights(W["wid"], l, E, d)
+            lg_ref = oracle.router_logits(x, wr)
+            lg_gpu = _router(b, torch, x, wr)
+            assert np.allclose(lg_gpu.cpu().numpy(), lg_ref, rtol=1e-5, atol=1e-5)
+            lay.path = None
+            xd = to_dev_u16(torch, x)
+            out = torch.zeros((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_forward(lay.ctx, xd, torch.from_numpy(lg_ref).to("cuda"), bsz, top_e, k, out)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(lay.ctx)
+            ref = lay.oracle.forward(x, lg_ref, top_e, k)
+            dbg = b.moe_sel_debug_selection(lay.ctx, bsz, top_e, k, lay.m, with_scores=False)
+            assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+            for t in range(bsz):
+                for s in range(top_e):
+                    assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (l, t, s)
+            err = rel_err(out_to_f64(torch, out), ref["y"])
+            print(f"layer {l}: max-rel-err {err:.2e}")
+            assert err <= TOL
+            y_ref = synth.f32_to_bf16_bits(ref["y"].astype(np.float32))
+            x_next = oracle.residual_rmsnorm(x, y_ref, EPS)
+            xn = torch.empty((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_residual_rmsnorm(xd, to_dev_u16(torch, y_ref), bsz, d, EPS, xn)
+            torch.cuda.synchronize()
+            got = xn.cpu().numpy().view(np.uint16).astype(np.int64)
+            assert np.abs((got & 0x7FFF) - (x_next.astype(np.int64) & 0x7FFF)).max() <= 1
+            x = x_next
+        finally:
+            lay.close()
+
+
+def test_long_chain_on_gpu_keeps_unit_rms_and_exact_budget(b, torch):
+    """A 12-layer chain at batch 32 run on the GPU alone (two prepared layers
+    alternating, each with its own router): after every layer the hidden state is
+    finite with unit root-mean-square (to bf16 rounding) and every routed pair
+    read exactly k channels."""
+    d, E, top_e, k = W["d"], W["n_experts"], W["top_e"], W["ks"][0]
+    bsz = 32
+    lays = [Layer(b, "qwen3_48l", max_batch=bsz, layer=l) for l in (0, 1)]
+    try:
+        wrs = [to_dev_u16(torch, synth.router_weights(W["wid"], l, E, d)) for l in (0, 1)]
+        x = to_dev_u16(torch, synth.tokens(W["wid"], 0, bsz, d))
+        lg = torch.empty((bsz, E), dtype=torch.float32, device="cuda")
+        y = torch.empty((bsz, d), dtype=torch.int16, device="cuda")
+        for l in range(12):
+            lay = lays[l % 2]
+            b.moe_sel_router_logits(x, wrs[l % 2], bsz, d, E, lg)
+            b.moe_sel_forward(lay.ctx, x, lg, bsz, top_e, k, y)
+            b.moe_sel_residual_rmsnorm(x, y, bsz, d, EPS, x)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(lay.ctx)
+            xs = oracle.bf16_bits_to_f64(x.cpu().numpy().view(np.uint16))
+            assert np.all(np.isfinite(xs))
+            rms = np.sqrt((xs * xs).mean(axis=1))
+            assert np.all(np.abs(rms - 1.0) <= 1e-2), (l, rms.min(), rms.max())
+            dbg = b.moe_sel_debug_selection(lay.ctx, bsz, top_e, k, lay.m, with_scores=False)
+            assert np.all(dbg["chan_count"] == k)
+    finally:
+        for lay in lays:
+            lay.close()

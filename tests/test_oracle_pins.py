@@ -418,3 +418,49 @@ def test_batch_rows_are_independent():
         assert np.array_equal(one["y"][0], full["y"][t])
         for s in range(2):
             assert np.array_equal(one["sel"][0][s], full["sel"][t][s])
+
+
+# ---------------------------------------------------------------------------
+# Decode-step glue: router logits and the renormalised residual stream
+# ---------------------------------------------------------------------------
+def test_f64_to_bf16_ties_to_even_and_carry():
+    vals = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 255.9, -1.2, 1.6, 0.0])
+    got = oracle.f64_to_bf16_bits(vals)
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: the even neighbour 1 wins;
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: 1 + 2^-6 is even.
+    assert got.tolist() == [0x3F80, 0x3F82, 0x4380, 0xBF9A, 0x3FCD, 0x0000]
+
+
+def test_f64_to_bf16_agrees_with_float32_bit_rounding():
+    # values exactly representable in binary32: a one-step rounding from float64
+    # and the binary32 bit trick of the input generator must agree
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(4000).astype(np.float32)
+    assert np.array_equal(oracle.f64_to_bf16_bits(v.astype(np.float64)), synth.f32_to_bf16_bits(v))
+
+
+def test_router_logits_one_hot_reads_a_column():
+    rng = np.random.default_rng(4)
+    d, E = 64, 9
+    w = synth.f32_to_bf16_bits(rng.standard_normal((E, d)).astype(np.float32))
+    x = np.zeros((2, d), np.uint16)
+    x[0, 5] = 0x3F80          # 1.0
+    x[1, 17] = 0x4000         # 2.0
+    lg = oracle.router_logits(x, w)
+    assert np.array_equal(lg[0], synth.bf16_bits_to_f32(w[:, 5]))
+    assert np.array_equal(lg[1], 2 * synth.bf16_bits_to_f32(w[:, 17]))
+
+
+def test_residual_rmsnorm_hand_cases():
+    d = 4
+    x = np.zeros((3, d), np.uint16)
+    y = np.zeros((3, d), np.uint16)
+    x[0] = [0x4040, 0x4080, 0, 0]          # (3, 4, 0, 0): rms 2.5 -> (1.2, 1.6, 0, 0)
+    x[1] = [0x3F80] * 4                    # constant 1 + (-3) = -2 everywhere -> -1
+    y[1] = [0xC040] * 4
+    x[2] = [0x4120, 0xC0A0, 0x3F00, 0x4000]
+    y[2] = x[2] ^ 0x8000                   # y = -x: the sum is zero, so is the output
+    out = oracle.residual_rmsnorm(x, y)
+    assert out[0].tolist() == [0x3F9A, 0x3FCD, 0, 0]
+    assert out[1].tolist() == [0xBF80] * 4
+    assert not (out[2] & 0x7FFF).any()
