@@ -242,10 +242,13 @@ hipError_t launch_any(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, 
     f.err = c->err;
     f.chunk = chunk;
     f.nc = std::max(1, (count + chunk - 1) / chunk);
+    const bool zblocks = !dense && base.r > 0;
+    f.ncs = f.nc + (zblocks ? 1 : 0);
+    f.n_z = zblocks ? pairs : 0;
     f.n_score = dense ? 0 : pairs * (base.m / moe_sel::kGroup);
     f.n_gather = pairs * f.nc;
     f.n_combine = base.batch * (base.d / 32);
-    const long total = (long)f.n_score + f.n_gather + f.n_combine;
+    const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
     const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
     if (total <= (long)bpc * c->num_cus) {
       c->last_path = MOE_SEL_PATH_SINGLE_LAUNCH;
@@ -447,7 +450,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     const size_t fp = (size_t)ctx->fused_max_batch * c.max_top_e;
     const size_t nc_max = (m + kMinChunk - 1) / kMinChunk;
     const size_t groups = m / moe_sel::kGroup, slices = d / 64;
-    ctx->xscore_count = fp * nc_max * m;
+    ctx->xscore_count = fp * (nc_max + 1) * m;
     ctx->zpart_count = fp * groups * std::max<size_t>(r, 1);
     ctx->partial_count = (size_t)ctx->fused_max_batch * slices * c.max_top_e * nc_max * 64;
     ctx->zcopy_count = (size_t)ctx->fused_max_batch * 2 * slices * c.max_top_e * std::max<size_t>(r, 1);

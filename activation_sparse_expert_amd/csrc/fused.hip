@@ -229,12 +229,12 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   __syncthreads();
   // publish (score, h_hat) of the 64 channels to each gather block of the pair
   const int j0 = g * kGroup;
-  for (int i = tid; i < a.nc * 64; i += kThreads) {
+  for (int i = tid; i < a.ncs * 64; i += kThreads) {
     const int c = i >> 6, l = i & 63;
     const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
-    st_coh64(&a.xscore[((size_t)p * a.nc + c) * a.m + j0 + l], v);
+    st_coh64(&a.xscore[((size_t)p * a.ncs + c) * a.m + j0 + l], v);
   }
-  // this group's share of Q^T h_hat over all of its channels, for chunk 0
+  // this group's share of Q^T h_hat over all of its channels, for the z block
   if (tid < r) {
     float z = 0.0f;
 #pragma unroll 16
@@ -251,15 +251,16 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
 // gather role
 // ---------------------------------------------------------------------------
 // Waits for the pair's m (score, h_hat) values in this block's own slots (and,
-// for chunk 0, the pair's zpart slots), then selects the pair's top-k: the
+// for the z block, the pair's zpart slots), then selects the pair's top-k: the
 // selected channels ascending in s_sel[0..k), the sketch activations in s_hh,
 // the zpart values in s_zp. Chunk 0 also records the selection for inspection.
-__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, Smem& sm, float* s_hh,
-                                              uint32_t* s_keys, int* s_sel, unsigned char* s_take, float* s_zp) {
+__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
+                                              float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
+                                              float* s_zp) {
   const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
   const int groups = m / kGroup;
-  uint64_t* slots = a.xscore + ((size_t)p * a.nc + c) * m;
-  const int nzp = (c == 0) ? groups * r : 0;
+  uint64_t* slots = a.xscore + ((size_t)p * a.ncs + c) * m;
+  const int nzp = with_zpart ? groups * r : 0;
   float* zslots = a.zpart + (size_t)p * groups * r;
   block_topk_prezero(sm.hist, sm.tmp);  // ordered before the select by the polling barrier
   uint64_t v[kMaxKeysPer];
@@ -376,7 +377,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
   const int first = c * C;
   int mine = count - first;
   mine = mine < 0 ? 0 : (mine > C ? C : mine);
-  if (!DENSE) gather_select(a, p, c, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  if (!DENSE) gather_select(a, p, c, false, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int e = sm.ids[slot];
   const float wp = sm.w[slot];
   if (!DENSE && c == 0 && tid == 0) {  // routing and selection of the pair, for inspection
@@ -403,33 +404,6 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
         gv[i][u] = *(const uint4*)(row + 8 * s);
         uv[i][u] = *(const uint4*)(row + d + 8 * s);
         dv[i][u] = *(const uint4*)(row + 2 * d + 8 * s);
-      }
-    }
-  }
-  // chunk 0: z = sum_g zpart[g] - sum_{j selected} h_hat_j Q[j, :]. Thread t owns
-  // 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass;
-  // its row loads go out together with the weight loads above.
-  float zacc[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) zacc[q] = 0.0f;
-  const bool zwork = !DENSE && r > 0 && c == 0;
-  if (zwork) {
-    const int cgs = r >> 3, cg = tid % cgs, row = tid / cgs, rows_per_pass = kThreads / cgs;
-    const uint16_t* Q = a.qmat + (size_t)e * m * r + 8 * cg;
-    for (int i0 = 0; i0 < count || i0 < groups; i0 += rows_per_pass * kZPass) {
-      uint4 qv[kZPass];
-#pragma unroll
-      for (int u = 0; u < kZPass; ++u) {
-        const int i = i0 + u * rows_per_pass + row;
-        qv[u] = i < count ? *(const uint4*)(Q + (size_t)s_sel[i] * r) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kZPass; ++u) {
-        const int i = i0 + u * rows_per_pass + row;
-        if (i < count) axpy8_bf16(-s_hh[s_sel[i]], qv[u], zacc);
-        if (i < groups)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) zacc[q] += s_zp[i * r + 8 * cg + q];
       }
     }
   }
@@ -477,8 +451,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
       for (int s = 0; s < SLOTS; ++s) axpy8_bf16(h, dv[i][s], yacc[s]);
     }
   }
-  // ---- results: down partial (slice-major [t][slice][producer][64]); chunk 0
-  // also hands z to every combine block of the token
+  // ---- result: down partial (slice-major [t][slice][producer][64])
   const int slices = d / 64;
   const int qt = a.top_e * a.nc;
   const int q = slot * a.nc + c;
@@ -492,25 +465,68 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
       for (int h2 = 0; h2 < 4; ++h2) st_coh2(dst + 2 * h2, yacc[u][2 * h2], yacc[u][2 * h2 + 1]);
     }
   }
-  if (zwork) {
+}
+
+// ---------------------------------------------------------------------------
+// z role: one block per pair (sparse, r > 0), off the gather blocks' critical
+// path: it selects like a gather block, then finishes the compensation
+// coordinates z = sum_g zpart[g] - sum_{j selected} h_hat_j Q[j, :] and hands
+// z to every combine block of the token.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsigned char* dyn) {
+  const int d = a.d, m = a.m, r = a.r;
+  const int t = p / a.top_e, slot = p % a.top_e;
+  const int tid = threadIdx.x;
+  const int groups = m / kGroup;
+  float* s_hh = (float*)dyn;                            // m
+  uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
+  int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m
+  unsigned char* s_take = dyn + 12 * (size_t)m;         // m
+  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // groups * r
+  float* s_zr = s_zp + groups * r;                      // kThreads x 8, then r
+  route(a, t, sm);
+  gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const int e = sm.ids[slot];
+  const int count = a.k;
+  // thread t owns 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass
+  float zacc[8];
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) s_zr[tid * 8 + qq] = zacc[qq];
-    __syncthreads();
-    // column sums over the threads sharing a column group (once), then one copy
-    // per combine block of the token
-    const int cgs = r >> 3;
-    float* s_zc = s_zr + kThreads * 8;  // r
-    if (tid < r) {
-      float z = 0.0f;
+  for (int q = 0; q < 8; ++q) zacc[q] = 0.0f;
+  const int cgs = r >> 3, cg = tid % cgs, row = tid / cgs, rows_per_pass = kThreads / cgs;
+  const uint16_t* Q = a.qmat + (size_t)e * m * r + 8 * cg;
+  for (int i0 = 0; i0 < count || i0 < groups; i0 += rows_per_pass * kZPass) {
+    uint4 qv[kZPass];
+#pragma unroll
+    for (int u = 0; u < kZPass; ++u) {
+      const int i = i0 + u * rows_per_pass + row;
+      qv[u] = i < count ? *(const uint4*)(Q + (size_t)s_sel[i] * r) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kZPass; ++u) {
+      const int i = i0 + u * rows_per_pass + row;
+      if (i < count) axpy8_bf16(-s_hh[s_sel[i]], qv[u], zacc);
+      if (i < groups)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) zacc[q] += s_zp[i * r + 8 * cg + q];
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) s_zr[tid * 8 + qq] = zacc[qq];
+  __syncthreads();
+  // column sums over the threads sharing a column group, then one copy per
+  // combine block of the token
+  float* s_zc = s_zr + kThreads * 8;  // r
+  if (tid < r) {
+    float z = 0.0f;
 #pragma unroll 8
-      for (int th = tid >> 3; th < kThreads; th += cgs) z += s_zr[th * 8 + (tid & 7)];
-      s_zc[tid] = z;
-    }
-    __syncthreads();
-    for (int i = tid; i < 2 * slices * r; i += kThreads) {
-      const int col = i % r, half_slice = i / r;
-      st_coh(&a.zcopy[(((size_t)t * 2 * slices + half_slice) * a.top_e + slot) * r + col], s_zc[col]);
-    }
+    for (int th = tid >> 3; th < kThreads; th += cgs) z += s_zr[th * 8 + (tid & 7)];
+    s_zc[tid] = z;
+  }
+  __syncthreads();
+  const int slices = d / 64;
+  for (int i = tid; i < 2 * slices * r; i += kThreads) {
+    const int col = i % r, half_slice = i / r;
+    st_coh(&a.zcopy[(((size_t)t * 2 * slices + half_slice) * a.top_e + slot) * r + col], s_zc[col]);
   }
 }
 
@@ -638,6 +654,13 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
     return;
   }
   bid -= a.n_gather;
+  if (!DENSE) {
+    if (bid < a.n_z) {
+      z_role(a, bid, sm, s_dyn);
+      return;
+    }
+    bid -= a.n_z;
+  }
   combine_role<DENSE>(a, bid, sm, s_dyn);
 }
 
@@ -673,7 +696,7 @@ int fused_blocks_per_cu(bool dense, int d, int m, int r) {
 }
 
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream) {
-  const int total = (dense ? 0 : a.n_score) + a.n_gather + a.n_combine;
+  const int total = (dense ? 0 : a.n_score + a.n_z) + a.n_gather + a.n_combine;
   void* args[] = {(void*)&a};
   return hipLaunchKernel(fused_kernel(dense, a.d), dim3(total), dim3(kThreads), args, fused_lds_bytes(a.d, a.m, a.r),
                          stream);

@@ -70,13 +70,14 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 // Single-launch forward (fused.hip): block roles score / gather / combine.
 struct FusedArgs : FwdArgs {
   // hand-off slots, each with one consumer, empty = 0xFFFFFFFF
-  uint64_t* xscore;  // [P][nc][m]        (score, h_hat) for gather block (pair, c)
-  float* zpart;      // [P][m/64][r]      per-group share of Q^T h_hat, for chunk 0
+  uint64_t* xscore;  // [P][ncs][m]       (score, h_hat) for gather block (pair, c) / the z block
+  float* zpart;      // [P][m/64][r]      per-group share of Q^T h_hat, for the z block
   float* partial;    // [B][d/64][top_e*nc][64] gate-weighted down partials, for combine
   float* zcopy;      // [B][d/32][top_e][r] z of each routed pair, for each combine block
   int* err;          // error bits (1: gather wait timed out, 2: combine wait timed out)
-  int n_score, n_gather, n_combine;
+  int n_score, n_gather, n_z, n_combine;
   int nc;            // gather blocks per pair
+  int ncs;           // consumer slots per pair: the gather blocks, then the z block (if any)
   int chunk;         // channels per gather block
 };
 
