@@ -23,7 +23,7 @@ MOE_SEL_OK, MOE_SEL_EINVAL, MOE_SEL_EUNSUPPORTED, MOE_SEL_ENOMEM, MOE_SEL_EDEVIC
 EXPORTED = (
     "moe_sel_abi_version", "moe_sel_status_str", "moe_sel_last_error",
     "moe_sel_prepare_expert_host", "moe_sel_prepare", "moe_sel_forward",
-    "moe_sel_forward_dense", "moe_sel_debug_selection", "moe_sel_export_expert",
+    "moe_sel_forward_dense", "moe_sel_forward_threshold", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
     "moe_sel_set_path", "moe_sel_last_path", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
 )
@@ -72,6 +72,7 @@ def _load():
                                            ctypes.POINTER(vp)]),
         "moe_sel_forward": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "moe_sel_forward_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp]),
+        "moe_sel_forward_threshold": (ctypes.c_int, [vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]),
         "moe_sel_debug_selection": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp]),
         "moe_sel_export_expert": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "moe_sel_get_config": (ctypes.c_int, [vp, ctypes.POINTER(moe_sel_config)]),
@@ -173,6 +174,12 @@ def moe_sel_forward(ctx, x, logits, batch, top_e, k_budget, out, stream=None):
     st = _lib.moe_sel_forward(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e), int(k_budget),
                               _dev_ptr(out), _stream(stream))
     _check(st, "moe_sel_forward")
+
+
+def moe_sel_forward_threshold(ctx, x, logits, batch, top_e, threshold, out, stream=None):
+    _check(_lib.moe_sel_forward_threshold(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e),
+                                          float(threshold), _dev_ptr(out), _stream(stream)),
+           "moe_sel_forward_threshold")
 
 
 def moe_sel_forward_dense(ctx, x, logits, batch, top_e, out, stream=None):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -526,6 +527,27 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
   ctx->last_batch = batch;
   ctx->last_top_e = top_e;
   ctx->last_k = k_budget;
+  ctx->last_stream = (hipStream_t)stream;
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_forward_threshold(moe_sel_ctx* ctx, const uint16_t* x, const float* logits, int32_t batch,
+                                         int32_t top_e, float threshold, uint16_t* out, void* stream) {
+  g_last_error.clear();
+  moe_sel_status st = check_forward(ctx, x, logits, batch, top_e, 0, out);
+  if (st != MOE_SEL_OK) return st;
+  if (!(threshold >= 0.0f) || !std::isfinite(threshold))
+    return fail(MOE_SEL_EINVAL, "threshold must be finite and non-negative");
+  DeviceGuard guard(ctx->device);
+  moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, 0, out);
+  a.thr_mode = 1;
+  std::memcpy(&a.thr_bits, &threshold, 4);
+  const hipError_t e = moe_sel::launch_forward(a, false, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  ctx->last_path = MOE_SEL_PATH_MULTI_KERNEL;
+  ctx->last_batch = batch;
+  ctx->last_top_e = top_e;
+  ctx->last_k = ctx->cfg.m;  // selections vary in length: rows of m entries, chan_count valid
   ctx->last_stream = (hipStream_t)stream;
   return MOE_SEL_OK;
 }

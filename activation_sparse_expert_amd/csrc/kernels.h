@@ -21,6 +21,8 @@ struct FwdArgs {
   const float* logits;     // [B][E]
   uint16_t* out;           // [B][d] bf16
   int batch, top_e, k;
+  int thr_mode;            // 1: keep channels with score > thr_bits instead of the top k
+  uint32_t thr_bits;       // binary32 bits of the (non-negative) threshold
   // workspace
   int8_t* xq;              // [B][d]
   int* xexp;               // [B]

@@ -527,6 +527,15 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
       }
     }
   }
+  if (a.thr_mode) {
+    // threshold selector: every channel whose score exceeds the threshold
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = tid + u * kThreads;
+      if (j < m && key[u] > a.thr_bits) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+    }
+  }
   __syncthreads();
   // ascending index list from the bitmap
   int* idx_out = a.sel_idx + (size_t)p * m;
@@ -952,7 +961,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
   // the largest union a tile can have: k channels per token, at most m
-  const int kmax = dense ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
+  const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
   const int kc = grouped_down_split(a.max_tiles, a.d, kmax, dense ? 0 : a.r);
   if (sw == 256)
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);

@@ -111,13 +111,16 @@ class Block:
                 lgs.append(torch.from_numpy(lb).to("cuda"))
                 outs.append(torch.zeros((bsz, d), dtype=torch.int16, device="cuda"))
 
-    def launch(self, n, k, bsz):
-        """Enqueue n forwards of `bsz` tokens (k=None: the dense-read block) on the stream."""
+    def launch(self, n, k, bsz, thr=None):
+        """Enqueue n forwards of `bsz` tokens (k=None: the dense-read block; thr: the
+        threshold selector) on the stream."""
         b, w, s = self.b, self.w, self.stream.cuda_stream
         xs, lgs, outs = self.inputs[bsz]
         for i in range(n):
             l, t = i % self.copies, (i // self.copies) % self.ntok
-            if k is None:
+            if thr is not None:
+                b.moe_sel_forward_threshold(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], thr, outs[l], s)
+            elif k is None:
                 b.moe_sel_forward_dense(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], outs[l], s)
             else:
                 b.moe_sel_forward(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], k, outs[l], s)
@@ -127,35 +130,35 @@ class Block:
             self.b.moe_sel_destroy(c)
 
 
-def time_block(torch, blk, k, steps, warmup, eager, bsz):
+def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None):
     """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones."""
     R = blk.copies * blk.ntok
     stream = blk.stream
     with torch.cuda.stream(stream):
-        blk.launch(R, k, bsz)  # eager pass over every (layer, token batch)
+        blk.launch(R, k, bsz, thr)  # eager pass over every (layer, token batch)
     torch.cuda.synchronize()
     for c in blk.ctxs:
         blk.b.moe_sel_check_device(c)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if eager:
         with torch.cuda.stream(stream):
-            blk.launch(warmup, k, bsz)
+            blk.launch(warmup, k, bsz, thr)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            blk.launch(steps, k, bsz)
+            blk.launch(steps, k, bsz, thr)
             ev1.record(stream)
         torch.cuda.synchronize()
     else:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            blk.launch(R, k, bsz)
+            blk.launch(R, k, bsz, thr)
         rem = steps % R
         g_rem = None
         if rem:
             g_rem = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_rem, stream=stream):
-                blk.launch(rem, k, bsz)
+                blk.launch(rem, k, bsz, thr)
         with torch.cuda.stream(stream):
             for _ in range(max(1, math.ceil(warmup / R))):
                 g.replay()
@@ -218,6 +221,8 @@ def main():
                     help="also time a 48-layer decode step at batch 1, 8 and 32 (0: skip)")
     ap.add_argument("--decode-layers", type=int, default=12, help="distinct prepared layers in the 48-layer stack")
     ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--threshold", type=int, default=1,
+                    help="also compare the calibrated threshold selector with top-k (0: skip)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -331,6 +336,8 @@ def main():
         }
         result["speedup_vs_dense"] = round(ms_dense / ms, 3)
 
+    if args.threshold and args.big_batch == 64:
+        result["threshold_vs_topk"] = threshold_experiment(b, synth, torch, blk, k, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(blk.host_layer0, w, k, args.cpu_seconds)
     blk.destroy()
@@ -341,6 +348,40 @@ def main():
         result["decode48"] = time_decode48(b, synth, torch, stream, args.decode_layers, args.decode_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def threshold_experiment(b, synth, torch, blk, k, steps, warmup):
+    """The calibrated threshold selector on the same scores as top-k: threshold set
+    on 64 calibration tokens for the 18% mean read, per-token read fractions on 256
+    other tokens, and the batch-1 time per call of both selectors."""
+    from activation_sparse_expert_amd import threshold as th
+    w = blk.w
+    d, m, n_exp, top_e = w["d"], w["m"], w["n_experts"], w["top_e"]
+    ctx, s = blk.ctxs[0], blk.stream.cuda_stream
+    out = torch.zeros((64, d), dtype=torch.int16, device="cuda")
+
+    def batch(i):
+        x = torch.from_numpy(synth.tokens(w["wid"], 0, 64, d, index=1000 + i).view(np.int16)).to("cuda")
+        lg = torch.from_numpy(synth.router_logits(w["wid"], 0, 64, n_exp, "normal", index=1000 + i)).to("cuda")
+        return x, lg
+
+    x, lg = batch(0)
+    b.moe_sel_forward(ctx, x, lg, 64, top_e, k, out, s)
+    scores = b.moe_sel_debug_selection(ctx, 64, top_e, k, m, with_scores=True)["score"]
+    thr = th.calibrate(scores, 0.18)
+    fr = []
+    for i in range(1, 5):
+        x, lg = batch(i)
+        b.moe_sel_forward_threshold(ctx, x, lg, 64, top_e, thr, out, s)
+        cnt = b.moe_sel_debug_selection(ctx, 64, top_e, m, m, with_scores=False)["chan_count"]
+        fr.append(th.read_fractions(cnt, m))
+    torch.cuda.synchronize()
+    ms_thr = time_block(torch, blk, None, steps // 4, warmup // 4, False, 1, thr=thr)
+    return {"calibration": "threshold on the scores of 64 calibration tokens for an 18% mean read",
+            "threshold": thr, "test_tokens": 256, "threshold_read_fraction": th.summary(np.concatenate(fr)),
+            "topk_read_fraction": round(k / m, 5),
+            "batch1_threshold_tokens_per_s": round(1 / (ms_thr * 1e-3), 1),
+            "batch1_threshold_path": "expert-grouped multi-kernel (counts vary per pair)"}
 
 
 def time_mixtral(b, synth, torch, stream, steps, eager):

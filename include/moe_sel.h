@@ -162,6 +162,22 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
                                uint16_t* out, void* stream);
 
 /*
+ * The threshold selector the pages contrast with top-k ("KAIST drops
+ * calibration from MoE decoding...", section "The threshold promises a budget
+ * but does not keep it"): each routed pair keeps every channel whose score
+ * (the same score as moe_sel_forward) is strictly above `threshold`, so the
+ * number of channels read varies from token to token. Everything else (scores,
+ * compensation of the skipped channels, combine) is as in moe_sel_forward.
+ * Runs on the multi-kernel path. moe_sel_debug_selection afterwards returns
+ * rows of m channel indices of which the first chan_count are valid.
+ *   threshold  finite, >= 0 (scores are non-negative)
+ * Other arguments and errors as moe_sel_forward.
+ */
+moe_sel_status moe_sel_forward_threshold(moe_sel_ctx* ctx, const uint16_t* x, const float* logits,
+                                         int32_t batch, int32_t top_e, float threshold,
+                                         uint16_t* out, void* stream);
+
+/*
  * The dense routed block on the same layout (every channel of every routed
  * expert is read, no sketch and no compensation): the baseline the selective
  * block is measured against. Arguments and errors as moe_sel_forward.

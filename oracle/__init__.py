@@ -20,6 +20,7 @@ from .moe_oracle import (  # noqa: F401
     route,
     router_logits,
     score_channels,
+    select_threshold,
     select_topk,
     silu_pinned,
     sketch_preacts,

@@ -258,6 +258,14 @@ def select_topk(score: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int64)
 
 
+def select_threshold(score: np.ndarray, threshold: float) -> np.ndarray:
+    """The threshold selector the pages contrast with top-k ([KAIST] "The threshold
+    promises a budget but does not keep it": channels whose score exceeds a
+    threshold tuned offline): indices with score > threshold, compared in binary32,
+    ascending. The number kept varies from token to token."""
+    return np.flatnonzero(np.asarray(score, np.float32) > np.float32(threshold))
+
+
 def expert_swiglu_selected(prep: dict, x: np.ndarray, sel: np.ndarray) -> np.ndarray:
     """Expert output from the selected channels only: sum_{j in S} silu(g_j) u_j down_j.
 
@@ -309,8 +317,12 @@ class OracleLayer:
             self._prep[e] = prepare_expert(wg, wu, wd, self.rank, self.tern_ratio)
         return self._prep[e]
 
-    def forward(self, x_bits: np.ndarray, logits: np.ndarray, top_e: int, k: int, compensate: bool = True):
+    def forward(self, x_bits: np.ndarray, logits: np.ndarray, top_e: int, k: int, compensate: bool = True,
+                threshold: float | None = None):
         """Selected-channel block for a batch; every token uses only its own channels.
+
+        With ``threshold`` given, each pair keeps the channels whose score exceeds
+        it instead of its top k (``k`` is then ignored).
 
         Returns a dict with y float64 [B][d] and, per token, the routed experts,
         gate weights, selected channels (ascending), h_hat and scores.
@@ -330,7 +342,7 @@ class OracleLayer:
             for slot, ex in enumerate(ids[t]):
                 prep = self.expert(ex)
                 h_hat, sc = score_channels(prep, q, e_t)
-                sel = select_topk(sc, k)
+                sel = select_topk(sc, k) if threshold is None else select_threshold(sc, threshold)
                 part = expert_swiglu_selected(prep, x, sel)
                 if compensate:
                     part = part + compensation(prep, h_hat, sel)

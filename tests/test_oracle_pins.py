@@ -464,3 +464,31 @@ def test_residual_rmsnorm_hand_cases():
     assert out[0].tolist() == [0x3F9A, 0x3FCD, 0, 0]
     assert out[1].tolist() == [0xBF80] * 4
     assert not (out[2] & 0x7FFF).any()
+
+
+# ---------------------------------------------------------------------------
+# Threshold selector (the baseline the pages contrast with top-k)
+# ---------------------------------------------------------------------------
+def test_threshold_just_below_the_kth_score_is_topk():
+    rng = np.random.default_rng(21)
+    for k in (1, 7, 40, 99):
+        sc = rng.random(100).astype(np.float32)   # distinct with probability one
+        kth = np.sort(sc)[::-1][k - 1]
+        thr = np.nextafter(kth, np.float32(-1.0))
+        assert np.array_equal(oracle.select_threshold(sc, thr), oracle.select_topk(sc, k))
+
+
+def test_threshold_edges_and_ties():
+    sc = np.array([0.0, 0.5, 0.5, 1.0, 0.25], np.float32)
+    assert oracle.select_threshold(sc, 1.0).tolist() == []           # strict: the maximum itself is not above
+    assert oracle.select_threshold(sc, 0.5).tolist() == [3]
+    assert oracle.select_threshold(sc, 0.25).tolist() == [1, 2, 3]   # equal scores move together
+    assert oracle.select_threshold(sc, 0.0).tolist() == [1, 2, 3, 4]
+
+
+def test_threshold_calibration_keeps_the_budget_on_its_own_sample():
+    from activation_sparse_expert_amd import threshold as th
+    rng = np.random.default_rng(22)
+    sc = rng.random((64, 8, 768)).astype(np.float32)
+    thr = th.calibrate(sc, 0.18)
+    assert abs((sc > np.float32(thr)).mean() - 0.18) <= 1.0 / sc.size
