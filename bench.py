@@ -111,54 +111,56 @@ class Block:
                 lgs.append(torch.from_numpy(lb).to("cuda"))
                 outs.append(torch.zeros((bsz, d), dtype=torch.int16, device="cuda"))
 
-    def launch(self, n, k, bsz, thr=None):
+    def launch(self, n, k, bsz, thr=None, top_e=None):
         """Enqueue n forwards of `bsz` tokens (k=None: the dense-read block; thr: the
-        threshold selector) on the stream."""
-        b, w, s = self.b, self.w, self.stream.cuda_stream
+        threshold selector; top_e: routed experts per token, default the trained
+        count) on the stream."""
+        b, s = self.b, self.stream.cuda_stream
+        te = self.w["top_e"] if top_e is None else top_e
         xs, lgs, outs = self.inputs[bsz]
         for i in range(n):
             l, t = i % self.copies, (i // self.copies) % self.ntok
             if thr is not None:
-                b.moe_sel_forward_threshold(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], thr, outs[l], s)
+                b.moe_sel_forward_threshold(self.ctxs[l], xs[l][t], lgs[l][t], bsz, te, thr, outs[l], s)
             elif k is None:
-                b.moe_sel_forward_dense(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], outs[l], s)
+                b.moe_sel_forward_dense(self.ctxs[l], xs[l][t], lgs[l][t], bsz, te, outs[l], s)
             else:
-                b.moe_sel_forward(self.ctxs[l], xs[l][t], lgs[l][t], bsz, w["top_e"], k, outs[l], s)
+                b.moe_sel_forward(self.ctxs[l], xs[l][t], lgs[l][t], bsz, te, k, outs[l], s)
 
     def destroy(self):
         for c in self.ctxs:
             self.b.moe_sel_destroy(c)
 
 
-def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None):
+def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None, top_e=None):
     """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones."""
     R = blk.copies * blk.ntok
     stream = blk.stream
     with torch.cuda.stream(stream):
-        blk.launch(R, k, bsz, thr)  # eager pass over every (layer, token batch)
+        blk.launch(R, k, bsz, thr, top_e)  # eager pass over every (layer, token batch)
     torch.cuda.synchronize()
     for c in blk.ctxs:
         blk.b.moe_sel_check_device(c)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if eager:
         with torch.cuda.stream(stream):
-            blk.launch(warmup, k, bsz, thr)
+            blk.launch(warmup, k, bsz, thr, top_e)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            blk.launch(steps, k, bsz, thr)
+            blk.launch(steps, k, bsz, thr, top_e)
             ev1.record(stream)
         torch.cuda.synchronize()
     else:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            blk.launch(R, k, bsz, thr)
+            blk.launch(R, k, bsz, thr, top_e)
         rem = steps % R
         g_rem = None
         if rem:
             g_rem = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_rem, stream=stream):
-                blk.launch(rem, k, bsz, thr)
+                blk.launch(rem, k, bsz, thr, top_e)
         with torch.cuda.stream(stream):
             for _ in range(max(1, math.ceil(warmup / R))):
                 g.replay()
@@ -221,6 +223,8 @@ def main():
                     help="also time a 48-layer decode step at batch 1, 8 and 32 (0: skip)")
     ap.add_argument("--decode-layers", type=int, default=12, help="distinct prepared layers in the 48-layer stack")
     ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--expert-sweep", type=int, default=1,
+                    help="also sweep routed experts per token below the trained count (0: skip)")
     ap.add_argument("--threshold", type=int, default=1,
                     help="also compare the calibrated threshold selector with top-k (0: skip)")
     args = ap.parse_args()
@@ -336,6 +340,8 @@ def main():
         }
         result["speedup_vs_dense"] = round(ms_dense / ms, 3)
 
+    if args.expert_sweep:
+        result["expert_count_sweep"] = expert_sweep(b, synth, torch, blk, args.steps // 2, args.warmup // 2)
     if args.threshold and args.big_batch == 64:
         result["threshold_vs_topk"] = threshold_experiment(b, synth, torch, blk, k, args.steps, args.warmup)
     if not args.no_cpu_baseline:
@@ -348,6 +354,41 @@ def main():
         result["decode48"] = time_decode48(b, synth, torch, stream, args.decode_layers, args.decode_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def expert_sweep(b, synth, torch, blk, steps, warmup, tops=(8, 6, 4, 2), n_dev=16):
+    """Routed experts per token below the trained top-8 composed with the channel
+    budget: batch-1 tokens/s, and the deviation from the dense top-8 block
+    (max over n_dev tokens of ||out - dense||_inf / ||dense||_inf)."""
+    w = blk.w
+    d, m, n_exp, top_e_trained = w["d"], w["m"], w["n_experts"], w["top_e"]
+    ctx, s = blk.ctxs[0], blk.stream.cuda_stream
+    x = torch.from_numpy(synth.tokens(w["wid"], 0, n_dev, d, index=2000).view(np.int16)).to("cuda")
+    lg = torch.from_numpy(synth.router_logits(w["wid"], 0, n_dev, n_exp, "normal", index=2000)).to("cuda")
+    ref = torch.zeros((n_dev, d), dtype=torch.int16, device="cuda")
+    b.moe_sel_forward_dense(ctx, x, lg, n_dev, top_e_trained, ref, s)
+    torch.cuda.synchronize()
+    ref_f = ref.view(torch.bfloat16).float().cpu().numpy()
+
+    def deviation(top_e, k):
+        o = torch.zeros((n_dev, d), dtype=torch.int16, device="cuda")
+        if k is None:
+            b.moe_sel_forward_dense(ctx, x, lg, n_dev, top_e, o, s)
+        else:
+            b.moe_sel_forward(ctx, x, lg, n_dev, top_e, k, o, s)
+        torch.cuda.synchronize()
+        of = o.view(torch.bfloat16).float().cpu().numpy()
+        return round(float((np.abs(of - ref_f).max(axis=1) / np.abs(ref_f).max(axis=1)).max()), 4)
+
+    rows = []
+    for top_e in tops:
+        for k in list(w["ks"]) + [None]:
+            ms = time_block(torch, blk, k, steps, warmup, False, 1, top_e=top_e)
+            rows.append({"top_e": top_e, "k": k if k is not None else m,
+                         "selector": "top-k" if k is not None else "dense",
+                         "tokens_per_s": round(1 / (ms * 1e-3), 1), "max_rel_dev_vs_dense_top8": deviation(top_e, k)})
+    return {"reference": f"dense block with the trained top-{top_e_trained}", "tokens_for_deviation": n_dev,
+            "rows": rows}
 
 
 def threshold_experiment(b, synth, torch, blk, k, steps, warmup):

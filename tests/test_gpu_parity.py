@@ -404,3 +404,15 @@ def test_mixtral_shape_parity(b, torch, mixtral, k):
     print(f"mixtral k={k}: max-rel-err {err:.2e}")
     assert err <= TOL
     assert abs(k / mixtral.m - {1864: 0.13, 2580: 0.18}[k]) <= 1 / (2 * mixtral.m)
+
+
+@pytest.mark.parametrize("top_e", [4, 2])
+def test_qwen3_fewer_routed_experts_than_trained(b, torch, qwen, top_e):
+    """Routing to fewer experts than the trained top-8, composed with the budget."""
+    w = synth.WORKLOADS["qwen3"]
+    x = synth.tokens(w["wid"], 0, 1, qwen.d, index=3)
+    logits = synth.router_logits(w["wid"], 0, 1, qwen.E, index=3)
+    out = _run(b, torch, qwen, x, logits, 138, top_e=top_e)
+    ref = qwen.oracle.forward(x, logits, top_e, 138)
+    _check_selection(b, qwen, ref, 1, top_e, 138)
+    assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
