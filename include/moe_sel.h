@@ -69,8 +69,10 @@ typedef enum moe_sel_status {
 
 /* How a forward call is executed on the GPU (same results either way). */
 typedef enum moe_sel_path {
-  MOE_SEL_PATH_AUTO = 0,          /* single launch when it fits, else one kernel per phase */
-  MOE_SEL_PATH_MULTI_KERNEL = 1,  /* one kernel per phase (any batch and shape) */
+  MOE_SEL_PATH_AUTO = 0,          /* single launch when it fits, else the multi-kernel path */
+  MOE_SEL_PATH_MULTI_KERNEL = 1,  /* pairs grouped by expert into tiles of up to 32 tokens, one kernel
+                                     per phase; every weight byte an expert needs is read once per
+                                     tile (the union of the tile tokens' selections) */
   MOE_SEL_PATH_SINGLE_LAUNCH = 2  /* one fused kernel; EUNSUPPORTED when it cannot be used */
 } moe_sel_path;
 
@@ -79,7 +81,8 @@ typedef struct moe_sel_config {
   uint32_t struct_size;  /* must be sizeof(moe_sel_config) */
   int32_t d;             /* hidden size: multiple of 64, 64 .. 16384 */
   int32_t n_experts;     /* experts E: 1 .. 1024 */
-  int32_t m;             /* intermediate channels per expert: multiple of 64, 64 .. 32768 */
+  int32_t m;             /* intermediate channels per expert: multiple of 64, 64 .. 32768
+                            (moe_sel_prepare supports m <= 16384: EUNSUPPORTED above) */
   int32_t rank;          /* compensation rank r: 0 .. min(d, m, 128) */
   int32_t max_top_e;     /* experts per token the layer was trained with: 1 .. min(E, 64) */
   int32_t max_batch;     /* largest batch a forward call may pass: 1 .. 4096 */
@@ -130,13 +133,19 @@ moe_sel_status moe_sel_prepare_expert_host(const moe_sel_config* cfg,
  * Build a context for one MoE layer: per-expert sketches, channel statistics
  * and low-rank maps (as moe_sel_prepare_expert_host), the channel-major weight
  * layout, and a workspace for cfg->max_batch tokens, all in device memory of
- * the current HIP device.
+ * the current HIP device. The sketches and statistics are computed on the host
+ * (exact sums); the low-rank maps are computed on the device in fp64 for all
+ * experts at once (Gram matrices, tridiagonalisation and projection on the GPU,
+ * the tridiagonal eigen-solves on host threads), or on the host when the
+ * environment variable MOE_SEL_LOWRANK is "host" (the same eigen-solver).
  *   w_gate, w_up [E][m][d], w_down [E][d][m]: host bf16 bit patterns.
- *   stream: hipStream_t used for the uploads (null = default stream). The call
- *           synchronises it before returning, so the caller may free the inputs.
+ *   stream: hipStream_t used for the uploads and the device work (null =
+ *           default stream). The call synchronises it before returning, so the
+ *           caller may free the inputs.
  *   out:    receives the new context (unchanged on error).
- * Errors: EINVAL (null pointer, invalid config), ENOMEM (host/device
- * allocation), EDEVICE (HIP error). Nothing is leaked on error.
+ * Errors: EINVAL (null pointer, invalid config), EUNSUPPORTED (m > 16384),
+ * ENOMEM (host/device allocation), EDEVICE (HIP error). Nothing is leaked on
+ * error.
  */
 moe_sel_status moe_sel_prepare(const moe_sel_config* cfg,
                                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
