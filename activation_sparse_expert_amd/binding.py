@@ -25,10 +25,11 @@ EXPORTED = (
     "moe_sel_prepare_expert_host", "moe_sel_prepare", "moe_sel_forward",
     "moe_sel_forward_dense", "moe_sel_forward_threshold", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
-    "moe_sel_set_path", "moe_sel_last_path", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
+    "moe_sel_set_path", "moe_sel_last_path", "moe_sel_set_score", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
+MOE_SEL_SCORE_FULL, MOE_SEL_SCORE_GATE_ONLY, MOE_SEL_SCORE_NO_DOWN_NORM = range(3)
 
 
 class moe_sel_config(ctypes.Structure):
@@ -81,6 +82,7 @@ def _load():
         "moe_sel_check_device": (ctypes.c_int, [vp]),
         "moe_sel_set_path": (ctypes.c_int, [vp, ctypes.c_int]),
         "moe_sel_last_path": (i32, [vp]),
+        "moe_sel_set_score": (ctypes.c_int, [vp, ctypes.c_int]),
         "moe_sel_router_logits": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "moe_sel_residual_rmsnorm": (ctypes.c_int, [vp, vp, i32, i32, ctypes.c_float, vp, vp]),
     }
@@ -233,6 +235,10 @@ def moe_sel_check_device(ctx):
 
 def moe_sel_set_path(ctx, path: int):
     _check(_lib.moe_sel_set_path(ctx, int(path)), "moe_sel_set_path")
+
+
+def moe_sel_set_score(ctx, kind: int):
+    _check(_lib.moe_sel_set_score(ctx, int(kind)), "moe_sel_set_score")
 
 
 def moe_sel_last_path(ctx) -> int:

@@ -61,6 +61,7 @@ struct moe_sel_ctx {
   int num_cus = 0;
   int fused_bpc_sparse = 0, fused_bpc_dense = 0;
   moe_sel_path path = MOE_SEL_PATH_AUTO;
+  moe_sel_score score_kind = MOE_SEL_SCORE_FULL;
   int last_path = -1;
   std::vector<void*> allocations;
   uint64_t device_bytes = 0;
@@ -194,6 +195,7 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.batch = batch;
   a.top_e = top_e;
   a.k = k;
+  a.score_kind = (int)c->score_kind;
   a.xq = c->xq;
   a.xexp = c->xexp;
   a.pair_expert = c->pair_expert;
@@ -667,6 +669,15 @@ moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path) {
 }
 
 int32_t moe_sel_last_path(const moe_sel_ctx* ctx) { return ctx ? ctx->last_path : -1; }
+
+moe_sel_status moe_sel_set_score(moe_sel_ctx* ctx, moe_sel_score kind) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (kind != MOE_SEL_SCORE_FULL && kind != MOE_SEL_SCORE_GATE_ONLY && kind != MOE_SEL_SCORE_NO_DOWN_NORM)
+    return fail(MOE_SEL_EINVAL, "unknown score kind");
+  ctx->score_kind = kind;
+  return MOE_SEL_OK;
+}
 
 moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg) {
   if (!ctx || !cfg) return fail(MOE_SEL_EINVAL, "ctx and cfg must be non-null");

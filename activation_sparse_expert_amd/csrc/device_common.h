@@ -48,12 +48,16 @@ __device__ __forceinline__ float silu_pinned(float z) {
 
 // Channel score from the exact integer sketch dots: G = alpha_g * Dg * 2^xexp,
 // U = alpha_u * Du * 2^xexp, h = silu_pinned(G) * U, score = |h| * ||down||.
-__device__ __forceinline__ void pinned_score(int dg, int du, int xexp, float4 st, float& h, float& score) {
+// kind (ablations of the score; h is the same for all): 0 = |h| * ||down||,
+// 1 = |silu_pinned(G)| * ||down|| (gate sketch only), 2 = |h| (no down norm).
+__device__ __forceinline__ void pinned_score(int dg, int du, int xexp, float4 st, float& h, float& score,
+                                             int kind = 0) {
 #pragma clang fp contract(off)
   const float g = __builtin_ldexpf(st.x * (float)dg, xexp);
   const float u = __builtin_ldexpf(st.y * (float)du, xexp);
-  h = silu_pinned(g) * u;
-  score = __builtin_fabsf(h) * st.z;
+  const float sg = silu_pinned(g);
+  h = sg * u;
+  score = kind == 1 ? __builtin_fabsf(sg) * st.z : (kind == 2 ? __builtin_fabsf(h) : __builtin_fabsf(h) * st.z);
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }

@@ -222,7 +222,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     const int dg = s_part[lane] + s_part[64 + lane];
     const int du = s_part[128 + lane] + s_part[192 + lane];
     float h, sc;
-    pinned_score(dg, du, e_t, st, h, sc);
+    pinned_score(dg, du, e_t, st, h, sc, a.score_kind);
     s_h[lane] = h;
     s_sc[lane] = sc;
   }

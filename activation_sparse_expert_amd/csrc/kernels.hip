@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
       const int xe = a.xexp[t], qs = a.xqsum[t];
       float h[4], sc[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) pinned_score(accg[v] - qs, accu[v] - qs, xe, st[v], h[v], sc[v]);
+      for (int v = 0; v < 4; ++v) pinned_score(accg[v] - qs, accu[v] - qs, xe, st[v], h[v], sc[v], a.score_kind);
       *(float4*)(a.hhat + (size_t)pp * m + ch0) = make_float4(h[0], h[1], h[2], h[3]);
       *(float4*)(a.score + (size_t)pp * m + ch0) = make_float4(sc[0], sc[1], sc[2], sc[3]);
       if (r > 0)

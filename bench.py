@@ -342,6 +342,7 @@ def main():
 
     if args.expert_sweep:
         result["expert_count_sweep"] = expert_sweep(b, synth, torch, blk, args.steps // 2, args.warmup // 2)
+        result["score_ablation"] = score_ablation(b, torch, blk, w["ks"])
     if args.threshold and args.big_batch == 64:
         result["threshold_vs_topk"] = threshold_experiment(b, synth, torch, blk, k, args.steps, args.warmup)
     if not args.no_cpu_baseline:
@@ -425,6 +426,39 @@ def threshold_experiment(b, synth, torch, blk, k, steps, warmup):
             "batch1_threshold_path": "expert-grouped multi-kernel (counts vary per pair)"}
 
 
+def score_ablation(b, torch, blk, ks, n_tok=4):
+    """Deviation from the dense block (max over n_tok batch-1 tokens of
+    ||out - dense||_inf / ||dense||_inf) for each channel score kind and budget."""
+    w = blk.w
+    ctx, s = blk.ctxs[0], blk.stream.cuda_stream
+    xs, lgs, _ = blk.inputs[1]
+    top_e = w["top_e"]
+    kinds = {"full": b.MOE_SEL_SCORE_FULL, "gate_only": b.MOE_SEL_SCORE_GATE_ONLY,
+             "no_down_norm": b.MOE_SEL_SCORE_NO_DOWN_NORM}
+
+    def run(k, kind=None):
+        outs = []
+        for t in range(n_tok):
+            o = torch.zeros((1, w["d"]), dtype=torch.int16, device="cuda")
+            if k is None:
+                b.moe_sel_forward_dense(ctx, xs[0][t], lgs[0][t], 1, top_e, o, s)
+            else:
+                b.moe_sel_forward(ctx, xs[0][t], lgs[0][t], 1, top_e, k, o, s)
+            outs.append(o)
+        torch.cuda.synchronize()
+        return np.concatenate([o.view(torch.bfloat16).float().cpu().numpy() for o in outs])
+
+    dense = run(None)
+    res = {}
+    for name, code in kinds.items():
+        b.moe_sel_set_score(ctx, code)
+        for k in ks:
+            o = run(k)
+            res[f"{name}_k{k}"] = round(float((np.abs(o - dense).max(axis=1) / np.abs(dense).max(axis=1)).max()), 4)
+    b.moe_sel_set_score(ctx, b.MOE_SEL_SCORE_FULL)
+    return {"max_rel_dev_vs_dense": res, "tokens": n_tok}
+
+
 def time_mixtral(b, synth, torch, stream, steps, eager):
     """Mixtral-8x7B-shaped block (d=4096, 8 experts, top-2, m=14336, r=64, LogNormal
     channel scales) at batch 1: both budgets and the dense-read block, over two
@@ -449,6 +483,7 @@ def time_mixtral(b, synth, torch, stream, steps, eager):
                     "algorithmic_bytes": byt, "achieved_GBs": round(byt / (ms_d * 1e-3) / 1e9, 1)}
     for k in w["ks"]:
         out[f"k{k}"]["speedup_vs_dense"] = round(ms_d / out[f"k{k}"]["ms_per_step"], 3)
+    out["score_ablation"] = score_ablation(b, torch, blk, w["ks"])
     blk.destroy()
     return out
 

@@ -68,6 +68,12 @@ typedef enum moe_sel_status {
 } moe_sel_status;
 
 /* How a forward call is executed on the GPU (same results either way). */
+typedef enum moe_sel_score {
+  MOE_SEL_SCORE_FULL = 0,          /* |silu(G) U| * ||down column|| (the default reading) */
+  MOE_SEL_SCORE_GATE_ONLY = 1,     /* |silu(G)| * ||down column|| */
+  MOE_SEL_SCORE_NO_DOWN_NORM = 2   /* |silu(G) U| */
+} moe_sel_score;
+
 typedef enum moe_sel_path {
   MOE_SEL_PATH_AUTO = 0,          /* single launch when it fits, else the multi-kernel path */
   MOE_SEL_PATH_MULTI_KERNEL = 1,  /* pairs grouped by expert into tiles of up to 32 tokens, one kernel
@@ -233,6 +239,20 @@ moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx);
  * Errors: EINVAL (null ctx or unknown path).
  */
 moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path);
+
+/*
+ * Channel score used by later forward calls on this context (default
+ * MOE_SEL_SCORE_FULL). The pages leave the score open ("KAIST drops calibration
+ * from MoE decoding...", section "A reader built from weights alone": channels
+ * are filtered with a ternary sketch); the alternatives are ablations of the
+ * default reading. Only the ranking changes: the sketch activations used by
+ * the compensation are the same for all kinds.
+ *   MOE_SEL_SCORE_FULL          |silu(G) * U| * ||W_down[:, j]||_2
+ *   MOE_SEL_SCORE_GATE_ONLY     |silu(G)| * ||W_down[:, j]||_2 (up sketch ignored)
+ *   MOE_SEL_SCORE_NO_DOWN_NORM  |silu(G) * U|
+ * Errors: EINVAL (null ctx or unknown kind).
+ */
+moe_sel_status moe_sel_set_score(moe_sel_ctx* ctx, moe_sel_score kind);
 
 /* Path taken by the last forward call on this context (MOE_SEL_PATH_MULTI_KERNEL
  * or MOE_SEL_PATH_SINGLE_LAUNCH), or -1 if none ran yet or ctx is null. */

@@ -9,6 +9,7 @@ See ``oracle.moe_oracle`` for the computation and the passages it follows.
 """
 from .moe_oracle import (  # noqa: F401
     ORACLE_CONSTANTS,
+    SCORE_KINDS,
     OracleLayer,
     bf16_bits_to_f64,
     compensation,

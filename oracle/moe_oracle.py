@@ -233,7 +233,10 @@ def sketch_preacts(prep: dict, q: np.ndarray, e: int):
     return g, u
 
 
-def score_channels(prep: dict, q: np.ndarray, e: int):
+SCORE_KINDS = ("full", "gate_only", "no_down_norm")
+
+
+def score_channels(prep: dict, q: np.ndarray, e: int, kind: str = "full"):
     """Sketch activations and channel scores for one (token, expert) pair.
 
     [KAIST] "The threshold promises a budget...": a channel matters when it
@@ -242,11 +245,21 @@ def score_channels(prep: dict, q: np.ndarray, e: int):
     U_hat = alpha_u * (t_u . q) * 2^e (integer dots are exact, each product
     rounded once to binary32, the power of two applied exactly);
     h_hat = silu_pinned(G_hat) * U_hat; score = |h_hat| * ||down_j||_2.
+    Ablations of the score (the pages leave it open; h_hat is unchanged):
+    ``gate_only``: |silu_pinned(G_hat)| * ||down_j||_2; ``no_down_norm``: |h_hat|.
     Returns (h_hat float32 [m], score float32 [m]).
     """
     g, u = sketch_preacts(prep, q, e)
-    h = (silu_pinned(g) * u).astype(F32)
-    score = (np.abs(h) * prep["c"].astype(F32)).astype(F32)
+    sg = silu_pinned(g)
+    h = (sg * u).astype(F32)
+    if kind == "full":
+        score = (np.abs(h) * prep["c"].astype(F32)).astype(F32)
+    elif kind == "gate_only":
+        score = (np.abs(sg) * prep["c"].astype(F32)).astype(F32)
+    elif kind == "no_down_norm":
+        score = np.abs(h).astype(F32)
+    else:
+        raise ValueError(f"unknown score kind {kind!r}")
     return h, score
 
 
@@ -318,7 +331,7 @@ class OracleLayer:
         return self._prep[e]
 
     def forward(self, x_bits: np.ndarray, logits: np.ndarray, top_e: int, k: int, compensate: bool = True,
-                threshold: float | None = None):
+                threshold: float | None = None, score_kind: str = "full"):
         """Selected-channel block for a batch; every token uses only its own channels.
 
         With ``threshold`` given, each pair keeps the channels whose score exceeds
@@ -341,7 +354,7 @@ class OracleLayer:
             row_s, row_h, row_sc = [], [], []
             for slot, ex in enumerate(ids[t]):
                 prep = self.expert(ex)
-                h_hat, sc = score_channels(prep, q, e_t)
+                h_hat, sc = score_channels(prep, q, e_t, score_kind)
                 sel = select_topk(sc, k) if threshold is None else select_threshold(sc, threshold)
                 part = expert_swiglu_selected(prep, x, sel)
                 if compensate:

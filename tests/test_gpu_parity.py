@@ -416,3 +416,21 @@ def test_qwen3_fewer_routed_experts_than_trained(b, torch, qwen, top_e):
     ref = qwen.oracle.forward(x, logits, top_e, 138)
     _check_selection(b, qwen, ref, 1, top_e, 138)
     assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+
+
+@pytest.mark.parametrize("kind", ["gate_only", "no_down_norm"])
+def test_score_ablation_kinds_match_oracle(b, torch, tiny, kind):
+    code = {"gate_only": b.MOE_SEL_SCORE_GATE_ONLY, "no_down_norm": b.MOE_SEL_SCORE_NO_DOWN_NORM}[kind]
+    rng = np.random.default_rng(30)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((3, tiny.E)).astype(np.float32)
+    b.moe_sel_set_score(tiny.ctx, code)
+    try:
+        out = _run(b, torch, tiny, x, logits, 92)
+        ref = tiny.oracle.forward(x, logits, tiny.top_e, 92, score_kind=kind)
+        _check_selection(b, tiny, ref, 3, tiny.top_e, 92)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_set_score(tiny.ctx, b.MOE_SEL_SCORE_FULL)
+    with pytest.raises(b.MoeSelError):
+        b.moe_sel_set_score(tiny.ctx, 7)

@@ -492,3 +492,32 @@ def test_threshold_calibration_keeps_the_budget_on_its_own_sample():
     sc = rng.random((64, 8, 768)).astype(np.float32)
     thr = th.calibrate(sc, 0.18)
     assert abs((sc > np.float32(thr)).mean() - 0.18) <= 1.0 / sc.size
+
+
+# ---------------------------------------------------------------------------
+# Score ablations: which weights each kind depends on
+# ---------------------------------------------------------------------------
+def _kind_scores(wg, wu, wd, x_bits, kind):
+    prep = oracle.prepare_expert(wg, wu, wd, 0)
+    q, e = oracle.quantize_token(x_bits)
+    return oracle.score_channels(prep, q, e, kind)
+
+
+def test_score_kinds_depend_on_the_right_weights():
+    d, m = 128, 64
+    wg, wu, wd = synth.expert_weights(0, 5, 0, d, m)
+    _, wu2, wd2 = synth.expert_weights(0, 6, 0, d, m)
+    x = synth.tokens(0, 5, 1, d)[0]
+    full = _kind_scores(wg, wu, wd, x, "full")[1]
+    gate = _kind_scores(wg, wu, wd, x, "gate_only")[1]
+    nodn = _kind_scores(wg, wu, wd, x, "no_down_norm")[1]
+    # gate-only ignores the up weights; no-down-norm ignores the down weights
+    assert np.array_equal(gate, _kind_scores(wg, wu2, wd, x, "gate_only")[1])
+    assert not np.array_equal(full, _kind_scores(wg, wu2, wd, x, "full")[1])
+    assert np.array_equal(nodn, _kind_scores(wg, wu, wd2, x, "no_down_norm")[1])
+    assert not np.array_equal(full, _kind_scores(wg, wu, wd2, x, "full")[1])
+    # the full score is the no-down-norm score scaled by the column norm (one rounding)
+    c = oracle.prepare_expert(wg, wu, wd, 0)["c"].astype(np.float32)
+    assert np.array_equal(full, (nodn * c).astype(np.float32))
+    # and h_hat does not depend on the kind
+    assert np.array_equal(_kind_scores(wg, wu, wd, x, "gate_only")[0], _kind_scores(wg, wu, wd, x, "full")[0])
