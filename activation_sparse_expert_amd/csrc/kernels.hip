@@ -159,6 +159,14 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
     const int p = t * a.top_e + tid;
     a.pair_expert[p] = s_sel[tid];
     a.pair_w[p] = __expf(s_selv[tid] - top) / denom;
+    if (a.batch == 1) {
+      // one token: the plan is one single-token tile per pair, in pair order
+      a.tile_expert[tid] = s_sel[tid];
+      a.tile_first[tid] = tid;
+      a.tile_n[tid] = 1;
+      a.tpair[tid] = tid;
+      if (tid == 0) *a.n_tiles = a.top_e;
+    }
   }
 
   // int8 activations with a power-of-two scale, and their sum
@@ -290,8 +298,11 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
   const int d = a.d, m = a.m, r = a.r;
   const int groups = m / kGroup;
   const int tile = blockIdx.x / groups, grp = blockIdx.x % groups;
-  if (tile >= *a.n_tiles) return;
+  // tile entries are read with the tile count (tile < max_tiles keeps them in
+  // bounds) and used only for live tiles
+  const int ntl = *a.n_tiles;
   const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  if (tile >= ntl) return;
   const int nsub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -397,13 +408,14 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 
 // ===========================================================================
 // Top-k per pair, one block per pair, each thread holding its keys in registers.
-// Non-negative binary32 scores order like their bit patterns. Radix passes over
-// the bits 31..20, 19..9 and 8..0 narrow down the bin holding the k-th largest
-// key: after each pass, keys in higher bins are taken and only keys in the
-// boundary bin stay candidates. As soon as the boundary bin holds at most
-// kSelCand keys they are ranked exactly by (score desc, index asc); if all
-// three passes run, the k-th key itself is known and equal keys are taken
-// lowest index first. Selections are gathered in a bitmap, which then yields
+// Non-negative binary32 scores order like their bit patterns. A first pass
+// histograms (key - min) >> shift over 2048 bins, the shift fitted to the keys'
+// range; keys in bins above the one holding the k-th largest key are taken, and
+// if that bin holds at most kSelCand keys they are ranked exactly by (score
+// desc, index asc). Otherwise (ties, clusters) radix passes over the bits
+// 31..20, 19..9 and 8..0 narrow the boundary bin down the same way; if all
+// three run, the k-th key itself is known and equal keys are taken lowest
+// index first. Selections are gathered in a bitmap, which then yields
 // the ascending index list by a word-level scan.
 // ===========================================================================
 constexpr int kSelCand = 256;
@@ -415,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
   __shared__ uint32_t s_bits[kSelMaxWords];
   __shared__ int s_tmp[kWaves + 2];
   __shared__ int s_sc[4];
+  __shared__ uint32_t s_mm[2 * kWaves];
   const int p = blockIdx.x;
   const int m = a.m, k = a.k, words = m / 32;
   const int tid = threadIdx.x;
@@ -428,20 +441,9 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
     key[u] = j < m ? keys[j] : 0u;
   }
   if (k > 0 && k < m) {
-    constexpr int kShift[3] = {20, 9, 0};
-    constexpr int kBins[3] = {2048, 2048, 512};
-    uint32_t prefix = 0;  // boundary bits above the current pass
-    int krem = k, level = 0, ncand = m;
-    for (; level < 3; ++level) {
-      const int sh = kShift[level], hi = level == 0 ? 32 : kShift[level - 1];
-      const uint32_t dmask = (uint32_t)kBins[level] - 1u;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if (tid + u * kThreads < m && (level == 0 || (key[u] >> hi) == prefix))
-          atomicAdd(&s_hist[(key[u] >> sh) & dmask], 1);
+    // boundary bin of the k-th largest key among 2048 bins; fills s_sc[0..2] =
+    // (bin, keys in higher bins, keys in the bin). Histogram zeroed by the caller.
+    auto find_bin = [&](int kr) {
       __syncthreads();
       int h[8], c = 0;
 #pragma unroll
@@ -451,10 +453,10 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
       }
       int total;
       const int before = block_excl_scan(c, s_tmp, &total);
-      int above = total - before - c;  // keys of this pass in bins above this thread's 8
+      int above = total - before - c;  // keys in bins above this thread's 8
 #pragma unroll
       for (int b = 7; b >= 0; --b) {
-        if (above < krem && krem <= above + h[b]) {
+        if (above < kr && kr <= above + h[b]) {
           s_sc[0] = tid * 8 + b;
           s_sc[1] = above;
           s_sc[2] = h[b];
@@ -462,33 +464,96 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
         above += h[b];
       }
       __syncthreads();
-      // keys of this pass in bins above the boundary bin are taken
-      const uint32_t dsel = (uint32_t)s_sc[0];
+    };
+    // Pass 0, adapted to the keys' range: digit = (key - min) >> shift spreads the
+    // keys over 2048 bins, so the boundary bin usually holds few keys.
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (tid + u * kThreads < m) {
+        kmin = min(kmin, key[u]);
+        kmax = max(kmax, key[u]);
+      }
+    kmin = ~wave_max_u(~kmin);
+    kmax = wave_max_u(kmax);
+    if ((tid & 63) == 0) {
+      s_mm[tid >> 6] = kmin;
+      s_mm[kWaves + (tid >> 6)] = kmax;
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
+    __syncthreads();
+    kmin = min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3]));
+    kmax = max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]));
+    int shift = 0;
+    while (((kmax - kmin) >> shift) >= 2048u) ++shift;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (tid + u * kThreads < m) atomicAdd(&s_hist[(key[u] - kmin) >> shift], 1);
+    find_bin(k);
+    // candidates: keys with ((key - cbase) >> cshift) == cval
+    uint32_t cbase = kmin, cval = (uint32_t)s_sc[0];
+    int cshift = shift;
+    int krem = k - s_sc[1], ncand = s_sc[2];
+    bool exact_key = false;
+    if (ncand <= kSelCand) {
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         const int j = tid + u * kThreads;
-        if (j < m && (level == 0 || (key[u] >> hi) == prefix) && ((key[u] >> sh) & dmask) > dsel)
-          atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+        if (j < m && ((key[u] - kmin) >> shift) > cval) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
       }
-      krem -= s_sc[1];
-      ncand = s_sc[2];
-      prefix = (prefix << (hi - sh)) | dsel;
-      if (ncand <= kSelCand) {
-        ++level;
-        break;
+    } else {
+      // ties or clusters: radix passes over the bits 31..20, 19..9 and 8..0 of the
+      // key; after each pass keys in higher bins are taken and only the boundary
+      // bin stays
+      constexpr int kShift[3] = {20, 9, 0};
+      constexpr int kBins[3] = {2048, 2048, 512};
+      uint32_t prefix = 0;  // boundary bits above the current pass
+      krem = k;
+      int level = 0;
+      for (; level < 3; ++level) {
+        const int sh = kShift[level], hi = level == 0 ? 32 : kShift[level - 1];
+        const uint32_t dmask = (uint32_t)kBins[level] - 1u;
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+          if (tid + u * kThreads < m && (level == 0 || (key[u] >> hi) == prefix))
+            atomicAdd(&s_hist[(key[u] >> sh) & dmask], 1);
+        find_bin(krem);
+        const uint32_t dsel = (uint32_t)s_sc[0];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const int j = tid + u * kThreads;
+          if (j < m && (level == 0 || (key[u] >> hi) == prefix) && ((key[u] >> sh) & dmask) > dsel)
+            atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+        }
+        krem -= s_sc[1];
+        ncand = s_sc[2];
+        prefix = (prefix << (hi - sh)) | dsel;
+        if (ncand <= kSelCand) {
+          ++level;
+          break;
+        }
       }
+      cbase = 0;
+      cshift = kShift[level - 1];
+      cval = prefix;
+      exact_key = ncand > kSelCand;  // all three passes ran: prefix is the k-th key itself
     }
-    const int sh = kShift[level - 1];
-    if (ncand <= kSelCand) {
+    if (!exact_key) {
       // rank the boundary bin's keys exactly
       int* ckey = s_hist;
       int* cidx = s_hist + kSelCand;
+      __syncthreads();
       if (tid == 0) s_tmp[kWaves + 1] = 0;
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         const int j = tid + u * kThreads;
-        if (j < m && (key[u] >> sh) == prefix) {
+        if (j < m && ((key[u] - cbase) >> cshift) == cval) {
           const int slot = atomicAdd(&s_tmp[kWaves + 1], 1);
           ckey[slot] = (int)key[u];
           cidx[slot] = j;
@@ -504,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
         if (rank < krem) atomicOr(&s_bits[ic >> 5], 1u << (ic & 31));
       }
     } else {
-      // prefix is the k-th largest key itself: its krem lowest-index copies, word by word
+      // the krem lowest-index copies of the k-th key, word by word
       __syncthreads();
       int run_eq = 0;
       for (int base = 0; base < words; base += kThreads) {
@@ -512,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
         uint32_t eq = 0;
         if (w < words)
 #pragma unroll 8
-          for (int b = 0; b < 32; ++b) eq |= (uint32_t)(keys[32 * w + b] == prefix) << b;
+          for (int b = 0; b < 32; ++b) eq |= (uint32_t)(keys[32 * w + b] == cval) << b;
         int eq_tot;
         const int eq_before = run_eq + block_excl_scan(__popc(eq), s_tmp, &eq_tot);
         int want = max(0, min(__popc(eq), krem - eq_before));
@@ -563,9 +628,9 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
 __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
   __shared__ int s_tmp[kWaves];
   const int tile = blockIdx.x;
-  if (tile >= *a.n_tiles) return;
+  const int ntl = *a.n_tiles, first = a.tile_first[tile], n = a.tile_n[tile];
+  if (tile >= ntl) return;
   const int m = a.m, words = m / 32;
-  const int first = a.tile_first[tile], n = a.tile_n[tile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* ul = a.ulist + (size_t)tile * m;
   uint64_t* um = a.umask + (size_t)tile * m;
@@ -635,11 +700,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
   const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
-  if (tile >= *a.n_tiles) return;
-  const int uc = a.ucount[tile];
+  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  if (tile >= ntl) return;
   const int nch = max(1, (uc + kCh - 1) / kCh);
   if (chunk >= nch) return;
-  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   const int nsub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -764,32 +829,42 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
   return s;
 }
 
-__global__ __launch_bounds__(kThreads) void k_zfin(FwdArgs a) {
-  __shared__ float s_part[kWaves][64];
+constexpr int kZThreads = 1024, kZWaves = kZThreads / 64;
+
+__global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
+  __shared__ float s_part[kZWaves][64];
   const int tile = blockIdx.x / kT, j = blockIdx.x % kT;
-  if (tile >= *a.n_tiles || j >= a.tile_n[tile]) return;
+  const int ntl = *a.n_tiles, tn = a.tile_n[tile], uc = a.ucount[tile], tf = a.tile_first[tile];
+  if (tile >= ntl || j >= tn) return;
   const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad, groups = m / kGroup;
-  const int uc = a.ucount[tile];
   const int nch = max(1, (uc + kCh - 1) / kCh);
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
-  const int pp = a.tpair[a.tile_first[tile] + j];
-  // wave q sums its quarter of the groups and of the gate/up blocks
+  const int pp = a.tpair[tf + j];
+  // wave q sums its sixteenth of the groups and of the gate/up blocks
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g0 = groups * q / kWaves, g1 = groups * (q + 1) / kWaves;
-  const int c0 = nch * q / kWaves, c1 = nch * (q + 1) / kWaves;
+  const int g0 = groups * q / kZWaves, g1 = groups * (q + 1) / kZWaves;
+  const int c0 = nch * q / kZWaves, c1 = nch * (q + 1) / kZWaves;
   const float* gz = a.gzpart + (size_t)pp * groups * r;
   const float* zs = a.zsel + (size_t)pp * maxch * r;
   for (int cb = 0; cb < kend - uc; cb += 64) {
     const int c = cb + lane;
     float z = 0.0f;
     if (c < r && !all_kept)
-      z = sum_strided<12>(gz + (size_t)g0 * r + c, r, g1 - g0) - sum_strided<16>(zs + (size_t)c0 * r + c, r, c1 - c0);
+      z = sum_strided<8>(gz + (size_t)g0 * r + c, r, g1 - g0) - sum_strided<8>(zs + (size_t)c0 * r + c, r, c1 - c0);
     s_part[q][lane] = z;
     __syncthreads();
-    if (q == 0 && c < kend - uc)
-      a.hbuf[(size_t)pp * kpad + uc + c] =
-          f32_to_bf16_dev((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]));
+    if (q == 0 && c < kend - uc) {
+      float zt[kZWaves];
+#pragma unroll
+      for (int w = 0; w < kZWaves; ++w) zt[w] = s_part[w][lane];
+      // pairwise, in a fixed order
+#pragma unroll
+      for (int h = kZWaves / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int w = 0; w < h; ++w) zt[w] += zt[w + h];
+      a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(zt[0]);
+    }
     __syncthreads();
   }
 }
@@ -804,6 +879,8 @@ __global__ __launch_bounds__(kThreads) void k_zfin(FwdArgs a) {
 // With few tiles the K range is split over kc blocks, each writing its own
 // partial output, which the combine adds in a fixed order.
 // ===========================================================================
+constexpr int kDownChCap = 1024;
+
 template <int NW>
 __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int kc) {
   constexpr int SW = 64 * NW;      // outputs per block
@@ -813,19 +890,20 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   constexpr int KS = RPT * CG;     // channels per stage
   constexpr int PITCH = KS + 8;    // halfwords per LDS row (one output)
   __shared__ __align__(16) uint16_t s_b[SW * PITCH];
+  __shared__ int s_ch[kDownChCap];  // the block's K-range rows: channel, or -1 - (row of P^T)
   const int d = a.d, m = a.m;
   const int slices = d / SW;
   const int per_tile = slices * kc;
   const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
   const int sl = rem % slices, kci = rem / slices;
-  if (tile >= *a.n_tiles) return;
-  const int uc = a.ucount[tile];
+  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
+  if (tile >= ntl) return;
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
   const int nst = (K + KS - 1) / KS;
   const int spc = (nst + kc - 1) / kc;
   const int st0 = kci * spc, st1 = min(nst, st0 + spc);
-  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   const int msub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -833,10 +911,21 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   const int kpad = a.kpad;
   const int og = tid % OG, cg = tid / OG;
   const size_t col = (size_t)SW * sl + 8 * og;
+  // rows k in [kb, kb + kn) of this block, read once here instead of on each
+  // stage's load path (an index load ahead of every weight load)
+  const int kb = KS * st0, kn = min(K, KS * st1) - kb;
+  const bool staged = kn <= kDownChCap;
+  if (staged)
+    for (int i = tid; i < kn; i += kThreads) {
+      const int k = kb + i;
+      s_ch[i] = k < uc ? ul[k] : -1 - (k - uc);
+    }
+  __syncthreads();
   auto brow = [&](int k) -> const uint16_t* {
     k = min(k, K - 1);
-    if (k < uc) return a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d + col;
-    return a.pmat + ((size_t)e * a.r + (k - uc)) * d + col;
+    const int c = staged ? s_ch[k - kb] : (k < uc ? ul[k] : -1 - (k - uc));
+    if (c >= 0) return a.wch + (((size_t)e * m + c) * 3 + 2) * d + col;
+    return a.pmat + ((size_t)e * a.r + (-1 - c)) * d + col;
   };
   const uint16_t* hrow[kMSub];
 #pragma unroll
@@ -945,7 +1034,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int pairs = a.batch * a.top_e;
   const int groups = a.m / kGroup;
   hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  if (a.batch > 1) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
     const size_t score_lds = ((size_t)kT * 64 + (size_t)64 * a.r) * 4;
     hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads), score_lds, stream, a);
@@ -958,7 +1047,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   }
   hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kThreads), 0, stream, a);
+  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
   // the largest union a tile can have: k channels per token, at most m
   const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
