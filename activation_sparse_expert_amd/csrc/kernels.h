@@ -67,6 +67,10 @@ constexpr int kMaxDownSplit = 64;
 int grouped_down_width(int d);
 // kmax: the largest union of channels a tile of the call can hold
 int grouped_down_split(int max_tiles, int d, int kmax, int r);
+// batch 1 (one token per tile): row-streaming gate/up and down kernels, and
+// the down projection's split of the K range
+bool grouped_b1_supported(int d);
+int grouped_down_split_b1(int kmax, int r);
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 

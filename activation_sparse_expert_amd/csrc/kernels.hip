@@ -407,101 +407,202 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 }
 
 // ===========================================================================
-// Top-k per pair, one block per pair, each thread holding its keys in registers.
-// Non-negative binary32 scores order like their bit patterns. A first pass
-// histograms (key - min) >> shift over 2048 bins, the shift fitted to the keys'
-// range; keys in bins above the one holding the k-th largest key are taken, and
-// if that bin holds at most kSelCand keys they are ranked exactly by (score
-// desc, index asc). Otherwise (ties, clusters) radix passes over the bits
-// 31..20, 19..9 and 8..0 narrow the boundary bin down the same way; if all
-// three run, the k-th key itself is known and equal keys are taken lowest
-// index first. Selections are gathered in a bitmap, which then yields
-// the ascending index list by a word-level scan.
+// Sketch scores for one-token tiles (batch 1), one block per (pair, 64-channel
+// group) with 8 waves = (matrix, quarter of the hidden dimension). Lane l is
+// channel l of the group and reads its 16-byte code piece of each 64-element
+// block, so one load instruction reads a block's 1 KiB of the group at once;
+// the token's x_q sits in LDS. The exact integer dots of the quarters are
+// added in LDS, then scores and h_hat as above, and the group's share of
+// Q^T h_hat.
+// ===========================================================================
+// batch-1 (one token per tile) kernels: 8 waves per block
+constexpr int kB1Threads = 512, kB1Waves = kB1Threads / 64;
+constexpr int kB1Pieces = 8;  // 16-byte pieces per lane and row: d <= 4096
+constexpr int kSB1Blk = 16;  // code blocks per wave in flight
+
+__global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a) {
+  extern __shared__ float s_dyn_sb1[];  // x_q [d] bytes, then Q rows [64][r]
+  __shared__ int s_part[kB1Waves][64];
+  __shared__ float s_h[64];
+  const int d = a.d, m = a.m, r = a.r, groups = m / kGroup;
+  const int tile = blockIdx.x / groups, grp = blockIdx.x % groups;
+  const int ntl = *a.n_tiles, e = a.tile_expert[tile], first = a.tile_first[tile];
+  if (tile >= ntl) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pp = a.tpair[first], t = pp / a.top_e;
+  int8_t* s_xq = (int8_t*)s_dyn_sb1;
+  float* s_q = s_dyn_sb1 + d / 4;
+  const int mat = wave & 1, quarter = wave >> 1;
+  const int nb = d / kBlock;
+  const int b0 = nb * quarter / 4, b1 = nb * (quarter + 1) / 4;
+  const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(d, m) +
+                                   codes_dword_index(d, m, grp, mat, 0, lane, 0));
+  uint4 cb[kSB1Blk];
+#pragma unroll
+  for (int i = 0; i < kSB1Blk; ++i) cb[i] = cp[(size_t)min(b0 + i, b1 - 1) * 64];
+  for (int i = tid; i < d / 16; i += kB1Threads) ((int4*)s_xq)[i] = ((const int4*)(a.xq + (size_t)t * d))[i];
+  if (r > 0)
+    for (int i = tid; i < 64 * r; i += kB1Threads)
+      s_q[i] = __uint_as_float((uint32_t)a.qmat[((size_t)e * m + 64 * grp) * r + i] << 16);
+  const float4 st = a.stats[(size_t)e * m + 64 * grp + lane];
+  const int xe = a.xexp[t], qs = a.xqsum[t];
+  __syncthreads();  // x_q in LDS
+  int acc = 0;
+  for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
+    if (c0 != b0) {
+#pragma unroll
+      for (int i = 0; i < kSB1Blk; ++i) cb[i] = cp[(size_t)min(c0 + i, b1 - 1) * 64];
+    }
+#pragma unroll
+    for (int i = 0; i < kSB1Blk; ++i) {
+      if (c0 + i < b1) {
+        const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
+        acc = dot_codes16(cb[i].x, xb[0], acc);
+        acc = dot_codes16(cb[i].y, xb[1], acc);
+        acc = dot_codes16(cb[i].z, xb[2], acc);
+        acc = dot_codes16(cb[i].w, xb[3], acc);
+      }
+    }
+  }
+  s_part[wave][lane] = acc;  // sum of (t + 1) x_q over the quarter
+  __syncthreads();
+  if (wave == 0) {
+    const int dg = s_part[0][lane] + s_part[2][lane] + s_part[4][lane] + s_part[6][lane];
+    const int du = s_part[1][lane] + s_part[3][lane] + s_part[5][lane] + s_part[7][lane];
+    float h, sc;
+    pinned_score(dg - qs, du - qs, xe, st, h, sc, a.score_kind);
+    const int j = 64 * grp + lane;
+    a.hhat[(size_t)pp * m + j] = h;
+    a.score[(size_t)pp * m + j] = sc;
+    s_h[lane] = h;
+  }
+  if (r == 0) return;
+  __syncthreads();
+  if (tid < r) {
+    float z = 0.0f;
+#pragma unroll 8
+    for (int ch = 0; ch < 64; ++ch) z += s_h[ch] * s_q[ch * r + tid];
+    a.gzpart[((size_t)pp * groups + grp) * r + tid] = z;
+  }
+}
+
+// ===========================================================================
+// Top-k per pair, one block of 16 waves per pair, each thread holding its keys
+// in registers. Non-negative binary32 scores order like their bit patterns,
+// whose bit 31 is clear. A histogram of the bits 30..19 (4096 bins, a
+// sixteenth of an octave each) finds the bin holding the k-th largest key;
+// keys in higher bins are taken, and when that bin holds at most kSelCand keys
+// they are ranked exactly by (score desc, index asc), four threads per
+// candidate. Otherwise (ties, clusters) radix passes over the bits 31..20,
+// 19..9 and 8..0 narrow the boundary bin down the same way; if all three run,
+// the k-th key itself is known and equal keys are taken lowest index first.
+// Selections are gathered in a bitmap, which then yields the ascending index
+// list by a word-level scan.
 // ===========================================================================
 constexpr int kSelCand = 256;
 constexpr int kSelMaxWords = 512;  // m <= 16384
+constexpr int kSelThreads = 1024, kSelWaves = kSelThreads / 64;
+constexpr int kSelBins = 4096;     // first pass: bits 30..19
+
+// exclusive scan over the 1024 threads of a select block; s_w: kSelWaves ints
+__device__ __forceinline__ int sel_excl_scan(int v, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int c = s_w[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Boundary bin of the kr-th largest key in a histogram of BPT * 1024 bins
+// (thread t owns bins BPT t .. BPT t + BPT - 1); writes s_sc[0..2] = (bin,
+// keys in higher bins, keys in the bin). Barriers inside.
+template <int BPT>
+__device__ __forceinline__ void sel_find_bin(const int* s_hist, int kr, int* s_tmp, int* s_sc) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  int h[BPT], c = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = s_hist[BPT * tid + i];
+    c += h[i];
+  }
+  int total;
+  const int before = sel_excl_scan(c, s_tmp, &total);
+  int above = total - before - c;  // keys in bins above this thread's
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {
+    if (above < kr && kr <= above + h[i]) {
+      s_sc[0] = BPT * tid + i;
+      s_sc[1] = above;
+      s_sc[2] = h[i];
+    }
+    above += h[i];
+  }
+  __syncthreads();
+}
+
+// A wave's predicate as bitmap words: the wave's lanes hold the 64 indices
+// j0 .. j0 + 63 (j0 a multiple of 64), so the two words are this wave's alone
+// in a pass. mark_wave ORs them in; store_wave writes them whole (words not
+// yet written). All lanes of the wave call.
+__device__ __forceinline__ void mark_wave(uint32_t* bits, int j0, bool pred) {
+  const uint64_t b = __ballot(pred);
+  const int lane = threadIdx.x & 63;
+  if (lane == 0 && (uint32_t)b) bits[j0 >> 5] |= (uint32_t)b;
+  if (lane == 32 && (uint32_t)(b >> 32)) bits[(j0 >> 5) + 1] |= (uint32_t)(b >> 32);
+}
+__device__ __forceinline__ void store_wave(uint32_t* bits, int j0, bool pred) {
+  const uint64_t b = __ballot(pred);
+  if ((threadIdx.x & 63) == 0) *(uint64_t*)(bits + (j0 >> 5)) = b;
+}
+
+// Key slot u of a thread is j = tid + 1024 u. Slots below nfull = m / 1024 are
+// valid in every thread, slot nfull only where j < m: the guard is a uniform
+// branch for the full slots, so the unrolled loops carry no per-key exec masks.
+// As m is a multiple of 64, a wave's slot is valid in all lanes or none.
+#define SEL_FOR_KEYS(BODY)                                     \
+  _Pragma("unroll") for (int u = 0; u < KPT; ++u) {            \
+    const int j = tid + u * kSelThreads;                       \
+    if (u < nfull || (u == nfull && j < m)) { BODY }           \
+  }
 
 template <int KPT>
-__global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
-  __shared__ int s_hist[2048];  // histogram of a pass, then candidate keys and indices
-  __shared__ uint32_t s_bits[kSelMaxWords];
-  __shared__ int s_tmp[kWaves + 2];
+__global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a) {
+  __shared__ __align__(16) int s_hist[kSelBins];  // histograms, then candidates
+  __shared__ __align__(8) uint32_t s_bits[kSelMaxWords];
+  __shared__ int s_tmp[kSelWaves + 2];
   __shared__ int s_sc[4];
-  __shared__ uint32_t s_mm[2 * kWaves];
   const int p = blockIdx.x;
   const int m = a.m, k = a.k, words = m / 32;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nfull = m / kSelThreads;
+  const bool topk = k > 0 && k < m;
   const uint32_t* keys = (const uint32_t*)(a.score + (size_t)p * m);
-  for (int w = tid; w < words; w += kThreads) s_bits[w] = k >= m ? 0xFFFFFFFFu : 0u;
-  // this thread's keys j = tid + 256 u, in registers for every pass
   uint32_t key[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int j = tid + u * kThreads;
-    key[u] = j < m ? keys[j] : 0u;
-  }
-  if (k > 0 && k < m) {
-    // boundary bin of the k-th largest key among 2048 bins; fills s_sc[0..2] =
-    // (bin, keys in higher bins, keys in the bin). Histogram zeroed by the caller.
-    auto find_bin = [&](int kr) {
-      __syncthreads();
-      int h[8], c = 0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        h[b] = s_hist[tid * 8 + b];
-        c += h[b];
-      }
-      int total;
-      const int before = block_excl_scan(c, s_tmp, &total);
-      int above = total - before - c;  // keys in bins above this thread's 8
-#pragma unroll
-      for (int b = 7; b >= 0; --b) {
-        if (above < kr && kr <= above + h[b]) {
-          s_sc[0] = tid * 8 + b;
-          s_sc[1] = above;
-          s_sc[2] = h[b];
-        }
-        above += h[b];
-      }
-      __syncthreads();
-    };
-    // Pass 0, adapted to the keys' range: digit = (key - min) >> shift spreads the
-    // keys over 2048 bins, so the boundary bin usually holds few keys.
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      if (tid + u * kThreads < m) {
-        kmin = min(kmin, key[u]);
-        kmax = max(kmax, key[u]);
-      }
-    kmin = ~wave_max_u(~kmin);
-    kmax = wave_max_u(kmax);
-    if ((tid & 63) == 0) {
-      s_mm[tid >> 6] = kmin;
-      s_mm[kWaves + (tid >> 6)] = kmax;
-    }
-#pragma unroll
-    for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
-    __syncthreads();
-    kmin = min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3]));
-    kmax = max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]));
-    int shift = 0;
-    while (((kmax - kmin) >> shift) >= 2048u) ++shift;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      if (tid + u * kThreads < m) atomicAdd(&s_hist[(key[u] - kmin) >> shift], 1);
-    find_bin(k);
-    // candidates: keys with ((key - cbase) >> cshift) == cval
-    uint32_t cbase = kmin, cval = (uint32_t)s_sc[0];
-    int cshift = shift;
+  SEL_FOR_KEYS(key[u] = keys[j];)
+  if (tid < words) s_bits[tid] = k >= m ? 0xFFFFFFFFu : 0u;
+  if (topk) *(int4*)(s_hist + 4 * tid) = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  if (topk) {
+    SEL_FOR_KEYS(atomicAdd(&s_hist[key[u] >> 19], 1);)
+    sel_find_bin<kSelBins / kSelThreads>(s_hist, k, s_tmp, s_sc);
+    // candidates: keys with (key >> cshift) == cval
+    uint32_t cval = (uint32_t)s_sc[0];
+    int cshift = 19;
     int krem = k - s_sc[1], ncand = s_sc[2];
     bool exact_key = false;
+    int nc = 0;  // this thread's candidates
     if (ncand <= kSelCand) {
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int j = tid + u * kThreads;
-        if (j < m && ((key[u] - kmin) >> shift) > cval) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
-      }
+      SEL_FOR_KEYS(const uint32_t dg = key[u] >> 19; store_wave(s_bits, j - lane, dg > cval); nc += dg == cval;)
     } else {
       // ties or clusters: radix passes over the bits 31..20, 19..9 and 8..0 of the
       // key; after each pass keys in higher bins are taken and only the boundary
@@ -515,21 +616,14 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
         const int sh = kShift[level], hi = level == 0 ? 32 : kShift[level - 1];
         const uint32_t dmask = (uint32_t)kBins[level] - 1u;
         __syncthreads();
-#pragma unroll
-        for (int b = 0; b < 8; ++b) s_hist[tid * 8 + b] = 0;
+        s_hist[2 * tid] = 0;
+        s_hist[2 * tid + 1] = 0;
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < KPT; ++u)
-          if (tid + u * kThreads < m && (level == 0 || (key[u] >> hi) == prefix))
-            atomicAdd(&s_hist[(key[u] >> sh) & dmask], 1);
-        find_bin(krem);
+        SEL_FOR_KEYS(if (level == 0 || (key[u] >> hi) == prefix) atomicAdd(&s_hist[(key[u] >> sh) & dmask], 1);)
+        sel_find_bin<2>(s_hist, krem, s_tmp, s_sc);
         const uint32_t dsel = (uint32_t)s_sc[0];
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-          const int j = tid + u * kThreads;
-          if (j < m && (level == 0 || (key[u] >> hi) == prefix) && ((key[u] >> sh) & dmask) > dsel)
-            atomicOr(&s_bits[j >> 5], 1u << (j & 31));
-        }
+        SEL_FOR_KEYS(mark_wave(s_bits, j - lane,
+                               (level == 0 || (key[u] >> hi) == prefix) && ((key[u] >> sh) & dmask) > dsel);)
         krem -= s_sc[1];
         ncand = s_sc[2];
         prefix = (prefix << (hi - sh)) | dsel;
@@ -538,88 +632,89 @@ __global__ __launch_bounds__(kThreads) void k_select(FwdArgs a) {
           break;
         }
       }
-      cbase = 0;
       cshift = kShift[level - 1];
       cval = prefix;
       exact_key = ncand > kSelCand;  // all three passes ran: prefix is the k-th key itself
+      if (!exact_key) {
+        SEL_FOR_KEYS(nc += (key[u] >> cshift) == cval;)
+      }
     }
     if (!exact_key) {
-      // rank the boundary bin's keys exactly
-      int* ckey = s_hist;
-      int* cidx = s_hist + kSelCand;
+      // the boundary bin's keys at scan positions, ranked exactly, four threads
+      // per candidate
+      uint64_t* ck = (uint64_t*)s_hist;  // kSelCand order keys
+      int* cidx = s_hist + 2 * kSelCand;
+      int ctot;
+      int slot = sel_excl_scan(nc, s_tmp, &ctot);
+      SEL_FOR_KEYS(if ((key[u] >> cshift) == cval) {
+        ck[slot] = order_key(key[u], j);
+        cidx[slot] = j;
+        ++slot;
+      })
       __syncthreads();
-      if (tid == 0) s_tmp[kWaves + 1] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int j = tid + u * kThreads;
-        if (j < m && ((key[u] - cbase) >> cshift) == cval) {
-          const int slot = atomicAdd(&s_tmp[kWaves + 1], 1);
-          ckey[slot] = (int)key[u];
-          cidx[slot] = j;
-        }
-      }
-      __syncthreads();
-      if (tid < ncand) {
-        const int ic = cidx[tid];
-        const uint64_t kc = order_key((uint32_t)ckey[tid], ic);
-        int rank = 0;
-#pragma unroll 8
-        for (int o = 0; o < ncand; ++o) rank += order_key((uint32_t)ckey[o], cidx[o]) > kc;
-        if (rank < krem) atomicOr(&s_bits[ic >> 5], 1u << (ic & 31));
+      const int c = tid >> 2, part = tid & 3;
+      const bool live = c < ncand;
+      const uint64_t kc = live ? ck[c] : 0ull;
+      int rank = 0;
+      if (live)
+#pragma unroll 4
+        for (int o = part; o < ncand; o += 4) rank += ck[o] > kc;
+      rank += __shfl_xor(rank, 1, 64);
+      rank += __shfl_xor(rank, 2, 64);
+      if (live && part == 0 && rank < krem) {
+        const int ic = cidx[c];
+        atomicOr(&s_bits[ic >> 5], 1u << (ic & 31));
       }
     } else {
-      // the krem lowest-index copies of the k-th key, word by word
+      // the krem lowest-index copies of the k-th key, one word per thread
       __syncthreads();
-      int run_eq = 0;
-      for (int base = 0; base < words; base += kThreads) {
-        const int w = base + tid;
-        uint32_t eq = 0;
-        if (w < words)
+      uint32_t eq = 0;
+      if (tid < words)
 #pragma unroll 8
-          for (int b = 0; b < 32; ++b) eq |= (uint32_t)(keys[32 * w + b] == cval) << b;
-        int eq_tot;
-        const int eq_before = run_eq + block_excl_scan(__popc(eq), s_tmp, &eq_tot);
-        int want = max(0, min(__popc(eq), krem - eq_before));
-        uint32_t takeq = 0, rest = eq;
-        while (want-- > 0) {
-          const uint32_t low = rest & (0u - rest);
-          takeq |= low;
-          rest ^= low;
-        }
-        if (w < words) s_bits[w] |= takeq;
-        run_eq += eq_tot;
+        for (int b = 0; b < 32; ++b) eq |= (uint32_t)(keys[32 * tid + b] == cval) << b;
+      int eq_tot;
+      const int eq_before = sel_excl_scan(__popc(eq), s_tmp, &eq_tot);
+      int want = max(0, min(__popc(eq), krem - eq_before));
+      uint32_t takeq = 0, rest = eq;
+      while (want-- > 0) {
+        const uint32_t low = rest & (0u - rest);
+        takeq |= low;
+        rest ^= low;
       }
+      if (tid < words) s_bits[tid] |= takeq;
     }
   }
   if (a.thr_mode) {
     // threshold selector: every channel whose score exceeds the threshold
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int j = tid + u * kThreads;
-      if (j < m && key[u] > a.thr_bits) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
-    }
+    SEL_FOR_KEYS(mark_wave(s_bits, j - lane, key[u] > a.thr_bits);)
   }
   __syncthreads();
-  // ascending index list from the bitmap
+  // ascending index list from the bitmap, one word per thread
   int* idx_out = a.sel_idx + (size_t)p * m;
-  int run = 0;
-  for (int base = 0; base < words; base += kThreads) {
-    const int w = base + tid;
-    const uint32_t u = w < words ? s_bits[w] : 0u;
-    int tot;
-    int pos = run + block_excl_scan(__popc(u), s_tmp, &tot);
-    uint32_t rest = u;
-    while (rest) {
-      idx_out[pos++] = 32 * w + __ffs(rest) - 1;
-      rest &= rest - 1u;
+  const uint32_t wb = tid < words ? s_bits[tid] : 0u;
+  int tot;
+  int pos = sel_excl_scan(__popc(wb), s_tmp, &tot);
+  uint32_t rest = wb;
+  // one token: tile p is pair p alone, and its union is the selection itself
+  int* ul = a.batch == 1 ? a.ulist + (size_t)p * m : nullptr;
+  uint64_t* um = a.batch == 1 ? a.umask + (size_t)p * m : nullptr;
+  while (rest) {
+    const int jj = 32 * tid + __ffs(rest) - 1;
+    if (ul) {
+      ul[pos] = jj;
+      um[pos] = 1ull;
     }
-    if (w < words) a.selbits[(size_t)p * words + w] = u;
-    run += tot;
+    idx_out[pos++] = jj;
+    rest &= rest - 1u;
   }
-  if (tid == 0) a.sel_count[p] = run;
+  if (tid < words) a.selbits[(size_t)p * words + tid] = wb;
+  if (tid == 0) {
+    a.sel_count[p] = tot;
+    if (ul) a.ucount[p] = tot;
+  }
 }
+#undef SEL_FOR_KEYS
 
 // ===========================================================================
 // Union of a tile's selections: ascending channel list and, per listed
@@ -807,6 +902,219 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   }
 }
 
+// sum of p[q * stride] for q < count in index order, N loads in flight at a time
+// (the last batch masked, so no tail runs one load per round trip)
+template <int N>
+__device__ __forceinline__ float sum_strided(const float* p, size_t stride, int count) {
+  float s = 0.0f;
+  for (int q = 0; q < count; q += N) {
+    float part[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) part[u] = q + u < count ? p[(size_t)(q + u) * stride] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if (q + u < count) s += part[u];
+  }
+  return s;
+}
+
+// ===========================================================================
+// Gate/up for one-token tiles (batch 1): the same 16-channel blocks as above,
+// computed as row dot products, since a single token leaves an MFMA's other
+// 15 columns empty. Wave w takes channels 2w and 2w + 1 of the block; lane l
+// holds the 16-byte pieces l + 64 i of x and of both rows, so each load
+// instruction reads 1 KiB of a row in one run. fp32 products summed per lane,
+// then over the wave. Sparse blocks also leave their channels' share of
+// Q^T h_hat, as above.
+// ===========================================================================
+
+__global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense) {
+  __shared__ float s_hz[kCh];
+  __shared__ float s_qr[kCh * 128];
+  const int d = a.d, m = a.m;
+  const int maxch = m / kCh;
+  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
+  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int e = a.tile_expert[tile], first = a.tile_first[tile];
+  if (tile >= ntl) return;
+  const int nch = max(1, (uc + kCh - 1) / kCh);
+  if (chunk >= nch) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = dense ? 0 : a.r;
+  const int pp = a.tpair[first];
+  const int* ul = a.ulist + (size_t)tile * m;
+  const int npc = d / 8;
+  // the compensation share's inputs, in flight with the weights
+  constexpr int kQPer = kCh * 128 / kB1Threads;  // r <= 128
+  float qv[kQPer];
+  if (r > 0) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int i = tid + u * kB1Threads;
+      const int ci = i / r, c = i % r, pos = kCh * chunk + ci;
+      qv[u] = i < kCh * r && pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16)
+                                      : 0.0f;
+    }
+    if (tid < kCh) {
+      const int pos = kCh * chunk + tid;
+      s_hz[tid] = pos < uc ? a.hhat[(size_t)pp * m + ul[pos]] : 0.0f;
+    }
+  }
+  const int pos0 = kCh * chunk + 2 * wave;
+  const uint16_t* xr = a.x + (size_t)(pp / a.top_e) * d;
+  const uint16_t* rows[2];
+#pragma unroll
+  for (int ci = 0; ci < 2; ++ci) {
+    const int ch = uc > 0 ? ul[min(pos0 + ci, uc - 1)] : 0;
+    rows[ci] = a.wch + ((size_t)e * m + ch) * 3 * d;
+  }
+  uint4 xv[kB1Pieces], gv[2][kB1Pieces], uv[2][kB1Pieces];
+#pragma unroll
+  for (int i = 0; i < kB1Pieces; ++i) {
+    const int pc = lane + 64 * i;
+    if (pc < npc) {
+      xv[i] = *(const uint4*)(xr + 8 * pc);
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) {
+        gv[ci][i] = *(const uint4*)(rows[ci] + 8 * pc);
+        uv[ci][i] = *(const uint4*)(rows[ci] + d + 8 * pc);
+      }
+    }
+  }
+  float sg[2] = {0.0f, 0.0f}, su[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kB1Pieces; ++i) {
+    if (lane + 64 * i < npc) {
+      float xf[8];
+      unpack8(xv[i], xf);
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) {
+        sg[ci] += dot8_bf16(gv[ci][i], xf);
+        su[ci] += dot8_bf16(uv[ci][i], xf);
+      }
+    }
+  }
+#pragma unroll
+  for (int ci = 0; ci < 2; ++ci) {
+    const float g = wave_sum(sg[ci]), u = wave_sum(su[ci]);
+    if (lane == 0 && pos0 + ci < uc) a.hbuf[(size_t)pp * a.kpad + pos0 + ci] = f32_to_bf16_dev(silu_f32(g) * u);
+  }
+  if (r == 0) return;
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = tid + u * kB1Threads;
+    if (i < kCh * r) s_qr[i] = qv[u];
+  }
+  __syncthreads();
+  if (tid < r) {
+    float z = 0.0f;
+#pragma unroll
+    for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci] * s_qr[ci * r + tid];
+    a.zsel[((size_t)pp * maxch + chunk) * r + tid] = z;
+  }
+}
+
+// ===========================================================================
+// Down projection for one-token tiles (batch 1): y = sum_k h_k B_k over the
+// tile's K rows (union channels' down columns, then the rows of P^T), as row
+// axpys. A block takes a slice of SW outputs and one of kc row ranges; in each
+// round wave w takes 8 rows, lane l the pieces l + 64 i of the slice, so each
+// load reads 1 KiB of a row in one run. Wave sums meet in LDS in a fixed
+// order; every block writes its partial, zero when its range is empty. A block
+// whose range reaches the P^T rows first finishes their activations z = Q^T
+// h_hat over the skipped channels: the score blocks' per-group shares minus
+// the gate/up blocks' selected-channel shares, in fp32.
+// ===========================================================================
+constexpr int kB1Rows = 8;  // rows per wave per round
+
+template <int NP>
+__global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, int kc) {
+  constexpr int SW = 512 * NP;
+  __shared__ float s_red[kB1Waves][SW];
+  __shared__ float s_zp[kB1Waves][64];
+  __shared__ float s_z[128];
+  const int d = a.d, m = a.m;
+  const int slices = d / SW;
+  const int per_tile = slices * kc;
+  const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
+  const int sl = rem % slices, kci = rem / slices;
+  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int e = a.tile_expert[tile], first = a.tile_first[tile];
+  if (tile >= ntl) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = dense ? 0 : a.r;
+  const int K = uc + r;
+  constexpr int kRound = kB1Waves * kB1Rows;
+  const int rpb = ((K + kc - 1) / kc + kRound - 1) / kRound * kRound;
+  const int kb = kci * rpb, ke = min(K, kb + rpb);
+  const int pp = a.tpair[first];
+  const int* ul = a.ulist + (size_t)tile * m;
+  const uint16_t* hr = a.hbuf + (size_t)pp * a.kpad;
+  const size_t col = (size_t)SW * sl;
+  if (r > 0 && ke > max(uc, kb)) {
+    const int groups = m / kGroup, maxch = m / kCh;
+    const int nch = max(1, (uc + kCh - 1) / kCh);
+    const bool all_kept = a.k >= m;
+    const int g0 = groups * wave / kB1Waves, g1 = groups * (wave + 1) / kB1Waves;
+    const int c0 = nch * wave / kB1Waves, c1 = nch * (wave + 1) / kB1Waves;
+    const float* gz = a.gzpart + (size_t)pp * groups * r;
+    const float* zs = a.zsel + (size_t)pp * maxch * r;
+    for (int cb = 0; cb < r; cb += 64) {
+      const int c = cb + lane;
+      float z = 0.0f;
+      if (c < r && !all_kept)
+        z = sum_strided<16>(gz + (size_t)g0 * r + c, r, g1 - g0) - sum_strided<16>(zs + (size_t)c0 * r + c, r, c1 - c0);
+      s_zp[wave][lane] = z;
+      __syncthreads();
+      if (wave == 0 && c < r) {
+        float zt[kB1Waves];
+#pragma unroll
+        for (int w = 0; w < kB1Waves; ++w) zt[w] = s_zp[w][lane];
+#pragma unroll
+        for (int h = kB1Waves / 2; h > 0; h >>= 1)
+#pragma unroll
+          for (int w = 0; w < h; ++w) zt[w] += zt[w + h];
+        s_z[c] = zt[0];
+      }
+      __syncthreads();
+    }
+  }
+  float acc[NP][8];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int o = 0; o < 8; ++o) acc[q][o] = 0.0f;
+  for (int k0 = kb + kB1Rows * wave; k0 < ke; k0 += kRound) {
+    uint4 wv[kB1Rows][NP];
+    float h[kB1Rows];
+#pragma unroll
+    for (int i = 0; i < kB1Rows; ++i) {
+      const int k = min(k0 + i, ke - 1);
+      const uint16_t* row = k < uc ? a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d
+                                   : a.pmat + ((size_t)e * a.r + (k - uc)) * d;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) wv[i][q] = *(const uint4*)(row + col + 8 * (lane + 64 * q));
+      h[i] = k0 + i >= ke ? 0.0f : (k < uc ? bf16f(hr[k]) : s_z[k - uc]);
+    }
+#pragma unroll
+    for (int i = 0; i < kB1Rows; ++i)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) axpy8_bf16(h[i], wv[i][q], acc[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int o = 0; o < 8; ++o) s_red[wave][8 * (lane + 64 * q) + o] = acc[q][o];
+  __syncthreads();
+  float* yp = a.ypart + ((size_t)kci * a.batch * a.top_e + pp) * d + col;
+  for (int o = tid; o < SW; o += kB1Threads) {
+    float y = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kB1Waves; ++w) y += s_red[w][o];
+    yp[o] = y;
+  }
+}
+
 // ===========================================================================
 // After gate/up, one block per (tile, token): z = Q^T h_hat over the
 // token's skipped channels, i.e. the score blocks' per-group shares (all
@@ -814,20 +1122,6 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
 // block order, written to the activation columns after the union; then zeros
 // up to the next multiple of 32 columns.
 // ===========================================================================
-template <int N>
-__device__ __forceinline__ float sum_strided(const float* p, size_t stride, int count) {
-  float s = 0.0f;
-  int q = 0;
-  for (; q + N <= count; q += N) {
-    float part[N];
-#pragma unroll
-    for (int u = 0; u < N; ++u) part[u] = p[(size_t)(q + u) * stride];
-#pragma unroll
-    for (int u = 0; u < N; ++u) s += part[u];
-  }
-  for (; q < count; ++q) s += p[(size_t)q * stride];
-  return s;
-}
 
 constexpr int kZThreads = 1024, kZWaves = kZThreads / 64;
 
@@ -1007,7 +1301,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   float y = 0.0f;
   for (int s = 0; s < a.top_e; ++s) {
     const int p = t * a.top_e + s;
-    y += a.pair_w[p] * sum_strided<16>(a.ypart + (size_t)p * a.d + i, kstride, kc);
+    y += a.pair_w[p] * sum_strided<32>(a.ypart + (size_t)p * a.d + i, kstride, kc);
   }
   a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(y);
 }
@@ -1018,6 +1312,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
 bool grouped_supported(int d, int m) { return d >= 64 && m / 32 <= kSelMaxWords; }
 
 int grouped_down_width(int d) { return d % 256 == 0 ? 256 : 64; }
+
+bool grouped_b1_supported(int d) { return d % 512 == 0 && d <= 64 * 8 * kB1Pieces; }
+
+int grouped_down_split_b1(int kmax, int r) {
+  const int rounds = (kmax + r + kB1Waves * kB1Rows - 1) / (kB1Waves * kB1Rows);
+  return std::max(1, std::min(kMaxDownSplit, rounds));
+}
 
 int grouped_down_split(int max_tiles, int d, int kmax, int r) {
   const int sw = grouped_down_width(d);
@@ -1031,26 +1332,49 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
 }
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
+  const bool b1 = a.batch == 1 && grouped_b1_supported(a.d);
   const int pairs = a.batch * a.top_e;
   const int groups = a.m / kGroup;
   hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
   if (a.batch > 1) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
-    const size_t score_lds = ((size_t)kT * 64 + (size_t)64 * a.r) * 4;
-    hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads), score_lds, stream, a);
-    if (a.m <= 4 * kThreads)
-      hipLaunchKernelGGL(k_select<4>, dim3(pairs), dim3(kThreads), 0, stream, a);
-    else if (a.m <= 16 * kThreads)
-      hipLaunchKernelGGL(k_select<16>, dim3(pairs), dim3(kThreads), 0, stream, a);
+    if (b1)
+      hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), (size_t)a.d + 256 * (size_t)a.r,
+                         stream, a);
     else
-      hipLaunchKernelGGL(k_select<64>, dim3(pairs), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads),
+                         ((size_t)kT * 64 + (size_t)64 * a.r) * 4, stream, a);
+    if (a.m <= kSelThreads)
+      hipLaunchKernelGGL(k_select<1>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
+    else if (a.m <= 4 * kSelThreads)
+      hipLaunchKernelGGL(k_select<4>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_select<16>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
   }
-  hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  if (!dense) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
+  // at batch 1 the select kernel writes the (one-token) unions itself
+  if (dense || a.batch > 1)
+    hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  if (b1)
+    hipLaunchKernelGGL(k_gate_up_b1, dim3(a.max_tiles * (a.m / kCh)), dim3(kB1Threads), 0, stream, a, dense ? 1 : 0);
+  else
+    hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  // the batch-1 down kernel finishes the compensation coordinates itself
+  if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
   // the largest union a tile can have: k channels per token, at most m
   const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
+  if (b1) {
+    const int kc1 = grouped_down_split_b1(kmax, dense ? 0 : a.r);
+    if (a.d % 1024 == 0)
+      hipLaunchKernelGGL(k_down_b1<2>, dim3(a.max_tiles * (a.d / 1024) * kc1), dim3(kB1Threads), 0, stream, a,
+                         dense ? 1 : 0, kc1);
+    else
+      hipLaunchKernelGGL(k_down_b1<1>, dim3(a.max_tiles * (a.d / 512) * kc1), dim3(kB1Threads), 0, stream, a,
+                         dense ? 1 : 0, kc1);
+    const int per_tok1 = (a.d + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok1), dim3(kThreads), 0, stream, a, kc1);
+    return hipGetLastError();
+  }
   const int kc = grouped_down_split(a.max_tiles, a.d, kmax, dense ? 0 : a.r);
   if (sw == 256)
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
