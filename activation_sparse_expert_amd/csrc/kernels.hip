@@ -1123,7 +1123,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
 // up to the next multiple of 32 columns.
 // ===========================================================================
 
-constexpr int kZThreads = 1024, kZWaves = kZThreads / 64;
+constexpr int kZThreads = 256, kZWaves = kZThreads / 64;
 
 __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
   __shared__ float s_part[kZWaves][64];
@@ -1135,7 +1135,7 @@ __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
   const int pp = a.tpair[tf + j];
-  // wave q sums its sixteenth of the groups and of the gate/up blocks
+  // wave q sums its quarter of the groups and of the gate/up blocks
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g0 = groups * q / kZWaves, g1 = groups * (q + 1) / kZWaves;
   const int c0 = nch * q / kZWaves, c1 = nch * (q + 1) / kZWaves;
@@ -1293,15 +1293,41 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
 // Gate-weighted sum over a token's experts, bf16 output.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
+  constexpr int N = 16;  // partial values in flight per thread
   const int per_tok = (a.d + kThreads - 1) / kThreads;
   const int t = blockIdx.x / per_tok, blk = blockIdx.x % per_tok;
   const int i = blk * kThreads + threadIdx.x;
   if (i >= a.d) return;
   const size_t kstride = (size_t)a.batch * a.top_e * a.d;
-  float y = 0.0f;
-  for (int s = 0; s < a.top_e; ++s) {
-    const int p = t * a.top_e + s;
-    y += a.pair_w[p] * sum_strided<32>(a.ypart + (size_t)p * a.d + i, kstride, kc);
+  const float* base = a.ypart + (size_t)t * a.top_e * a.d + i;
+  // the token's partials v = s kc + q (pair s, split q) in batches of N; each
+  // pair's splits are summed in order, then weighted
+  const int total = a.top_e * kc;
+  float y = 0.0f, ps = 0.0f;
+  int s = 0, q = 0;  // pair and split of the next value to add
+  for (int v0 = 0; v0 < total; v0 += N) {
+    float part[N];
+    int ls = v0 / kc, lq = v0 % kc;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      part[u] = v0 + u < total ? base[(size_t)lq * kstride + (size_t)ls * a.d] : 0.0f;
+      if (++lq == kc) {
+        lq = 0;
+        ++ls;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      if (v0 + u < total) {
+        ps += part[u];
+        if (++q == kc) {
+          y += a.pair_w[t * a.top_e + s] * ps;
+          ps = 0.0f;
+          q = 0;
+          ++s;
+        }
+      }
+    }
   }
   a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(y);
 }
