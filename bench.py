@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--mixtral", type=int, default=1,
                     help="also time the Mixtral-shaped block at batch 1 (0: skip)")
     ap.add_argument("--mixtral-steps", type=int, default=256)
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the Mixtral-shaped block's score-kind ablation (counter runs)")
     ap.add_argument("--decode48", type=int, default=1,
                     help="also time a 48-layer decode step at batch 1, 8 and 32 (0: skip)")
     ap.add_argument("--decode-layers", type=int, default=12, help="distinct prepared layers in the 48-layer stack")
@@ -350,7 +352,8 @@ def main():
     blk.destroy()
     del blk
     if args.mixtral:
-        result["mixtral"] = time_mixtral(b, synth, torch, stream, args.mixtral_steps, args.eager)
+        result["mixtral"] = time_mixtral(b, synth, torch, stream, args.mixtral_steps, args.eager,
+                                         ablation=not args.no_ablation)
     if args.decode48:
         result["decode48"] = time_decode48(b, synth, torch, stream, args.decode_layers, args.decode_steps)
 
@@ -459,7 +462,7 @@ def score_ablation(b, torch, blk, ks, n_tok=4):
     return {"max_rel_dev_vs_dense": res, "tokens": n_tok}
 
 
-def time_mixtral(b, synth, torch, stream, steps, eager):
+def time_mixtral(b, synth, torch, stream, steps, eager, ablation=True):
     """Mixtral-8x7B-shaped block (d=4096, 8 experts, top-2, m=14336, r=64, LogNormal
     channel scales) at batch 1: both budgets and the dense-read block, over two
     rotated layer copies and eight tokens each (16 calls, about 3 GB of weights)."""
@@ -483,7 +486,8 @@ def time_mixtral(b, synth, torch, stream, steps, eager):
                     "algorithmic_bytes": byt, "achieved_GBs": round(byt / (ms_d * 1e-3) / 1e9, 1)}
     for k in w["ks"]:
         out[f"k{k}"]["speedup_vs_dense"] = round(ms_d / out[f"k{k}"]["ms_per_step"], 3)
-    out["score_ablation"] = score_ablation(b, torch, blk, w["ks"])
+    if ablation:
+        out["score_ablation"] = score_ablation(b, torch, blk, w["ks"])
     blk.destroy()
     return out
 
