@@ -420,33 +420,159 @@ constexpr int kB1Threads = 512, kB1Waves = kB1Threads / 64;
 constexpr int kB1Pieces = 8;  // 16-byte pieces per lane and row: d <= 4096
 constexpr int kSB1Blk = 16;  // code blocks per wave in flight
 
-__global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a) {
+// Routing of the one token of a batch-1 call by a 512-thread block
+// (n_experts <= 256), the same order as the routing kernel: the rank of a logit
+// is the count of larger order keys (larger logit first, lower index first),
+// two threads per expert; gate weights are the softmax over the chosen logits.
+__device__ __forceinline__ void route_b1(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
+                                         uint64_t* s_key, float* s_val) {
+  const int tid = threadIdx.x;
+  if (tid < n_experts) {
+    const float v = logits[tid];
+    s_key[tid] = order_key(float_order_bits(v), tid);
+    s_val[tid] = v;
+  }
+  __syncthreads();
+  const int i = tid >> 1, half = tid & 1;
+  int rank = 0;
+  if (i < n_experts) {
+    const uint64_t ki = s_key[i];
+    for (int j = half; j < n_experts; j += 2) rank += s_key[j] > ki;
+  }
+  rank += __shfl_xor(rank, 1, 64);
+  if (i < n_experts && half == 0 && rank < top_e) s_ids[rank] = i;
+  __syncthreads();
+  if (tid < top_e) {
+    const float top = s_val[s_ids[0]];
+    float den = 0.0f;
+    for (int s = 0; s < top_e; ++s) den += __expf(s_val[s_ids[s]] - top);
+    s_w[tid] = __expf(s_val[s_ids[tid]] - top) / den;
+  }
+  __syncthreads();
+}
+
+// self_route (batch 1, no routing kernel launched): every block routes the
+// token and quantises x itself, as the routing kernel would, and the blocks of
+// group 0 write their pair's routing and one-token plan for the later kernels.
+__global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_route) {
   extern __shared__ float s_dyn_sb1[];  // x_q [d] bytes, then Q rows [64][r]
   __shared__ int s_part[kB1Waves][64];
   __shared__ float s_h[64];
+  __shared__ uint64_t s_rkey[256];
+  __shared__ float s_rval[256];
+  __shared__ int s_ids[64];
+  __shared__ float s_w[64];
+  __shared__ int s_red[2][kB1Waves];
   const int d = a.d, m = a.m, r = a.r, groups = m / kGroup;
   const int tile = blockIdx.x / groups, grp = blockIdx.x % groups;
-  const int ntl = *a.n_tiles, e = a.tile_expert[tile], first = a.tile_first[tile];
-  if (tile >= ntl) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pp = a.tpair[first], t = pp / a.top_e;
+  const int npc = d / 8;
   int8_t* s_xq = (int8_t*)s_dyn_sb1;
   float* s_q = s_dyn_sb1 + d / 4;
+  int e, pp;
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  if (self_route) {
+    if (tile >= a.top_e) return;  // one single-token tile per routed pair
+    if (tid < npc) xv = *(const uint4*)(a.x + 8 * tid);
+    route_b1(a.logits, a.n_experts, a.top_e, s_ids, s_w, s_rkey, s_rval);
+    pp = tile;
+    e = s_ids[tile];
+  } else {
+    const int ntl = *a.n_tiles;
+    e = a.tile_expert[tile];
+    const int first = a.tile_first[tile];
+    if (tile >= ntl) return;
+    pp = a.tpair[first];
+  }
+  const int t = pp / a.top_e;
   const int mat = wave & 1, quarter = wave >> 1;
   const int nb = d / kBlock;
   const int b0 = nb * quarter / 4, b1 = nb * (quarter + 1) / 4;
   const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(d, m) +
                                    codes_dword_index(d, m, grp, mat, 0, lane, 0));
+  // every global load first: codes, Q rows, statistics, and x_q when it comes from the routing kernel
   uint4 cb[kSB1Blk];
 #pragma unroll
   for (int i = 0; i < kSB1Blk; ++i) cb[i] = cp[(size_t)min(b0 + i, b1 - 1) * 64];
-  for (int i = tid; i < d / 16; i += kB1Threads) ((int4*)s_xq)[i] = ((const int4*)(a.xq + (size_t)t * d))[i];
-  if (r > 0)
-    for (int i = tid; i < 64 * r; i += kB1Threads)
-      s_q[i] = __uint_as_float((uint32_t)a.qmat[((size_t)e * m + 64 * grp) * r + i] << 16);
+  constexpr int kQv = 64 * 128 * 2 / 16 / kB1Threads;  // 16-byte Q pieces per thread, r <= 128
+  const int qpieces = 8 * r;
+  const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * m + 64 * grp) * r);
+  uint4 qv[kQv];
+#pragma unroll
+  for (int u = 0; u < kQv; ++u) {
+    const int i = tid + u * kB1Threads;
+    qv[u] = i < qpieces ? qsrc[i] : make_uint4(0, 0, 0, 0);
+  }
   const float4 st = a.stats[(size_t)e * m + 64 * grp + lane];
-  const int xe = a.xexp[t], qs = a.xqsum[t];
-  __syncthreads();  // x_q in LDS
+  int4 xqv = make_int4(0, 0, 0, 0);
+  if (!self_route && tid < d / 16) xqv = ((const int4*)(a.xq + (size_t)t * d))[tid];
+  int xe, qs;
+  if (self_route) {
+    // int8 activations with a power-of-two scale, and their sum
+    uint32_t amax = 0;
+    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) amax = max(amax, max(w4[h] & 0x7FFFu, (w4[h] >> 16) & 0x7FFFu));
+    amax = wave_max_u(amax);
+    if (lane == 0) s_red[0][wave] = (int)amax;
+    __syncthreads();
+    amax = (uint32_t)s_red[0][0];
+#pragma unroll
+    for (int w = 1; w < kB1Waves; ++w) amax = max(amax, (uint32_t)s_red[0][w]);
+    xe = 0;
+    if (amax != 0) {
+      const float av = __uint_as_float(amax << 16);
+      int ex;
+      (void)__builtin_frexpf(av, &ex);  // av = f * 2^ex, f in [0.5, 1)
+      xe = ex - 7;
+      if (__builtin_ldexpf(av, -xe) > 127.0f) xe += 1;
+    }
+    int qsum = 0;
+    if (tid < npc) {
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t bits = (w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+        const int qi = amax ? (int)__builtin_rintf(__builtin_ldexpf(__uint_as_float(bits << 16), -xe)) : 0;
+        qsum += qi;
+        packed[h >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (h & 3));
+      }
+      *(uint2*)(s_xq + 8 * tid) = make_uint2(packed[0], packed[1]);
+    }
+    qsum = wave_sum_i(qsum);
+    if (lane == 0) s_red[1][wave] = qsum;
+    if (grp == 0 && tid == 0) {
+      a.pair_expert[pp] = e;
+      a.pair_w[pp] = s_w[pp];
+      a.tile_expert[pp] = e;
+      a.tile_first[pp] = pp;
+      a.tile_n[pp] = 1;
+      a.tpair[pp] = pp;
+      if (pp == 0) *a.n_tiles = a.top_e;
+    }
+    __syncthreads();
+    qs = 0;
+#pragma unroll
+    for (int w = 0; w < kB1Waves; ++w) qs += s_red[1][w];
+  } else {
+    xe = a.xexp[t];
+    qs = a.xqsum[t];
+    if (tid < d / 16) ((int4*)s_xq)[tid] = xqv;
+  }
+#pragma unroll
+  for (int u = 0; u < kQv; ++u) {
+    const int i = tid + u * kB1Threads;
+    if (i < qpieces) {
+      const uint4 q4 = qv[u];
+      const uint32_t w4[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        s_q[8 * i + 2 * h] = bf16lo(w4[h]);
+        s_q[8 * i + 2 * h + 1] = bf16hi(w4[h]);
+      }
+    }
+  }
+  __syncthreads();  // x_q and the Q rows in LDS
   int acc = 0;
   for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
     if (c0 != b0) {
@@ -955,11 +1081,9 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
       qv[u] = i < kCh * r && pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16)
                                       : 0.0f;
     }
-    if (tid < kCh) {
-      const int pos = kCh * chunk + tid;
-      s_hz[tid] = pos < uc ? a.hhat[(size_t)pp * m + ul[pos]] : 0.0f;
-    }
   }
+  float hzv = 0.0f;
+  if (r > 0 && tid < kCh && kCh * chunk + tid < uc) hzv = a.hhat[(size_t)pp * m + ul[kCh * chunk + tid]];
   const int pos0 = kCh * chunk + 2 * wave;
   const uint16_t* xr = a.x + (size_t)(pp / a.top_e) * d;
   const uint16_t* rows[2];
@@ -1005,6 +1129,7 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
     const int i = tid + u * kB1Threads;
     if (i < kCh * r) s_qr[i] = qv[u];
   }
+  if (tid < kCh) s_hz[tid] = hzv;
   __syncthreads();
   if (tid < r) {
     float z = 0.0f;
@@ -1359,14 +1484,16 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const bool b1 = a.batch == 1 && grouped_b1_supported(a.d);
+  // batch 1: the score blocks route and quantise the token themselves
+  const bool self_route = b1 && !dense && a.n_experts <= 256;
   const int pairs = a.batch * a.top_e;
   const int groups = a.m / kGroup;
-  hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
+  if (!self_route) hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
   if (a.batch > 1) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
     if (b1)
       hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), (size_t)a.d + 256 * (size_t)a.r,
-                         stream, a);
+                         stream, a, self_route ? 1 : 0);
     else
       hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads),
                          ((size_t)kT * 64 + (size_t)64 * a.r) * 4, stream, a);
