@@ -1060,15 +1060,18 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
   const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this wave's two channel indices, read with the tile's entries before the union size is known
+  const int pos0 = kCh * chunk + 2 * wave;
+  const int* ul = a.ulist + (size_t)tile * m;
+  const int ul0 = ul[min(pos0, m - 1)], ul1 = ul[min(pos0 + 1, m - 1)];
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile];
   if (tile >= ntl) return;
   const int nch = max(1, (uc + kCh - 1) / kCh);
   if (chunk >= nch) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = dense ? 0 : a.r;
   const int pp = a.tpair[first];
-  const int* ul = a.ulist + (size_t)tile * m;
   const int npc = d / 8;
   // the compensation share's inputs, in flight with the weights
   constexpr int kQPer = kCh * 128 / kB1Threads;  // r <= 128
@@ -1084,25 +1087,24 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
   }
   float hzv = 0.0f;
   if (r > 0 && tid < kCh && kCh * chunk + tid < uc) hzv = a.hhat[(size_t)pp * m + ul[kCh * chunk + tid]];
-  const int pos0 = kCh * chunk + 2 * wave;
   const uint16_t* xr = a.x + (size_t)(pp / a.top_e) * d;
   const uint16_t* rows[2];
+  bool live[2];
 #pragma unroll
   for (int ci = 0; ci < 2; ++ci) {
-    const int ch = uc > 0 ? ul[min(pos0 + ci, uc - 1)] : 0;
-    rows[ci] = a.wch + ((size_t)e * m + ch) * 3 * d;
+    live[ci] = pos0 + ci < uc;
+    rows[ci] = a.wch + ((size_t)e * m + min(max(ci ? ul1 : ul0, 0), m - 1)) * 3 * d;
   }
   uint4 xv[kB1Pieces], gv[2][kB1Pieces], uv[2][kB1Pieces];
 #pragma unroll
   for (int i = 0; i < kB1Pieces; ++i) {
     const int pc = lane + 64 * i;
-    if (pc < npc) {
-      xv[i] = *(const uint4*)(xr + 8 * pc);
+    xv[i] = pc < npc ? *(const uint4*)(xr + 8 * pc) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int ci = 0; ci < 2; ++ci) {
-        gv[ci][i] = *(const uint4*)(rows[ci] + 8 * pc);
-        uv[ci][i] = *(const uint4*)(rows[ci] + d + 8 * pc);
-      }
+    for (int ci = 0; ci < 2; ++ci) {
+      const bool ld = pc < npc && live[ci];
+      gv[ci][i] = ld ? *(const uint4*)(rows[ci] + 8 * pc) : make_uint4(0, 0, 0, 0);
+      uv[ci][i] = ld ? *(const uint4*)(rows[ci] + d + 8 * pc) : make_uint4(0, 0, 0, 0);
     }
   }
   float sg[2] = {0.0f, 0.0f}, su[2] = {0.0f, 0.0f};
@@ -1153,8 +1155,9 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
 constexpr int kB1Rows = 8;  // rows per wave per round
 
 template <int NP>
-__global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, int kc) {
+__global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, int kc, int rpb) {
   constexpr int SW = 512 * NP;
+  constexpr int kRound = kB1Waves * kB1Rows;
   __shared__ float s_red[kB1Waves][SW];
   __shared__ float s_zp[kB1Waves][64];
   __shared__ float s_z[128];
@@ -1163,20 +1166,43 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
   const int per_tile = slices * kc;
   const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
   const int sl = rem % slices, kci = rem / slices;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // rows [kb, kb + rpb) of the K range (rpb from the launch: kc rpb covers the
+  // largest K); the first round's channel indices are read with the tile's
+  // entries, before the union size is known
+  const int kb = kci * rpb;
+  const int* ul = a.ulist + (size_t)tile * m;
+  int ulv[kB1Rows];
+#pragma unroll
+  for (int i = 0; i < kB1Rows; ++i) ulv[i] = ul[min(kb + kB1Rows * wave + i, m - 1)];
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile];
   if (tile >= ntl) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
-  constexpr int kRound = kB1Waves * kB1Rows;
-  const int rpb = ((K + kc - 1) / kc + kRound - 1) / kRound * kRound;
-  const int kb = kci * rpb, ke = min(K, kb + rpb);
+  const int ke = min(K, kb + rpb);
   const int pp = a.tpair[first];
-  const int* ul = a.ulist + (size_t)tile * m;
   const uint16_t* hr = a.hbuf + (size_t)pp * a.kpad;
   const size_t col = (size_t)SW * sl;
+  uint4 wv[kB1Rows][NP];
+  // loads of the rows k0 .. k0 + 7 (channel indices from ulv in the first round)
+  auto load_round = [&](int k0, bool first_round) {
+#pragma unroll
+    for (int i = 0; i < kB1Rows; ++i) {
+      const int k = k0 + i;
+      if (k < ke) {
+        const int ch = first_round ? ulv[i] : (k < uc ? ul[k] : 0);
+        const uint16_t* row = k < uc ? a.wch + (((size_t)e * m + min(max(ch, 0), m - 1)) * 3 + 2) * d
+                                     : a.pmat + ((size_t)e * a.r + (k - uc)) * d;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) wv[i][q] = *(const uint4*)(row + col + 8 * (lane + 64 * q));
+      }
+    }
+  };
+  int k0 = kb + kB1Rows * wave;
+  if (k0 < ke) load_round(k0, true);
   if (r > 0 && ke > max(uc, kb)) {
+    // this block's rows reach P^T: z = Q^T h_hat over the skipped channels
     const int groups = m / kGroup, maxch = m / kCh;
     const int nch = max(1, (uc + kCh - 1) / kCh);
     const bool all_kept = a.k >= m;
@@ -1209,22 +1235,17 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
   for (int q = 0; q < NP; ++q)
 #pragma unroll
     for (int o = 0; o < 8; ++o) acc[q][o] = 0.0f;
-  for (int k0 = kb + kB1Rows * wave; k0 < ke; k0 += kRound) {
-    uint4 wv[kB1Rows][NP];
-    float h[kB1Rows];
+  for (; k0 < ke; k0 += kRound) {
 #pragma unroll
     for (int i = 0; i < kB1Rows; ++i) {
-      const int k = min(k0 + i, ke - 1);
-      const uint16_t* row = k < uc ? a.wch + (((size_t)e * m + ul[k]) * 3 + 2) * d
-                                   : a.pmat + ((size_t)e * a.r + (k - uc)) * d;
+      const int k = k0 + i;
+      if (k < ke) {
+        const float h = k < uc ? bf16f(hr[k]) : s_z[k - uc];
 #pragma unroll
-      for (int q = 0; q < NP; ++q) wv[i][q] = *(const uint4*)(row + col + 8 * (lane + 64 * q));
-      h[i] = k0 + i >= ke ? 0.0f : (k < uc ? bf16f(hr[k]) : s_z[k - uc]);
+        for (int q = 0; q < NP; ++q) axpy8_bf16(h, wv[i][q], acc[q]);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kB1Rows; ++i)
-#pragma unroll
-      for (int q = 0; q < NP; ++q) axpy8_bf16(h[i], wv[i][q], acc[q]);
+    if (k0 + kRound < ke) load_round(k0 + kRound, false);
   }
 #pragma unroll
   for (int q = 0; q < NP; ++q)
@@ -1418,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
 // Gate-weighted sum over a token's experts, bf16 output.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
-  constexpr int N = 16;  // partial values in flight per thread
+  constexpr int N = 32;  // partial values in flight per thread
   const int per_tok = (a.d + kThreads - 1) / kThreads;
   const int t = blockIdx.x / per_tok, blk = blockIdx.x % per_tok;
   const int i = blk * kThreads + threadIdx.x;
@@ -1518,12 +1539,16 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
   if (b1) {
     const int kc1 = grouped_down_split_b1(kmax, dense ? 0 : a.r);
+    // rows per block: a multiple of one round with kc1 blocks covering the largest K
+    constexpr int kRound = kB1Waves * kB1Rows;
+    const int kall = kmax + (dense ? 0 : a.r);
+    const int rpb = ((kall + kc1 - 1) / kc1 + kRound - 1) / kRound * kRound;
     if (a.d % 1024 == 0)
       hipLaunchKernelGGL(k_down_b1<2>, dim3(a.max_tiles * (a.d / 1024) * kc1), dim3(kB1Threads), 0, stream, a,
-                         dense ? 1 : 0, kc1);
+                         dense ? 1 : 0, kc1, rpb);
     else
       hipLaunchKernelGGL(k_down_b1<1>, dim3(a.max_tiles * (a.d / 512) * kc1), dim3(kB1Threads), 0, stream, a,
-                         dense ? 1 : 0, kc1);
+                         dense ? 1 : 0, kc1, rpb);
     const int per_tok1 = (a.d + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok1), dim3(kThreads), 0, stream, a, kc1);
     return hipGetLastError();
