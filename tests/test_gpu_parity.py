@@ -333,6 +333,56 @@ def test_graph_replay_matches_eager_multi_kernel(b, torch, tiny_layer):
     b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
 
 
+def test_graph_replay_matches_eager_batch1_rows(b, torch, qwen_layer):
+    """The batch-1 grouped kernels (the score blocks route and write the plan,
+    row-streaming gate/up and down) under graph capture: sparse, fewer experts,
+    dense and threshold calls replayed several times, with batch-4 calls that
+    rewrite the plan and unions in between, reproduce the eager outputs."""
+    lay = qwen_layer
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_MULTI_KERNEL)
+    lay.path = None
+    w = synth.WORKLOADS["qwen3"]
+    n = 4
+    xh = [synth.tokens(w["wid"], 0, 1, lay.d, index=20 + i) for i in range(n)]
+    lh = [synth.router_logits(w["wid"], 0, 1, lay.E, index=20 + i) for i in range(n)]
+    xs = [to_dev_u16(torch, v) for v in xh]
+    lgs = [to_dev_f32(torch, v) for v in lh]
+    outs = [torch.zeros((1, lay.d), dtype=torch.int16, device="cuda") for _ in range(n)]
+    stream = torch.cuda.Stream()
+    s = stream.cuda_stream
+
+    def calls():
+        b.moe_sel_forward(lay.ctx, xs[0], lgs[0], 1, lay.top_e, 138, outs[0], s)
+        b.moe_sel_forward(lay.ctx, xs[1], lgs[1], 1, 6, 100, outs[1], s)
+        b.moe_sel_forward_dense(lay.ctx, xs[2], lgs[2], 1, lay.top_e, outs[2], s)
+        b.moe_sel_forward_threshold(lay.ctx, xs[3], lgs[3], 1, lay.top_e, 0.3, outs[3], s)
+
+    with torch.cuda.stream(stream):
+        calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    # the eager outputs are the oracle's to the usual tolerance
+    ref = lay.oracle.forward(xh[0], lh[0], lay.top_e, 138)
+    assert rel_err(out_to_f64(torch, eager[0]), ref["y"]) <= TOL
+    xb = to_dev_u16(torch, synth.tokens(w["wid"], 0, 4, lay.d, index=30))
+    lb = to_dev_f32(torch, synth.router_logits(w["wid"], 0, 4, lay.E, index=30))
+    junk = torch.zeros((4, lay.d), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        b.moe_sel_forward(lay.ctx, xb, lb, 4, lay.top_e, 77 + rep, junk)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        b.moe_sel_check_device(lay.ctx)
+        for i in range(n):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
+
+
 def test_tiles_split_across_many_tokens_per_expert(b, torch):
     """200 tokens over 8 experts (top-2): experts receive more tokens than one
     expert tile holds, so their pairs span several tiles; every token still
