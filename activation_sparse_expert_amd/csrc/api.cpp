@@ -428,7 +428,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     const size_t need =
         (size_t)moe_sel::grouped_down_split(moe_sel::grouped_max_tiles(pp, c.n_experts), c.d, c.m, c.rank) * pp * d;
     ypart_count = std::max(ypart_count, need);
-    if (pp <= c.max_top_e)  // batch-1 calls
+    if (pp <= c.max_top_e || 2 * pp <= c.n_experts)  // calls with one pair per tile
       ypart_count = std::max(ypart_count, (size_t)moe_sel::grouped_down_split_b1(c.m, c.rank) * pp * d);
   }
   ALLOC(ypart, ypart_count);

@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 // ===========================================================================
 // Routing and activation quantisation, one block per token.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a, int pair_tiles) {
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_v[kWaves];
@@ -159,13 +159,13 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a) {
     const int p = t * a.top_e + tid;
     a.pair_expert[p] = s_sel[tid];
     a.pair_w[p] = __expf(s_selv[tid] - top) / denom;
-    if (a.batch == 1) {
-      // one token: the plan is one single-token tile per pair, in pair order
-      a.tile_expert[tid] = s_sel[tid];
-      a.tile_first[tid] = tid;
-      a.tile_n[tid] = 1;
-      a.tpair[tid] = tid;
-      if (tid == 0) *a.n_tiles = a.top_e;
+    if (pair_tiles) {
+      // the plan is one single-token tile per pair, in pair order
+      a.tile_expert[p] = s_sel[tid];
+      a.tile_first[p] = p;
+      a.tile_n[p] = 1;
+      a.tpair[p] = p;
+      if (p == 0) *a.n_tiles = a.batch * a.top_e;
     }
   }
 
@@ -451,9 +451,10 @@ __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int
   __syncthreads();
 }
 
-// self_route (batch 1, no routing kernel launched): every block routes the
-// token and quantises x itself, as the routing kernel would, and the blocks of
-// group 0 write their pair's routing and one-token plan for the later kernels.
+// self_route (one pair per tile, no routing kernel launched): every block
+// routes its token and quantises its x itself, as the routing kernel would, and
+// the blocks of group 0 write their pair's routing and one-token tile for the
+// later kernels.
 __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_route) {
   extern __shared__ float s_dyn_sb1[];  // x_q [d] bytes, then Q rows [64][r]
   __shared__ int s_part[kB1Waves][64];
@@ -472,11 +473,12 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   int e, pp;
   uint4 xv = make_uint4(0, 0, 0, 0);
   if (self_route) {
-    if (tile >= a.top_e) return;  // one single-token tile per routed pair
-    if (tid < npc) xv = *(const uint4*)(a.x + 8 * tid);
-    route_b1(a.logits, a.n_experts, a.top_e, s_ids, s_w, s_rkey, s_rval);
+    if (tile >= a.batch * a.top_e) return;  // one single-token tile per routed pair
+    const int tt = tile / a.top_e;
+    if (tid < npc) xv = *(const uint4*)(a.x + (size_t)tt * d + 8 * tid);
+    route_b1(a.logits + (size_t)tt * a.n_experts, a.n_experts, a.top_e, s_ids, s_w, s_rkey, s_rval);
     pp = tile;
-    e = s_ids[tile];
+    e = s_ids[tile % a.top_e];
   } else {
     const int ntl = *a.n_tiles;
     e = a.tile_expert[tile];
@@ -543,12 +545,12 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     if (lane == 0) s_red[1][wave] = qsum;
     if (grp == 0 && tid == 0) {
       a.pair_expert[pp] = e;
-      a.pair_w[pp] = s_w[pp];
+      a.pair_w[pp] = s_w[pp % a.top_e];
       a.tile_expert[pp] = e;
       a.tile_first[pp] = pp;
       a.tile_n[pp] = 1;
       a.tpair[pp] = pp;
-      if (pp == 0) *a.n_tiles = a.top_e;
+      if (pp == 0) *a.n_tiles = a.batch * a.top_e;
     }
     __syncthreads();
     qs = 0;
@@ -702,7 +704,7 @@ __device__ __forceinline__ void store_wave(uint32_t* bits, int j0, bool pred) {
   }
 
 template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a) {
+__global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tiles) {
   __shared__ __align__(16) int s_hist[kSelBins];  // histograms, then candidates
   __shared__ __align__(8) uint32_t s_bits[kSelMaxWords];
   __shared__ int s_tmp[kSelWaves + 2];
@@ -822,9 +824,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a) {
   int tot;
   int pos = sel_excl_scan(__popc(wb), s_tmp, &tot);
   uint32_t rest = wb;
-  // one token: tile p is pair p alone, and its union is the selection itself
-  int* ul = a.batch == 1 ? a.ulist + (size_t)p * m : nullptr;
-  uint64_t* um = a.batch == 1 ? a.umask + (size_t)p * m : nullptr;
+  // one pair per tile: tile p is pair p alone, and its union is the selection itself
+  int* ul = pair_tiles ? a.ulist + (size_t)p * m : nullptr;
+  uint64_t* um = pair_tiles ? a.umask + (size_t)p * m : nullptr;
   while (rest) {
     const int jj = 32 * tid + __ffs(rest) - 1;
     if (ul) {
@@ -1504,13 +1506,19 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
 }
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
-  const bool b1 = a.batch == 1 && grouped_b1_supported(a.d);
-  // batch 1: the score blocks route and quantise the token themselves
-  const bool self_route = b1 && !dense && a.n_experts <= 256;
   const int pairs = a.batch * a.top_e;
+  // One pair per tile (row kernels, no plan, no union) at batch 1, and for
+  // sparse calls whose pairs are at most half the experts, so that experts
+  // seldom repeat and reading an expert's rows once per pair costs little over
+  // once per expert. Otherwise pairs are grouped by expert into tiles.
+  const bool pair_tiles = grouped_b1_supported(a.d) && (a.batch == 1 || (!dense && 2 * pairs <= a.n_experts));
+  const bool b1 = pair_tiles;
+  // the score blocks route and quantise their tokens themselves
+  const bool self_route = pair_tiles && !dense && a.n_experts <= 256;
   const int groups = a.m / kGroup;
-  if (!self_route) hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a);
-  if (a.batch > 1) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  if (!self_route)
+    hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a, pair_tiles ? 1 : 0);
+  if (!pair_tiles) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
     if (b1)
       hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), (size_t)a.d + 256 * (size_t)a.r,
@@ -1518,25 +1526,27 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     else
       hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads),
                          ((size_t)kT * 64 + (size_t)64 * a.r) * 4, stream, a);
+    const int pt = pair_tiles ? 1 : 0;
     if (a.m <= kSelThreads)
-      hipLaunchKernelGGL(k_select<1>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_select<1>, dim3(pairs), dim3(kSelThreads), 0, stream, a, pt);
     else if (a.m <= 4 * kSelThreads)
-      hipLaunchKernelGGL(k_select<4>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_select<4>, dim3(pairs), dim3(kSelThreads), 0, stream, a, pt);
     else
-      hipLaunchKernelGGL(k_select<16>, dim3(pairs), dim3(kSelThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_select<16>, dim3(pairs), dim3(kSelThreads), 0, stream, a, pt);
   }
-  // at batch 1 the select kernel writes the (one-token) unions itself
-  if (dense || a.batch > 1)
+  // with one pair per tile the select kernel writes the unions itself
+  if (dense || !pair_tiles)
     hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   if (b1)
     hipLaunchKernelGGL(k_gate_up_b1, dim3(a.max_tiles * (a.m / kCh)), dim3(kB1Threads), 0, stream, a, dense ? 1 : 0);
   else
     hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  // the batch-1 down kernel finishes the compensation coordinates itself
+  // the row down kernel finishes the compensation coordinates itself
   if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
-  // the largest union a tile can have: k channels per token, at most m
-  const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * std::min(a.batch, kT));
+  // the largest union a tile can have: k channels per token of the tile, at most m
+  const int tile_tokens = pair_tiles ? 1 : std::min(a.batch, kT);
+  const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * tile_tokens);
   if (b1) {
     const int kc1 = grouped_down_split_b1(kmax, dense ? 0 : a.r);
     // rows per block: a multiple of one round with kc1 blocks covering the largest K

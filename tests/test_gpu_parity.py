@@ -228,6 +228,30 @@ def test_qwen3_shape_parity(b, torch, qwen, k):
     assert abs(k / qwen.m - {100: 0.13, 138: 0.18}[k]) <= 1 / (2 * qwen.m)
 
 
+@pytest.mark.parametrize("top_e,k", [(8, 138), (6, 100)])
+def test_qwen3_small_batch_parity(b, torch, qwen_layer, top_e, k):
+    """Four tokens on the expert-grouped path: 32 or 24 routed pairs over 128
+    experts, so every pair gets a tile of its own (the row kernels, no plan or
+    union launch); selections and outputs match the oracle token by token, and
+    the dense block of the same tokens stays on expert tiles."""
+    lay = qwen_layer
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_MULTI_KERNEL)
+    lay.path = "multi_kernel"
+    try:
+        w = synth.WORKLOADS["qwen3"]
+        x = synth.tokens(w["wid"], 0, 4, lay.d, index=40)
+        logits = synth.router_logits(w["wid"], 0, 4, lay.E, index=40)
+        out = _run(b, torch, lay, x, logits, k, top_e=top_e)
+        ref = lay.oracle.forward(x, logits, top_e, k)
+        _check_selection(b, lay, ref, 4, top_e, k)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+        dense = _run(b, torch, lay, x, logits, 0, top_e=top_e, dense=True)
+        assert rel_err(out_to_f64(torch, dense), lay.oracle.forward_dense(x, logits, top_e)) <= TOL
+    finally:
+        b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
+        lay.path = None
+
+
 def test_qwen3_shape_dense_parity(b, torch, qwen):
     w = synth.WORKLOADS["qwen3"]
     x = synth.tokens(w["wid"], 0, 1, qwen.d, index=1)
