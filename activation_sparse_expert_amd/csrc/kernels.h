@@ -67,6 +67,14 @@ constexpr int kMaxDownSplit = 64;
 int grouped_down_width(int d);
 // kmax: the largest union of channels a tile of the call can hold
 int grouped_down_split(int max_tiles, int d, int kmax, int r);
+// One routed pair per tile (row kernels, no plan or union launch): batch 1,
+// and sparse calls whose routed pairs are at most half the experts, so that
+// experts seldom repeat and reading an expert's rows once per pair costs little
+// over once per expert tile (at two pairs per expert the tile kernels win).
+// Such calls need no more tile slots than expert tiles would.
+inline bool grouped_pair_tiles(int batch, int top_e, int n_experts, bool dense) {
+  return batch == 1 || (!dense && 2 * batch * top_e <= n_experts);
+}
 // batch 1 (one token per tile): row-streaming gate/up and down kernels, and
 // the down projection's split of the K range
 bool grouped_b1_supported(int d);

@@ -1507,11 +1507,9 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int pairs = a.batch * a.top_e;
-  // One pair per tile (row kernels, no plan, no union) at batch 1, and for
-  // sparse calls whose pairs are at most half the experts, so that experts
-  // seldom repeat and reading an expert's rows once per pair costs little over
-  // once per expert. Otherwise pairs are grouped by expert into tiles.
-  const bool pair_tiles = grouped_b1_supported(a.d) && (a.batch == 1 || (!dense && 2 * pairs <= a.n_experts));
+  // One pair per tile (row kernels, no plan, no union) or pairs grouped by
+  // expert into tiles of up to kT tokens; max_tiles >= pairs in the first case.
+  const bool pair_tiles = grouped_b1_supported(a.d) && grouped_pair_tiles(a.batch, a.top_e, a.n_experts, dense);
   const bool b1 = pair_tiles;
   // the score blocks route and quantise their tokens themselves
   const bool self_route = pair_tiles && !dense && a.n_experts <= 256;
