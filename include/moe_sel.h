@@ -67,18 +67,22 @@ typedef enum moe_sel_status {
   MOE_SEL_EDEVICE = 4        /* the HIP runtime reported an error */
 } moe_sel_status;
 
-/* How a forward call is executed on the GPU (same results either way). */
+/* Channel score used to rank a pair's channels (moe_sel_set_score). */
 typedef enum moe_sel_score {
   MOE_SEL_SCORE_FULL = 0,          /* |silu(G) U| * ||down column|| (the default reading) */
   MOE_SEL_SCORE_GATE_ONLY = 1,     /* |silu(G)| * ||down column|| */
   MOE_SEL_SCORE_NO_DOWN_NORM = 2   /* |silu(G) U| */
 } moe_sel_score;
 
+/* How a forward call is executed on the GPU (same selections either way; outputs
+ * differ only in fp32 summation order). */
 typedef enum moe_sel_path {
   MOE_SEL_PATH_AUTO = 0,          /* single launch when it fits, else the multi-kernel path */
-  MOE_SEL_PATH_MULTI_KERNEL = 1,  /* pairs grouped by expert into tiles of up to 32 tokens, one kernel
-                                     per phase; every weight byte an expert needs is read once per
-                                     tile (the union of the tile tokens' selections) */
+  MOE_SEL_PATH_MULTI_KERNEL = 1,  /* one kernel per phase. Pairs are grouped by expert into tiles of up
+                                     to 32 tokens, and every weight byte an expert needs is read once
+                                     per tile (the union of the tile tokens' selections); at batch 1,
+                                     and for sparse calls whose routed pairs are at most half the
+                                     experts, every pair is a tile of its own */
   MOE_SEL_PATH_SINGLE_LAUNCH = 2  /* one fused kernel; EUNSUPPORTED when it cannot be used */
 } moe_sel_path;
 
