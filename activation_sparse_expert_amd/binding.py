@@ -26,6 +26,7 @@ EXPORTED = (
     "moe_sel_forward_dense", "moe_sel_forward_threshold", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
     "moe_sel_set_path", "moe_sel_last_path", "moe_sel_set_score", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
+    "moe_sel_residual_rmsnorm_router",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
@@ -85,6 +86,7 @@ def _load():
         "moe_sel_set_score": (ctypes.c_int, [vp, ctypes.c_int]),
         "moe_sel_router_logits": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "moe_sel_residual_rmsnorm": (ctypes.c_int, [vp, vp, i32, i32, ctypes.c_float, vp, vp]),
+        "moe_sel_residual_rmsnorm_router": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -265,3 +267,9 @@ def moe_sel_router_logits(x, w_router, batch, d, n_experts, logits, stream=None)
 def moe_sel_residual_rmsnorm(x, y, batch, d, eps, out, stream=None):
     _check(_lib.moe_sel_residual_rmsnorm(_dev_ptr(x), _dev_ptr(y), int(batch), int(d), float(eps),
                                          _dev_ptr(out), _stream(stream)), "moe_sel_residual_rmsnorm")
+
+
+def moe_sel_residual_rmsnorm_router(x, y, w_router, batch, d, n_experts, eps, x_out, logits, stream=None):
+    _check(_lib.moe_sel_residual_rmsnorm_router(_dev_ptr(x), _dev_ptr(y), _dev_ptr(w_router), int(batch), int(d),
+                                                int(n_experts), float(eps), _dev_ptr(x_out), _dev_ptr(logits),
+                                                _stream(stream)), "moe_sel_residual_rmsnorm_router")

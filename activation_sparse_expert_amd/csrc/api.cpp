@@ -717,4 +717,26 @@ moe_sel_status moe_sel_residual_rmsnorm(const uint16_t* x, const uint16_t* y, in
   return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
 }
 
+moe_sel_status moe_sel_residual_rmsnorm_router(const uint16_t* x, const uint16_t* y, const uint16_t* w_router,
+                                               int32_t batch, int32_t d, int32_t n_experts, float eps, uint16_t* x_out,
+                                               float* logits, void* stream) {
+  g_last_error.clear();
+  if (!x || !y || !w_router || !x_out || !logits)
+    return fail(MOE_SEL_EINVAL, "x, y, w_router, x_out and logits must be non-null");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w_router) || !aligned16(x_out) || ((uintptr_t)logits & 3u))
+    return fail(MOE_SEL_EINVAL, "x, y, w_router and x_out must be 16-byte aligned, logits 4-byte aligned");
+  if (batch < 1 || batch > 65535) return fail(MOE_SEL_EINVAL, "batch must be in [1, 65535]");
+  if (d < 64 || d > 4096 || d % 64) return fail(MOE_SEL_EINVAL, "d must be a multiple of 64 in [64, 4096]");
+  if (n_experts < 1 || n_experts > 1024) return fail(MOE_SEL_EINVAL, "n_experts must be in [1, 1024]");
+  if (!(eps > 0.0f) || !(eps < 1.0f)) return fail(MOE_SEL_EINVAL, "eps must be in (0, 1)");
+  const size_t row = (size_t)batch * d * 2;
+  auto overlap = [row](const void* p, const void* q) {
+    return (const char*)p < (const char*)q + row && (const char*)q < (const char*)p + row;
+  };
+  if (overlap(x_out, x) || overlap(x_out, y)) return fail(MOE_SEL_EINVAL, "x_out must not overlap x or y");
+  const hipError_t e =
+      moe_sel::launch_resnorm_router(x, y, w_router, batch, d, n_experts, eps, x_out, logits, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
 }  // extern "C"

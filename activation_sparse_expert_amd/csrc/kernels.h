@@ -107,5 +107,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w, int batch, int d,
                          hipStream_t stream);
 hipError_t launch_resnorm(const uint16_t* x, const uint16_t* y, int batch, int d, float eps, uint16_t* out,
                           hipStream_t stream);
+hipError_t launch_resnorm_router(const uint16_t* x, const uint16_t* y, const uint16_t* w, int batch, int d,
+                                 int n_experts, float eps, uint16_t* x_out, float* logits, hipStream_t stream);
 
 }  // namespace moe_sel

@@ -508,7 +508,8 @@ def time_decode48(b, synth, torch, stream, distinct, steps, batches=(1, 8, 32), 
         del wg, wu, wd
         wrs.append(torch.from_numpy(synth.router_weights(w["wid"], l, n_exp, d).view(np.int16)).to("cuda"))
     out = {"workload": f"{n_layers} stacked Qwen3-shaped layers (d={d}, {n_exp} experts, top-{top_e}, m={m}), "
-                       f"k={k} ({k / m:.1%}), r={r}; router and residual RMS renormalisation per layer",
+                       f"k={k} ({k / m:.1%}), r={r}; router and residual RMS renormalisation per layer "
+                       "(one launch between layers)",
            "distinct_layers": distinct, "setup_s": round(time.time() - t0, 1), "steps": steps}
     s = stream.cuda_stream
     for bsz in batches:
@@ -517,15 +518,23 @@ def time_decode48(b, synth, torch, stream, distinct, steps, batches=(1, 8, 32), 
         lg = torch.empty((bsz, n_exp), dtype=torch.float32, device="cuda")
         y = torch.empty((bsz, d), dtype=torch.int16, device="cuda")
 
+        xb = (x, torch.empty_like(x))  # the hidden state alternates between two buffers
+
         def step(dense):
+            # router of layer 0; between layers one launch renormalises the residual
+            # stream and applies the next layer's router; the last layer renormalises
+            b.moe_sel_router_logits(xb[0], wrs[0], bsz, d, n_exp, lg, s)
             for l in range(n_layers):
                 c = ctxs[l % distinct]
-                b.moe_sel_router_logits(x, wrs[l % distinct], bsz, d, n_exp, lg, s)
+                xc, xn = xb[l % 2], xb[(l + 1) % 2]
                 if dense:
-                    b.moe_sel_forward_dense(c, x, lg, bsz, top_e, y, s)
+                    b.moe_sel_forward_dense(c, xc, lg, bsz, top_e, y, s)
                 else:
-                    b.moe_sel_forward(c, x, lg, bsz, top_e, k, y, s)
-                b.moe_sel_residual_rmsnorm(x, y, bsz, d, eps, x, s)
+                    b.moe_sel_forward(c, xc, lg, bsz, top_e, k, y, s)
+                if l + 1 < n_layers:
+                    b.moe_sel_residual_rmsnorm_router(xc, y, wrs[(l + 1) % distinct], bsz, d, n_exp, eps, xn, lg, s)
+                else:
+                    b.moe_sel_residual_rmsnorm(xc, y, bsz, d, eps, xn, s)
 
         res = {}
         for dense in (False, True):

@@ -277,7 +277,7 @@ void moe_sel_destroy(moe_sel_ctx* ctx);
  * blocks inside decoding ("KAIST drops calibration from MoE decoding, speeds
  * up blocks by up to 2.69x over vLLM", opening paragraph); these two calls
  * chain blocks into a many-layer decode step with a router per layer and the
- * residual stream renormalised between layers.
+ * residual stream renormalised between layers; the third does both at once.
  *
  * moe_sel_router_logits: logits[t][e] = sum_i x[t][i] * w_router[e][i], fp32
  * accumulation of the bf16 products.
@@ -299,6 +299,23 @@ moe_sel_status moe_sel_router_logits(const uint16_t* x, const uint16_t* w_router
  */
 moe_sel_status moe_sel_residual_rmsnorm(const uint16_t* x, const uint16_t* y, int32_t batch, int32_t d, float eps,
                                         uint16_t* out, void* stream);
+
+/*
+ * moe_sel_residual_rmsnorm_router: both calls above in one launch, for the step
+ * from one layer to the next: x_out = the renormalised residual stream (as
+ * moe_sel_residual_rmsnorm, the mean square summed in another order, so an
+ * element may differ by one bf16 step) and logits = the next layer's router
+ * applied to x_out (as moe_sel_router_logits).
+ *   x, y      [batch][d] bf16 bits, device, 16-byte aligned
+ *   w_router  [n_experts][d] bf16 bits, device, 16-byte aligned (caller-owned)
+ *   x_out     [batch][d] bf16 bits, device, 16-byte aligned; must not overlap x or y
+ *   logits    [batch][n_experts] fp32, device, written
+ *   batch 1..65535, d a multiple of 64 in [64, 4096], n_experts 1..1024, eps in (0, 1).
+ * Asynchronous on stream. Errors: EINVAL (checked before enqueueing), EDEVICE.
+ */
+moe_sel_status moe_sel_residual_rmsnorm_router(const uint16_t* x, const uint16_t* y, const uint16_t* w_router,
+                                               int32_t batch, int32_t d, int32_t n_experts, float eps,
+                                               uint16_t* x_out, float* logits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,30 @@ def test_residual_rmsnorm_matches_oracle_within_one_bf16_step(b, torch):
     assert np.abs((got & 0x7FFF) - (ref & 0x7FFF)).max() <= 1
 
 
+def test_residual_rmsnorm_router_matches_oracle(b, torch):
+    """The one-launch step to the next layer: the renormalised state within one
+    bf16 step of the oracle's, the logits the oracle's router applied to it."""
+    d, E = W["d"], W["n_experts"]
+    x = synth.tokens(W["wid"], 2, 8, d)
+    y = synth.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((8, d)).astype(np.float32) * 0.3)
+    wr = synth.router_weights(W["wid"], 1, E, d)
+    xo = torch.empty((8, d), dtype=torch.int16, device="cuda")
+    lg = torch.empty((8, E), dtype=torch.float32, device="cuda")
+    b.moe_sel_residual_rmsnorm_router(to_dev_u16(torch, x), to_dev_u16(torch, y), to_dev_u16(torch, wr), 8, d, E, EPS,
+                                      xo, lg)
+    torch.cuda.synchronize()
+    got_bits = xo.cpu().numpy().view(np.uint16)
+    got = got_bits.astype(np.int64)
+    ref = oracle.residual_rmsnorm(x, y, EPS).astype(np.int64)
+    assert np.all((got >> 15) == (ref >> 15))
+    assert np.abs((got & 0x7FFF) - (ref & 0x7FFF)).max() <= 1
+    ref_lg = oracle.router_logits(got_bits, wr)
+    assert np.allclose(lg.cpu().numpy(), ref_lg, rtol=1e-5, atol=1e-5)
+    with pytest.raises(b.MoeSelError):  # x_out may not overlap the inputs
+        xd = to_dev_u16(torch, x)
+        b.moe_sel_residual_rmsnorm_router(xd, to_dev_u16(torch, y), to_dev_u16(torch, wr), 8, d, E, EPS, xd, lg)
+
+
 def test_glue_argument_errors(b, torch):
     x = torch.zeros((1, 64), dtype=torch.int16, device="cuda")
     lg = torch.zeros((1, 4), dtype=torch.float32, device="cuda")
