@@ -407,21 +407,22 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 }
 
 // ===========================================================================
-// Sketch scores for one-token tiles (batch 1), one block per (pair, 64-channel
-// group) with 8 waves = (matrix, quarter of the hidden dimension). Lane l is
+// Sketch scores for one-pair tiles (batch 1 and small sparse batches), one
+// block per (pair, 64-channel group) with 8 waves = (matrix, quarter of the
+// hidden dimension). Lane l is
 // channel l of the group and reads its 16-byte code piece of each 64-element
 // block, so one load instruction reads a block's 1 KiB of the group at once;
 // the token's x_q sits in LDS. The exact integer dots of the quarters are
 // added in LDS, then scores and h_hat as above, and the group's share of
 // Q^T h_hat.
 // ===========================================================================
-// batch-1 (one token per tile) kernels: 8 waves per block
+// kernels for one-pair tiles (batch 1, small sparse batches): 8 waves per block
 constexpr int kB1Threads = 512, kB1Waves = kB1Threads / 64;
 constexpr int kB1Pieces = 8;  // 16-byte pieces per lane and row: d <= 4096
 constexpr int kSB1Blk = 16;  // code blocks per wave in flight
 
-// Routing of the one token of a batch-1 call by a 512-thread block
-// (n_experts <= 256), the same order as the routing kernel: the rank of a logit
+// Routing of one token by a 512-thread block (n_experts <= 256), the same
+// order as the routing kernel: the rank of a logit
 // is the count of larger order keys (larger logit first, lower index first),
 // two threads per expert; gate weights are the softmax over the chosen logits.
 __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
@@ -1047,7 +1048,7 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
 }
 
 // ===========================================================================
-// Gate/up for one-token tiles (batch 1): the same 16-channel blocks as above,
+// Gate/up for one-pair tiles (one token each): the same 16-channel blocks as above,
 // computed as row dot products, since a single token leaves an MFMA's other
 // 15 columns empty. Wave w takes channels 2w and 2w + 1 of the block; lane l
 // holds the 16-byte pieces l + 64 i of x and of both rows, so each load
@@ -1144,7 +1145,7 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense)
 }
 
 // ===========================================================================
-// Down projection for one-token tiles (batch 1): y = sum_k h_k B_k over the
+// Down projection for one-pair tiles (one token each): y = sum_k h_k B_k over the
 // tile's K rows (union channels' down columns, then the rows of P^T), as row
 // axpys. A block takes a slice of SW outputs and one of kc row ranges; in each
 // round wave w takes 8 rows, lane l the pieces l + 64 i of the slice, so each
