@@ -39,6 +39,10 @@ WORKLOADS = {
                       rank=32, batch=64, routing="zipf", channel_scale=False, layers=1),
     "qwen3_48l": dict(wid=4, d=2048, n_experts=128, top_e=8, m=768, ks=(137,),
                       rank=32, batch=1, routing="router", channel_scale=False, layers=48),
+    # many small experts (a parity case, not a benchmark): more experts than one
+    # block of the one-pair-tile score kernel routes itself
+    "wide": dict(wid=5, d=512, n_experts=320, top_e=4, m=256, ks=(46,), rank=8,
+                 batch=1, routing="normal", channel_scale=False, layers=1),
 }
 
 WEIGHT_STD = 0.02

@@ -252,6 +252,27 @@ def test_qwen3_small_batch_parity(b, torch, qwen_layer, top_e, k):
         lay.path = None
 
 
+@pytest.mark.parametrize("bsz", [1, 4])
+def test_many_experts_parity(b, torch, bsz):
+    """320 experts (more than the score blocks route themselves): one pair per
+    tile with the routing kernel writing the plan, on the grouped path, at batch
+    1 and 4; selections bit-exact, outputs within tolerance."""
+    lay = Layer(b, "wide", max_batch=4)
+    try:
+        b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_MULTI_KERNEL)
+        lay.path = "multi_kernel"
+        w = synth.WORKLOADS["wide"]
+        k = w["ks"][0]
+        x = synth.tokens(w["wid"], 0, bsz, lay.d, index=3)
+        logits = synth.router_logits(w["wid"], 0, bsz, lay.E, index=3)
+        out = _run(b, torch, lay, x, logits, k)
+        ref = lay.oracle.forward(x, logits, lay.top_e, k)
+        _check_selection(b, lay, ref, bsz, lay.top_e, k)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        lay.close()
+
+
 def test_qwen3_shape_dense_parity(b, torch, qwen):
     w = synth.WORKLOADS["qwen3"]
     x = synth.tokens(w["wid"], 0, 1, qwen.d, index=1)
