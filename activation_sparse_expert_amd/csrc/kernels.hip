@@ -825,15 +825,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   int tot;
   int pos = sel_excl_scan(__popc(wb), s_tmp, &tot);
   uint32_t rest = wb;
-  // one pair per tile: tile p is pair p alone, and its union is the selection itself
+  // one pair per tile: tile p is pair p alone, and its union is the selection
+  // itself (the row kernels that read it need no token masks)
   int* ul = pair_tiles ? a.ulist + (size_t)p * m : nullptr;
-  uint64_t* um = pair_tiles ? a.umask + (size_t)p * m : nullptr;
   while (rest) {
     const int jj = 32 * tid + __ffs(rest) - 1;
-    if (ul) {
-      ul[pos] = jj;
-      um[pos] = 1ull;
-    }
+    if (ul) ul[pos] = jj;
     idx_out[pos++] = jj;
     rest &= rest - 1u;
   }
@@ -1057,12 +1054,13 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
 // Q^T h_hat, as above.
 // ===========================================================================
 
-__global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense) {
+// nchg: chunks per tile in the grid, enough for the largest union of the call
+__global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense, int nchg) {
   __shared__ float s_hz[kCh];
   __shared__ float s_qr[kCh * 128];
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
-  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
+  const int tile = blockIdx.x / nchg, chunk = blockIdx.x % nchg;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // this wave's two channel indices, read with the tile's entries before the union size is known
   const int pos0 = kCh * chunk + 2 * wave;
@@ -1536,16 +1534,18 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   // with one pair per tile the select kernel writes the unions itself
   if (dense || !pair_tiles)
     hipLaunchKernelGGL(k_union, dim3(a.max_tiles), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  if (b1)
-    hipLaunchKernelGGL(k_gate_up_b1, dim3(a.max_tiles * (a.m / kCh)), dim3(kB1Threads), 0, stream, a, dense ? 1 : 0);
-  else
-    hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
-  // the row down kernel finishes the compensation coordinates itself
-  if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
-  const int sw = grouped_down_width(a.d);
   // the largest union a tile can have: k channels per token of the tile, at most m
   const int tile_tokens = pair_tiles ? 1 : std::min(a.batch, kT);
   const int kmax = (dense || a.thr_mode) ? a.m : (int)std::min<long>(a.m, (long)a.k * tile_tokens);
+  if (b1) {
+    const int nchg = std::max(1, (kmax + kCh - 1) / kCh);
+    hipLaunchKernelGGL(k_gate_up_b1, dim3(a.max_tiles * nchg), dim3(kB1Threads), 0, stream, a, dense ? 1 : 0, nchg);
+  } else {
+    hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
+  }
+  // the row down kernel finishes the compensation coordinates itself
+  if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
+  const int sw = grouped_down_width(a.d);
   if (b1) {
     const int kc1 = grouped_down_split_b1(kmax, dense ? 0 : a.r);
     // rows per block: a multiple of one round with kc1 blocks covering the largest K
