@@ -31,6 +31,7 @@ SOURCES = [
     ("kernels.hip", DEVICE),
     ("fused.hip", DEVICE),
     ("lowrank_device.hip", DEVICE),
+    ("sketch_device.hip", DEVICE),
     ("decode_glue.hip", DEVICE),
     ("api.cpp", DEVICE),
     ("prepare_host.cpp", HOST_EXACT),

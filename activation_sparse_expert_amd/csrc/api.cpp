@@ -118,9 +118,17 @@ bool lowrank_on_device(const moe_sel_config& c) {
   return !(env && std::strcmp(env, "host") == 0);
 }
 
+// The sketch codes and statistics are built on the device (bit-identical);
+// MOE_SEL_SKETCH=host builds them on the host threads instead.
+bool sketch_on_device() {
+  const char* env = std::getenv("MOE_SEL_SKETCH");
+  return !(env && std::strcmp(env, "host") == 0);
+}
+
 struct PrepJob {
   const moe_sel_config* cfg;
   bool host_lowrank;
+  bool host_sketch;
   const uint16_t *wg, *wu, *wd;
   uint32_t* codes;
   float* stats;
@@ -135,8 +143,10 @@ void prep_one(int e, void* arg) {
   const moe_sel_config& c = *j->cfg;
   const size_t md = (size_t)c.m * c.d;
   moe_sel::ExpertPrep out;
-  out.codes = j->codes + (size_t)e * moe_sel::codes_dwords_per_expert(c.d, c.m);
-  out.stats = j->stats + (size_t)e * c.m * 4;
+  if (j->host_sketch) {
+    out.codes = j->codes + (size_t)e * moe_sel::codes_dwords_per_expert(c.d, c.m);
+    out.stats = j->stats + (size_t)e * c.m * 4;
+  }
   out.wch = j->wch + (size_t)e * 3 * md;
   if (c.rank > 0 && j->host_lowrank) {
     out.p_bf16 = j->pmat + (size_t)e * c.rank * c.d;
@@ -382,12 +392,16 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     return hip_fail(he, "hipGetDevice");
   }
   // host staging of the prepared layer
+  const bool dev_sketch = sketch_on_device();
+  const size_t n_codes = E * moe_sel::codes_dwords_per_expert(c.d, c.m);
   std::vector<uint32_t> h_codes;
   std::vector<float> h_stats;
   std::vector<uint16_t> h_wch, h_p, h_q;
   try {
-    h_codes.resize(E * moe_sel::codes_dwords_per_expert(c.d, c.m));
-    h_stats.resize(E * m * 4);
+    if (!dev_sketch) {
+      h_codes.resize(n_codes);
+      h_stats.resize(E * m * 4);
+    }
     h_wch.resize(E * m * 3 * d);
     h_p.resize(std::max<size_t>(E * r * d, 1));
     h_q.resize(std::max<size_t>(E * m * r, 1));
@@ -397,8 +411,8 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   }
   std::vector<std::string> errors(E);
   const bool dev_lowrank = lowrank_on_device(c);
-  PrepJob job{&c, !dev_lowrank, w_gate, w_up, w_down, h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(),
-              h_q.data(), &errors};
+  PrepJob job{&c,           !dev_lowrank, !dev_sketch, w_gate,   w_up,     w_down,
+              h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
   moe_sel::parallel_for((int)E, 0, prep_one, &job);
   for (size_t e = 0; e < E; ++e)
     if (!errors[e].empty()) {
@@ -408,7 +422,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   moe_sel_status st = MOE_SEL_OK;
 #define ALLOC(ptr, n) \
   if (st == MOE_SEL_OK) st = dev_alloc(ctx, &ctx->ptr, (n))
-  ALLOC(codes, h_codes.size());
+  ALLOC(codes, n_codes);
   ALLOC(stats, E * m);
   ALLOC(wch, h_wch.size());
   ALLOC(pmat, h_p.size());
@@ -482,6 +496,16 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
              {ctx->qmat, h_q.data(), h_q.size() * 2}};
   for (int ui = 0; ui < 5; ++ui) {
     const Up& u = ups[ui];
+    if (ui < 2 && dev_sketch) continue;
+    if (ui == 3 && dev_sketch) {
+      // codes and statistics from the channel rows now on the device
+      const std::string err = moe_sel::sketch_stats_device(ctx->wch, c.n_experts, c.d, c.m, c.tern_ratio,
+                                                           ctx->codes, (float*)ctx->stats, s);
+      if (!err.empty()) {
+        free_ctx(ctx);
+        return fail(MOE_SEL_EDEVICE, err);
+      }
+    }
     if (ui == 3 && dev_lowrank) {
       // maps from the channel rows now on the device
       const std::string err = moe_sel::lowrank_maps_device(ctx->wch, c.n_experts, c.d, c.m, c.rank, h_p.data(),

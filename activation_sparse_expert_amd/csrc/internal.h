@@ -78,6 +78,13 @@ void eigvecs_from_tridiag(const double* refl, int n, int r, const Tridiag& T, st
 std::string lowrank_maps_device(const uint16_t* wch_dev, int n_experts, int d, int m, int r, uint16_t* p_out,
                                 uint16_t* q_out, void* stream);
 
+// Ternary sketch codes and the stats [E][m] float4 {alpha_gate, alpha_up,
+// ||down_j||, 0} of all experts built on the device from the channel-major rows
+// (wch_dev, [E][m][3][d]), bit-identical to prepare_expert's. Queued on
+// `stream`; empty string on success.
+std::string sketch_stats_device(const uint16_t* wch_dev, int n_experts, int d, int m, double ratio,
+                                uint32_t* codes_dev, float* stats_dev, void* stream);
+
 // Returns an empty string on success, else the failure message.
 std::string prepare_expert(const moe_sel_config& cfg, const uint16_t* w_gate, const uint16_t* w_up,
                            const uint16_t* w_down, const ExpertPrep& out);

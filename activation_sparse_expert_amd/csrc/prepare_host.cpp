@@ -443,11 +443,18 @@ std::string prepare_expert(const moe_sel_config& cfg, const uint16_t* w_gate, co
   for (size_t i = 0, n = (size_t)m * d; i < n; ++i)
     if (((w_gate[i] >> 7) & 0xFF) == 0xFF || ((w_up[i] >> 7) & 0xFF) == 0xFF || ((w_down[i] >> 7) & 0xFF) == 0xFF)
       return "weights contain inf or nan";
+  // the sketch may be built elsewhere (on the device): skip it when no output asks for it
+  const bool sketch = out.tern_gate || out.tern_up || out.alpha_gate || out.alpha_up || out.down_norm ||
+                      out.nnz_gate || out.nnz_up || out.stats || out.codes;
   std::vector<int8_t> tg((size_t)d), tu((size_t)d);
   for (int j = 0; j < m; ++j) {
-    const RowStats sg = sketch_row(w_gate + (size_t)j * d, d, cfg.tern_ratio, tg.data());
-    const RowStats su = sketch_row(w_up + (size_t)j * d, d, cfg.tern_ratio, tu.data());
-    const float c = column_norm(w_down, d, m, j);
+    RowStats sg{0.0f, 0}, su{0.0f, 0};
+    float c = 0.0f;
+    if (sketch) {
+      sg = sketch_row(w_gate + (size_t)j * d, d, cfg.tern_ratio, tg.data());
+      su = sketch_row(w_up + (size_t)j * d, d, cfg.tern_ratio, tu.data());
+      c = column_norm(w_down, d, m, j);
+    }
     if (out.tern_gate) std::memcpy(out.tern_gate + (size_t)j * d, tg.data(), d);
     if (out.tern_up) std::memcpy(out.tern_up + (size_t)j * d, tu.data(), d);
     if (out.alpha_gate) out.alpha_gate[j] = sg.alpha;

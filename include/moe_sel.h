@@ -143,11 +143,14 @@ moe_sel_status moe_sel_prepare_expert_host(const moe_sel_config* cfg,
  * Build a context for one MoE layer: per-expert sketches, channel statistics
  * and low-rank maps (as moe_sel_prepare_expert_host), the channel-major weight
  * layout, and a workspace for cfg->max_batch tokens, all in device memory of
- * the current HIP device. The sketches and statistics are computed on the host
- * (exact sums); the low-rank maps are computed on the device in fp64 for all
- * experts at once (Gram matrices, tridiagonalisation and projection on the GPU,
- * the tridiagonal eigen-solves on host threads), or on the host when the
- * environment variable MOE_SEL_LOWRANK is "host" (the same eigen-solver).
+ * the current HIP device. The sketches and statistics are computed on the
+ * device from the channel-major rows, bit-identical to the host preparation
+ * (exact per-binade integer sums, rounded once to double), or on host threads
+ * when the environment variable MOE_SEL_SKETCH is "host". The low-rank maps are
+ * computed on the device in fp64 for all experts at once (Gram matrices,
+ * tridiagonalisation and projection on the GPU, the tridiagonal eigen-solves on
+ * host threads), or on the host when MOE_SEL_LOWRANK is "host" (the same
+ * eigen-solver).
  *   w_gate, w_up [E][m][d], w_down [E][d][m]: host bf16 bit patterns.
  *   stream: hipStream_t used for the uploads and the device work (null =
  *           default stream). The call synchronises it before returning, so the
