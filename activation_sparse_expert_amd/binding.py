@@ -18,7 +18,7 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_sel.so")
 
-MOE_SEL_OK, MOE_SEL_EINVAL, MOE_SEL_EUNSUPPORTED, MOE_SEL_ENOMEM, MOE_SEL_EDEVICE = range(5)
+MOE_SEL_OK, MOE_SEL_EINVAL, MOE_SEL_EUNSUPPORTED, MOE_SEL_ENOMEM, MOE_SEL_EDEVICE, MOE_SEL_EIO = range(6)
 
 EXPORTED = (
     "moe_sel_abi_version", "moe_sel_status_str", "moe_sel_last_error",
@@ -26,7 +26,7 @@ EXPORTED = (
     "moe_sel_forward_dense", "moe_sel_forward_threshold", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
     "moe_sel_set_path", "moe_sel_last_path", "moe_sel_set_score", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
-    "moe_sel_residual_rmsnorm_router",
+    "moe_sel_residual_rmsnorm_router", "moe_sel_save", "moe_sel_load",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
@@ -87,6 +87,8 @@ def _load():
         "moe_sel_router_logits": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "moe_sel_residual_rmsnorm": (ctypes.c_int, [vp, vp, i32, i32, ctypes.c_float, vp, vp]),
         "moe_sel_residual_rmsnorm_router": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp]),
+        "moe_sel_save": (ctypes.c_int, [vp, ctypes.c_char_p]),
+        "moe_sel_load": (ctypes.c_int, [ctypes.c_char_p, vp, ctypes.POINTER(vp)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -171,6 +173,18 @@ def moe_sel_prepare(cfg: moe_sel_config, w_gate, w_up, w_down, stream=None) -> i
     st = _lib.moe_sel_prepare(ctypes.byref(cfg), _host_ptr(w_gate, np.uint16), _host_ptr(w_up, np.uint16),
                               _host_ptr(w_down, np.uint16), _stream(stream), ctypes.byref(ctx))
     _check(st, "moe_sel_prepare")
+    return ctx.value
+
+
+def moe_sel_save(ctx, path):
+    """Write the prepared layer of ctx to path."""
+    _check(_lib.moe_sel_save(ctx, os.fsencode(path)), "moe_sel_save")
+
+
+def moe_sel_load(path, stream=None) -> int:
+    """Build a context from a file written by moe_sel_save; returns its handle."""
+    ctx = ctypes.c_void_p()
+    _check(_lib.moe_sel_load(os.fsencode(path), _stream(stream), ctypes.byref(ctx)), "moe_sel_load")
     return ctx.value
 
 

@@ -322,111 +322,23 @@ std::string validate_config(const moe_sel_config* c) {
 
 }  // namespace moe_sel
 
-extern "C" {
+namespace {
 
-int32_t moe_sel_abi_version(void) { return MOE_SEL_ABI_VERSION; }
-
-const char* moe_sel_status_str(moe_sel_status s) {
-  switch (s) {
-    case MOE_SEL_OK: return "ok";
-    case MOE_SEL_EINVAL: return "invalid argument";
-    case MOE_SEL_EUNSUPPORTED: return "unsupported";
-    case MOE_SEL_ENOMEM: return "out of memory";
-    case MOE_SEL_EDEVICE: return "device error";
-  }
-  return "unknown status";
-}
-
-const char* moe_sel_last_error(void) { return g_last_error.c_str(); }
-
-moe_sel_status moe_sel_prepare_expert_host(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
-                                           const uint16_t* w_down, int8_t* tern_gate, int8_t* tern_up,
-                                           float* alpha_gate, float* alpha_up, float* down_norm, int32_t* nnz_gate,
-                                           int32_t* nnz_up, uint16_t* p_bf16, uint16_t* q_bf16) {
-  g_last_error.clear();
-  const std::string bad = moe_sel::validate_config(cfg);
-  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
-  if (!w_gate || !w_up || !w_down) return fail(MOE_SEL_EINVAL, "weights must be non-null");
-  moe_sel::ExpertPrep out;
-  out.tern_gate = tern_gate;
-  out.tern_up = tern_up;
-  out.alpha_gate = alpha_gate;
-  out.alpha_up = alpha_up;
-  out.down_norm = down_norm;
-  out.nnz_gate = nnz_gate;
-  out.nnz_up = nnz_up;
-  out.p_bf16 = p_bf16;
-  out.q_bf16 = q_bf16;
-  try {
-    const std::string err = moe_sel::prepare_expert(*cfg, w_gate, w_up, w_down, out);
-    if (!err.empty()) return fail(MOE_SEL_EINVAL, err);
-  } catch (const std::bad_alloc&) {
-    return fail(MOE_SEL_ENOMEM, "host allocation failed");
-  } catch (...) {
-    return fail(MOE_SEL_EINVAL, "unexpected exception");
-  }
-  return MOE_SEL_OK;
-}
-
-moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
-                               const uint16_t* w_down, void* stream, moe_sel_ctx** out) {
-  g_last_error.clear();
-  const std::string bad = moe_sel::validate_config(cfg);
-  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
-  if (!w_gate || !w_up || !w_down || !out) return fail(MOE_SEL_EINVAL, "weights and out must be non-null");
-  if (!moe_sel::grouped_supported(cfg->d, cfg->m))
-    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(cfg->m) + " is above the per-pair selection limit (16384)");
-  const moe_sel_config c = *cfg;
+// Every device buffer of a layer: the prepared arrays (left for the caller to
+// fill) and the forward workspace sized for cfg.max_batch tokens.
+moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
+  const moe_sel_config& c = ctx->cfg;
   const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
   const size_t pairs = (size_t)c.max_batch * c.max_top_e;
-  moe_sel_ctx* ctx = nullptr;
-  try {
-    ctx = new moe_sel_ctx();
-  } catch (...) {
-    return fail(MOE_SEL_ENOMEM, "host allocation failed");
-  }
-  ctx->cfg = c;
-  hipError_t he = hipGetDevice(&ctx->device);
-  if (he != hipSuccess) {
-    free_ctx(ctx);
-    return hip_fail(he, "hipGetDevice");
-  }
-  // host staging of the prepared layer
-  const bool dev_sketch = sketch_on_device();
   const size_t n_codes = E * moe_sel::codes_dwords_per_expert(c.d, c.m);
-  std::vector<uint32_t> h_codes;
-  std::vector<float> h_stats;
-  std::vector<uint16_t> h_wch, h_p, h_q;
-  try {
-    if (!dev_sketch) {
-      h_codes.resize(n_codes);
-      h_stats.resize(E * m * 4);
-    }
-    h_wch.resize(E * m * 3 * d);
-    h_p.resize(std::max<size_t>(E * r * d, 1));
-    h_q.resize(std::max<size_t>(E * m * r, 1));
-  } catch (...) {
-    free_ctx(ctx);
-    return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
-  }
-  std::vector<std::string> errors(E);
-  const bool dev_lowrank = lowrank_on_device(c);
-  PrepJob job{&c,           !dev_lowrank, !dev_sketch, w_gate,   w_up,     w_down,
-              h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
-  moe_sel::parallel_for((int)E, 0, prep_one, &job);
-  for (size_t e = 0; e < E; ++e)
-    if (!errors[e].empty()) {
-      free_ctx(ctx);
-      return fail(MOE_SEL_EINVAL, "expert " + std::to_string(e) + ": " + errors[e]);
-    }
   moe_sel_status st = MOE_SEL_OK;
 #define ALLOC(ptr, n) \
   if (st == MOE_SEL_OK) st = dev_alloc(ctx, &ctx->ptr, (n))
   ALLOC(codes, n_codes);
   ALLOC(stats, E * m);
-  ALLOC(wch, h_wch.size());
-  ALLOC(pmat, h_p.size());
-  ALLOC(qmat, h_q.size());
+  ALLOC(wch, E * m * 3 * d);
+  ALLOC(pmat, std::max<size_t>(E * r * d, 1));
+  ALLOC(qmat, std::max<size_t>(E * m * r, 1));
   ALLOC(xq, (size_t)c.max_batch * d);
   ALLOC(xexp, (size_t)c.max_batch);
   ALLOC(pair_expert, pairs);
@@ -480,6 +392,191 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     ALLOC(err, 1);
   }
 #undef ALLOC
+  return st;
+}
+
+// After the prepared arrays are queued on s: empty hand-off slots and the
+// device properties of the single-launch path, then wait for s.
+moe_sel_status finish_layer(moe_sel_ctx* ctx, hipStream_t s) {
+  const moe_sel_config& c = ctx->cfg;
+  hipError_t he = hipSuccess;
+  if (ctx->xscore) {
+    he = reset_handoff(ctx, s);
+    if (he == hipSuccess) {
+      he = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, ctx->device);
+      ctx->fused_bpc_sparse = moe_sel::fused_blocks_per_cu(false, c.d, c.m, c.rank);
+      ctx->fused_bpc_dense = moe_sel::fused_blocks_per_cu(true, c.d, c.m, c.rank);
+    }
+    if (he != hipSuccess) return hip_fail(he, "fused path set-up");
+  }
+  he = hipStreamSynchronize(s);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize");
+  return MOE_SEL_OK;
+}
+
+// A context for cfg on the current device, with no buffers yet.
+moe_sel_status new_ctx(const moe_sel_config& c, moe_sel_ctx** out) {
+  moe_sel_ctx* ctx = nullptr;
+  try {
+    ctx = new moe_sel_ctx();
+  } catch (...) {
+    return fail(MOE_SEL_ENOMEM, "host allocation failed");
+  }
+  ctx->cfg = c;
+  const hipError_t he = hipGetDevice(&ctx->device);
+  if (he != hipSuccess) {
+    free_ctx(ctx);
+    return hip_fail(he, "hipGetDevice");
+  }
+  *out = ctx;
+  return MOE_SEL_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Saved layers. A file holds, little-endian:
+//   char magic[8] = "MOESELv1"; uint32 format = 1; uint32 zero;
+//   int32 d, n_experts, m, rank, max_top_e, max_batch; double tern_ratio;
+//   uint64 bytes of each prepared array: codes, stats, wch, pmat, qmat;
+//   the five arrays, device layout, in that order;
+//   uint64 FNV-1a hash of the arrays taken over 64-bit little-endian words.
+// ---------------------------------------------------------------------------
+constexpr char kMagic[8] = {'M', 'O', 'E', 'S', 'E', 'L', 'v', '1'};
+constexpr uint32_t kFormat = 1;
+constexpr size_t kStage = (size_t)64 << 20;  // bytes staged on the host at a time
+constexpr uint64_t kFnvBasis = 0xCBF29CE484222325ull, kFnvPrime = 0x100000001B3ull;
+
+struct SavedArray {
+  void* dev;
+  size_t bytes;
+};
+
+// Bytes of the prepared arrays of a layer (all multiples of 8).
+void prepared_bytes(const moe_sel_config& c, uint64_t (&b)[5]) {
+  const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
+  b[0] = E * moe_sel::codes_dwords_per_expert(c.d, c.m) * 4;
+  b[1] = E * m * 16;
+  b[2] = E * m * 3 * d * 2;
+  b[3] = E * r * d * 2;
+  b[4] = E * m * r * 2;
+}
+
+// The prepared arrays of a context: codes, stats, wch, pmat, qmat.
+void prepared_arrays(const moe_sel_ctx* ctx, SavedArray (&arr)[5]) {
+  uint64_t b[5];
+  prepared_bytes(ctx->cfg, b);
+  void* const dev[5] = {ctx->codes, ctx->stats, ctx->wch, ctx->pmat, ctx->qmat};
+  for (int i = 0; i < 5; ++i) arr[i] = {dev[i], (size_t)b[i]};
+}
+
+uint64_t fnv_words(uint64_t h, const unsigned char* p, size_t bytes) {
+  for (size_t i = 0; i + 8 <= bytes; i += 8) {
+    uint64_t w;
+    std::memcpy(&w, p + i, 8);
+    h = (h ^ w) * kFnvPrime;
+  }
+  return h;
+}
+
+struct FileCloser {
+  FILE* f;
+  ~FileCloser() {
+    if (f) std::fclose(f);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_sel_abi_version(void) { return MOE_SEL_ABI_VERSION; }
+
+const char* moe_sel_status_str(moe_sel_status s) {
+  switch (s) {
+    case MOE_SEL_OK: return "ok";
+    case MOE_SEL_EINVAL: return "invalid argument";
+    case MOE_SEL_EUNSUPPORTED: return "unsupported";
+    case MOE_SEL_ENOMEM: return "out of memory";
+    case MOE_SEL_EDEVICE: return "device error";
+    case MOE_SEL_EIO: return "file error";
+  }
+  return "unknown status";
+}
+
+const char* moe_sel_last_error(void) { return g_last_error.c_str(); }
+
+moe_sel_status moe_sel_prepare_expert_host(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                                           const uint16_t* w_down, int8_t* tern_gate, int8_t* tern_up,
+                                           float* alpha_gate, float* alpha_up, float* down_norm, int32_t* nnz_gate,
+                                           int32_t* nnz_up, uint16_t* p_bf16, uint16_t* q_bf16) {
+  g_last_error.clear();
+  const std::string bad = moe_sel::validate_config(cfg);
+  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
+  if (!w_gate || !w_up || !w_down) return fail(MOE_SEL_EINVAL, "weights must be non-null");
+  moe_sel::ExpertPrep out;
+  out.tern_gate = tern_gate;
+  out.tern_up = tern_up;
+  out.alpha_gate = alpha_gate;
+  out.alpha_up = alpha_up;
+  out.down_norm = down_norm;
+  out.nnz_gate = nnz_gate;
+  out.nnz_up = nnz_up;
+  out.p_bf16 = p_bf16;
+  out.q_bf16 = q_bf16;
+  try {
+    const std::string err = moe_sel::prepare_expert(*cfg, w_gate, w_up, w_down, out);
+    if (!err.empty()) return fail(MOE_SEL_EINVAL, err);
+  } catch (const std::bad_alloc&) {
+    return fail(MOE_SEL_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(MOE_SEL_EINVAL, "unexpected exception");
+  }
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, void* stream, moe_sel_ctx** out) {
+  g_last_error.clear();
+  const std::string bad = moe_sel::validate_config(cfg);
+  if (!bad.empty()) return fail(MOE_SEL_EINVAL, bad);
+  if (!w_gate || !w_up || !w_down || !out) return fail(MOE_SEL_EINVAL, "weights and out must be non-null");
+  if (!moe_sel::grouped_supported(cfg->d, cfg->m))
+    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(cfg->m) + " is above the per-pair selection limit (16384)");
+  const moe_sel_config c = *cfg;
+  const size_t E = c.n_experts, d = c.d, m = c.m, r = c.rank;
+  moe_sel_ctx* ctx = nullptr;
+  moe_sel_status st = new_ctx(c, &ctx);
+  if (st != MOE_SEL_OK) return st;
+  hipError_t he = hipSuccess;
+  // host staging of the prepared layer
+  const bool dev_sketch = sketch_on_device();
+  const size_t n_codes = E * moe_sel::codes_dwords_per_expert(c.d, c.m);
+  std::vector<uint32_t> h_codes;
+  std::vector<float> h_stats;
+  std::vector<uint16_t> h_wch, h_p, h_q;
+  try {
+    if (!dev_sketch) {
+      h_codes.resize(n_codes);
+      h_stats.resize(E * m * 4);
+    }
+    h_wch.resize(E * m * 3 * d);
+    h_p.resize(std::max<size_t>(E * r * d, 1));
+    h_q.resize(std::max<size_t>(E * m * r, 1));
+  } catch (...) {
+    free_ctx(ctx);
+    return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
+  }
+  std::vector<std::string> errors(E);
+  const bool dev_lowrank = lowrank_on_device(c);
+  PrepJob job{&c,           !dev_lowrank, !dev_sketch, w_gate,   w_up,     w_down,
+              h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
+  moe_sel::parallel_for((int)E, 0, prep_one, &job);
+  for (size_t e = 0; e < E; ++e)
+    if (!errors[e].empty()) {
+      free_ctx(ctx);
+      return fail(MOE_SEL_EINVAL, "expert " + std::to_string(e) + ": " + errors[e]);
+    }
+  st = alloc_layer(ctx);
   if (st != MOE_SEL_OK) {
     free_ctx(ctx);
     return st;
@@ -521,22 +618,120 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
       return hip_fail(he, "hipMemcpyAsync");
     }
   }
-  if (ctx->xscore) {
-    he = reset_handoff(ctx, s);
-    if (he == hipSuccess) {
-      he = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, ctx->device);
-      ctx->fused_bpc_sparse = moe_sel::fused_blocks_per_cu(false, c.d, c.m, c.rank);
-      ctx->fused_bpc_dense = moe_sel::fused_blocks_per_cu(true, c.d, c.m, c.rank);
-    }
-    if (he != hipSuccess) {
-      free_ctx(ctx);
-      return hip_fail(he, "fused path set-up");
-    }
-  }
-  he = hipStreamSynchronize(s);
-  if (he != hipSuccess) {
+  st = finish_layer(ctx, s);
+  if (st != MOE_SEL_OK) {
     free_ctx(ctx);
-    return hip_fail(he, "hipStreamSynchronize");
+    return st;
+  }
+  *out = ctx;
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_save(const moe_sel_ctx* ctx, const char* path) {
+  g_last_error.clear();
+  if (!ctx || !path) return fail(MOE_SEL_EINVAL, "ctx and path must be non-null");
+  DeviceGuard guard(ctx->device);
+  SavedArray arr[5];
+  prepared_arrays(ctx, arr);
+  std::vector<unsigned char> stage;
+  try {
+    stage.resize(kStage);
+  } catch (...) {
+    return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
+  }
+  FileCloser fc{std::fopen(path, "wb")};
+  if (!fc.f) return fail(MOE_SEL_EIO, std::string("cannot open ") + path + " for writing");
+  const moe_sel_config& c = ctx->cfg;
+  const uint32_t head[2] = {kFormat, 0u};
+  const int32_t dims[6] = {c.d, c.n_experts, c.m, c.rank, c.max_top_e, c.max_batch};
+  uint64_t sizes[5];
+  for (int i = 0; i < 5; ++i) sizes[i] = arr[i].bytes;
+  bool ok = std::fwrite(kMagic, 1, 8, fc.f) == 8 && std::fwrite(head, 4, 2, fc.f) == 2 &&
+            std::fwrite(dims, 4, 6, fc.f) == 6 && std::fwrite(&c.tern_ratio, 8, 1, fc.f) == 1 &&
+            std::fwrite(sizes, 8, 5, fc.f) == 5;
+  uint64_t h = kFnvBasis;
+  for (int i = 0; ok && i < 5; ++i)
+    for (size_t off = 0; ok && off < arr[i].bytes; off += kStage) {
+      const size_t n = std::min(kStage, arr[i].bytes - off);
+      const hipError_t e = hipMemcpy(stage.data(), (const unsigned char*)arr[i].dev + off, n, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+      h = fnv_words(h, stage.data(), n);
+      ok = std::fwrite(stage.data(), 1, n, fc.f) == n;
+    }
+  ok = ok && std::fwrite(&h, 8, 1, fc.f) == 1;
+  const int closed = std::fclose(fc.f);
+  fc.f = nullptr;
+  if (!ok || closed != 0) return fail(MOE_SEL_EIO, std::string("write to ") + path + " failed");
+  return MOE_SEL_OK;
+}
+
+moe_sel_status moe_sel_load(const char* path, void* stream, moe_sel_ctx** out) {
+  g_last_error.clear();
+  if (!path || !out) return fail(MOE_SEL_EINVAL, "path and out must be non-null");
+  FileCloser fc{std::fopen(path, "rb")};
+  if (!fc.f) return fail(MOE_SEL_EIO, std::string("cannot open ") + path);
+  const std::string bad_file = std::string(path) + " is not a saved layer: ";
+  char magic[8];
+  uint32_t head[2];
+  int32_t dims[6];
+  moe_sel_config c{};
+  c.struct_size = sizeof(moe_sel_config);
+  uint64_t sizes[5];
+  if (std::fread(magic, 1, 8, fc.f) != 8 || std::memcmp(magic, kMagic, 8) != 0)
+    return fail(MOE_SEL_EIO, bad_file + "wrong magic");
+  if (std::fread(head, 4, 2, fc.f) != 2 || head[0] != kFormat || head[1] != 0u)
+    return fail(MOE_SEL_EIO, bad_file + "unknown format version");
+  if (std::fread(dims, 4, 6, fc.f) != 6 || std::fread(&c.tern_ratio, 8, 1, fc.f) != 1 ||
+      std::fread(sizes, 8, 5, fc.f) != 5)
+    return fail(MOE_SEL_EIO, bad_file + "truncated header");
+  c.d = dims[0];
+  c.n_experts = dims[1];
+  c.m = dims[2];
+  c.rank = dims[3];
+  c.max_top_e = dims[4];
+  c.max_batch = dims[5];
+  const std::string bad = moe_sel::validate_config(&c);
+  if (!bad.empty()) return fail(MOE_SEL_EIO, bad_file + bad);
+  if (!moe_sel::grouped_supported(c.d, c.m))
+    return fail(MOE_SEL_EUNSUPPORTED, "m = " + std::to_string(c.m) + " is above the per-pair selection limit (16384)");
+  uint64_t expect[5];
+  prepared_bytes(c, expect);
+  for (int i = 0; i < 5; ++i)
+    if (sizes[i] != expect[i]) return fail(MOE_SEL_EIO, bad_file + "array sizes do not match its shape");
+  moe_sel_ctx* ctx = nullptr;
+  moe_sel_status st = new_ctx(c, &ctx);
+  if (st != MOE_SEL_OK) return st;
+  st = alloc_layer(ctx);
+  SavedArray arr[5];
+  prepared_arrays(ctx, arr);
+  std::vector<unsigned char> stage;
+  if (st == MOE_SEL_OK) try {
+      stage.resize(kStage);
+    } catch (...) {
+      st = fail(MOE_SEL_ENOMEM, "host staging allocation failed");
+    }
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t h = kFnvBasis;
+  for (int i = 0; st == MOE_SEL_OK && i < 5; ++i)
+    for (size_t off = 0; st == MOE_SEL_OK && off < arr[i].bytes; off += kStage) {
+      const size_t n = std::min(kStage, arr[i].bytes - off);
+      if (std::fread(stage.data(), 1, n, fc.f) != n) {
+        st = fail(MOE_SEL_EIO, bad_file + "truncated data");
+        break;
+      }
+      h = fnv_words(h, stage.data(), n);
+      hipError_t e = hipMemcpyAsync((unsigned char*)arr[i].dev + off, stage.data(), n, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);  // the staging buffer is reused
+      if (e != hipSuccess) st = hip_fail(e, "hipMemcpyAsync");
+    }
+  uint64_t stored = 0;
+  if (st == MOE_SEL_OK && (std::fread(&stored, 8, 1, fc.f) != 1 || stored != h))
+    st = fail(MOE_SEL_EIO, bad_file + "checksum mismatch");
+  if (st == MOE_SEL_OK && std::fgetc(fc.f) != EOF) st = fail(MOE_SEL_EIO, bad_file + "trailing bytes");
+  if (st == MOE_SEL_OK) st = finish_layer(ctx, s);
+  if (st != MOE_SEL_OK) {
+    free_ctx(ctx);
+    return st;
   }
   *out = ctx;
   return MOE_SEL_OK;

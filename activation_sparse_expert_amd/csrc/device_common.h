@@ -370,6 +370,22 @@ __device__ __forceinline__ uint64_t order_key(uint32_t ordered_value, int index)
 // below top_e are the routed experts, and the gate weights are the softmax over
 // their logits. s_scr: 2 * n_experts uint64 + n_experts ints of LDS scratch.
 // Barriers inside; s_ids / s_w valid when it returns.
+// Gate weights of the routed experts, in place: s_w[0..top_e) holds their
+// logits in rank order (largest first) and receives the softmax over them. The
+// exponentials are taken in parallel by wave 0 and the denominator is summed in
+// rank order. The caller synchronises before and after.
+__device__ __forceinline__ void route_softmax(float* s_w, int top_e) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const float v = lane < top_e ? s_w[lane] : 0.0f;
+    const float top = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    const float ex = __expf(v - top);
+    float den = 0.0f;
+    for (int s = 0; s < top_e; ++s) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
+    if (lane < top_e) s_w[lane] = ex / den;
+  }
+}
+
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void block_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
                                             void* s_scr) {
@@ -401,15 +417,15 @@ __device__ __forceinline__ void block_route(const float* logits, int n_experts, 
     }
   }
   __syncthreads();
-  for (int i = tid; i < n_experts; i += kThreads)
-    if (s_rank[i] < top_e) s_ids[s_rank[i]] = i;
-  __syncthreads();
-  if (tid < top_e) {
-    const float top = s_val[s_ids[0]];
-    float den = 0.0f;
-    for (int s = 0; s < top_e; ++s) den += __expf(s_val[s_ids[s]] - top);
-    s_w[tid] = __expf(s_val[s_ids[tid]] - top) / den;
+  for (int i = tid; i < n_experts; i += kThreads) {
+    const int rk = s_rank[i];
+    if (rk < top_e) {
+      s_ids[rk] = i;
+      s_w[rk] = s_val[i];
+    }
   }
+  __syncthreads();
+  route_softmax(s_w, top_e);
   __syncthreads();
 }
 

@@ -441,14 +441,12 @@ __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int
     for (int j = half; j < n_experts; j += 2) rank += s_key[j] > ki;
   }
   rank += __shfl_xor(rank, 1, 64);
-  if (i < n_experts && half == 0 && rank < top_e) s_ids[rank] = i;
-  __syncthreads();
-  if (tid < top_e) {
-    const float top = s_val[s_ids[0]];
-    float den = 0.0f;
-    for (int s = 0; s < top_e; ++s) den += __expf(s_val[s_ids[s]] - top);
-    s_w[tid] = __expf(s_val[s_ids[tid]] - top) / den;
+  if (i < n_experts && half == 0 && rank < top_e) {
+    s_ids[rank] = i;
+    s_w[rank] = s_val[i];
   }
+  __syncthreads();
+  route_softmax(s_w, top_e);
   __syncthreads();
 }
 

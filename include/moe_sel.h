@@ -64,7 +64,8 @@ typedef enum moe_sel_status {
   MOE_SEL_EINVAL = 1,        /* an argument is null, misaligned or out of range */
   MOE_SEL_EUNSUPPORTED = 2,  /* well-formed, but outside what this library implements */
   MOE_SEL_ENOMEM = 3,        /* a host or device allocation failed */
-  MOE_SEL_EDEVICE = 4        /* the HIP runtime reported an error */
+  MOE_SEL_EDEVICE = 4,       /* the HIP runtime reported an error */
+  MOE_SEL_EIO = 5            /* a file could not be opened, read or written, or is not a saved layer */
 } moe_sel_status;
 
 /* Channel score used to rank a pair's channels (moe_sel_set_score). */
@@ -270,6 +271,34 @@ moe_sel_status moe_sel_get_config(const moe_sel_ctx* ctx, moe_sel_config* cfg);
 
 /* Device bytes owned by the context (weights, sketch, maps and workspace). */
 uint64_t moe_sel_device_bytes(const moe_sel_ctx* ctx);
+
+/*
+ * Write the prepared layer of ctx to a file: its shape (the config) and the
+ * arrays moe_sel_prepare built from the weights alone (page "KAIST drops
+ * calibration from MoE decoding, speeds up blocks by up to 2.69x over vLLM",
+ * section "A reader built from weights alone"): the 2-bit sketch codes, the
+ * per-channel statistics, the channel-major bf16 weights and the rank-r maps,
+ * in their device layouts, followed by a 64-bit FNV-1a hash of the arrays. The
+ * forward workspace is not saved. An existing file is replaced.
+ *   path: file name (host string).
+ * Synchronous (copies the arrays from the device). Errors: EINVAL (null
+ * argument), EIO (the file cannot be written), ENOMEM, EDEVICE.
+ */
+moe_sel_status moe_sel_save(const moe_sel_ctx* ctx, const char* path);
+
+/*
+ * Build a context on the current HIP device from a file written by
+ * moe_sel_save, without preparing again: forward calls on it give the same
+ * results as on the context that was saved (its path and score settings start
+ * at their defaults).
+ *   stream: hipStream_t used for the uploads (null = default stream); the call
+ *           synchronises it before returning.
+ *   out:    receives the new context (unchanged on error).
+ * Errors: EINVAL (null argument), EIO (the file cannot be opened, is not a
+ * saved layer, is truncated, has trailing bytes or fails its hash check),
+ * EUNSUPPORTED (m > 16384), ENOMEM, EDEVICE. Nothing is leaked on error.
+ */
+moe_sel_status moe_sel_load(const char* path, void* stream, moe_sel_ctx** out);
 
 /* Release a context and all its device memory. Null is a no-op. The caller
  * must make sure no enqueued call on it is still running. */

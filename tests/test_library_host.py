@@ -150,3 +150,37 @@ def test_lowrank_map_qwen_shape_flat_spectrum():
     ref = p @ q.T
     got = om.bf16_bits_to_f64(lib_out["p_bf16"]).T @ om.bf16_bits_to_f64(lib_out["q_bf16"]).T
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 6e-3
+
+
+def _saved_header(d=256, E=8, m=512, r=8, top_e=2, batch=1, ratio=0.7, sizes=None, magic=b"MOESELv1", fmt=1):
+    import struct
+    cfg = b.make_config(d, E, m, r, top_e, batch)
+    if sizes is None:
+        sizes = (E * m * d // 2, E * m * 16, E * m * 3 * d * 2, E * r * d * 2, E * m * r * 2)
+    return struct.pack("<8sII6id5Q", magic, fmt, 0, cfg.d, cfg.n_experts, cfg.m, cfg.rank, cfg.max_top_e,
+                       cfg.max_batch, ratio, *sizes)
+
+
+def test_load_rejects_bad_files_before_touching_a_device(tmp_path):
+    """Headers are checked before any device call, so these run without a GPU."""
+    with pytest.raises(b.MoeSelError) as ei:
+        b.moe_sel_load(tmp_path / "missing.moesel")
+    assert ei.value.status == b.MOE_SEL_EIO
+    cases = {
+        "wrong magic": _saved_header(magic=b"NOTSAVED"),
+        "format version": _saved_header(fmt=2),
+        "truncated header": _saved_header()[:40],
+        "d must be": _saved_header(d=96),
+        "array sizes": _saved_header(sizes=(1, 2, 3, 4, 5)),
+    }
+    for what, blob in cases.items():
+        p = tmp_path / "bad.moesel"
+        p.write_bytes(blob)
+        with pytest.raises(b.MoeSelError) as ei:
+            b.moe_sel_load(p)
+        assert ei.value.status == b.MOE_SEL_EIO, what
+        assert what in str(ei.value), (what, str(ei.value))
+    with pytest.raises(b.MoeSelError) as ei:
+        b.moe_sel_save(None, tmp_path / "x.moesel")
+    assert ei.value.status == b.MOE_SEL_EINVAL
+    assert b.moe_sel_status_str(b.MOE_SEL_EIO) == "file error"
