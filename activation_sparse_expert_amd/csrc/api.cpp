@@ -258,12 +258,20 @@ hipError_t launch_any(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, 
     const bool zblocks = !dense && base.r > 0;
     f.ncs = f.nc + (zblocks ? 1 : 0);
     f.n_z = zblocks ? pairs : 0;
-    f.n_score = dense ? 0 : pairs * (base.m / moe_sel::kGroup);
     f.n_gather = pairs * f.nc;
     f.n_combine = base.batch * (base.d / 32);
-    const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
     const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
-    if (total <= (long)bpc * c->num_cus) {
+    const long capacity = (long)bpc * c->num_cus;
+    // score blocks of 32 channels spread the sketch over more CUs; 64 when that grid would not fit
+    f.score_ch = moe_sel::kFusedScoreChMin;
+    f.n_score = dense ? 0 : pairs * (base.m / f.score_ch);
+    if (!dense && ((long)f.n_score + f.n_gather + f.n_z + f.n_combine > capacity ||
+                   !moe_sel::fused_narrow_score_ok(base.m, base.r))) {
+      f.score_ch = 2 * moe_sel::kFusedScoreChMin;
+      f.n_score = pairs * (base.m / f.score_ch);
+    }
+    const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
+    if (total <= capacity) {
       c->last_path = MOE_SEL_PATH_SINGLE_LAUNCH;
       return moe_sel::launch_fused(f, dense, stream);
     }
@@ -380,9 +388,9 @@ moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
     ctx->fused_max_batch = std::min(c.max_batch, kFusedMaxBatch);
     const size_t fp = (size_t)ctx->fused_max_batch * c.max_top_e;
     const size_t nc_max = (m + kMinChunk - 1) / kMinChunk;
-    const size_t groups = m / moe_sel::kGroup, slices = d / 64;
+    const size_t slices = d / 64;
     ctx->xscore_count = fp * (nc_max + 1) * m;
-    ctx->zpart_count = fp * groups * std::max<size_t>(r, 1);
+    ctx->zpart_count = fp * (m / moe_sel::kFusedScoreChMin) * std::max<size_t>(r, 1);
     ctx->partial_count = (size_t)ctx->fused_max_batch * slices * c.max_top_e * nc_max * 64;
     ctx->zcopy_count = (size_t)ctx->fused_max_batch * 2 * slices * c.max_top_e * std::max<size_t>(r, 1);
     ALLOC(xscore, ctx->xscore_count);

@@ -182,21 +182,23 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
 // 2-bit offset-binary codes (t + 1) of 16 hidden elements against 16 int8
 // activations: the four byte-aligned 2-bit fields of each shift line up with
 // four consecutive activations.
-__device__ __forceinline__ int dot_codes16(uint32_t cw, int4 x, int acc) {
-  acc = __builtin_amdgcn_sdot4((int)(cw & 0x03030303u), x.x, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 2) & 0x03030303u), x.y, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 4) & 0x03030303u), x.z, acc, false);
-  acc = __builtin_amdgcn_sdot4((int)((cw >> 6) & 0x03030303u), x.w, acc, false);
-  return acc;
+// Sum of code * x_q over the 16 elements of one code dword, accumulated in three
+// parts so that the codes need masks but only one shift: the codes of elements
+// 4..7 enter multiplied by 4 and those of elements 8..15 by 16 (every byte stays
+// within int8: code << 4 <= 32). The exact sum is code_acc_total().
+struct CodeAcc {
+  int s1 = 0, s4 = 0, s16 = 0;
+};
+
+__device__ __forceinline__ void dot_codes16(uint32_t cw, int4 x, CodeAcc& a) {
+  a.s1 = __builtin_amdgcn_sdot4((int)(cw & 0x03030303u), x.x, a.s1, false);
+  a.s4 = __builtin_amdgcn_sdot4((int)(cw & 0x0C0C0C0Cu), x.y, a.s4, false);
+  a.s16 = __builtin_amdgcn_sdot4((int)(cw & 0x30303030u), x.z, a.s16, false);
+  a.s16 = __builtin_amdgcn_sdot4((int)((cw >> 2) & 0x30303030u), x.w, a.s16, false);
 }
 
-__device__ __forceinline__ int byte_sum4(int4 x, int acc) {
-  acc = __builtin_amdgcn_sdot4(x.x, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.y, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.z, 0x01010101, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.w, 0x01010101, acc, false);
-  return acc;
-}
+// s4 and s16 are exact multiples of 4 and 16, so the shifts divide exactly
+__device__ __forceinline__ int code_acc_total(const CodeAcc& a) { return a.s1 + (a.s4 >> 2) + (a.s16 >> 4); }
 
 // exclusive count of `flag` over the block in thread order; *total = block count.
 // Uses s_tmp[kWaves]; contains barriers (all threads must call).
@@ -359,17 +361,13 @@ __device__ __forceinline__ uint32_t float_order_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
 }
+// Order bits of a logit: -0 and +0 are equal values, so both map to +0's bits
+// (ties between them then go to the lower index).
+__device__ __forceinline__ uint32_t logit_order_bits(float f) { return float_order_bits(f == 0.0f ? 0.0f : f); }
 __device__ __forceinline__ uint64_t order_key(uint32_t ordered_value, int index) {
   return ((uint64_t)ordered_value << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)index);
 }
 
-// ---------------------------------------------------------------------------
-// Routing of one token by the whole block (n_experts <= 1024): the rank of every
-// logit (larger first, lower index first) is the count of larger order keys,
-// computed by all threads in parallel over parts of the expert range; ranks
-// below top_e are the routed experts, and the gate weights are the softmax over
-// their logits. s_scr: 2 * n_experts uint64 + n_experts ints of LDS scratch.
-// Barriers inside; s_ids / s_w valid when it returns.
 // Gate weights of the routed experts, in place: s_w[0..top_e) holds their
 // logits in rank order (largest first) and receives the softmax over them. The
 // exponentials are taken in parallel by wave 0 and the denominator is summed in
@@ -386,16 +384,96 @@ __device__ __forceinline__ void route_softmax(float* s_w, int top_e) {
   }
 }
 
+// Maximum of v over the 64 lanes, returned to every lane: DPP moves within rows
+// of 16 lanes (quad swaps, then rotations by 4 and 8), then the row broadcasts
+// of lanes 15 and 31, which leave the total in lane 63. No LDS traffic.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast 15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast 31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Routing by one wave for small top_e: lane l holds the logits of experts
+// l + 64 u; each of top_e rounds takes the wave-wide maximum of the remaining
+// order bits and, among the experts holding it, the lowest index (a ballot per
+// slot, slots in index order). Writes s_ids[rank] and the logit in s_w[rank].
+template <int KPER>
+__device__ __forceinline__ void wave_topk_route(const float* logits, int n_experts, int top_e, int* s_ids,
+                                                float* s_w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ob[KPER];
+  float val[KPER];
+  bool alive[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int idx = lane + 64 * u;
+    alive[u] = idx < n_experts;
+    val[u] = alive[u] ? logits[idx] : 0.0f;
+    ob[u] = logit_order_bits(val[u]);
+  }
+  for (int s = 0; s < top_e; ++s) {
+    uint32_t best = 0;
+#pragma unroll
+    for (int u = 0; u < KPER; ++u)
+      if (alive[u]) best = max(best, ob[u]);
+    const uint32_t m = wave_max_dpp(best);
+    int win_u = -1;
+    uint64_t win_mask = 0;
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const uint64_t bm = __ballot(alive[u] && ob[u] == m);
+      if (win_u < 0 && bm) {
+        win_u = u;
+        win_mask = bm;
+      }
+    }
+    const int win_lane = __builtin_ctzll(win_mask);
+#pragma unroll
+    for (int u = 0; u < KPER; ++u)
+      if (u == win_u && lane == win_lane) {
+        alive[u] = false;
+        s_ids[s] = lane + 64 * u;
+        s_w[s] = val[u];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Routing of one token by the whole block (n_experts <= 1024): for top_e <= 16
+// and n_experts <= 256 by one wave (wave_topk_route); otherwise the rank of
+// every logit (larger first, lower index first) is the count of larger order
+// keys, computed by all threads in parallel over parts of the expert range, and
+// ranks below top_e are the routed experts. The gate weights are the softmax
+// over their logits (skipped when with_weights is false). s_scr: 2 * n_experts
+// uint64 + n_experts ints of LDS scratch. Barriers inside; s_ids (and s_w)
+// valid when it returns.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void block_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
-                                            void* s_scr) {
+                                            void* s_scr, bool with_weights = true) {
   const int tid = threadIdx.x;
+  if (top_e <= 16 && n_experts <= 256) {  // few rounds: one wave, no block-wide ranking
+    if (tid < 64) {
+      if (n_experts <= 64) wave_topk_route<1>(logits, n_experts, top_e, s_ids, s_w);
+      else if (n_experts <= 128) wave_topk_route<2>(logits, n_experts, top_e, s_ids, s_w);
+      else wave_topk_route<4>(logits, n_experts, top_e, s_ids, s_w);
+    }
+    __syncthreads();
+    if (with_weights) {
+      route_softmax(s_w, top_e);
+      __syncthreads();
+    }
+    return;
+  }
   uint64_t* s_key = (uint64_t*)s_scr;
   int* s_rank = (int*)(s_key + n_experts);
   float* s_val = (float*)(s_rank + n_experts);
   for (int i = tid; i < n_experts; i += kThreads) {
     const float v = logits[i];
-    s_key[i] = order_key(float_order_bits(v), i);
+    s_key[i] = order_key(logit_order_bits(v), i);
     s_val[i] = v;
     s_rank[i] = 0;
   }
@@ -425,8 +503,10 @@ __device__ __forceinline__ void block_route(const float* logits, int n_experts, 
     }
   }
   __syncthreads();
-  route_softmax(s_w, top_e);
-  __syncthreads();
+  if (with_weights) {
+    route_softmax(s_w, top_e);
+    __syncthreads();
+  }
 }
 
 // Compiler-level ordering of LDS accesses inside one wavefront (a wave's LDS

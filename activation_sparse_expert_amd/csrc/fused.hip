@@ -3,7 +3,7 @@
 // One kernel runs the whole block; its workgroups take one of three roles by
 // block index, producers always below their consumers:
 //
-//   [0, n_score)            score    one (token, expert) pair x 64 channels:
+//   [0, n_score)            score    one (token, expert) pair x 32 (or 64) channels:
 //                                    route + quantise (redundant per block), the
 //                                    2-bit sketch GEMV, pinned channel scores,
 //                                    h_hat, and this group's share of Q^T h_hat;
@@ -56,7 +56,7 @@ constexpr int kMaxChunkDense = 16;
 constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
 constexpr int kScoreBlk = 16;        // sketch blocks loaded together per wave
 constexpr int kZPass = 4;            // compensation row passes loaded together
-constexpr int kMaxZPart = 4;         // zpart values per thread (groups * r <= 1024)
+constexpr int kMaxZPart = 4;         // zpart values per thread ((m / 32) * r <= 1024)
 constexpr int kMaxP = 4;             // 16-byte P pieces per combine thread (top_e * r <= 256)
 constexpr int kCombPer = 24;         // partial values per combine thread per poll batch
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
@@ -73,6 +73,7 @@ struct Smem {
   int tmp[kWaves + 2];
   float red[kWaves][2 * kMaxChunkDense];
   uint32_t amax[kWaves];
+  int qsum[kWaves][4];             // per wave: sum of x_q over each quarter of d (the score role's split)
 };
 
 __device__ __forceinline__ bool empty(float v) { return __float_as_uint(v) == kEmpty; }
@@ -105,7 +106,9 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int d, uint4 (&xv)[SLO
   }
 }
 
-// int8 activations with a power-of-two scale into LDS; returns the exponent
+// int8 activations with a power-of-two scale into LDS; returns the exponent.
+// Each wave's sums of x_q over the four quarters of d (64-element blocks
+// [nb q / 4, nb (q + 1) / 4)) go to sm.qsum (read them after the next barrier).
 template <int SLOTS>
 __device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, int8_t* xq, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -130,6 +133,8 @@ __device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, 
     e_t = ex - 7;
     if (__builtin_ldexpf(av, -e_t) > 127.0f) e_t += 1;
   }
+  int qs[4] = {0, 0, 0, 0};
+  const int nb = nslots >> 3;
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     const int s = tid + u * kThreads;
@@ -137,59 +142,92 @@ __device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, 
       float f[8];
       unpack8(xv[u], f);
       uint32_t lo = 0, hi = 0;
+      int sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        lo |= ((uint32_t)(int)__builtin_rintf(__builtin_ldexpf(f[q], -e_t)) & 0xFFu) << (8 * q);
-        hi |= ((uint32_t)(int)__builtin_rintf(__builtin_ldexpf(f[q + 4], -e_t)) & 0xFFu) << (8 * q);
+        const int a = (int)__builtin_rintf(__builtin_ldexpf(f[q], -e_t));
+        const int b = (int)__builtin_rintf(__builtin_ldexpf(f[q + 4], -e_t));
+        lo |= ((uint32_t)a & 0xFFu) << (8 * q);
+        hi |= ((uint32_t)b & 0xFFu) << (8 * q);
+        sum += a + b;
       }
       *(uint2*)(xq + 8 * s) = make_uint2(lo, hi);
+      const int b = s >> 3;
+      const int q = (b >= nb / 4) + (b >= nb * 2 / 4) + (b >= nb * 3 / 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k == q) qs[k] += sum;
     }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    qs[k] = wave_sum_i(qs[k]);
+    if (lane == 0) sm.qsum[wave][k] = qs[k];
   }
   return e_t;
 }
 
-__device__ __forceinline__ void route(const FusedArgs& a, int t, Smem& sm) {
-  block_route(a.logits + (size_t)t * a.n_experts, a.n_experts, a.top_e, sm.ids, sm.w, sm.route);
+__device__ __forceinline__ void route(const FusedArgs& a, int t, Smem& sm, bool with_weights = true) {
+  block_route(a.logits + (size_t)t * a.n_experts, a.n_experts, a.top_e, sm.ids, sm.w, sm.route, with_weights);
 }
 
 // ---------------------------------------------------------------------------
-// score role
+// score role: one (token, expert) pair x SC = a.score_ch channels (32 or 64),
+// so that a pair's sketch bytes spread over m / SC blocks
 // ---------------------------------------------------------------------------
-template <int SLOTS>
+template <int SLOTS, int SC>
 __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
-  const int groups = a.m / kGroup;
-  const int p = bid / groups, g = bid % groups;
+  constexpr int lps = 64 / SC;  // lane groups per wave: 2 (SC = 32) or 1
+  const int zg = a.m / SC;
+  const int p = bid / zg, sb = bid % zg;
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = a.r;
   int8_t* s_xq = (int8_t*)dyn;                               // d bytes
-  uint16_t* s_q = (uint16_t*)(dyn + a.d);                    // 64 x r bf16
-  float* s_h = (float*)(dyn + a.d + 64 * r * 2);             // 64
-  float* s_sc = s_h + 64;                                    // 64
+  uint16_t* s_q = (uint16_t*)(dyn + a.d);                    // SC x r bf16
+  float* s_h = (float*)(dyn + a.d + 64 * r * 2);             // SC
+  float* s_sc = s_h + 64;                                    // SC
   int* s_part = (int*)(s_sc + 64);                           // kWaves x 64
 
   uint4 xv[SLOTS];
   load_x<SLOTS>(a.x + (size_t)t * a.d, a.d, xv);  // in flight during the routing
-  route(a, t, sm);
+  route(a, t, sm, false);                          // the expert only: no gate weights here
   const int e = sm.ids[slot];
-  // every global load of this block: the sketch codes, the group's Q rows, its statistics
-  const int mat = wave >> 1, half = wave & 1;
+  // every global load of this block: the sketch codes, the SC Q rows, the statistics.
+  // Lane = (lane group, channel c); wave = (matrix, half of the d parts). The d
+  // range splits into 2 * lps parts of whole 64-element blocks (quarters for
+  // SC = 32, halves for 64); a load instruction reads lps runs of 64 * 16 / lps
+  // bytes of one code block row each.
+  const int c = lane & (SC - 1), mat = wave >> 1;
+  constexpr int nparts = 2 * lps;
+  const int part = (wave & 1) * lps + lane / SC;
+  const int j0 = sb * SC;  // first channel of the block
   const int nb = a.d / kBlock;
-  const int b0 = half ? nb / 2 : 0, b1 = half ? nb : nb / 2;
+  const int b0 = nb * part / nparts, b1 = nb * (part + 1) / nparts;  // empty when nb is small
   const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
-                                   codes_dword_index(a.d, a.m, g, mat, 0, lane, 0));
+                                   codes_dword_index(a.d, a.m, j0 / kGroup, mat, 0, j0 % kGroup + c, 0));
   uint4 cb[kScoreBlk];
 #pragma unroll
-  for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)min(b0 + i, b1 - 1) * 64];
-  const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * a.m + (size_t)g * kGroup) * r);
-  const int qpieces = 8 * r;  // 64 rows x r bf16 / 8
-  uint4 qv[4];
+  for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)max(min(b0 + i, b1 - 1), 0) * 64];
+  const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * a.m + (size_t)j0) * r);
+  const int qpieces = SC * r / 8;
+  constexpr int kQv = SC * 128 / 8 / kThreads;  // pieces per thread for r <= 128
+  uint4 qv[kQv];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qv[u] = qpieces ? qsrc[min(tid + u * kThreads, qpieces - 1)] : make_uint4(0, 0, 0, 0);
-  const float4 st = a.stats[(size_t)e * a.m + g * kGroup + lane];
+  for (int u = 0; u < kQv; ++u)
+    if (tid + u * kThreads < qpieces) qv[u] = qsrc[tid + u * kThreads];
+  const float4 st = a.stats[(size_t)e * a.m + j0 + c];
   const int e_t = quantise_to_lds<SLOTS>(xv, a.d, s_xq, sm);
   __syncthreads();  // x_q in LDS
-  int acc = 0, qs = 0;
+  // sum of x_q over this thread's part of d: quarters sum directly, halves are two quarters
+  const int q0 = part * 4 / nparts, q1 = (part + 1) * 4 / nparts;
+  int qs = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q >= q0 && q < q1) qs += sm.qsum[w][q];
+  CodeAcc acc;
   for (int c0 = b0; c0 < b1; c0 += kScoreBlk) {
     if (c0 != b0) {
 #pragma unroll
@@ -199,49 +237,46 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     for (int i = 0; i < kScoreBlk; ++i) {
       if (c0 + i < b1) {
         const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
-        const int4 x0 = xb[0], x1 = xb[1], x2 = xb[2], x3 = xb[3];
-        acc = dot_codes16(cb[i].x, x0, acc);
-        acc = dot_codes16(cb[i].y, x1, acc);
-        acc = dot_codes16(cb[i].z, x2, acc);
-        acc = dot_codes16(cb[i].w, x3, acc);
-        qs = byte_sum4(x0, qs);
-        qs = byte_sum4(x1, qs);
-        qs = byte_sum4(x2, qs);
-        qs = byte_sum4(x3, qs);
+        dot_codes16(cb[i].x, xb[0], acc);
+        dot_codes16(cb[i].y, xb[1], acc);
+        dot_codes16(cb[i].z, xb[2], acc);
+        dot_codes16(cb[i].w, xb[3], acc);
       }
     }
   }
-  s_part[wave * 64 + lane] = acc - qs;  // sum (code - 1) * q = sum t * q
+  s_part[wave * 64 + lane] = code_acc_total(acc) - qs;  // sum (code - 1) * q = sum t * q
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kQv; ++u) {
     const int i = tid + u * kThreads;
     if (i < qpieces) ((uint4*)s_q)[i] = qv[u];
   }
   __syncthreads();
-  if (wave == 0) {
-    const int dg = s_part[lane] + s_part[64 + lane];
-    const int du = s_part[128 + lane] + s_part[192 + lane];
+  if (tid < SC) {  // every part of each matrix: waves 0, 1 (gate) and 2, 3 (up), all lane groups
+    int dg = 0, du = 0;
+    for (int k = 0; k < 64; k += SC) {
+      dg += s_part[k + c] + s_part[64 + k + c];
+      du += s_part[128 + k + c] + s_part[192 + k + c];
+    }
     float h, sc;
     pinned_score(dg, du, e_t, st, h, sc, a.score_kind);
-    s_h[lane] = h;
-    s_sc[lane] = sc;
+    s_h[c] = h;
+    s_sc[c] = sc;
   }
   __syncthreads();
-  // publish (score, h_hat) of the 64 channels to each gather block of the pair
-  const int j0 = g * kGroup;
-  for (int i = tid; i < a.ncs * 64; i += kThreads) {
-    const int c = i >> 6, l = i & 63;
+  // publish (score, h_hat) of the block's channels to each gather block of the pair
+  for (int i = tid; i < a.ncs * SC; i += kThreads) {
+    const int cc = i / SC, l = i % SC;
     const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
-    st_coh64(&a.xscore[((size_t)p * a.ncs + c) * a.m + j0 + l], v);
+    st_coh64(&a.xscore[((size_t)p * a.ncs + cc) * a.m + j0 + l], v);
   }
-  // this group's share of Q^T h_hat over all of its channels, for the z block
+  // this block's share of Q^T h_hat over its channels, for the z block
   if (tid < r) {
     float z = 0.0f;
 #pragma unroll 16
-    for (int j = 0; j < 64; ++j) z += s_h[j] * bf16f(s_q[j * r + tid]);
-    st_coh(&a.zpart[((size_t)p * groups + g) * r + tid], z);
+    for (int j = 0; j < SC; ++j) z += s_h[j] * bf16f(s_q[j * r + tid]);
+    st_coh(&a.zpart[((size_t)p * zg + sb) * r + tid], z);
   }
-  if (tid < 64) {  // for inspection only
+  if (tid < SC) {  // for inspection only
     st_coh(&a.hhat[(size_t)p * a.m + j0 + tid], s_h[tid]);
     st_coh(&a.score[(size_t)p * a.m + j0 + tid], s_sc[tid]);
   }
@@ -258,10 +293,10 @@ __device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, 
                                               float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
                                               float* s_zp) {
   const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
-  const int groups = m / kGroup;
+  const int zg = m / a.score_ch;
   uint64_t* slots = a.xscore + ((size_t)p * a.ncs + c) * m;
-  const int nzp = with_zpart ? groups * r : 0;
-  float* zslots = a.zpart + (size_t)p * groups * r;
+  const int nzp = with_zpart ? zg * r : 0;
+  float* zslots = a.zpart + (size_t)p * zg * r;
   block_topk_prezero(sm.hist, sm.tmp);  // ordered before the select by the polling barrier
   uint64_t v[kMaxKeysPer];
   float zv[kMaxZPart];
@@ -347,18 +382,16 @@ template <bool DENSE, int SLOTS>
 __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
   constexpr int kMaxChunk = DENSE ? kMaxChunkDense : kMaxChunkSparse;
   const int C = a.chunk;
-  const int d = a.d, m = a.m, r = a.r;
+  const int d = a.d, m = a.m;
   const int p = bid / a.nc, c = bid % a.nc;
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int groups = m / kGroup;
   const int nslots = d / 8;  // 16-byte pieces of a hidden vector
   float* s_hh = (float*)dyn;                            // m
   uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
   int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m: the selection, ascending
   unsigned char* s_take = dyn + 12 * (size_t)m;         // m
-  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // groups * r (chunk 0)
-  float* s_zr = s_zp + groups * (r > 0 ? r : 1);        // kThreads x 8 (chunk 0)
+  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zpart rows: the z block's only
 
   float xv[SLOTS][8];
   const uint16_t* xrow = a.x + (size_t)t * d;
@@ -477,13 +510,13 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
   const int d = a.d, m = a.m, r = a.r;
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x;
-  const int groups = m / kGroup;
+  const int zg = m / a.score_ch;                        // zpart rows: one per score block
   float* s_hh = (float*)dyn;                            // m
   uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
   int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m
   unsigned char* s_take = dyn + 12 * (size_t)m;         // m
-  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // groups * r
-  float* s_zr = s_zp + groups * r;                      // kThreads x 8, then r
+  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zg * r
+  float* s_zr = s_zp + zg * r;                          // kThreads x 8, then r
   route(a, t, sm);
   gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int e = sm.ids[slot];
@@ -494,7 +527,7 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
   for (int q = 0; q < 8; ++q) zacc[q] = 0.0f;
   const int cgs = r >> 3, cg = tid % cgs, row = tid / cgs, rows_per_pass = kThreads / cgs;
   const uint16_t* Q = a.qmat + (size_t)e * m * r + 8 * cg;
-  for (int i0 = 0; i0 < count || i0 < groups; i0 += rows_per_pass * kZPass) {
+  for (int i0 = 0; i0 < count || i0 < zg; i0 += rows_per_pass * kZPass) {
     uint4 qv[kZPass];
 #pragma unroll
     for (int u = 0; u < kZPass; ++u) {
@@ -505,7 +538,7 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
     for (int u = 0; u < kZPass; ++u) {
       const int i = i0 + u * rows_per_pass + row;
       if (i < count) axpy8_bf16(-s_hh[s_sel[i]], qv[u], zacc);
-      if (i < groups)
+      if (i < zg)
 #pragma unroll
         for (int q = 0; q < 8; ++q) zacc[q] += s_zp[i * r + 8 * cg + q];
     }
@@ -644,7 +677,8 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   int bid = blockIdx.x;
   if (!DENSE) {
     if (bid < a.n_score) {
-      score_role<SLOTS>(a, bid, sm, s_dyn);
+      if (a.score_ch == kFusedScoreChMin) score_role<SLOTS, kFusedScoreChMin>(a, bid, sm, s_dyn);
+      else score_role<SLOTS, 2 * kFusedScoreChMin>(a, bid, sm, s_dyn);
       return;
     }
     bid -= a.n_score;
@@ -668,14 +702,16 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
 
 bool fused_supported(int d, int m, int r, int top_e) {
   return d <= 4096 && m <= kMaxKeysPer * kThreads && top_e * r <= 256 && top_e <= 64 &&
-         (m / kGroup) * r <= kMaxZPart * kThreads && (r == 0 || (kThreads % r == 0 && r % 8 == 0));
+         (m / (2 * kFusedScoreChMin)) * r <= kMaxZPart * kThreads && (r == 0 || (kThreads % r == 0 && r % 8 == 0));
 }
 
 int fused_max_chunk(bool dense) { return dense ? kMaxChunkDense : kMaxChunkSparse; }
 
+bool fused_narrow_score_ok(int m, int r) { return (m / kFusedScoreChMin) * r <= kMaxZPart * kThreads; }
+
 size_t fused_lds_bytes(int d, int m, int r) {
   const size_t score = (size_t)d + 128 * (size_t)r + 512 + 1024;
-  const size_t gather = 13 * (size_t)m + 4 * (size_t)(m / kGroup) * (size_t)std::max(r, 1) + (size_t)kThreads * 8 * 4 +
+  const size_t gather = 13 * (size_t)m + 4 * (size_t)(m / kFusedScoreChMin) * (size_t)std::max(r, 1) + (size_t)kThreads * 8 * 4 +
                         4 * (size_t)std::max(r, 1);
   const size_t combine = (size_t)kThreads * 8 * 4 + 256 * 4 + 8 * 32 * 4;
   return std::max(score, std::max(gather, combine));

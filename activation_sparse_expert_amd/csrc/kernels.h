@@ -86,7 +86,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 struct FusedArgs : FwdArgs {
   // hand-off slots, each with one consumer, empty = 0xFFFFFFFF
   uint64_t* xscore;  // [P][ncs][m]       (score, h_hat) for gather block (pair, c) / the z block
-  float* zpart;      // [P][m/64][r]      per-group share of Q^T h_hat, for the z block
+  float* zpart;      // [P][m/score_ch][r] each score block's share of Q^T h_hat, for the z block
   float* partial;    // [B][d/64][top_e*nc][64] gate-weighted down partials, for combine
   float* zcopy;      // [B][d/32][top_e][r] z of each routed pair, for each combine block
   int* err;          // error bits (1: gather wait timed out, 2: combine wait timed out)
@@ -94,10 +94,13 @@ struct FusedArgs : FwdArgs {
   int nc;            // gather blocks per pair
   int ncs;           // consumer slots per pair: the gather blocks, then the z block (if any)
   int chunk;         // channels per gather block
+  int score_ch;      // channels per score block: 32, or 64 when the grid of 32 would not fit
 };
 
+constexpr int kFusedScoreChMin = 32;  // fewest channels per score block of the single-launch kernel
 bool fused_supported(int d, int m, int r, int top_e);
 int fused_max_chunk(bool dense);
+bool fused_narrow_score_ok(int m, int r);  // kFusedScoreChMin-channel score blocks fit the z block's slots
 size_t fused_lds_bytes(int d, int m, int r);
 int fused_blocks_per_cu(bool dense, int d, int m, int r);
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream);

@@ -430,7 +430,7 @@ __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int
   const int tid = threadIdx.x;
   if (tid < n_experts) {
     const float v = logits[tid];
-    s_key[tid] = order_key(float_order_bits(v), tid);
+    s_key[tid] = order_key(logit_order_bits(v), tid);
     s_val[tid] = v;
   }
   __syncthreads();
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     }
   }
   __syncthreads();  // x_q and the Q rows in LDS
-  int acc = 0;
+  CodeAcc acc;
   for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
     if (c0 != b0) {
 #pragma unroll
@@ -584,14 +584,14 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     for (int i = 0; i < kSB1Blk; ++i) {
       if (c0 + i < b1) {
         const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
-        acc = dot_codes16(cb[i].x, xb[0], acc);
-        acc = dot_codes16(cb[i].y, xb[1], acc);
-        acc = dot_codes16(cb[i].z, xb[2], acc);
-        acc = dot_codes16(cb[i].w, xb[3], acc);
+        dot_codes16(cb[i].x, xb[0], acc);
+        dot_codes16(cb[i].y, xb[1], acc);
+        dot_codes16(cb[i].z, xb[2], acc);
+        dot_codes16(cb[i].w, xb[3], acc);
       }
     }
   }
-  s_part[wave][lane] = acc;  // sum of (t + 1) x_q over the quarter
+  s_part[wave][lane] = code_acc_total(acc);  // sum of (t + 1) x_q over the quarter
   __syncthreads();
   if (wave == 0) {
     const int dg = s_part[0][lane] + s_part[2][lane] + s_part[4][lane] + s_part[6][lane];

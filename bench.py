@@ -16,7 +16,10 @@ sketch or map byte is reused within copies*tokens calls (over 1 GB of traffic,
 several times the 256 MB last-level cache). The sequence of forwards is captured
 once in a HIP graph and replayed; the timed region is bracketed by
 torch.cuda.synchronize() and HIP events recorded on the launch stream.
-`--eager` launches every forward directly instead (for profilers).
+`--eager` launches every forward directly instead (for profilers). The batch-1
+figure is also given as its spread over the graph replays (p10 / median / p90
+per forward) and as single-call latency: one forward launched on its own,
+event-timed and synchronised, over 200 calls (sparse and dense).
 
 Prints ONE JSON line. Only one GPU is supported (`--gpus 1`).
 """
@@ -132,8 +135,10 @@ class Block:
             self.b.moe_sel_destroy(c)
 
 
-def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None, top_e=None):
-    """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones."""
+def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None, top_e=None, spread=None):
+    """Milliseconds per forward over `steps` timed forwards after `warmup` untimed ones.
+    With a dict `spread` (graph timing only), also fills the p10 / median / p90 of
+    the per-forward time of each graph replay, in microseconds."""
     R = blk.copies * blk.ntok
     stream = blk.stream
     with torch.cuda.stream(stream):
@@ -165,17 +170,58 @@ def time_block(torch, blk, k, steps, warmup, eager, bsz, thr=None, top_e=None):
             for _ in range(max(1, math.ceil(warmup / R))):
                 g.replay()
         torch.cuda.synchronize()
+        n_rep = steps // R
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)] if spread is not None else None
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            for _ in range(steps // R):
+            if evs:
+                evs[0].record(stream)
+            for i in range(n_rep):
                 g.replay()
+                if evs:
+                    evs[i + 1].record(stream)
             if g_rem is not None:
                 g_rem.replay()
             ev1.record(stream)
         torch.cuda.synchronize()
+        if evs and n_rep:
+            per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 / R for i in range(n_rep)])
+            spread.update({"replays": n_rep, "forwards_per_replay": R, "p10_us": round(float(np.percentile(per, 10)), 3),
+                           "median_us": round(float(np.median(per)), 3),
+                           "p90_us": round(float(np.percentile(per, 90)), 3)})
     for c in blk.ctxs:
         blk.b.moe_sel_check_device(c)  # raises if a bounded wait gave up
     return ev0.elapsed_time(ev1) / steps
+
+
+def single_call_latency(torch, blk, k, bsz, n=200, warmup=20):
+    """Latency of one forward launched on its own (eager launch, event-timed,
+    synchronised after each call), in microseconds: p10 / median / p90 over n calls."""
+    stream = blk.stream
+    with torch.cuda.stream(stream):
+        blk.launch(warmup, k, bsz)
+    torch.cuda.synchronize()
+    R = blk.copies * blk.ntok
+    xs, lgs, outs = blk.inputs[bsz]
+    te = blk.w["top_e"]
+    b, s = blk.b, stream.cuda_stream
+    times = []
+    for i in range(n):
+        l, t = i % blk.copies, (i // blk.copies) % blk.ntok
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            if k is None:
+                b.moe_sel_forward_dense(blk.ctxs[l], xs[l][t], lgs[l][t], bsz, te, outs[l], s)
+            else:
+                b.moe_sel_forward(blk.ctxs[l], xs[l][t], lgs[l][t], bsz, te, k, outs[l], s)
+            ev1.record(stream)
+        ev1.synchronize()
+        times.append(ev0.elapsed_time(ev1) * 1e3)
+    del R
+    times = np.array(times)
+    return {"calls": n, "p10_us": round(float(np.percentile(times, 10)), 3), "median_us": round(float(np.median(times)), 3),
+            "p90_us": round(float(np.percentile(times, 90)), 3)}
 
 
 def copy_ceiling(torch, stream, nbytes=1 << 30, reps=8):
@@ -252,8 +298,12 @@ def main():
     blk = Block(b, synth, torch, w, args.copies, args.tokens, stream, args.big_batch)
     setup_s = time.time() - t0
 
-    ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager, batch)
+    spread = {}
+    ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager, batch, spread=spread)
     path = b.moe_sel_last_path(blk.ctxs[0])
+    single_call = {"sparse": single_call_latency(torch, blk, k, batch)}
+    if not args.no_dense:
+        single_call["dense"] = single_call_latency(torch, blk, None, batch)
     single = path == b.MOE_SEL_PATH_SINGLE_LAUNCH
     extra_k = {}
     if not args.no_extra_budgets:
@@ -329,6 +379,9 @@ def main():
         },
         "setup_s": round(setup_s, 1),
     }
+    if spread:
+        result["graph_replay_spread"] = spread
+    result["single_call"] = single_call
     if extra_k:
         result["other_budgets"] = extra_k
     if big is not None:

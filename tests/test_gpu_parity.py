@@ -88,6 +88,30 @@ def test_device_layout_round_trip(b, tiny):
         assert np.array_equal(dev["down_norm"].view(np.uint32), prep["c"].view(np.uint32))
 
 
+def test_routing_ties_and_signed_zeros(b, torch, tiny):
+    """Equal logits go to the lower expert index, and -0 equals +0 (so a -0 at a
+    lower index comes first); each row also runs alone (batch 1)."""
+    k = synth.WORKLOADS["tiny"]["ks"][0]
+    E = tiny.E
+    rows = np.full((4, E), -1.0, np.float32)
+    rows[0, :] = np.where(np.arange(E) % 2 == 0, -0.0, 0.0)          # all zero, mixed signs
+    rows[1, [5, 2, 7]] = 1.5                                          # a three-way tie
+    rows[2, 1], rows[2, 3] = -0.0, 0.0                                # -0 before +0
+    rows[3, 3], rows[3, 1] = 0.0, -0.0
+    rows[3, 6] = 2.0
+    x = synth.tokens(0, 0, 4, tiny.d)
+    for lg, xx in [(rows, x)] + [(rows[i:i + 1], x[i:i + 1]) for i in range(4)]:
+        bsz = lg.shape[0]
+        out = _run(b, torch, tiny, xx, lg, k)
+        ref = tiny.oracle.forward(xx, lg, tiny.top_e, k)
+        _check_selection(b, tiny, ref, bsz, tiny.top_e, k)
+        err = rel_err(out_to_f64(torch, out), ref["y"])
+        assert err <= TOL, err
+    ids = tiny.oracle.forward(x, rows, tiny.top_e, k)["expert_ids"]
+    assert ids[0].tolist() == [0, 1] and ids[1].tolist() == [2, 5] and ids[2].tolist() == [1, 3]
+    assert ids[3].tolist() == [6, 1]
+
+
 def test_tiny_workload_parity(b, torch, tiny):
     k = synth.WORKLOADS["tiny"]["ks"][0]
     x = synth.tokens(0, 0, 1, tiny.d)
