@@ -584,7 +584,7 @@ __device__ __forceinline__ void block_topk_radix(const uint32_t (&key)[KPT], int
 // by pairwise comparison in the order (larger key first, lower index first). A
 // bucket of more than kThreads keys falls back to the three-pass threshold.
 // Returns per-key ascending output ranks in sel[] (-1 if not selected) and the
-// count. 1 <= k < m. s_hist: 2048 ints; s_cand: 2 * kThreads ints; s_take: m
+// count. 1 <= k < m. s_hist: 2048 ints; s_cand: 2 * kThreads ints, 8-byte aligned; s_take: m
 // bytes; s_tmp: kWaves + 2 ints. Barriers inside (all threads call).
 // Callers that pass PREZEROED have cleared s_hist and s_tmp[kWaves + 1] and
 // passed a block barrier since.
@@ -630,25 +630,28 @@ __device__ __forceinline__ int block_topk_select_strided(const uint32_t (&key)[K
   const int ncand = s_hist[2];
   bool take[KPT];
   if (ncand <= kThreads) {
-    int* ckey = s_cand;
-    int* cidx = s_cand + kThreads;
+    uint64_t* ck = (uint64_t*)s_cand;  // order keys of the bucket's keys
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int j = tid * per + u;
       if (u < per && j < m && (key[u] >> 20) == D) {
         const int slot = atomicAdd(&s_tmp[kWaves + 1], 1);
-        ckey[slot] = (int)key[u];
-        cidx[slot] = j;
+        ck[slot] = order_key(key[u], j);
       }
     }
     __syncthreads();
-    if (tid < ncand) {
-      const int ic = cidx[tid];
-      const uint64_t kc = order_key((uint32_t)ckey[tid], ic);
+    // nt consecutive threads per candidate, each counting larger keys among every
+    // nt-th candidate; the index comes back out of the order key
+    const int nt = ncand <= kThreads / 4 ? 4 : (ncand <= kThreads / 2 ? 2 : 1);
+    const int ci = tid / nt, part = tid % nt;
+    if (ci < ncand) {
+      const uint64_t kc = ck[ci];
       int rank = 0;
 #pragma unroll 8
-      for (int o = 0; o < ncand; ++o) rank += order_key((uint32_t)ckey[o], cidx[o]) > kc;
-      s_take[ic] = rank < krem;
+      for (int o = part; o < ncand; o += nt) rank += ck[o] > kc;
+      if (nt >= 2) rank += __shfl_xor(rank, 1, 64);
+      if (nt >= 4) rank += __shfl_xor(rank, 2, 64);
+      if (part == 0) s_take[0xFFFFFFFFu - (uint32_t)kc] = rank < krem;
     }
     __syncthreads();
 #pragma unroll

@@ -1434,47 +1434,54 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     }
 }
 
-// ===========================================================================
-// Gate-weighted sum over a token's experts, bf16 output.
-// ===========================================================================
+// Per token and 64 outputs (one block): the four waves take contiguous quarters
+// of the token's (pair, split) partials, each thread loading its quarter's
+// values of one output, up to N in flight, and adding them gate-weighted; the
+// quarters are then added in wave order and the sum is written as bf16. Spread
+// over d / 64 blocks per token, the partials stream through many CUs at once.
 __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
-  constexpr int N = 32;  // partial values in flight per thread
-  const int per_tok = (a.d + kThreads - 1) / kThreads;
-  const int t = blockIdx.x / per_tok, blk = blockIdx.x % per_tok;
-  const int i = blk * kThreads + threadIdx.x;
-  if (i >= a.d) return;
+  constexpr int N = 16;  // partial values in flight per thread
+  __shared__ float s_y[kWaves][64];
+  const int per_tok = a.d / 64;
+  const int t = blockIdx.x / per_tok;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = (blockIdx.x % per_tok) * 64 + lane;
   const size_t kstride = (size_t)a.batch * a.top_e * a.d;
   const float* base = a.ypart + (size_t)t * a.top_e * a.d + i;
-  // the token's partials v = s kc + q (pair s, split q) in batches of N; each
-  // pair's splits are summed in order, then weighted
+  const float* w = a.pair_w + (size_t)t * a.top_e;
   const int total = a.top_e * kc;
-  float y = 0.0f, ps = 0.0f;
-  int s = 0, q = 0;  // pair and split of the next value to add
-  for (int v0 = 0; v0 < total; v0 += N) {
+  const int v_lo = total * wave / kWaves, v_hi = total * (wave + 1) / kWaves;
+  float y = 0.0f;
+  for (int v0 = v_lo; v0 < v_hi; v0 += N) {
     float part[N];
-    int ls = v0 / kc, lq = v0 % kc;
+    int ls = v0 / kc, lq = v0 % kc;  // pair and split of value v0
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      part[u] = v0 + u < total ? base[(size_t)lq * kstride + (size_t)ls * a.d] : 0.0f;
+      part[u] = v0 + u < v_hi ? base[(size_t)lq * kstride + (size_t)ls * a.d] : 0.0f;
       if (++lq == kc) {
         lq = 0;
         ++ls;
       }
     }
+    ls = v0 / kc;
+    lq = v0 % kc;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      if (v0 + u < total) {
-        ps += part[u];
-        if (++q == kc) {
-          y += a.pair_w[t * a.top_e + s] * ps;
-          ps = 0.0f;
-          q = 0;
-          ++s;
-        }
+      if (v0 + u < v_hi) y += w[ls] * part[u];
+      if (++lq == kc) {
+        lq = 0;
+        ++ls;
       }
     }
   }
-  a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(y);
+  s_y[wave][lane] = y;
+  __syncthreads();
+  if (wave == 0) {
+    float o = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kWaves; ++g) o += s_y[g][lane];
+    a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(o);
+  }
 }
 
 }  // namespace
@@ -1556,8 +1563,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     else
       hipLaunchKernelGGL(k_down_b1<1>, dim3(a.max_tiles * (a.d / 512) * kc1), dim3(kB1Threads), 0, stream, a,
                          dense ? 1 : 0, kc1, rpb);
-    const int per_tok1 = (a.d + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok1), dim3(kThreads), 0, stream, a, kc1);
+    hipLaunchKernelGGL(k_combine, dim3(a.batch * (a.d / 64)), dim3(kThreads), 0, stream, a, kc1);
     return hipGetLastError();
   }
   const int kc = grouped_down_split(a.max_tiles, a.d, kmax, dense ? 0 : a.r);
@@ -1565,8 +1571,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
   else
     hipLaunchKernelGGL(k_down_g<1>, dim3(a.max_tiles * (a.d / 64) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
-  const int per_tok = (a.d + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(k_combine, dim3(a.batch * per_tok), dim3(kThreads), 0, stream, a, kc);
+  hipLaunchKernelGGL(k_combine, dim3(a.batch * (a.d / 64)), dim3(kThreads), 0, stream, a, kc);
   return hipGetLastError();
 }
 
