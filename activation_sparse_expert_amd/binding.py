@@ -30,7 +30,7 @@ EXPORTED = (
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
-MOE_SEL_SCORE_FULL, MOE_SEL_SCORE_GATE_ONLY, MOE_SEL_SCORE_NO_DOWN_NORM = range(3)
+MOE_SEL_SCORE_FULL, MOE_SEL_SCORE_GATE_ONLY, MOE_SEL_SCORE_NO_DOWN_NORM, MOE_SEL_SCORE_X_INT16 = range(4)
 
 
 class moe_sel_config(ctypes.Structure):

@@ -73,6 +73,9 @@ struct moe_sel_ctx {
 namespace {
 
 constexpr int kFusedMaxBatch = 8;   // single-launch path: up to this many tokens
+constexpr const char* kUnsupportedCall =
+    "this call cannot run on the chosen path (a forced single launch that does not fit, or int16 score "
+    "activations on a multi-kernel call whose score blocks do not route themselves)";
 constexpr int kMinChunk = 8;        // fewest channels per gather block
 constexpr int kTargetGather = 512;  // aim for about this many gather blocks
 
@@ -236,7 +239,8 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
 
 // The single-launch path when its blocks all fit on the device at once, else
 // the one-kernel-per-phase path.
-// Returns hipErrorNotSupported when the single-launch path is required but cannot be used.
+// Returns hipErrorNotSupported when the single-launch path is required but cannot be used, or when the
+// multi-kernel path cannot run the call (int16 score activations without self-routing score blocks).
 hipError_t launch_any(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, hipStream_t stream) {
   const int pairs = base.batch * base.top_e;
   const bool want_fused = c->path != MOE_SEL_PATH_MULTI_KERNEL && !force_multi_kernel();
@@ -753,7 +757,7 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
   DeviceGuard guard(ctx->device);
   const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, k_budget, out);
   const hipError_t e = launch_any(ctx, a, false, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, "single-launch path cannot run this call");
+  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, kUnsupportedCall);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   ctx->last_batch = batch;
   ctx->last_top_e = top_e;
@@ -791,7 +795,7 @@ moe_sel_status moe_sel_forward_dense(moe_sel_ctx* ctx, const uint16_t* x, const 
   DeviceGuard guard(ctx->device);
   const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, ctx->cfg.m, out);
   const hipError_t e = launch_any(ctx, a, true, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, "single-launch path cannot run this call");
+  if (e == hipErrorNotSupported) return fail(MOE_SEL_EUNSUPPORTED, kUnsupportedCall);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return MOE_SEL_OK;
 }
@@ -902,7 +906,8 @@ int32_t moe_sel_last_path(const moe_sel_ctx* ctx) { return ctx ? ctx->last_path 
 moe_sel_status moe_sel_set_score(moe_sel_ctx* ctx, moe_sel_score kind) {
   g_last_error.clear();
   if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
-  if (kind != MOE_SEL_SCORE_FULL && kind != MOE_SEL_SCORE_GATE_ONLY && kind != MOE_SEL_SCORE_NO_DOWN_NORM)
+  if (kind != MOE_SEL_SCORE_FULL && kind != MOE_SEL_SCORE_GATE_ONLY && kind != MOE_SEL_SCORE_NO_DOWN_NORM &&
+      kind != MOE_SEL_SCORE_X_INT16)
     return fail(MOE_SEL_EINVAL, "unknown score kind");
   ctx->score_kind = kind;
   return MOE_SEL_OK;

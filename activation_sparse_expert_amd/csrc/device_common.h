@@ -57,6 +57,7 @@ __device__ __forceinline__ void pinned_score(int dg, int du, int xexp, float4 st
   const float u = __builtin_ldexpf(st.y * (float)du, xexp);
   const float sg = silu_pinned(g);
   h = sg * u;
+  // kind 3 (int16 activations) ranks by the full score
   score = kind == 1 ? __builtin_fabsf(sg) * st.z : (kind == 2 ? __builtin_fabsf(h) : __builtin_fabsf(h) * st.z);
 }
 
@@ -199,6 +200,27 @@ __device__ __forceinline__ void dot_codes16(uint32_t cw, int4 x, CodeAcc& a) {
 
 // s4 and s16 are exact multiples of 4 and 16, so the shifts divide exactly
 __device__ __forceinline__ int code_acc_total(const CodeAcc& a) { return a.s1 + (a.s4 >> 2) + (a.s16 >> 4); }
+
+// The same with four unsigned activation bytes per dword (the low bytes of
+// int16 activations): codes and bytes both unsigned, sums below 2^31.
+__device__ __forceinline__ void dot_codes16_u(uint32_t cw, int4 x, CodeAcc& a) {
+  a.s1 = (int)__builtin_amdgcn_udot4(cw & 0x03030303u, (uint32_t)x.x, (uint32_t)a.s1, false);
+  a.s4 = (int)__builtin_amdgcn_udot4(cw & 0x0C0C0C0Cu, (uint32_t)x.y, (uint32_t)a.s4, false);
+  a.s16 = (int)__builtin_amdgcn_udot4(cw & 0x30303030u, (uint32_t)x.z, (uint32_t)a.s16, false);
+  a.s16 = (int)__builtin_amdgcn_udot4((cw >> 2) & 0x30303030u, (uint32_t)x.w, (uint32_t)a.s16, false);
+}
+
+// Score activations: int8 (the method) or int16 (an ablation of the score),
+// q = rint(x * 2^-e) with the smallest e that keeps max|q| <= 2^(bits-1) - 1.
+// amax_bits: the largest |x| as bf16 bits (non-zero).
+__device__ __forceinline__ int score_exponent(uint32_t amax_bits, bool x16) {
+  const float av = __uint_as_float(amax_bits << 16);
+  int ex;
+  (void)__builtin_frexpf(av, &ex);  // av = f * 2^ex, f in [0.5, 1)
+  int e = x16 ? ex - 15 : ex - 7;
+  if (__builtin_ldexpf(av, -e) > (x16 ? 32767.0f : 127.0f)) e += 1;
+  return e;
+}
 
 // exclusive count of `flag` over the block in thread order; *total = block count.
 // Uses s_tmp[kWaves]; contains barriers (all threads must call).

@@ -106,11 +106,13 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int d, uint4 (&xv)[SLO
   }
 }
 
-// int8 activations with a power-of-two scale into LDS; returns the exponent.
-// Each wave's sums of x_q over the four quarters of d (64-element blocks
+// int8 activations with a power-of-two scale into LDS (xq[0, d)); returns the
+// exponent. With x16 the activations are int16, stored as their high bytes in
+// xq[0, d) and their low bytes in xq[d, 2d). Each wave's sums of the
+// activations over the four quarters of d (64-element blocks
 // [nb q / 4, nb (q + 1) / 4)) go to sm.qsum (read them after the next barrier).
 template <int SLOTS>
-__device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, int8_t* xq, Smem& sm) {
+__device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, int8_t* xq, Smem& sm, bool x16) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nslots = d / 8;
   uint32_t amax = 0;
@@ -125,14 +127,7 @@ __device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, 
   __syncthreads();
   amax = sm.amax[0];
   for (int w = 1; w < kWaves; ++w) amax = max(amax, sm.amax[w]);
-  int e_t = 0;
-  if (amax != 0) {
-    const float av = __uint_as_float(amax << 16);
-    int ex;
-    (void)__builtin_frexpf(av, &ex);  // av = f * 2^ex, f in [0.5, 1)
-    e_t = ex - 7;
-    if (__builtin_ldexpf(av, -e_t) > 127.0f) e_t += 1;
-  }
+  const int e_t = amax ? score_exponent(amax, x16) : 0;
   int qs[4] = {0, 0, 0, 0};
   const int nb = nslots >> 3;
 #pragma unroll
@@ -141,17 +136,20 @@ __device__ __forceinline__ int quantise_to_lds(const uint4 (&xv)[SLOTS], int d, 
     if (s < nslots) {
       float f[8];
       unpack8(xv[u], f);
-      uint32_t lo = 0, hi = 0;
+      uint32_t lo = 0, hi = 0, lo2 = 0, hi2 = 0;  // bytes 0..3 and 4..7: high (or only) bytes, then low bytes
       int sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int a = (int)__builtin_rintf(__builtin_ldexpf(f[q], -e_t));
         const int b = (int)__builtin_rintf(__builtin_ldexpf(f[q + 4], -e_t));
-        lo |= ((uint32_t)a & 0xFFu) << (8 * q);
-        hi |= ((uint32_t)b & 0xFFu) << (8 * q);
+        lo |= ((uint32_t)(x16 ? a >> 8 : a) & 0xFFu) << (8 * q);
+        hi |= ((uint32_t)(x16 ? b >> 8 : b) & 0xFFu) << (8 * q);
+        lo2 |= ((uint32_t)a & 0xFFu) << (8 * q);
+        hi2 |= ((uint32_t)b & 0xFFu) << (8 * q);
         sum += a + b;
       }
       *(uint2*)(xq + 8 * s) = make_uint2(lo, hi);
+      if (x16) *(uint2*)(xq + d + 8 * s) = make_uint2(lo2, hi2);
       const int b = s >> 3;
       const int q = (b >= nb / 4) + (b >= nb * 2 / 4) + (b >= nb * 3 / 4);
 #pragma unroll
@@ -183,9 +181,10 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = a.r;
-  int8_t* s_xq = (int8_t*)dyn;                               // d bytes
-  uint16_t* s_q = (uint16_t*)(dyn + a.d);                    // SC x r bf16
-  float* s_h = (float*)(dyn + a.d + 64 * r * 2);             // SC
+  const bool x16 = a.score_kind == 3;                        // int16 activations (score ablation)
+  int8_t* s_xq = (int8_t*)dyn;                               // 2d bytes: x_q (int8), or high then low bytes
+  uint16_t* s_q = (uint16_t*)(dyn + 2 * a.d);                // SC x r bf16
+  float* s_h = (float*)(dyn + 2 * a.d + 64 * r * 2);         // SC
   float* s_sc = s_h + 64;                                    // SC
   int* s_part = (int*)(s_sc + 64);                           // kWaves x 64
 
@@ -217,7 +216,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   for (int u = 0; u < kQv; ++u)
     if (tid + u * kThreads < qpieces) qv[u] = qsrc[tid + u * kThreads];
   const float4 st = a.stats[(size_t)e * a.m + j0 + c];
-  const int e_t = quantise_to_lds<SLOTS>(xv, a.d, s_xq, sm);
+  const int e_t = quantise_to_lds<SLOTS>(xv, a.d, s_xq, sm, x16);
   __syncthreads();  // x_q in LDS
   // sum of x_q over this thread's part of d: quarters sum directly, halves are two quarters
   const int q0 = part * 4 / nparts, q1 = (part + 1) * 4 / nparts;
@@ -227,7 +226,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (q >= q0 && q < q1) qs += sm.qsum[w][q];
-  CodeAcc acc;
+  CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
   for (int c0 = b0; c0 < b1; c0 += kScoreBlk) {
     if (c0 != b0) {
 #pragma unroll
@@ -241,10 +240,18 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
         dot_codes16(cb[i].y, xb[1], acc);
         dot_codes16(cb[i].z, xb[2], acc);
         dot_codes16(cb[i].w, xb[3], acc);
+        if (x16) {
+          const int4* xl = (const int4*)(s_xq + a.d + 64 * (c0 + i));
+          dot_codes16_u(cb[i].x, xl[0], acc_lo);
+          dot_codes16_u(cb[i].y, xl[1], acc_lo);
+          dot_codes16_u(cb[i].z, xl[2], acc_lo);
+          dot_codes16_u(cb[i].w, xl[3], acc_lo);
+        }
       }
     }
   }
-  s_part[wave * 64 + lane] = code_acc_total(acc) - qs;  // sum (code - 1) * q = sum t * q
+  const int cx = x16 ? 256 * code_acc_total(acc) + code_acc_total(acc_lo) : code_acc_total(acc);
+  s_part[wave * 64 + lane] = cx - qs;  // sum (code - 1) * q = sum t * q
 #pragma unroll
   for (int u = 0; u < kQv; ++u) {
     const int i = tid + u * kThreads;
@@ -710,7 +717,7 @@ int fused_max_chunk(bool dense) { return dense ? kMaxChunkDense : kMaxChunkSpars
 bool fused_narrow_score_ok(int m, int r) { return (m / kFusedScoreChMin) * r <= kMaxZPart * kThreads; }
 
 size_t fused_lds_bytes(int d, int m, int r) {
-  const size_t score = (size_t)d + 128 * (size_t)r + 512 + 1024;
+  const size_t score = 2 * (size_t)d + 128 * (size_t)r + 512 + 1024;
   const size_t gather = 13 * (size_t)m + 4 * (size_t)(m / kFusedScoreChMin) * (size_t)std::max(r, 1) + (size_t)kThreads * 8 * 4 +
                         4 * (size_t)std::max(r, 1);
   const size_t combine = (size_t)kThreads * 8 * 4 + 256 * 4 + 8 * 32 * 4;

@@ -21,7 +21,7 @@ struct FwdArgs {
   const float* logits;     // [B][E]
   uint16_t* out;           // [B][d] bf16
   int batch, top_e, k;
-  int score_kind;          // 0 full score, 1 gate sketch only, 2 without the down-column norm
+  int score_kind;          // 0 full score, 1 gate sketch only, 2 without the down-column norm, 3 full on int16 x
   int thr_mode;            // 1: keep channels with score > thr_bits instead of the top k
   uint32_t thr_bits;       // binary32 bits of the (non-negative) threshold
   // workspace

@@ -455,7 +455,7 @@ __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int
 // the blocks of group 0 write their pair's routing and one-token tile for the
 // later kernels.
 __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_route) {
-  extern __shared__ float s_dyn_sb1[];  // x_q [d] bytes, then Q rows [64][r]
+  extern __shared__ float s_dyn_sb1[];  // x_q [2d] bytes (int8, or int16 high then low bytes), then Q rows [64][r]
   __shared__ int s_part[kB1Waves][64];
   __shared__ float s_h[64];
   __shared__ uint64_t s_rkey[256];
@@ -468,7 +468,8 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int npc = d / 8;
   int8_t* s_xq = (int8_t*)s_dyn_sb1;
-  float* s_q = s_dyn_sb1 + d / 4;
+  float* s_q = s_dyn_sb1 + d / 2;
+  const bool x16 = a.score_kind == 3;  // int16 activations (score ablation; self-routing calls only)
   int e, pp;
   uint4 xv = make_uint4(0, 0, 0, 0);
   if (self_route) {
@@ -520,25 +521,20 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     amax = (uint32_t)s_red[0][0];
 #pragma unroll
     for (int w = 1; w < kB1Waves; ++w) amax = max(amax, (uint32_t)s_red[0][w]);
-    xe = 0;
-    if (amax != 0) {
-      const float av = __uint_as_float(amax << 16);
-      int ex;
-      (void)__builtin_frexpf(av, &ex);  // av = f * 2^ex, f in [0.5, 1)
-      xe = ex - 7;
-      if (__builtin_ldexpf(av, -xe) > 127.0f) xe += 1;
-    }
+    xe = amax ? score_exponent(amax, x16) : 0;
     int qsum = 0;
     if (tid < npc) {
-      uint32_t packed[2] = {0u, 0u};
+      uint32_t packed[2] = {0u, 0u}, low[2] = {0u, 0u};
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
         const uint32_t bits = (w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
         const int qi = amax ? (int)__builtin_rintf(__builtin_ldexpf(__uint_as_float(bits << 16), -xe)) : 0;
         qsum += qi;
-        packed[h >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (h & 3));
+        packed[h >> 2] |= ((uint32_t)(x16 ? qi >> 8 : qi) & 0xFFu) << (8 * (h & 3));
+        low[h >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (h & 3));
       }
       *(uint2*)(s_xq + 8 * tid) = make_uint2(packed[0], packed[1]);
+      if (x16) *(uint2*)(s_xq + d + 8 * tid) = make_uint2(low[0], low[1]);
     }
     qsum = wave_sum_i(qsum);
     if (lane == 0) s_red[1][wave] = qsum;
@@ -574,7 +570,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     }
   }
   __syncthreads();  // x_q and the Q rows in LDS
-  CodeAcc acc;
+  CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
   for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
     if (c0 != b0) {
 #pragma unroll
@@ -588,10 +584,18 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
         dot_codes16(cb[i].y, xb[1], acc);
         dot_codes16(cb[i].z, xb[2], acc);
         dot_codes16(cb[i].w, xb[3], acc);
+        if (x16) {
+          const int4* xl = (const int4*)(s_xq + d + 64 * (c0 + i));
+          dot_codes16_u(cb[i].x, xl[0], acc_lo);
+          dot_codes16_u(cb[i].y, xl[1], acc_lo);
+          dot_codes16_u(cb[i].z, xl[2], acc_lo);
+          dot_codes16_u(cb[i].w, xl[3], acc_lo);
+        }
       }
     }
   }
-  s_part[wave][lane] = code_acc_total(acc);  // sum of (t + 1) x_q over the quarter
+  // sum of (t + 1) x_q over the quarter
+  s_part[wave][lane] = x16 ? 256 * code_acc_total(acc) + code_acc_total(acc_lo) : code_acc_total(acc);
   __syncthreads();
   if (wave == 0) {
     const int dg = s_part[0][lane] + s_part[2][lane] + s_part[4][lane] + s_part[6][lane];
@@ -1517,13 +1521,15 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const bool b1 = pair_tiles;
   // the score blocks route and quantise their tokens themselves
   const bool self_route = pair_tiles && !dense && a.n_experts <= 256;
+  // int16 score activations exist only where the score blocks quantise x themselves
+  if (!dense && a.score_kind == 3 && !self_route) return hipErrorNotSupported;
   const int groups = a.m / kGroup;
   if (!self_route)
     hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a, pair_tiles ? 1 : 0);
   if (!pair_tiles) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
     if (b1)
-      hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), (size_t)a.d + 256 * (size_t)a.r,
+      hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), 2 * (size_t)a.d + 256 * (size_t)a.r,
                          stream, a, self_route ? 1 : 0);
     else
       hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads),

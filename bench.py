@@ -490,7 +490,7 @@ def score_ablation(b, torch, blk, ks, n_tok=4):
     xs, lgs, _ = blk.inputs[1]
     top_e = w["top_e"]
     kinds = {"full": b.MOE_SEL_SCORE_FULL, "gate_only": b.MOE_SEL_SCORE_GATE_ONLY,
-             "no_down_norm": b.MOE_SEL_SCORE_NO_DOWN_NORM}
+             "no_down_norm": b.MOE_SEL_SCORE_NO_DOWN_NORM, "x_int16": b.MOE_SEL_SCORE_X_INT16}
 
     def run(k, kind=None):
         outs = []

@@ -72,7 +72,8 @@ typedef enum moe_sel_status {
 typedef enum moe_sel_score {
   MOE_SEL_SCORE_FULL = 0,          /* |silu(G) U| * ||down column|| (the default reading) */
   MOE_SEL_SCORE_GATE_ONLY = 1,     /* |silu(G)| * ||down column|| */
-  MOE_SEL_SCORE_NO_DOWN_NORM = 2   /* |silu(G) U| */
+  MOE_SEL_SCORE_NO_DOWN_NORM = 2,  /* |silu(G) U| */
+  MOE_SEL_SCORE_X_INT16 = 3        /* the full score, on int16 instead of int8 activations */
 } moe_sel_score;
 
 /* How a forward call is executed on the GPU (same selections either way; outputs
@@ -253,11 +254,18 @@ moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path);
  * MOE_SEL_SCORE_FULL). The pages leave the score open ("KAIST drops calibration
  * from MoE decoding...", section "A reader built from weights alone": channels
  * are filtered with a ternary sketch); the alternatives are ablations of the
- * default reading. Only the ranking changes: the sketch activations used by
- * the compensation are the same for all kinds.
+ * default reading. For the first three only the ranking changes: the sketch
+ * activations used by the compensation are the same for them.
  *   MOE_SEL_SCORE_FULL          |silu(G) * U| * ||W_down[:, j]||_2
  *   MOE_SEL_SCORE_GATE_ONLY     |silu(G)| * ||W_down[:, j]||_2 (up sketch ignored)
  *   MOE_SEL_SCORE_NO_DOWN_NORM  |silu(G) * U|
+ *   MOE_SEL_SCORE_X_INT16       the full score with G and U from int16
+ *                               activations: q = rint(x 2^-e), max|q| <= 32767
+ *                               (h_hat changes with it). Runs on the single
+ *                               launch and on multi-kernel calls with one pair
+ *                               per tile whose score blocks route themselves
+ *                               (n_experts <= 256); other calls fail with
+ *                               EUNSUPPORTED.
  * Errors: EINVAL (null ctx or unknown kind).
  */
 moe_sel_status moe_sel_set_score(moe_sel_ctx* ctx, moe_sel_score kind);

@@ -175,21 +175,24 @@ def route(logits_row: np.ndarray, top_e: int):
     return ids.astype(np.int64), ex / ex.sum()
 
 
-def quantize_token(x_bits: np.ndarray):
-    """int8 activations with a power-of-two scale, used only inside the score.
+def quantize_token(x_bits: np.ndarray, bits: int = 8):
+    """Integer activations with a power-of-two scale, used only inside the score.
 
     Reading (pages silent on the precision of x in the score): with
-    a = max|x|, e = ilogb(a) - 6, raised by one if a * 2^-e > 127;
-    q = round-half-even(x * 2^-e). Then max|q| <= 127 and x ~= q * 2^e.
+    a = max|x| and qmax = 2^(bits-1) - 1, e = ilogb(a) - (bits - 2), raised by
+    one if a * 2^-e > qmax; q = round-half-even(x * 2^-e). Then max|q| <= qmax
+    and x ~= q * 2^e. bits = 8 is the method's score; bits = 16 is the int16
+    ablation of the score.
     Returns (q int64 [d], e int).
     """
+    qmax = float(2 ** (bits - 1) - 1)
     x = bf16_bits_to_f64(x_bits)
     a = float(np.max(np.abs(x))) if x.size else 0.0
     if a == 0.0:
         return np.zeros(x.shape, np.int64), 0
     _, ex = math.frexp(a)          # a = f * 2^ex, f in [0.5, 1)
-    e = (ex - 1) - 6
-    if a * 2.0 ** (-e) > 127.0:
+    e = (ex - 1) - (bits - 2)
+    if a * 2.0 ** (-e) > qmax:
         e += 1
     q = np.rint(x * 2.0 ** (-e)).astype(np.int64)
     return q, e
@@ -223,8 +226,9 @@ def silu_pinned(z) -> np.ndarray:
 def sketch_preacts(prep: dict, q: np.ndarray, e: int):
     """Sketch estimates of the gate and up pre-activations of every channel.
 
-    G_hat_j = binary32(alpha_g_j * (t_g[j] . q)) * 2^e, likewise U_hat_j; the
-    integer dot is exact (|t . q| <= 127 d < 2^24, so it is exact in binary32 too).
+    G_hat_j = binary32(alpha_g_j * binary32(t_g[j] . q)) * 2^e, likewise U_hat_j.
+    The integer dot is exact; its binary32 value is exact for int8 activations
+    (|t . q| <= 127 d < 2^24) and rounded to nearest even for int16 ones.
     """
     dg = prep["tern_g"].astype(np.int64) @ q
     du = prep["tern_u"].astype(np.int64) @ q
@@ -233,7 +237,7 @@ def sketch_preacts(prep: dict, q: np.ndarray, e: int):
     return g, u
 
 
-SCORE_KINDS = ("full", "gate_only", "no_down_norm")
+SCORE_KINDS = ("full", "gate_only", "no_down_norm", "x_int16")
 
 
 def score_channels(prep: dict, q: np.ndarray, e: int, kind: str = "full"):
@@ -247,12 +251,14 @@ def score_channels(prep: dict, q: np.ndarray, e: int, kind: str = "full"):
     h_hat = silu_pinned(G_hat) * U_hat; score = |h_hat| * ||down_j||_2.
     Ablations of the score (the pages leave it open; h_hat is unchanged):
     ``gate_only``: |silu_pinned(G_hat)| * ||down_j||_2; ``no_down_norm``: |h_hat|.
+    ``x_int16`` is the full score on int16 activations: the caller passes the
+    int16 q and e of quantize_token(x, 16).
     Returns (h_hat float32 [m], score float32 [m]).
     """
     g, u = sketch_preacts(prep, q, e)
     sg = silu_pinned(g)
     h = (sg * u).astype(F32)
-    if kind == "full":
+    if kind in ("full", "x_int16"):
         score = (np.abs(h) * prep["c"].astype(F32)).astype(F32)
     elif kind == "gate_only":
         score = (np.abs(sg) * prep["c"].astype(F32)).astype(F32)
@@ -349,7 +355,7 @@ class OracleLayer:
         sels, hs, scores = [], [], []
         for t in range(b):
             x = bf16_bits_to_f64(x_bits[t])
-            q, e_t = quantize_token(x_bits[t])
+            q, e_t = quantize_token(x_bits[t], 16 if score_kind == "x_int16" else 8)
             ids[t], gw[t] = route(logits[t], top_e)
             row_s, row_h, row_sc = [], [], []
             for slot, ex in enumerate(ids[t]):

@@ -553,3 +553,44 @@ def test_score_ablation_kinds_match_oracle(b, torch, tiny, kind):
         b.moe_sel_set_score(tiny.ctx, b.MOE_SEL_SCORE_FULL)
     with pytest.raises(b.MoeSelError):
         b.moe_sel_set_score(tiny.ctx, 7)
+
+
+def test_int16_activation_score_single_launch_and_unsupported_paths(b, torch, tiny):
+    """The int16-activation score ablation: bit-exact selections and scores on the
+    single launch; multi-kernel calls whose score blocks do not quantise x
+    themselves refuse it with EUNSUPPORTED."""
+    rng = np.random.default_rng(31)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, tiny.d)).astype(np.float32))
+    logits = rng.standard_normal((3, tiny.E)).astype(np.float32)
+    b.moe_sel_set_score(tiny.ctx, b.MOE_SEL_SCORE_X_INT16)
+    try:
+        if tiny.path == "single_launch":
+            out = _run(b, torch, tiny, x, logits, 92)
+            ref = tiny.oracle.forward(x, logits, tiny.top_e, 92, score_kind="x_int16")
+            _check_selection(b, tiny, ref, 3, tiny.top_e, 92)
+            assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+            ref8 = tiny.oracle.forward(x, logits, tiny.top_e, 92)
+            assert any(not np.array_equal(u, v) for u, v in zip(ref["h_hat"][0], ref8["h_hat"][0]))
+        else:
+            for bsz in (3, 1):
+                with pytest.raises(b.MoeSelError) as ei:
+                    _run(b, torch, tiny, x[:bsz], logits[:bsz], 92)
+                assert ei.value.status == b.MOE_SEL_EUNSUPPORTED
+    finally:
+        b.moe_sel_set_score(tiny.ctx, b.MOE_SEL_SCORE_FULL)
+
+
+def test_int16_activation_score_batch1_rows(b, torch, qwen):
+    """Batch-1 calls on both paths: the single launch and the multi-kernel path
+    with one pair per tile (its score blocks route and quantise x themselves)."""
+    w = synth.WORKLOADS["qwen3"]
+    x = synth.tokens(w["wid"], 0, 1, qwen.d, index=5)
+    logits = synth.router_logits(w["wid"], 0, 1, qwen.E, index=5)
+    b.moe_sel_set_score(qwen.ctx, b.MOE_SEL_SCORE_X_INT16)
+    try:
+        out = _run(b, torch, qwen, x, logits, 138)
+        ref = qwen.oracle.forward(x, logits, qwen.top_e, 138, score_kind="x_int16")
+        _check_selection(b, qwen, ref, 1, qwen.top_e, 138)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_set_score(qwen.ctx, b.MOE_SEL_SCORE_FULL)
