@@ -722,6 +722,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   SEL_FOR_KEYS(key[u] = keys[j];)
   if (tid < words) s_bits[tid] = k >= m ? 0xFFFFFFFFu : 0u;
   if (topk) *(int4*)(s_hist + 4 * tid) = make_int4(0, 0, 0, 0);
+  if (tid == 0) s_sc[3] = 0;  // candidate slots taken in the first pass
   __syncthreads();
   if (topk) {
     SEL_FOR_KEYS(atomicAdd(&s_hist[key[u] >> 19], 1);)
@@ -731,9 +732,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
     int cshift = 19;
     int krem = k - s_sc[1], ncand = s_sc[2];
     bool exact_key = false;
-    int nc = 0;  // this thread's candidates
+    bool placed = false;  // candidates already in s_hist (first pass)
+    int nc = 0;           // this thread's candidates
+    uint64_t* ck = (uint64_t*)s_hist;  // kSelCand order keys (the histogram is consumed)
+    int* cidx = s_hist + 2 * kSelCand;
     if (ncand <= kSelCand) {
-      SEL_FOR_KEYS(const uint32_t dg = key[u] >> 19; store_wave(s_bits, j - lane, dg > cval); nc += dg == cval;)
+      // keys above the boundary bin into the bitmap; the bin's keys take slots
+      // one by one (there are few) instead of from a block scan
+      SEL_FOR_KEYS(const uint32_t dg = key[u] >> 19; store_wave(s_bits, j - lane, dg > cval); if (dg == cval) {
+        const int slot = atomicAdd(&s_sc[3], 1);
+        ck[slot] = order_key(key[u], j);
+        cidx[slot] = j;
+      })
+      placed = true;
     } else {
       // ties or clusters: radix passes over the bits 31..20, 19..9 and 8..0 of the
       // key; after each pass keys in higher bins are taken and only the boundary
@@ -771,17 +782,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
       }
     }
     if (!exact_key) {
-      // the boundary bin's keys at scan positions, ranked exactly, four threads
-      // per candidate
-      uint64_t* ck = (uint64_t*)s_hist;  // kSelCand order keys
-      int* cidx = s_hist + 2 * kSelCand;
-      int ctot;
-      int slot = sel_excl_scan(nc, s_tmp, &ctot);
-      SEL_FOR_KEYS(if ((key[u] >> cshift) == cval) {
-        ck[slot] = order_key(key[u], j);
-        cidx[slot] = j;
-        ++slot;
-      })
+      // the boundary bin's keys (after the radix passes: at scan positions),
+      // ranked exactly, four threads per candidate
+      if (!placed) {
+        int ctot;
+        int slot = sel_excl_scan(nc, s_tmp, &ctot);
+        SEL_FOR_KEYS(if ((key[u] >> cshift) == cval) {
+          ck[slot] = order_key(key[u], j);
+          cidx[slot] = j;
+          ++slot;
+        })
+      }
       __syncthreads();
       const int c = tid >> 2, part = tid & 3;
       const bool live = c < ncand;
