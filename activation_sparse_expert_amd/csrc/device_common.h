@@ -241,118 +241,6 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* s_tmp, int* tota
   return before + below;
 }
 
-// ---------------------------------------------------------------------------
-// Routing of one token by a single wave: the top_e largest logits (lower
-// expert index first on equal logits), best first, and the softmax over them.
-// n_experts <= 1024, top_e <= 64. Results in s_ids / s_w (LDS), written by lane 0..top_e-1.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void wave_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w) {
-  const int lane = threadIdx.x & 63;
-  constexpr int kPer = 16;
-  float v[kPer];
-  bool live[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int idx = lane + 64 * u;
-    live[u] = idx < n_experts;
-    v[u] = live[u] ? logits[idx] : 0.0f;
-  }
-  float top = 0.0f, mine = 0.0f;
-  int mine_id = 0;
-  for (int s = 0; s < top_e; ++s) {
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (live[u] && (bi == 0x7FFFFFFF || v[u] > bv)) {
-        bv = v[u];
-        bi = lane + 64 * u;
-      }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (lane + 64 * u == bi) live[u] = false;
-    if (s == 0) top = bv;
-    if (lane == s) {
-      mine = bv;
-      mine_id = bi;
-    }
-  }
-  const float ex = lane < top_e ? __expf(mine - top) : 0.0f;
-  const float den = wave_sum(ex);
-  if (lane < top_e) {
-    s_ids[lane] = mine_id;
-    s_w[lane] = ex / den;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Top-k threshold over m non-negative binary32 scores held as bit patterns in
-// LDS (their integer order is their value order): four 8-bit most-significant
-// digit passes. Returns the k-th largest key T and krem = how many keys equal
-// to T are selected (the lowest-index ones). 1 <= k < m. All threads call.
-// s_hist[256], s_tmp[kWaves], s_misc[2] are LDS scratch.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void block_topk_threshold(const uint32_t* s_keys, int m, int k, int* s_hist, int* s_tmp,
-                                                     int* s_misc, uint32_t& T, int& krem_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t prefix = 0, pmask = 0;
-  int krem = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (int base = 0; base < m; base += kThreads) {
-      const int j = base + tid;
-      const uint32_t key = j < m ? s_keys[j] : 0u;
-      const bool act = j < m && (key & pmask) == prefix;
-      const int dg = (int)((key >> shift) & 255u);
-      if (pass == 0) {
-        // few distinct top digits: one LDS atomic per distinct digit per wave
-        uint64_t todo = __ballot(act);
-        while (todo) {
-          const int leader = __builtin_ctzll(todo);
-          const int ldg = __shfl(dg, leader, 64);
-          const uint64_t same = __ballot(act && dg == ldg);
-          if (lane == leader) atomicAdd(&s_hist[ldg], __popcll(same));
-          todo &= ~same;
-        }
-      } else if (act) {
-        atomicAdd(&s_hist[dg], 1);
-      }
-    }
-    __syncthreads();
-    // thread tid owns bin 255 - tid: an inclusive scan over threads is a suffix scan over bins
-    const int c = s_hist[255 - tid];
-    int incl = c;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_tmp[wave] = incl;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) incl += s_tmp[w];
-    if (incl - c < krem && krem <= incl) {
-      s_misc[0] = 255 - tid;
-      s_misc[1] = incl - c;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)s_misc[0] << shift;
-    pmask |= 255u << shift;
-    krem -= s_misc[1];
-    __syncthreads();
-  }
-  T = prefix;
-  krem_out = krem;
-}
-
 // Writes the selected channel indices (all keys > T, then the krem lowest-index
 // keys == T), ascending, to out[0..k). Returns k. All threads call.
 __device__ __forceinline__ int block_compact(const uint32_t* s_keys, int m, uint32_t T, int krem, int* out,
@@ -712,49 +600,16 @@ __device__ __forceinline__ int block_topk_select_strided(const uint32_t (&key)[K
   return sel_total;
 }
 
-// Ascending ranks of the selected keys (all keys > T, then the krem lowest-index
-// keys == T): sel[u] = rank of key u of this thread, or -1. Returns the count.
-template <int KPT>
-__device__ __forceinline__ int block_select_ranks(const uint32_t (&key)[KPT], int per, int m, uint32_t T, int krem,
-                                                  int* s_tmp, int (&sel)[KPT]) {
-  const int tid = threadIdx.x;
-  int n_eq = 0;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) n_eq += (u < per && tid * per + u < m && key[u] == T);
-  int eq_total;
-  int eq_before = block_excl_scan(n_eq, s_tmp, &eq_total);
-  int n_sel = 0;
-  bool take[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const bool valid = u < per && tid * per + u < m;
-    const bool eq = valid && key[u] == T;
-    take[u] = valid && (key[u] > T || (eq && eq_before < krem));
-    eq_before += eq;
-    n_sel += take[u];
-  }
-  int sel_total;
-  int r = block_excl_scan(n_sel, s_tmp, &sel_total);
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    sel[u] = take[u] ? r : -1;
-    r += take[u];
-  }
-  return sel_total;
-}
-
 // ---------------------------------------------------------------------------
 // Cross-workgroup hand-off without cache maintenance. Data that crosses
 // workgroups is written and read with device-coherent accesses (agent-scope
 // relaxed atomics: stores write through to the device coherence point, loads
 // read from it, on every XCD), so no L2 write-back or invalidate is needed.
-// Producer: coherent stores, wait_stores() (every wave waits until its stores
-// are acknowledged), barrier, then one coherent flag store per consumer.
-// Consumer: one wave polls its flags with coherent loads, the block syncs, then
-// reads the data with coherent loads; it clears the flags it consumed (each
-// flag has exactly one consumer, so every call starts from zeroed flags and
-// HIP-graph replays stay valid). Waits are bounded: on time-out an error bit is
-// set and the block proceeds.
+// The single-launch kernel polls the data itself: a slot holds an empty
+// sentinel until its producer's coherent store lands, its one consumer polls
+// it with coherent loads and writes the sentinel back, so every call and
+// every HIP-graph replay starts from empty slots. Waits are bounded by
+// kSpinLimit polls; on time-out an error bit is set and the block proceeds.
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 21;
 
@@ -770,34 +625,6 @@ __device__ __forceinline__ void st_coh2(float* p, float a, float b) {
 }
 __device__ __forceinline__ float ld_coh(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 ld_coh2(const float* p) {
-  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-// every outstanding vector memory access of this wave (loads and stores) done
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ void set_flag(int* flag) { st_coh(flag, 1); }
-
-// One wave polls n flags, then clears them. Returns false on time-out.
-__device__ __forceinline__ bool wave_wait_flags(int* flags, int n) {
-  const int lane = threadIdx.x & 63;
-  int spins = 0;
-  bool ok = true;
-  while (true) {
-    bool all = true;
-    for (int i = lane; i < n; i += 64)
-      all &= __hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    if (__all(all)) break;
-    if (++spins > kSpinLimit) {
-      ok = false;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  for (int i = lane; i < n; i += 64) st_coh(&flags[i], 0);
-  return ok;
 }
 
 }  // namespace dev
