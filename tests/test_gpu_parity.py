@@ -594,3 +594,37 @@ def test_int16_activation_score_batch1_rows(b, torch, qwen):
         assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
     finally:
         b.moe_sel_set_score(qwen.ctx, b.MOE_SEL_SCORE_FULL)
+
+
+@pytest.mark.parametrize("d", [64, 192])
+@pytest.mark.parametrize("path", PATHS)
+def test_small_and_uneven_hidden_sizes(b, torch, d, path):
+    """Hidden sizes below four 64-element blocks (some score-block quarters of d are
+    empty) and an odd block count, on both paths, batch 1 and 3."""
+    E, m, top_e, r, k = 4, 128, 2, 8, 24
+    wg, wu, wd = synth.layer_weights(0, 9, E, d, m)
+    cfg = b.make_config(d, E, m, r, top_e, 4)
+    ctx = b.moe_sel_prepare(cfg, wg, wu, wd)
+    try:
+        b.moe_sel_set_path(ctx, b.MOE_SEL_PATH_AUTO if path == "single_launch" else b.MOE_SEL_PATH_MULTI_KERNEL)
+        ref_layer = oracle.OracleLayer(lambda e: (wg[e], wu[e], wd[e]), E, d, m, r)
+        for bsz in (1, 3):
+            x = synth.tokens(0, 9, bsz, d, index=d)
+            logits = synth.router_logits(0, 9, bsz, E, index=d)
+            print(f"[run] d={d} path={path} B={bsz}", flush=True)
+            out = torch.zeros((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_forward(ctx, to_dev_u16(torch, x), to_dev_f32(torch, logits), bsz, top_e, k, out)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(ctx)
+            want = b.MOE_SEL_PATH_SINGLE_LAUNCH if path == "single_launch" else b.MOE_SEL_PATH_MULTI_KERNEL
+            assert b.moe_sel_last_path(ctx) == want
+            ref = ref_layer.forward(x, logits, top_e, k)
+            dbg = b.moe_sel_debug_selection(ctx, bsz, top_e, k, m, with_scores=True)
+            assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+            for t in range(bsz):
+                for s in range(top_e):
+                    assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (t, s)
+                    assert np.array_equal(dbg["score"][t, s].view(np.uint32), ref["score"][t][s].view(np.uint32))
+            assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_destroy(ctx)
