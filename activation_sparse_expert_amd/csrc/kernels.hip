@@ -99,58 +99,68 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a, int pair_ti
     xv[u] = pc < npc ? *(const uint4*)(x + 8 * pc) : make_uint4(0, 0, 0, 0);
   }
 
-  // top_e experts: repeated block arg-max, larger logit first, lower index on ties
+  // top_e experts, larger logit first, lower index on ties (-0 equal to +0): one
+  // wave's DPP rounds for few experts and picks, else repeated block arg-max
   const float* L = a.logits + (size_t)t * a.n_experts;
-  constexpr int kMaxPer = 4;  // n_experts <= 1024
-  float v[kMaxPer];
-  bool live[kMaxPer];
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int idx = tid + u * kThreads;
-    live[u] = idx < a.n_experts;
-    v[u] = live[u] ? L[idx] : 0.0f;
-  }
-  for (int s = 0; s < a.top_e; ++s) {
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+  if (a.top_e <= 16 && a.n_experts <= 256) {
+    if (wave == 0) {
+      if (a.n_experts <= 64) wave_topk_route<1>(L, a.n_experts, a.top_e, s_sel, s_selv);
+      else if (a.n_experts <= 128) wave_topk_route<2>(L, a.n_experts, a.top_e, s_sel, s_selv);
+      else wave_topk_route<4>(L, a.n_experts, a.top_e, s_sel, s_selv);
+    }
+    __syncthreads();
+  } else {
+    constexpr int kMaxPer = 4;  // n_experts <= 1024
+    float v[kMaxPer];
+    bool live[kMaxPer];
     for (int u = 0; u < kMaxPer; ++u) {
       const int idx = tid + u * kThreads;
-      if (live[u] && (bi == 0x7FFFFFFF || v[u] > bv)) {
-        bv = v[u];
-        bi = idx;
-      }
+      live[u] = idx < a.n_experts;
+      v[u] = live[u] ? L[idx] : 0.0f;
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-      if (take) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      s_v[wave] = bv;
-      s_i[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float fv = s_v[0];
-      int fi = s_i[0];
-      for (int w = 1; w < kWaves; ++w) {
-        const int oi = s_i[w];
-        const float ov = s_v[w];
-        if (oi != 0x7FFFFFFF && (fi == 0x7FFFFFFF || ov > fv || (ov == fv && oi < fi))) {
-          fv = ov;
-          fi = oi;
+    for (int s = 0; s < a.top_e; ++s) {
+      float bv = 0.0f;
+      int bi = 0x7FFFFFFF;
+      for (int u = 0; u < kMaxPer; ++u) {
+        const int idx = tid + u * kThreads;
+        if (live[u] && (bi == 0x7FFFFFFF || v[u] > bv)) {
+          bv = v[u];
+          bi = idx;
         }
       }
-      s_sel[s] = fi;
-      s_selv[s] = fv;
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+        if (take) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane == 0) {
+        s_v[wave] = bv;
+        s_i[wave] = bi;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float fv = s_v[0];
+        int fi = s_i[0];
+        for (int w = 1; w < kWaves; ++w) {
+          const int oi = s_i[w];
+          const float ov = s_v[w];
+          if (oi != 0x7FFFFFFF && (fi == 0x7FFFFFFF || ov > fv || (ov == fv && oi < fi))) {
+            fv = ov;
+            fi = oi;
+          }
+        }
+        s_sel[s] = fi;
+        s_selv[s] = fv;
+      }
+      __syncthreads();
+      const int chosen = s_sel[s];
+      for (int u = 0; u < kMaxPer; ++u)
+        if (tid + u * kThreads == chosen) live[u] = false;
     }
-    __syncthreads();
-    const int chosen = s_sel[s];
-    for (int u = 0; u < kMaxPer; ++u)
-      if (tid + u * kThreads == chosen) live[u] = false;
   }
   if (tid < a.top_e) {
     const float top = s_selv[0];
@@ -855,6 +865,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
 }
 #undef SEL_FOR_KEYS
 
+// 32 x 32 bit-matrix transpose in registers (Hacker's Delight, "Transposing a
+// bit matrix"): five rounds of masked swaps of 16-, 8-, 4-, 2- and 1-bit blocks.
+// Afterwards bit i of A[b] is what bit b of A[i] was.
+__device__ __forceinline__ void transpose32(uint32_t (&A)[32]) {
+  constexpr uint32_t kMask[5] = {0x55555555u, 0x33333333u, 0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
+#pragma unroll
+  for (int lj = 4; lj >= 0; --lj) {
+    const int j = 1 << lj;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int k = ((q >> lj) << (lj + 1)) | (q & (j - 1));  // rows with bit lj clear
+      const uint32_t t = ((A[k] >> j) ^ A[k | j]) & kMask[lj];
+      A[k] ^= t << j;
+      A[k | j] ^= t;
+    }
+  }
+}
+
 // ===========================================================================
 // Union of a tile's selections: ascending channel list and, per listed
 // channel, the mask of the tile's tokens that selected it. One block per tile.
@@ -904,16 +932,16 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     }
     int tot;
     int pos = run + block_excl_scan(__popc(u), s_tmp, &tot);
-    uint32_t rest = u;
-    while (rest) {
-      const int bit = __ffs(rest) - 1;
-      rest &= rest - 1u;
-      uint64_t mk = 0;
+    // token masks of the word's 32 channels at once: v[bit] bit i = token i selected it
+    static_assert(kT == 32, "the union masks transpose a 32 x 32 bit matrix");
+    transpose32(v);
 #pragma unroll
-      for (int i = 0; i < kT; ++i) mk |= (uint64_t)((v[i] >> bit) & 1u) << i;
-      ul[pos] = 32 * w + bit;
-      um[pos] = mk;
-      ++pos;
+    for (int bit = 0; bit < 32; ++bit) {
+      if ((u >> bit) & 1u) {
+        ul[pos] = 32 * w + bit;
+        um[pos] = (uint64_t)v[bit];
+        ++pos;
+      }
     }
     run += tot;
   }
