@@ -628,3 +628,38 @@ def test_small_and_uneven_hidden_sizes(b, torch, d, path):
             assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
     finally:
         b.moe_sel_destroy(ctx)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_wide_rank_score_blocks_of_64_channels(b, torch, path):
+    """Rank 64 with 1024 channels: 32-channel score blocks would leave the
+    rank-r partial sums more slots than a z block holds, so the single launch
+    scores 64 channels per block (the multi-kernel path is the control).
+    Selections and scores bit-exact, outputs within tolerance, batch 1 and 2."""
+    E, d, m, r, top_e, k = 8, 512, 1024, 64, 4, 133
+    wg, wu, wd = synth.layer_weights(0, 11, E, d, m)
+    cfg = b.make_config(d, E, m, r, top_e, 2)
+    ctx = b.moe_sel_prepare(cfg, wg, wu, wd)
+    try:
+        want = b.MOE_SEL_PATH_SINGLE_LAUNCH if path == "single_launch" else b.MOE_SEL_PATH_MULTI_KERNEL
+        b.moe_sel_set_path(ctx, want)
+        ref_layer = oracle.OracleLayer(lambda e: (wg[e], wu[e], wd[e]), E, d, m, r)
+        for bsz in (1, 2):
+            x = synth.tokens(0, 11, bsz, d, index=bsz)
+            logits = synth.router_logits(0, 11, bsz, E, index=bsz)
+            print(f"[run] m={m} r={r} path={path} B={bsz}", flush=True)
+            out = torch.zeros((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_forward(ctx, to_dev_u16(torch, x), to_dev_f32(torch, logits), bsz, top_e, k, out)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(ctx)
+            assert b.moe_sel_last_path(ctx) == want
+            ref = ref_layer.forward(x, logits, top_e, k)
+            dbg = b.moe_sel_debug_selection(ctx, bsz, top_e, k, m, with_scores=True)
+            assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+            for t in range(bsz):
+                for s in range(top_e):
+                    assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (t, s)
+                    assert np.array_equal(dbg["score"][t, s].view(np.uint32), ref["score"][t][s].view(np.uint32))
+            assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_destroy(ctx)
