@@ -308,56 +308,139 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 }
 
 // Routing by one wave for small top_e: lane l holds the logits of experts
-// l + 64 u; each of top_e rounds takes the wave-wide maximum of the remaining
-// order bits and, among the experts holding it, the lowest index (a ballot per
-// slot, slots in index order). Writes s_ids[rank] and the logit in s_w[rank].
+// l + 64 u and keeps the largest order bits it has left (0 once it has none:
+// no live key is below 0). Each of top_e rounds takes the wave-wide maximum of
+// the lanes' bests; when one lane holds it, that lane takes its lowest u
+// holding it (the lower index). When several do, the lowest index is the lowest
+// u holding it, then the lowest lane (a ballot per u). The winning lane writes
+// s_ids[rank] and the logit in s_w[rank], and recomputes its best.
 template <int KPER>
 __device__ __forceinline__ void wave_topk_route(const float* logits, int n_experts, int top_e, int* s_ids,
                                                 float* s_w) {
   const int lane = threadIdx.x & 63;
   uint32_t ob[KPER];
   float val[KPER];
-  bool alive[KPER];
+  uint32_t alive = 0;  // bit u: expert lane + 64 u not yet taken
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
     const int idx = lane + 64 * u;
-    alive[u] = idx < n_experts;
-    val[u] = alive[u] ? logits[idx] : 0.0f;
+    if (idx < n_experts) alive |= 1u << u;
+    val[u] = idx < n_experts ? logits[idx] : 0.0f;
     ob[u] = logit_order_bits(val[u]);
   }
+  uint32_t best = 0;
+#pragma unroll
+  for (int u = 0; u < KPER; ++u)
+    if ((alive >> u) & 1) best = max(best, ob[u]);
   for (int s = 0; s < top_e; ++s) {
-    uint32_t best = 0;
-#pragma unroll
-    for (int u = 0; u < KPER; ++u)
-      if (alive[u]) best = max(best, ob[u]);
     const uint32_t m = wave_max_dpp(best);
-    int win_u = -1;
-    uint64_t win_mask = 0;
+    uint64_t wmask = __ballot(alive != 0 && best == m);
+    int forced_u = -1;
+    if (__popcll(wmask) > 1) {
 #pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const uint64_t bm = __ballot(alive[u] && ob[u] == m);
-      if (win_u < 0 && bm) {
-        win_u = u;
-        win_mask = bm;
+      for (int u = 0; u < KPER; ++u) {
+        const uint64_t bm = __ballot(((alive >> u) & 1) && ob[u] == m);
+        if (forced_u < 0 && bm) {
+          forced_u = u;
+          wmask = bm;
+        }
       }
     }
-    const int win_lane = __builtin_ctzll(win_mask);
+    if (lane == __builtin_ctzll(wmask)) {
+      int wu = forced_u;
 #pragma unroll
-    for (int u = 0; u < KPER; ++u)
-      if (u == win_u && lane == win_lane) {
-        alive[u] = false;
-        s_ids[s] = lane + 64 * u;
-        s_w[s] = val[u];
-      }
+      for (int u = KPER - 1; u >= 0; --u)
+        if (forced_u < 0 && ((alive >> u) & 1) && ob[u] == m) wu = u;
+      alive &= ~(1u << wu);
+      s_ids[s] = lane + 64 * wu;
+      float w = val[0];
+#pragma unroll
+      for (int u = 1; u < KPER; ++u)
+        if (u == wu) w = val[u];
+      s_w[s] = w;
+      best = 0;
+#pragma unroll
+      for (int u = 0; u < KPER; ++u)
+        if ((alive >> u) & 1) best = max(best, ob[u]);
+    }
   }
 }
 
+// Compiler-level ordering of LDS accesses inside one wavefront (a wave's LDS
+// operations execute in order, so wave-synchronous code needs no s_barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Routing by rank for n_experts <= 64 * KPER (at most 256): lane l of every wave
+// holds the order keys (order bits, then lower index first) of experts l + 64 u,
+// and wave w counts, for each of them, the larger keys among the experts
+// [w * len, (w + 1) * len), reading that range two keys at a time from a copy the
+// wave wrote itself (no barrier). After one block barrier the four counts of
+// expert i sum to its rank, and the ranks below top_e are the routed experts.
+// Keys past n_experts are 0, below every live key. s_scr: 16 * 64 * KPER bytes.
+template <int KPER>
+__device__ __forceinline__ void rank_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
+                                           void* s_scr) {
+  constexpr int kSpan = 64 * KPER;       // experts covered, padded
+  constexpr int kLen = kSpan / kWaves;   // experts each wave compares against (16, 32 or 64)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t* s_key = (uint64_t*)s_scr;                  // wave w's range at w * kLen
+  uint32_t* s_cnt = (uint32_t*)(s_key + kSpan);        // per expert: byte w = wave w's count
+  float* s_val = (float*)(s_cnt + kSpan);
+  uint64_t key[KPER];
+  float val[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int i = lane + 64 * u;
+    val[u] = i < n_experts ? logits[i] : 0.0f;
+    key[u] = i < n_experts ? order_key(logit_order_bits(val[u]), i) : 0ull;
+  }
+  // the wave's comparison range is register u = r0 / 64 of lanes r0 % 64 .. + kLen
+  const int r0 = wave * kLen, l0 = r0 % 64;
+  if (lane >= l0 && lane < l0 + kLen) {
+    uint64_t kk = key[0];
+#pragma unroll
+    for (int u = 1; u < KPER; ++u)
+      if (u == r0 / 64) kk = key[u];
+    s_key[r0 + lane - l0] = kk;
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) s_val[lane + 64 * u] = val[u];
+  }
+  wave_lds_sync();
+  int rk[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) rk[u] = 0;
+  const ulonglong2* kp = (const ulonglong2*)(s_key + r0);
+#pragma unroll 4
+  for (int j = 0; j < kLen / 2; ++j) {
+    const ulonglong2 kk = kp[j];
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) rk[u] += (int)(kk.x > key[u]) + (int)(kk.y > key[u]);
+  }
+  unsigned char* cnt = (unsigned char*)s_cnt;
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) cnt[4 * (lane + 64 * u) + wave] = (unsigned char)rk[u];
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_experts; i += kThreads) {
+    const int r = (int)__builtin_amdgcn_udot4(s_cnt[i], 0x01010101u, 0u, false);
+    if (r < top_e) {
+      s_ids[r] = i;
+      s_w[r] = s_val[i];
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// Routing of one token by the whole block (n_experts <= 1024): for top_e <= 16
-// and n_experts <= 256 by one wave (wave_topk_route); otherwise the rank of
-// every logit (larger first, lower index first) is the count of larger order
-// keys, computed by all threads in parallel over parts of the expert range, and
-// ranks below top_e are the routed experts. The gate weights are the softmax
+// Routing of one token by the whole block (n_experts <= 1024): for n_experts <=
+// 256 by rank_route; otherwise the rank of every logit (larger first, lower
+// index first) is the count of larger order keys, computed by all threads in
+// parallel over parts of the expert range, and ranks below top_e are the routed
+// experts. The gate weights are the softmax
 // over their logits (skipped when with_weights is false). s_scr: 2 * n_experts
 // uint64 + n_experts ints of LDS scratch. Barriers inside; s_ids (and s_w)
 // valid when it returns.
@@ -365,13 +448,10 @@ __device__ __forceinline__ void wave_topk_route(const float* logits, int n_exper
 __device__ __forceinline__ void block_route(const float* logits, int n_experts, int top_e, int* s_ids, float* s_w,
                                             void* s_scr, bool with_weights = true) {
   const int tid = threadIdx.x;
-  if (top_e <= 16 && n_experts <= 256) {  // few rounds: one wave, no block-wide ranking
-    if (tid < 64) {
-      if (n_experts <= 64) wave_topk_route<1>(logits, n_experts, top_e, s_ids, s_w);
-      else if (n_experts <= 128) wave_topk_route<2>(logits, n_experts, top_e, s_ids, s_w);
-      else wave_topk_route<4>(logits, n_experts, top_e, s_ids, s_w);
-    }
-    __syncthreads();
+  if (n_experts <= 256) {
+    if (n_experts <= 64) rank_route<1>(logits, n_experts, top_e, s_ids, s_w, s_scr);
+    else if (n_experts <= 128) rank_route<2>(logits, n_experts, top_e, s_ids, s_w, s_scr);
+    else rank_route<4>(logits, n_experts, top_e, s_ids, s_w, s_scr);
     if (with_weights) {
       route_softmax(s_w, top_e);
       __syncthreads();
@@ -417,13 +497,6 @@ __device__ __forceinline__ void block_route(const float* logits, int n_experts, 
     route_softmax(s_w, top_e);
     __syncthreads();
   }
-}
-
-// Compiler-level ordering of LDS accesses inside one wavefront (a wave's LDS
-// operations execute in order, so wave-synchronous code needs no s_barrier).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
 }
 
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {

@@ -205,16 +205,19 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   const int b0 = nb * part / nparts, b1 = nb * (part + 1) / nparts;  // empty when nb is small
   const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
                                    codes_dword_index(a.d, a.m, j0 / kGroup, mat, 0, j0 % kGroup + c, 0));
+  const uint4* pb = cp + (size_t)b0 * 64;  // the part's first code block; blocks are 1 KiB apart
+  const int nblk = b1 - b0;
   uint4 cb[kScoreBlk];
 #pragma unroll
-  for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)max(min(b0 + i, b1 - 1), 0) * 64];
+  for (int i = 0; i < kScoreBlk; ++i)
+    if (i < nblk) cb[i] = pb[i * 64];
   const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * a.m + (size_t)j0) * r);
   const int qpieces = SC * r / 8;
   constexpr int kQv = SC * 128 / 8 / kThreads;  // pieces per thread for r <= 128
   uint4 qv[kQv];
 #pragma unroll
   for (int u = 0; u < kQv; ++u)
-    if (tid + u * kThreads < qpieces) qv[u] = qsrc[tid + u * kThreads];
+    qv[u] = tid + u * kThreads < qpieces ? qsrc[tid + u * kThreads] : make_uint4(0, 0, 0, 0);
   const float4 st = a.stats[(size_t)e * a.m + j0 + c];
   const int e_t = quantise_to_lds<SLOTS>(xv, a.d, s_xq, sm, x16);
   __syncthreads();  // x_q in LDS
@@ -227,21 +230,22 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     for (int q = 0; q < 4; ++q)
       if (q >= q0 && q < q1) qs += sm.qsum[w][q];
   CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
-  for (int c0 = b0; c0 < b1; c0 += kScoreBlk) {
-    if (c0 != b0) {
+  for (int c0 = 0; c0 < nblk; c0 += kScoreBlk) {
+    if (c0 != 0) {
 #pragma unroll
-      for (int i = 0; i < kScoreBlk; ++i) cb[i] = cp[(size_t)min(c0 + i, b1 - 1) * 64];
+      for (int i = 0; i < kScoreBlk; ++i)
+        if (c0 + i < nblk) cb[i] = pb[(c0 + i) * 64];
     }
 #pragma unroll
     for (int i = 0; i < kScoreBlk; ++i) {
-      if (c0 + i < b1) {
-        const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
+      if (c0 + i < nblk) {
+        const int4* xb = (const int4*)(s_xq + 64 * (b0 + c0 + i));
         dot_codes16(cb[i].x, xb[0], acc);
         dot_codes16(cb[i].y, xb[1], acc);
         dot_codes16(cb[i].z, xb[2], acc);
         dot_codes16(cb[i].w, xb[3], acc);
         if (x16) {
-          const int4* xl = (const int4*)(s_xq + a.d + 64 * (c0 + i));
+          const int4* xl = (const int4*)(s_xq + a.d + 64 * (b0 + c0 + i));
           dot_codes16_u(cb[i].x, xl[0], acc_lo);
           dot_codes16_u(cb[i].y, xl[1], acc_lo);
           dot_codes16_u(cb[i].z, xl[2], acc_lo);
