@@ -54,7 +54,7 @@ using namespace dev;
 constexpr int kMaxChunkSparse = 8;   // channels per gather block, all loaded at once
 constexpr int kMaxChunkDense = 16;
 constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
-constexpr int kScoreBlk = 16;        // sketch blocks loaded together per wave
+constexpr int kScoreBlk = 16;        // sketch blocks in flight per lane group pair (d = 2048 in one batch)
 constexpr int kZPass = 4;            // compensation row passes loaded together
 constexpr int kMaxZPart = 4;         // zpart values per thread ((m / 32) * r <= 1024)
 constexpr int kMaxP = 4;             // 16-byte P pieces per combine thread (top_e * r <= 256)
@@ -203,14 +203,19 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   const int j0 = sb * SC;  // first channel of the block
   const int nb = a.d / kBlock;
   const int b0 = nb * part / nparts, b1 = nb * (part + 1) / nparts;  // empty when nb is small
-  const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
-                                   codes_dword_index(a.d, a.m, j0 / kGroup, mat, 0, j0 % kGroup + c, 0));
-  const uint4* pb = cp + (size_t)b0 * 64;  // the part's first code block; blocks are 1 KiB apart
-  const int nblk = b1 - b0;
-  uint4 cb[kScoreBlk];
+  // code block b of this lane's channel and matrix sits 1 KiB * b past the row
+  // start; loads are addressed as a block-uniform base plus a 32-bit lane offset,
+  // every lane issuing all of them (clamped to its part's last block, or block 0
+  // for an empty part), so none is masked
+  constexpr int kSB = kScoreBlk / lps;  // blocks per load batch: a part of d = 2048
+  const char* cbase = (const char*)(a.codes + (size_t)e * codes_dwords_per_expert(a.d, a.m) +
+                                    codes_dword_index(a.d, a.m, j0 / kGroup, 0, 0, 0, 0));
+  const uint32_t row_off = (uint32_t)codes_dword_index(a.d, a.m, 0, mat, 0, j0 % kGroup + c, 0) * 4u;
+  const int nblk = b1 - b0, blast = max(b1 - 1, 0);
+  uint4 cb[kSB];
 #pragma unroll
-  for (int i = 0; i < kScoreBlk; ++i)
-    if (i < nblk) cb[i] = pb[i * 64];
+  for (int i = 0; i < kSB; ++i)
+    cb[i] = *(const uint4*)(cbase + (row_off + (uint32_t)min(b0 + i, blast) * 1024u));
   const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * a.m + (size_t)j0) * r);
   const int qpieces = SC * r / 8;
   constexpr int kQv = SC * 128 / 8 / kThreads;  // pieces per thread for r <= 128
@@ -230,14 +235,14 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     for (int q = 0; q < 4; ++q)
       if (q >= q0 && q < q1) qs += sm.qsum[w][q];
   CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
-  for (int c0 = 0; c0 < nblk; c0 += kScoreBlk) {
+  for (int c0 = 0; c0 < nblk; c0 += kSB) {
     if (c0 != 0) {
 #pragma unroll
-      for (int i = 0; i < kScoreBlk; ++i)
-        if (c0 + i < nblk) cb[i] = pb[(c0 + i) * 64];
+      for (int i = 0; i < kSB; ++i)
+        cb[i] = *(const uint4*)(cbase + (row_off + (uint32_t)min(b0 + c0 + i, blast) * 1024u));
     }
 #pragma unroll
-    for (int i = 0; i < kScoreBlk; ++i) {
+    for (int i = 0; i < kSB; ++i) {
       if (c0 + i < nblk) {
         const int4* xb = (const int4*)(s_xq + 64 * (b0 + c0 + i));
         dot_codes16(cb[i].x, xb[0], acc);
