@@ -305,20 +305,21 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
 // for the z block, the pair's zpart slots), then selects the pair's top-k: the
 // selected channels ascending in s_sel[0..k), the sketch activations in s_hh,
 // the zpart values in s_zp. Chunk 0 also records the selection for inspection.
-__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
-                                              float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
-                                              float* s_zp) {
+template <int MK>  // key slots per thread: m <= MK * kThreads
+__device__ __forceinline__ void gather_select_mk(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
+                                                 float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
+                                                 float* s_zp) {
   const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
   const int zg = m / a.score_ch;
   uint64_t* slots = a.xscore + ((size_t)p * a.ncs + c) * m;
   const int nzp = with_zpart ? zg * r : 0;
   float* zslots = a.zpart + (size_t)p * zg * r;
   block_topk_prezero(sm.hist, sm.tmp);  // ordered before the select by the polling barrier
-  uint64_t v[kMaxKeysPer];
+  uint64_t v[MK];
   float zv[kMaxZPart];
   uint32_t pending = 0;  // bit u: key slot u; bit 16 + u: zpart slot u
 #pragma unroll
-  for (int u = 0; u < kMaxKeysPer; ++u) {
+  for (int u = 0; u < MK; ++u) {
     v[u] = 0ull;
     if (tid + u * kThreads < m) pending |= 1u << u;
   }
@@ -330,13 +331,13 @@ __device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, 
   int spins = 0;
   while (true) {
 #pragma unroll
-    for (int u = 0; u < kMaxKeysPer; ++u)
+    for (int u = 0; u < MK; ++u)
       if ((pending >> u) & 1) v[u] = ld_coh64(slots + tid + u * kThreads);
 #pragma unroll
     for (int u = 0; u < kMaxZPart; ++u)
       if ((pending >> (16 + u)) & 1) zv[u] = ld_coh(zslots + tid + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kMaxKeysPer; ++u)
+    for (int u = 0; u < MK; ++u)
       if ((uint32_t)v[u] != kEmpty) pending &= ~(1u << u);
 #pragma unroll
     for (int u = 0; u < kMaxZPart; ++u)
@@ -345,7 +346,7 @@ __device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, 
     if (!keep_polling(spins, a.err, 1)) break;
   }
 #pragma unroll
-  for (int u = 0; u < kMaxKeysPer; ++u) {
+  for (int u = 0; u < MK; ++u) {
     const int j = tid + u * kThreads;
     if (j < m) {
       s_keys[j] = (uint32_t)v[u];
@@ -366,32 +367,30 @@ __device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, 
     for (int j = tid; j < k; j += kThreads) s_sel[j] = j;
     __syncthreads();
   } else {
-    constexpr int KPT = kMaxKeysPer;
-    uint32_t key[KPT];
+    uint32_t key[MK];
     const int per = (m + kThreads - 1) / kThreads;  // consecutive keys per thread
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
+    for (int u = 0; u < MK; ++u) {
       const int j = tid * per + u;
       key[u] = (u < per && j < m) ? s_keys[j] : 0u;
     }
-    int sel[KPT];
-    if (per <= 4) {
-      uint32_t k4[4] = {key[0], key[1], key[2], key[3]};
-      int s4[4];
-      block_topk_select_strided<4, true>(k4, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, s4);
+    int sel[MK];
+    block_topk_select_strided<MK, true>(key, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, sel);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (s4[u] >= 0) s_sel[s4[u]] = tid * per + u;
-    } else {
-      block_topk_select_strided<KPT, true>(key, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, sel);
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if (sel[u] >= 0) s_sel[sel[u]] = tid * per + u;
-    }
+    for (int u = 0; u < MK; ++u)
+      if (sel[u] >= 0) s_sel[sel[u]] = tid * per + u;
     __syncthreads();
   }
   if (c == 0)
     for (int i = tid; i < k; i += kThreads) a.sel_idx[(size_t)p * m + i] = s_sel[i];  // for inspection only
+}
+
+// The select with as few key slots per thread as m allows (4 covers m <= 1024).
+__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
+                                              float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
+                                              float* s_zp) {
+  if (a.m <= 4 * kThreads) gather_select_mk<4>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  else gather_select_mk<kMaxKeysPer>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
 }
 
 template <bool DENSE, int SLOTS>
