@@ -86,6 +86,17 @@ __device__ __forceinline__ float dot8_bf16(uint4 w, const float* x) {
   return s;
 }
 
+// The same dot with x also as eight bf16 (packed pairs): four v_dot2_f32_bf16,
+// each adding two exact bf16 products to the binary32 accumulator.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_bf16_packed(uint4 w, uint4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+  return acc;
+}
+
 __device__ __forceinline__ void axpy8_bf16(float a, uint4 w, float* y) {
   y[0] += a * bf16lo(w.x); y[1] += a * bf16hi(w.x);
   y[2] += a * bf16lo(w.y); y[3] += a * bf16hi(w.y);

@@ -396,7 +396,9 @@ __device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, 
 template <bool DENSE, int SLOTS>
 __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& sm, unsigned char* dyn) {
   constexpr int kMaxChunk = DENSE ? kMaxChunkDense : kMaxChunkSparse;
-  const int C = a.chunk;
+  // sparse chunks are always kMaxChunkSparse channels (checked at launch), so
+  // their loads carry no runtime guard and each use waits only for its own load
+  const int C = DENSE ? a.chunk : kMaxChunkSparse;
   const int d = a.d, m = a.m;
   const int p = bid / a.nc, c = bid % a.nc;
   const int t = p / a.top_e, slot = p % a.top_e;
@@ -408,17 +410,12 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
   unsigned char* s_take = dyn + 12 * (size_t)m;         // m
   float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zpart rows: the z block's only
 
-  float xv[SLOTS][8];
+  uint4 xv[SLOTS];  // eight bf16 of x per slot (zero past d)
   const uint16_t* xrow = a.x + (size_t)t * d;
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     const int s = tid + u * kThreads;
-    if (s < nslots) {
-      unpack8(*(const uint4*)(xrow + 8 * s), xv[u]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xv[u][q] = 0.0f;
-    }
+    xv[u] = s < nslots ? *(const uint4*)(xrow + 8 * s) : make_uint4(0, 0, 0, 0);
   }
   route(a, t, sm);
   const int count = DENSE ? m : a.k;
@@ -442,6 +439,8 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
     const int ii = mine > 0 ? min(i, mine - 1) : 0;
     jj[i] = DENSE ? min(first + ii, m - 1) : (mine > 0 ? s_sel[first + ii] : 0);
   }
+  // gate and up rows of every channel first, then the down rows: the SwiGLU dots
+  // wait only for the former, and run while the down rows are in flight
 #pragma unroll
   for (int i = 0; i < kMaxChunk; ++i) {
     if (i < C) {
@@ -451,6 +450,16 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
         const int s = min(tid + u * kThreads, nslots - 1);
         gv[i][u] = *(const uint4*)(row + 8 * s);
         uv[i][u] = *(const uint4*)(row + d + 8 * s);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxChunk; ++i) {
+    if (i < C) {
+      const uint16_t* row = wbase + (size_t)jj[i] * 3 * d;
+#pragma unroll
+      for (int u = 0; u < SLOTS; ++u) {
+        const int s = min(tid + u * kThreads, nslots - 1);
         dv[i][u] = *(const uint4*)(row + 2 * d + 8 * s);
       }
     }
@@ -464,8 +473,8 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
     if (i < C) {
 #pragma unroll
       for (int u = 0; u < SLOTS; ++u) {
-        gs[i] += dot8_bf16(gv[i][u], xv[u]);
-        us[i] += dot8_bf16(uv[i][u], xv[u]);
+        gs[i] = dot8_bf16_packed(gv[i][u], xv[u], gs[i]);
+        us[i] = dot8_bf16_packed(uv[i][u], xv[u], us[i]);
       }
     }
   }
@@ -747,6 +756,7 @@ int fused_blocks_per_cu(bool dense, int d, int m, int r) {
 }
 
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream) {
+  if (dense ? (a.chunk != 8 && a.chunk != kMaxChunkDense) : a.chunk != kMaxChunkSparse) return hipErrorInvalidValue;
   const int total = (dense ? 0 : a.n_score + a.n_z) + a.n_gather + a.n_combine;
   void* args[] = {(void*)&a};
   return hipLaunchKernel(fused_kernel(dense, a.d), dim3(total), dim3(kThreads), args, fused_lds_bytes(a.d, a.m, a.r),
