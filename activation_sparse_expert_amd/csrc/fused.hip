@@ -495,15 +495,21 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
   for (int u = 0; u < SLOTS; ++u)
 #pragma unroll
     for (int q = 0; q < 8; ++q) yacc[u][q] = 0.0f;
+  // lane i of every wave finishes channel i's activation (the wave partial sums
+  // in wave order); the axpys take it from that lane
+  float hl = 0.0f;
+  if (lane < C && lane < mine) {
+    float g = 0.0f, u = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      g += sm.red[w][2 * lane];
+      u += sm.red[w][2 * lane + 1];
+    }
+    hl = wp * (silu_f32(g) * u);
+  }
 #pragma unroll
   for (int i = 0; i < kMaxChunk; ++i) {
     if (i < C && i < mine) {
-      float g = 0.0f, u = 0.0f;
-      for (int w = 0; w < kWaves; ++w) {
-        g += sm.red[w][2 * i];
-        u += sm.red[w][2 * i + 1];
-      }
-      const float h = wp * (silu_f32(g) * u);
+      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), i));
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) axpy8_bf16(h, dv[i][s], yacc[s]);
     }
@@ -617,48 +623,27 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
     pv[u] = npieces ? *(const uint4*)(a.pmat + ((size_t)sm.ids[s] * r + cc) * d + 64 * sl + 32 * hf + 8 * part)
                     : make_uint4(0, 0, 0, 0);
   }
-  // every wave polls its own slots: partial values of producers pg + 8 u, and (threads
-  // below top_e * r) one z value
   const float* src = a.partial + ((size_t)t * slices + sl) * qt * 64 + 32 * hf + el;
   float* zsrc = a.zcopy + ((size_t)t * 2 * slices + hs) * a.top_e * rdiv;
   const bool zthread = r > 0 && tid < a.top_e * r;
-  float z = 0.0f;
-  bool zpend = zthread;
-  float y = 0.0f;
   int spins = 0;
-  // producers in batches of 8 * kCombPer; values are summed in producer order
-  for (int base = 0; base < qt; base += 8 * kCombPer) {
-    const float* bsrc = src + (size_t)(base + pg) * 64;
-    float v[kCombPer];
-    uint32_t pending = 0;
-#pragma unroll
-    for (int u = 0; u < kCombPer; ++u) {
-      v[u] = 0.0f;
-      if (base + pg + 8 * u < qt) pending |= 1u << u;
-    }
+  // z first (it usually lands before the last partial), so that P z for these
+  // elements is done while the partials are still arriving
+  if (r > 0) {
+    float z = 0.0f;
+    bool zpend = zthread;
     while (true) {
-#pragma unroll
-      for (int u = 0; u < kCombPer; ++u)
-        if ((pending >> u) & 1) v[u] = ld_coh(bsrc + (size_t)u * 512);
-      if (zpend) z = ld_coh(zsrc + tid);
-#pragma unroll
-      for (int u = 0; u < kCombPer; ++u)
-        if (!empty(v[u])) pending &= ~(1u << u);
-      if (zpend && !empty(z)) zpend = false;
-      if (__all(pending == 0 && !zpend)) break;
+      if (zpend) {
+        z = ld_coh(zsrc + tid);
+        if (!empty(z)) zpend = false;
+      }
+      if (__all(!zpend)) break;
       if (!keep_polling(spins, a.err, 2)) break;
     }
-#pragma unroll
-    for (int u = 0; u < kCombPer; ++u) {
-      if (base + pg + 8 * u < qt) {
-        y += v[u];
-        clear_coh(const_cast<float*>(bsrc) + (size_t)u * 512);
-      }
+    if (zthread) {
+      s_z[tid] = z;
+      clear_coh(zsrc + tid);
     }
-  }
-  if (zthread) {
-    s_z[tid] = z;
-    clear_coh(zsrc + tid);
   }
   __syncthreads();
   // P z for these elements: every thread's pieces share part (tid & 3): elements 8*part..+7
@@ -677,14 +662,44 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
 #pragma unroll
   for (int q = 0; q < 8; ++q) s_red[tid * 8 + q] = pz[q];
   __syncthreads();
+  float yz = 0.0f;
   {
     // element el = 8 * part + qq: threads th == part (mod 4); this thread takes th = part + 4 (pg + 8 n)
     const int part = el >> 3, qq = el & 7;
-    float yz = 0.0f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) yz += s_red[(part + 4 * (pg + 8 * n)) * 8 + qq];
-    s_y[pg * 32 + el] = y + yz;
   }
+  // every wave polls its own slots: partial values of producers pg + 8 u, in
+  // batches of 8 * kCombPer; values are summed in producer order
+  float y = 0.0f;
+  for (int base = 0; base < qt; base += 8 * kCombPer) {
+    const float* bsrc = src + (size_t)(base + pg) * 64;
+    float v[kCombPer];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int u = 0; u < kCombPer; ++u) {
+      v[u] = 0.0f;
+      if (base + pg + 8 * u < qt) pending |= 1u << u;
+    }
+    while (true) {
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u)
+        if ((pending >> u) & 1) v[u] = ld_coh(bsrc + (size_t)u * 512);
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u)
+        if (!empty(v[u])) pending &= ~(1u << u);
+      if (__all(pending == 0)) break;
+      if (!keep_polling(spins, a.err, 2)) break;
+    }
+#pragma unroll
+    for (int u = 0; u < kCombPer; ++u) {
+      if (base + pg + 8 * u < qt) {
+        y += v[u];
+        clear_coh(const_cast<float*>(bsrc) + (size_t)u * 512);
+      }
+    }
+  }
+  s_y[pg * 32 + el] = y + yz;
   __syncthreads();
   if (tid < 32) {
     float o = 0.0f;
