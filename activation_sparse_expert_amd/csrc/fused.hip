@@ -56,6 +56,7 @@ constexpr int kMaxChunkDense = 16;
 constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
 constexpr int kScoreBlk = 16;        // sketch blocks in flight per lane group pair (d = 2048 in one batch)
 constexpr int kZPass = 4;            // compensation row passes loaded together
+constexpr int kZWarm = 16;           // Q pieces per thread in flight while the z block warms L2
 constexpr int kMaxZPart = 4;         // zpart values per thread ((m / 32) * r <= 1024)
 constexpr int kMaxP = 4;             // 16-byte P pieces per combine thread (top_e * r <= 256)
 constexpr int kCombPer = 24;         // partial values per combine thread per poll batch
@@ -548,8 +549,27 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
   float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zg * r
   float* s_zr = s_zp + zg * r;                          // kThreads x 8, then r
   route(a, t, sm);
-  gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int e = sm.ids[slot];
+  {
+    // read the expert's whole Q (m x r bf16) once while the scores are still being
+    // computed, so that the selected rows read after the select come from this
+    // XCD's L2; the values only feed a store that k >= 0 (checked at launch) rules out
+    const uint4* qall = (const uint4*)(a.qmat + (size_t)e * m * r);
+    const int n16 = m * r / 8;
+    uint32_t acc = 0;
+    for (int b = 0; b < n16; b += kZWarm * kThreads) {
+      uint4 qw[kZWarm];
+#pragma unroll
+      for (int u = 0; u < kZWarm; ++u) {
+        const int i = b + u * kThreads + tid;
+        qw[u] = i < n16 ? qall[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kZWarm; ++u) acc ^= qw[u].x ^ qw[u].y ^ qw[u].z ^ qw[u].w;
+    }
+    if (a.k < 0 && tid == 0) a.err[0] = (int)acc;
+  }
+  gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int count = a.k;
   // thread t owns 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass
   float zacc[8];
