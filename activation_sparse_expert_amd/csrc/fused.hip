@@ -280,18 +280,22 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     s_sc[c] = sc;
   }
   __syncthreads();
-  // publish (score, h_hat) of the block's channels to each gather block of the pair
-  for (int i = tid; i < a.ncs * SC; i += kThreads) {
-    const int cc = i / SC, l = i % SC;
-    const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
-    st_coh64(&a.xscore[((size_t)p * a.ncs + cc) * a.m + j0 + l], v);
-  }
-  // this block's share of Q^T h_hat over its channels, for the z block
-  if (tid < r) {
-    float z = 0.0f;
+  if (wave == kWaves - 1) {
+    // the last wave: this block's share of Q^T h_hat over its channels, for the z
+    // block, at the same time as the other waves publish the scores
+    for (int col = lane; col < r; col += 64) {
+      float z = 0.0f;
 #pragma unroll 16
-    for (int j = 0; j < SC; ++j) z += s_h[j] * bf16f(s_q[j * r + tid]);
-    st_coh(&a.zpart[((size_t)p * zg + sb) * r + tid], z);
+      for (int j = 0; j < SC; ++j) z += s_h[j] * bf16f(s_q[j * r + col]);
+      st_coh(&a.zpart[((size_t)p * zg + sb) * r + col], z);
+    }
+  } else {
+    // publish (score, h_hat) of the block's channels to each gather block of the pair
+    for (int i = tid; i < a.ncs * SC; i += kThreads - 64) {
+      const int cc = i / SC, l = i % SC;
+      const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
+      st_coh64(&a.xscore[((size_t)p * a.ncs + cc) * a.m + j0 + l], v);
+    }
   }
   if (tid < SC) {  // for inspection only
     st_coh(&a.hhat[(size_t)p * a.m + j0 + tid], s_h[tid]);
