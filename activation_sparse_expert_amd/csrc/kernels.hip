@@ -1153,12 +1153,10 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
 #pragma unroll
   for (int i = 0; i < kB1Pieces; ++i) {
     if (lane + 64 * i < npc) {
-      float xf[8];
-      unpack8(xv[i], xf);
 #pragma unroll
       for (int ci = 0; ci < 2; ++ci) {
-        sg[ci] += dot8_bf16(gv[ci][i], xf);
-        su[ci] += dot8_bf16(uv[ci][i], xf);
+        sg[ci] = dot8_bf16_packed(gv[ci][i], xv[i], sg[ci]);
+        su[ci] = dot8_bf16_packed(uv[ci][i], xv[i], su[ci]);
       }
     }
   }
