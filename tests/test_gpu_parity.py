@@ -663,3 +663,41 @@ def test_wide_rank_score_blocks_of_64_channels(b, torch, path):
             assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
     finally:
         b.moe_sel_destroy(ctx)
+
+
+@pytest.mark.parametrize("m", [2048, 4096])
+@pytest.mark.parametrize("path", PATHS)
+def test_many_channels_single_launch_select(b, torch, m, path):
+    """More than 1024 channels per expert, up to the single launch's largest
+    (4096): the gather and z blocks select with sixteen key slots per thread
+    (the multi-kernel path is the control). Selections and scores bit-exact,
+    outputs within tolerance, batch 1 and 2 (batch 1 only at 4096 channels,
+    where the grid of two tokens no longer fits on the chip at once)."""
+    E, d, r, top_e = 4, 256, 8, 2
+    k = (m * 3) // 20  # 15% of the channels
+    wg, wu, wd = synth.layer_weights(0, 13, E, d, m)
+    cfg = b.make_config(d, E, m, r, top_e, 2)
+    ctx = b.moe_sel_prepare(cfg, wg, wu, wd)
+    try:
+        want = b.MOE_SEL_PATH_SINGLE_LAUNCH if path == "single_launch" else b.MOE_SEL_PATH_MULTI_KERNEL
+        b.moe_sel_set_path(ctx, want)
+        ref_layer = oracle.OracleLayer(lambda e: (wg[e], wu[e], wd[e]), E, d, m, r)
+        for bsz in ((1, 2) if m < 4096 else (1,)):
+            x = synth.tokens(0, 13, bsz, d, index=m + bsz)
+            logits = synth.router_logits(0, 13, bsz, E, index=m + bsz)
+            print(f"[run] m={m} k={k} path={path} B={bsz}", flush=True)
+            out = torch.zeros((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_forward(ctx, to_dev_u16(torch, x), to_dev_f32(torch, logits), bsz, top_e, k, out)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(ctx)
+            assert b.moe_sel_last_path(ctx) == want
+            ref = ref_layer.forward(x, logits, top_e, k)
+            dbg = b.moe_sel_debug_selection(ctx, bsz, top_e, k, m, with_scores=True)
+            assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+            for t in range(bsz):
+                for s in range(top_e):
+                    assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (t, s)
+                    assert np.array_equal(dbg["score"][t, s].view(np.uint32), ref["score"][t][s].view(np.uint32))
+            assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_destroy(ctx)
