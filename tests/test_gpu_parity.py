@@ -701,3 +701,41 @@ def test_many_channels_single_launch_select(b, torch, m, path):
             assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
     finally:
         b.moe_sel_destroy(ctx)
+
+
+@pytest.mark.parametrize("E", [192, 256])
+@pytest.mark.parametrize("path", PATHS)
+def test_routing_up_to_256_experts_with_ties(b, torch, E, path):
+    """Routing ranks for 129 to 256 experts (four keys per lane, a padded last
+    lane block at 192) with heavy ties among the logits and signed zeros: the
+    routed experts, selections and scores bit-exact against the oracle, outputs
+    within tolerance, batch 1 and 2."""
+    d, m, r, top_e, k = 128, 256, 8, 8, 40
+    wg, wu, wd = synth.layer_weights(0, 17, E, d, m)
+    cfg = b.make_config(d, E, m, r, top_e, 2)
+    ctx = b.moe_sel_prepare(cfg, wg, wu, wd)
+    try:
+        want = b.MOE_SEL_PATH_SINGLE_LAUNCH if path == "single_launch" else b.MOE_SEL_PATH_MULTI_KERNEL
+        b.moe_sel_set_path(ctx, want)
+        ref_layer = oracle.OracleLayer(lambda e: (wg[e], wu[e], wd[e]), E, d, m, r)
+        rng = np.random.default_rng(E)
+        for bsz in (1, 2):
+            x = synth.tokens(0, 17, bsz, d, index=E + bsz)
+            logits = (rng.integers(-3, 4, size=(bsz, E)) * 0.5).astype(np.float32)  # few distinct values
+            logits[logits == 0] = np.where(rng.random(int((logits == 0).sum())) < 0.5, -0.0, 0.0)
+            print(f"[run] E={E} path={path} B={bsz}", flush=True)
+            out = torch.zeros((bsz, d), dtype=torch.int16, device="cuda")
+            b.moe_sel_forward(ctx, to_dev_u16(torch, x), to_dev_f32(torch, logits), bsz, top_e, k, out)
+            torch.cuda.synchronize()
+            b.moe_sel_check_device(ctx)
+            assert b.moe_sel_last_path(ctx) == want
+            ref = ref_layer.forward(x, logits, top_e, k)
+            dbg = b.moe_sel_debug_selection(ctx, bsz, top_e, k, m, with_scores=True)
+            assert np.array_equal(dbg["expert_ids"], ref["expert_ids"])
+            for t in range(bsz):
+                for s in range(top_e):
+                    assert np.array_equal(dbg["chan_idx"][t, s], ref["sel"][t][s]), (t, s)
+                    assert np.array_equal(dbg["score"][t, s].view(np.uint32), ref["score"][t][s].view(np.uint32))
+            assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        b.moe_sel_destroy(ctx)
