@@ -26,7 +26,8 @@ EXPORTED = (
     "moe_sel_forward_dense", "moe_sel_forward_threshold", "moe_sel_debug_selection", "moe_sel_export_expert",
     "moe_sel_get_config", "moe_sel_device_bytes", "moe_sel_destroy", "moe_sel_check_device",
     "moe_sel_set_path", "moe_sel_last_path", "moe_sel_set_score", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
-    "moe_sel_residual_rmsnorm_router", "moe_sel_save", "moe_sel_load",
+    "moe_sel_residual_rmsnorm_router", "moe_sel_save", "moe_sel_load", "moe_sel_set_wait_limit",
+    "moe_sel_debug_silu", "moe_sel_debug_score", "moe_sel_read_stream", "moe_sel_debug_fail_alloc",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
@@ -76,7 +77,7 @@ def _load():
         "moe_sel_forward_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp]),
         "moe_sel_forward_threshold": (ctypes.c_int, [vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]),
         "moe_sel_debug_selection": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp]),
-        "moe_sel_export_expert": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_sel_export_expert": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "moe_sel_get_config": (ctypes.c_int, [vp, ctypes.POINTER(moe_sel_config)]),
         "moe_sel_device_bytes": (ctypes.c_uint64, [vp]),
         "moe_sel_destroy": (None, [vp]),
@@ -89,6 +90,11 @@ def _load():
         "moe_sel_residual_rmsnorm_router": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp]),
         "moe_sel_save": (ctypes.c_int, [vp, ctypes.c_char_p]),
         "moe_sel_load": (ctypes.c_int, [ctypes.c_char_p, vp, ctypes.POINTER(vp)]),
+        "moe_sel_set_wait_limit": (ctypes.c_int, [vp, i32]),
+        "moe_sel_debug_silu": (ctypes.c_int, [vp, vp, ctypes.c_int64, vp]),
+        "moe_sel_debug_score": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp]),
+        "moe_sel_read_stream": (ctypes.c_int, [vp, ctypes.c_uint64, vp, vp]),
+        "moe_sel_debug_fail_alloc": (ctypes.c_int, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -223,13 +229,14 @@ def moe_sel_export_expert(ctx, expert, cfg: moe_sel_config):
     m, d, r = cfg.m, cfg.d, cfg.rank
     out = dict(tern_gate=np.zeros((m, d), np.int8), tern_up=np.zeros((m, d), np.int8),
                alpha_gate=np.zeros(m, np.float32), alpha_up=np.zeros(m, np.float32),
-               down_norm=np.zeros(m, np.float32))
+               down_norm=np.zeros(m, np.float32), nnz_gate=np.zeros(m, np.int32), nnz_up=np.zeros(m, np.int32))
     if r > 0:
         out["p_bf16"] = np.zeros((r, d), np.uint16)
         out["q_bf16"] = np.zeros((m, r), np.uint16)
     st = _lib.moe_sel_export_expert(ctx, int(expert), out["tern_gate"].ctypes.data, out["tern_up"].ctypes.data,
                                     out["alpha_gate"].ctypes.data, out["alpha_up"].ctypes.data,
-                                    out["down_norm"].ctypes.data, _host_ptr(out.get("p_bf16"), np.uint16),
+                                    out["down_norm"].ctypes.data, out["nnz_gate"].ctypes.data,
+                                    out["nnz_up"].ctypes.data, _host_ptr(out.get("p_bf16"), np.uint16),
                                     _host_ptr(out.get("q_bf16"), np.uint16))
     _check(st, "moe_sel_export_expert")
     return out
@@ -247,6 +254,32 @@ def moe_sel_device_bytes(ctx) -> int:
 
 def moe_sel_check_device(ctx):
     _check(_lib.moe_sel_check_device(ctx), "moe_sel_check_device")
+
+
+def moe_sel_set_wait_limit(ctx, polls: int):
+    _check(_lib.moe_sel_set_wait_limit(ctx, int(polls)), "moe_sel_set_wait_limit")
+
+
+def moe_sel_debug_silu(z, out, n, stream=None):
+    """out[i] = the pinned binary32 silu of z[i] (device fp32 arrays)."""
+    _check(_lib.moe_sel_debug_silu(_dev_ptr(z), _dev_ptr(out), int(n), _stream(stream)), "moe_sel_debug_silu")
+
+
+def moe_sel_debug_score(dot_gate, dot_up, xexp, stats, kind, h_hat, score, n, stream=None):
+    """Pinned score of n channels from their integer sketch dots (device arrays)."""
+    _check(_lib.moe_sel_debug_score(_dev_ptr(dot_gate), _dev_ptr(dot_up), _dev_ptr(xexp), _dev_ptr(stats), int(kind),
+                                    _dev_ptr(h_hat), _dev_ptr(score), int(n), _stream(stream)), "moe_sel_debug_score")
+
+
+def moe_sel_read_stream(buf, nbytes, sink, stream=None):
+    """Read every byte of a device buffer once (the measured read ceiling)."""
+    _check(_lib.moe_sel_read_stream(_dev_ptr(buf), int(nbytes), _dev_ptr(sink), _stream(stream)),
+           "moe_sel_read_stream")
+
+
+def moe_sel_debug_fail_alloc(nth: int):
+    """Make the nth allocation the library attempts from now on fail (0 disarms)."""
+    _check(_lib.moe_sel_debug_fail_alloc(int(nth)), "moe_sel_debug_fail_alloc")
 
 
 def moe_sel_set_path(ctx, path: int):

@@ -33,8 +33,10 @@ SOURCES = [
     ("lowrank_device.hip", DEVICE),
     ("sketch_device.hip", DEVICE),
     ("decode_glue.hip", DEVICE),
+    ("debug_device.hip", DEVICE),
     ("api.cpp", DEVICE),
     ("prepare_host.cpp", HOST_EXACT),
+    ("fault.cpp", HOST_EXACT),
 ]
 
 

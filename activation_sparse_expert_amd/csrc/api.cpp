@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -60,6 +61,7 @@ struct moe_sel_ctx {
   int fused_max_batch = 0;
   int num_cus = 0;
   int fused_bpc_sparse = 0, fused_bpc_dense = 0;
+  int spin_limit = moe_sel::kDefaultWaitPolls;
   moe_sel_path path = MOE_SEL_PATH_AUTO;
   moe_sel_score score_kind = MOE_SEL_SCORE_FULL;
   int last_path = -1;
@@ -94,7 +96,7 @@ template <typename T>
 moe_sel_status dev_alloc(moe_sel_ctx* c, T** p, size_t count) {
   const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
   void* q = nullptr;
-  const hipError_t e = hipMalloc(&q, bytes);
+  const hipError_t e = (hipError_t)moe_sel::checked_device_malloc(&q, bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(MOE_SEL_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
@@ -130,6 +132,7 @@ bool sketch_on_device() {
 
 struct PrepJob {
   const moe_sel_config* cfg;
+  std::atomic<bool>* out_of_memory;
   bool host_lowrank;
   bool host_sketch;
   const uint16_t *wg, *wu, *wd;
@@ -160,6 +163,7 @@ void prep_one(int e, void* arg) {
                                               j->wd + (size_t)e * md, out);
   } catch (const std::bad_alloc&) {
     (*j->errors)[e] = "host allocation failed";
+    j->out_of_memory->store(true);
   } catch (...) {
     (*j->errors)[e] = "unexpected exception";
   }
@@ -237,48 +241,59 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   return a;
 }
 
+// The single-launch plan of a call (block counts, chunking) with the context's
+// hand-off buffers, or false when the call cannot run as one launch (shape,
+// batch, or a grid that would not be resident all at once).
+bool plan_fused(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, moe_sel::FusedArgs* out) {
+  const int pairs = base.batch * base.top_e;
+  if (!c->fused_max_batch || base.batch > c->fused_max_batch ||
+      !moe_sel::fused_supported(base.d, base.m, base.r, base.top_e))
+    return false;
+  const int count = dense ? base.m : base.k;
+  int chunk = kMinChunk;
+  while (chunk < moe_sel::fused_max_chunk(dense) && (size_t)pairs * ((count + chunk - 1) / chunk) > (size_t)kTargetGather)
+    chunk *= 2;
+  moe_sel::FusedArgs f;
+  static_cast<moe_sel::FwdArgs&>(f) = base;
+  f.xscore = c->xscore;
+  f.zpart = c->zpart;
+  f.partial = c->partial;
+  f.zcopy = c->zcopy;
+  f.err = c->err;
+  f.spin_limit = c->spin_limit;
+  f.chunk = chunk;
+  f.nc = std::max(1, (count + chunk - 1) / chunk);
+  const bool zblocks = !dense && base.r > 0;
+  f.ncs = f.nc + (zblocks ? 1 : 0);
+  f.n_z = zblocks ? pairs : 0;
+  f.n_gather = pairs * f.nc;
+  f.n_combine = base.batch * (base.d / 32);
+  const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
+  const long capacity = (long)bpc * c->num_cus;
+  // score blocks of 32 channels spread the sketch over more CUs; 64 when that grid would not fit
+  f.score_ch = moe_sel::kFusedScoreChMin;
+  f.n_score = dense ? 0 : pairs * (base.m / f.score_ch);
+  if (!dense && ((long)f.n_score + f.n_gather + f.n_z + f.n_combine > capacity ||
+                 !moe_sel::fused_narrow_score_ok(base.m, base.r))) {
+    f.score_ch = 2 * moe_sel::kFusedScoreChMin;
+    f.n_score = pairs * (base.m / f.score_ch);
+  }
+  const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
+  if (total > capacity) return false;
+  *out = f;
+  return true;
+}
+
 // The single-launch path when its blocks all fit on the device at once, else
 // the one-kernel-per-phase path.
 // Returns hipErrorNotSupported when the single-launch path is required but cannot be used, or when the
 // multi-kernel path cannot run the call (int16 score activations without self-routing score blocks).
 hipError_t launch_any(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, hipStream_t stream) {
-  const int pairs = base.batch * base.top_e;
   const bool want_fused = c->path != MOE_SEL_PATH_MULTI_KERNEL && !force_multi_kernel();
-  if (want_fused && c->xscore && base.batch <= c->fused_max_batch &&
-      moe_sel::fused_supported(base.d, base.m, base.r, base.top_e)) {
-    const int count = dense ? base.m : base.k;
-    int chunk = kMinChunk;
-    while (chunk < moe_sel::fused_max_chunk(dense) && (size_t)pairs * ((count + chunk - 1) / chunk) > (size_t)kTargetGather)
-      chunk *= 2;
-    moe_sel::FusedArgs f;
-    static_cast<moe_sel::FwdArgs&>(f) = base;
-    f.xscore = c->xscore;
-    f.zpart = c->zpart;
-    f.partial = c->partial;
-    f.zcopy = c->zcopy;
-    f.err = c->err;
-    f.chunk = chunk;
-    f.nc = std::max(1, (count + chunk - 1) / chunk);
-    const bool zblocks = !dense && base.r > 0;
-    f.ncs = f.nc + (zblocks ? 1 : 0);
-    f.n_z = zblocks ? pairs : 0;
-    f.n_gather = pairs * f.nc;
-    f.n_combine = base.batch * (base.d / 32);
-    const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
-    const long capacity = (long)bpc * c->num_cus;
-    // score blocks of 32 channels spread the sketch over more CUs; 64 when that grid would not fit
-    f.score_ch = moe_sel::kFusedScoreChMin;
-    f.n_score = dense ? 0 : pairs * (base.m / f.score_ch);
-    if (!dense && ((long)f.n_score + f.n_gather + f.n_z + f.n_combine > capacity ||
-                   !moe_sel::fused_narrow_score_ok(base.m, base.r))) {
-      f.score_ch = 2 * moe_sel::kFusedScoreChMin;
-      f.n_score = pairs * (base.m / f.score_ch);
-    }
-    const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
-    if (total <= capacity) {
-      c->last_path = MOE_SEL_PATH_SINGLE_LAUNCH;
-      return moe_sel::launch_fused(f, dense, stream);
-    }
+  moe_sel::FusedArgs f;
+  if (want_fused && c->xscore && plan_fused(c, base, dense, &f)) {
+    c->last_path = MOE_SEL_PATH_SINGLE_LAUNCH;
+    return moe_sel::launch_fused(f, dense, stream);
   }
   if (c->path == MOE_SEL_PATH_SINGLE_LAUNCH) return hipErrorNotSupported;
   c->last_path = MOE_SEL_PATH_MULTI_KERNEL;
@@ -315,6 +330,11 @@ struct DeviceGuard {
 }  // namespace
 
 namespace moe_sel {
+
+int checked_device_malloc(void** p, size_t bytes) {
+  if (alloc_fault_hit()) return (int)hipErrorOutOfMemory;
+  return (int)hipMalloc(p, bytes);
+}
 
 std::string validate_config(const moe_sel_config* c) {
   if (!c) return "config is null";
@@ -567,6 +587,7 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
   std::vector<float> h_stats;
   std::vector<uint16_t> h_wch, h_p, h_q;
   try {
+    if (moe_sel::alloc_fault_hit()) throw std::bad_alloc();
     if (!dev_sketch) {
       h_codes.resize(n_codes);
       h_stats.resize(E * m * 4);
@@ -579,14 +600,15 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
   }
   std::vector<std::string> errors(E);
+  std::atomic<bool> out_of_memory{false};
   const bool dev_lowrank = lowrank_on_device(c);
-  PrepJob job{&c,           !dev_lowrank, !dev_sketch, w_gate,   w_up,     w_down,
+  PrepJob job{&c,           &out_of_memory, !dev_lowrank, !dev_sketch, w_gate,     w_up,       w_down,
               h_codes.data(), h_stats.data(), h_wch.data(), h_p.data(), h_q.data(), &errors};
   moe_sel::parallel_for((int)E, 0, prep_one, &job);
   for (size_t e = 0; e < E; ++e)
     if (!errors[e].empty()) {
       free_ctx(ctx);
-      return fail(MOE_SEL_EINVAL, "expert " + std::to_string(e) + ": " + errors[e]);
+      return fail(out_of_memory.load() ? MOE_SEL_ENOMEM : MOE_SEL_EINVAL, "expert " + std::to_string(e) + ": " + errors[e]);
     }
   st = alloc_layer(ctx);
   if (st != MOE_SEL_OK) {
@@ -617,11 +639,15 @@ moe_sel_status moe_sel_prepare(const moe_sel_config* cfg, const uint16_t* w_gate
     }
     if (ui == 3 && dev_lowrank) {
       // maps from the channel rows now on the device
-      const std::string err = moe_sel::lowrank_maps_device(ctx->wch, c.n_experts, c.d, c.m, c.rank, h_p.data(),
-                                                           h_q.data(), s);
+      std::string err;
+      try {
+        err = moe_sel::lowrank_maps_device(ctx->wch, c.n_experts, c.d, c.m, c.rank, h_p.data(), h_q.data(), s);
+      } catch (const std::bad_alloc&) {
+        err = std::string(moe_sel::kNoDeviceMemory) + "host staging of the low-rank maps";
+      }
       if (!err.empty()) {
         free_ctx(ctx);
-        return fail(MOE_SEL_EDEVICE, err);
+        return fail(err.rfind(moe_sel::kNoDeviceMemory, 0) == 0 ? MOE_SEL_ENOMEM : MOE_SEL_EDEVICE, err);
       }
     }
     he = hipMemcpyAsync(u.dst, u.src, u.bytes, hipMemcpyHostToDevice, s);
@@ -647,6 +673,7 @@ moe_sel_status moe_sel_save(const moe_sel_ctx* ctx, const char* path) {
   prepared_arrays(ctx, arr);
   std::vector<unsigned char> stage;
   try {
+    if (moe_sel::alloc_fault_hit()) throw std::bad_alloc();
     stage.resize(kStage);
   } catch (...) {
     return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
@@ -718,6 +745,7 @@ moe_sel_status moe_sel_load(const char* path, void* stream, moe_sel_ctx** out) {
   prepared_arrays(ctx, arr);
   std::vector<unsigned char> stage;
   if (st == MOE_SEL_OK) try {
+      if (moe_sel::alloc_fault_hit()) throw std::bad_alloc();
       stage.resize(kStage);
     } catch (...) {
       st = fail(MOE_SEL_ENOMEM, "host staging allocation failed");
@@ -827,8 +855,8 @@ moe_sel_status moe_sel_debug_selection(moe_sel_ctx* ctx, int32_t* expert_ids, fl
 }
 
 moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert, int8_t* tern_gate, int8_t* tern_up,
-                                     float* alpha_gate, float* alpha_up, float* down_norm, uint16_t* p_bf16,
-                                     uint16_t* q_bf16) {
+                                     float* alpha_gate, float* alpha_up, float* down_norm, int32_t* nnz_gate,
+                                     int32_t* nnz_up, uint16_t* p_bf16, uint16_t* q_bf16) {
   g_last_error.clear();
   if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
   if (expert < 0 || expert >= ctx->cfg.n_experts) return fail(MOE_SEL_EINVAL, "expert out of range");
@@ -836,21 +864,31 @@ moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert, int8_t* t
   const int d = ctx->cfg.d, m = ctx->cfg.m, r = ctx->cfg.rank;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-  if (tern_gate || tern_up) {
+  if (tern_gate || tern_up || nnz_gate || nnz_up) {
     const size_t nd = moe_sel::codes_dwords_per_expert(d, m);
-    std::vector<uint32_t> codes(nd);
+    std::vector<uint32_t> codes;
+    try {
+      codes.resize(nd);
+    } catch (const std::bad_alloc&) {
+      return fail(MOE_SEL_ENOMEM, "host staging allocation failed");
+    }
     if ((e = hipMemcpy(codes.data(), ctx->codes + (size_t)expert * nd, nd * 4, hipMemcpyDeviceToHost)) != hipSuccess)
       return hip_fail(e, "hipMemcpy");
     for (int j = 0; j < m; ++j)
       for (int mat = 0; mat < 2; ++mat) {
         int8_t* dst = mat == 0 ? tern_gate : tern_up;
-        if (!dst) continue;
+        int32_t* nnz = mat == 0 ? nnz_gate : nnz_up;
+        if (!dst && !nnz) continue;
+        int32_t kept = 0;
         for (int i = 0; i < d; ++i) {
           const int b = i / moe_sel::kBlock, w = (i % moe_sel::kBlock) / 16, a = (i % 16) / 4, ii = i % 4;
           const uint32_t word = codes[moe_sel::codes_dword_index(d, m, j / moe_sel::kGroup, mat, b,
                                                                  j % moe_sel::kGroup, w)];
-          dst[(size_t)j * d + i] = (int8_t)((int)((word >> (8 * ii + 2 * a)) & 3u) - 1);
+          const int t = (int)((word >> (8 * ii + 2 * a)) & 3u) - 1;
+          kept += t != 0;
+          if (dst) dst[(size_t)j * d + i] = (int8_t)t;
         }
+        if (nnz) nnz[j] = kept;
       }
   }
   if (alpha_gate || alpha_up || down_norm) {
@@ -890,6 +928,14 @@ moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx) {
   (void)hipDeviceSynchronize();
   return fail(MOE_SEL_EDEVICE, "a cross-block wait timed out (bits " + std::to_string(bits) +
                                    "); outputs of the affected calls are invalid");
+}
+
+moe_sel_status moe_sel_set_wait_limit(moe_sel_ctx* ctx, int32_t polls) {
+  g_last_error.clear();
+  if (!ctx) return fail(MOE_SEL_EINVAL, "ctx is null");
+  if (polls < 0 || polls > (1 << 30)) return fail(MOE_SEL_EINVAL, "polls must be in [0, 2^30]");
+  ctx->spin_limit = polls;
+  return MOE_SEL_OK;
 }
 
 moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path) {
@@ -969,6 +1015,50 @@ moe_sel_status moe_sel_residual_rmsnorm_router(const uint16_t* x, const uint16_t
   const hipError_t e =
       moe_sel::launch_resnorm_router(x, y, w_router, batch, d, n_experts, eps, x_out, logits, (hipStream_t)stream);
   return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
+moe_sel_status moe_sel_debug_silu(const float* z, float* out, int64_t n, void* stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(MOE_SEL_EINVAL, "n must be non-negative");
+  if (n == 0) return MOE_SEL_OK;
+  if (!z || !out) return fail(MOE_SEL_EINVAL, "z and out must be non-null");
+  if (((uintptr_t)z & 3u) || ((uintptr_t)out & 3u)) return fail(MOE_SEL_EINVAL, "z and out must be 4-byte aligned");
+  const hipError_t e = moe_sel::launch_debug_silu(z, out, n, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
+moe_sel_status moe_sel_debug_score(const int32_t* dot_gate, const int32_t* dot_up, const int32_t* xexp,
+                                   const float* stats, moe_sel_score kind, float* h_hat, float* score, int64_t n,
+                                   void* stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(MOE_SEL_EINVAL, "n must be non-negative");
+  if (kind != MOE_SEL_SCORE_FULL && kind != MOE_SEL_SCORE_GATE_ONLY && kind != MOE_SEL_SCORE_NO_DOWN_NORM &&
+      kind != MOE_SEL_SCORE_X_INT16)
+    return fail(MOE_SEL_EINVAL, "unknown score kind");
+  if (n == 0) return MOE_SEL_OK;
+  if (!dot_gate || !dot_up || !xexp || !stats || !h_hat || !score)
+    return fail(MOE_SEL_EINVAL, "every array must be non-null");
+  if (!aligned16(stats)) return fail(MOE_SEL_EINVAL, "stats must be 16-byte aligned");
+  const hipError_t e = moe_sel::launch_debug_score(dot_gate, dot_up, xexp, (const float4*)stats, (int)kind, h_hat,
+                                                   score, n, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
+moe_sel_status moe_sel_read_stream(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  if (!buf || !sink) return fail(MOE_SEL_EINVAL, "buf and sink must be non-null");
+  if (!aligned16(buf) || bytes % 16) return fail(MOE_SEL_EINVAL, "buf must be 16-byte aligned and bytes a multiple of 16");
+  if (((uintptr_t)sink & 3u)) return fail(MOE_SEL_EINVAL, "sink must be 4-byte aligned");
+  if (bytes == 0) return MOE_SEL_OK;
+  const hipError_t e = moe_sel::launch_read_stream(buf, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SEL_OK : hip_fail(e, "kernel launch");
+}
+
+moe_sel_status moe_sel_debug_fail_alloc(int32_t nth) {
+  g_last_error.clear();
+  if (nth < 0) return fail(MOE_SEL_EINVAL, "nth must be non-negative");
+  moe_sel::arm_alloc_fault(nth);
+  return MOE_SEL_OK;
 }
 
 }  // extern "C"

@@ -106,6 +106,7 @@ __device__ __forceinline__ void axpy8_bf16(float a, uint4 w, float* y) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16_dev(float v) {
   uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // a NaN stays a (quiet) NaN
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
@@ -623,6 +624,9 @@ __device__ __forceinline__ int block_topk_select_strided(const uint32_t (&key)[K
   const int krem = k - s_hist[1];
   const int ncand = s_hist[2];
   bool take[KPT];
+  // the radix fallback clears s_hist; every thread has read the three words
+  // above before it passes this barrier (the candidate branch writes no s_hist)
+  if (ncand > kThreads) __syncthreads();
   if (ncand <= kThreads) {
     uint64_t* ck = (uint64_t*)s_cand;  // order keys of the bucket's keys
 #pragma unroll
@@ -692,11 +696,10 @@ __device__ __forceinline__ int block_topk_select_strided(const uint32_t (&key)[K
 // The single-launch kernel polls the data itself: a slot holds an empty
 // sentinel until its producer's coherent store lands, its one consumer polls
 // it with coherent loads and writes the sentinel back, so every call and
-// every HIP-graph replay starts from empty slots. Waits are bounded by
-// kSpinLimit polls; on time-out an error bit is set and the block proceeds.
+// every HIP-graph replay starts from empty slots. Waits are bounded (a poll
+// count the host sets); a wait that gives up sets an error bit and turns the
+// results it feeds into NaN, and the block proceeds.
 // ---------------------------------------------------------------------------
-constexpr int kSpinLimit = 1 << 21;
-
 __device__ __forceinline__ void st_coh(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -709,6 +712,9 @@ __device__ __forceinline__ void st_coh2(float* p, float a, float b) {
 }
 __device__ __forceinline__ float ld_coh(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dev

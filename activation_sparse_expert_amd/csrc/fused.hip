@@ -87,15 +87,19 @@ __device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ void clear_coh(float* p) { st_coh(p, __uint_as_float(kEmpty)); }
 
-// one bounded wait step; returns false once the spin budget is exhausted
-__device__ __forceinline__ bool keep_polling(int& spins, int* err, int bit) {
-  if (++spins > kSpinLimit) {
-    if (threadIdx.x == 0) atomicOr(err, bit);
-    return false;
-  }
-  __builtin_amdgcn_s_sleep(2);
-  return true;
+// Bounded waits: a wait loop calls spent() before each poll round and gives up
+// once `limit` rounds have been polled (at once for limit 0). The decision is
+// uniform over the threads that wait together. gave_up() records it: lane 0 of
+// every wave that gave up sets the error bit.
+__device__ __forceinline__ bool spent(int& spins, int limit) {
+  if (spins >= limit) return true;
+  if (spins++ > 0) __builtin_amdgcn_s_sleep(2);
+  return false;
 }
+__device__ __forceinline__ void gave_up(int* err, int bit) {
+  if ((threadIdx.x & 63) == 0) atomicOr(err, bit);
+}
+constexpr float kPoison = __builtin_nanf("");
 
 template <int SLOTS>
 __device__ __forceinline__ void load_x(const uint16_t* x, int d, uint4 (&xv)[SLOTS]) {
@@ -311,7 +315,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
 // selected channels ascending in s_sel[0..k), the sketch activations in s_hh,
 // the zpart values in s_zp. Chunk 0 also records the selection for inspection.
 template <int MK>  // key slots per thread: m <= MK * kThreads
-__device__ __forceinline__ void gather_select_mk(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
+__device__ __forceinline__ bool gather_select_mk(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
                                                  float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
                                                  float* s_zp) {
   const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
@@ -334,7 +338,12 @@ __device__ __forceinline__ void gather_select_mk(const FusedArgs& a, int p, int 
     if (tid + u * kThreads < nzp) pending |= 1u << (16 + u);
   }
   int spins = 0;
+  bool bad = false;
   while (true) {
+    if (spent(spins, a.spin_limit)) {
+      bad = true;
+      break;
+    }
 #pragma unroll
     for (int u = 0; u < MK; ++u)
       if ((pending >> u) & 1) v[u] = ld_coh64(slots + tid + u * kThreads);
@@ -348,7 +357,15 @@ __device__ __forceinline__ void gather_select_mk(const FusedArgs& a, int p, int 
     for (int u = 0; u < kMaxZPart; ++u)
       if (!empty(zv[u])) pending &= ~(1u << (16 + u));
     if (__syncthreads_and(pending == 0)) break;
-    if (!keep_polling(spins, a.err, 1)) break;
+  }
+  if (bad) {
+    // slots still empty after giving up hold no score: rank them as 0 (the
+    // sentinel's key bits would index past the select's histogram) with a NaN
+    // sketch activation; the caller poisons what it publishes
+    gave_up(a.err, 1);
+#pragma unroll
+    for (int u = 0; u < MK; ++u)
+      if ((uint32_t)v[u] == kEmpty) v[u] = (uint64_t)__float_as_uint(kPoison) << 32;
   }
 #pragma unroll
   for (int u = 0; u < MK; ++u) {
@@ -388,14 +405,16 @@ __device__ __forceinline__ void gather_select_mk(const FusedArgs& a, int p, int 
   }
   if (c == 0)
     for (int i = tid; i < k; i += kThreads) a.sel_idx[(size_t)p * m + i] = s_sel[i];  // for inspection only
+  return bad;
 }
 
 // The select with as few key slots per thread as m allows (4 covers m <= 1024).
-__device__ __forceinline__ void gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
+// Returns true when the wait for the scores gave up.
+__device__ __forceinline__ bool gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
                                               float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
                                               float* s_zp) {
-  if (a.m <= 4 * kThreads) gather_select_mk<4>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
-  else gather_select_mk<kMaxKeysPer>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  if (a.m <= 4 * kThreads) return gather_select_mk<4>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  return gather_select_mk<kMaxKeysPer>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
 }
 
 template <bool DENSE, int SLOTS>
@@ -427,7 +446,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
   const int first = c * C;
   int mine = count - first;
   mine = mine < 0 ? 0 : (mine > C ? C : mine);
-  if (!DENSE) gather_select(a, p, c, false, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const bool bad = DENSE ? false : gather_select(a, p, c, false, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int e = sm.ids[slot];
   const float wp = sm.w[slot];
   if (!DENSE && c == 0 && tid == 0) {  // routing and selection of the pair, for inspection
@@ -519,6 +538,11 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
       for (int s = 0; s < SLOTS; ++s) axpy8_bf16(h, dv[i][s], yacc[s]);
     }
   }
+  if (bad)  // the selection came from incomplete scores: publish NaN
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) yacc[u][q] = kPoison;
   // ---- result: down partial (slice-major [t][slice][producer][64])
   const int slices = d / 64;
   const int qt = a.top_e * a.nc;
@@ -573,7 +597,7 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
     }
     if (a.k < 0 && tid == 0) a.err[0] = (int)acc;
   }
-  gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const bool bad = gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
   const int count = a.k;
   // thread t owns 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass
   float zacc[8];
@@ -607,7 +631,7 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
     float z = 0.0f;
 #pragma unroll 8
     for (int th = tid >> 3; th < kThreads; th += cgs) z += s_zr[th * 8 + (tid & 7)];
-    s_zc[tid] = z;
+    s_zc[tid] = bad ? kPoison : z;
   }
   __syncthreads();
   const int slices = d / 64;
@@ -635,6 +659,9 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
   float* s_z = s_red + kThreads * 8;          // top_e x r
   float* s_y = s_z + 256;                     // 8 x 32
 
+  // an earlier wait on this context gave up: its late stores may sit in slots
+  // that this call reads, so the output is NaN until the host clears the error
+  const bool poisoned = ld_coh(a.err) != 0;
   route(a, t, sm);
   // prefetch P[e][c][32 elements] for the token's experts: top_e * r rows of 64 bytes
   const int npieces = a.top_e * r * 4;
@@ -657,12 +684,16 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
     float z = 0.0f;
     bool zpend = zthread;
     while (true) {
+      if (spent(spins, a.spin_limit)) {
+        gave_up(a.err, 2);
+        z = kPoison;
+        break;
+      }
       if (zpend) {
         z = ld_coh(zsrc + tid);
         if (!empty(z)) zpend = false;
       }
       if (__all(!zpend)) break;
-      if (!keep_polling(spins, a.err, 2)) break;
     }
     if (zthread) {
       s_z[tid] = z;
@@ -706,6 +737,11 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
       if (base + pg + 8 * u < qt) pending |= 1u << u;
     }
     while (true) {
+      if (spent(spins, a.spin_limit)) {
+        gave_up(a.err, 2);
+        y = kPoison;
+        break;
+      }
 #pragma unroll
       for (int u = 0; u < kCombPer; ++u)
         if ((pending >> u) & 1) v[u] = ld_coh(bsrc + (size_t)u * 512);
@@ -713,7 +749,6 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
       for (int u = 0; u < kCombPer; ++u)
         if (!empty(v[u])) pending &= ~(1u << u);
       if (__all(pending == 0)) break;
-      if (!keep_polling(spins, a.err, 2)) break;
     }
 #pragma unroll
     for (int u = 0; u < kCombPer; ++u) {
@@ -729,7 +764,7 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
     float o = 0.0f;
 #pragma unroll
     for (int g = 0; g < 8; ++g) o += s_y[g * 32 + tid];
-    a.out[(size_t)t * d + 64 * sl + 32 * hf + tid] = f32_to_bf16_dev(o);
+    a.out[(size_t)t * d + 64 * sl + 32 * hf + tid] = f32_to_bf16_dev(poisoned ? kPoison : o);
   }
 }
 

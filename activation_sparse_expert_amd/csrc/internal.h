@@ -96,6 +96,17 @@ std::string validate_config(const moe_sel_config* cfg);
 uint16_t f32_to_bf16(float v);
 float bf16_to_f32(uint16_t b);
 
+// Allocation fault injection for tests of the out-of-memory paths: once armed
+// with n >= 1, the n-th allocation the library attempts after that fails (and
+// the injector disarms). Host allocations throw std::bad_alloc there; device
+// allocations return hipErrorOutOfMemory (checked_device_malloc).
+void arm_alloc_fault(int n);
+bool alloc_fault_hit();
+// hipMalloc behind the fault injector.
+int checked_device_malloc(void** p, size_t bytes);  // a hipError_t value
+// Message prefix of a device workspace that could not be allocated.
+constexpr const char* kNoDeviceMemory = "out of device memory: ";
+
 // Run fn(i) for i in [0, n) on up to `threads` host threads (0 = all cores).
 void parallel_for(int n, int threads, void (*fn)(int, void*), void* arg);
 

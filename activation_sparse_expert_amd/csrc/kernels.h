@@ -89,7 +89,9 @@ struct FusedArgs : FwdArgs {
   float* zpart;      // [P][m/score_ch][r] each score block's share of Q^T h_hat, for the z block
   float* partial;    // [B][d/64][top_e*nc][64] gate-weighted down partials, for combine
   float* zcopy;      // [B][d/32][top_e][r] z of each routed pair, for each combine block
-  int* err;          // error bits (1: gather wait timed out, 2: combine wait timed out)
+  int* err;          // error bits (1: gather wait timed out, 2: combine wait timed out); sticky until
+                     // the host clears them, and while set every combine block writes NaN
+  int spin_limit;    // polls before a cross-block wait gives up (0: every wait gives up at once)
   int n_score, n_gather, n_z, n_combine;
   int nc;            // gather blocks per pair
   int ncs;           // consumer slots per pair: the gather blocks, then the z block (if any)
@@ -104,6 +106,15 @@ bool fused_narrow_score_ok(int m, int r);  // kFusedScoreChMin-channel score blo
 size_t fused_lds_bytes(int d, int m, int r);
 int fused_blocks_per_cu(bool dense, int d, int m, int r);
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream);
+
+// polls before a cross-block wait of the single-launch kernel gives up, unless the host sets another limit
+constexpr int kDefaultWaitPolls = 1 << 21;
+
+// Inspection and measurement kernels (debug_device.hip)
+hipError_t launch_debug_silu(const float* z, float* out, int64_t n, hipStream_t s);
+hipError_t launch_debug_score(const int32_t* dg, const int32_t* du, const int32_t* xexp, const float4* stats,
+                              int kind, float* h, float* score, int64_t n, hipStream_t s);
+hipError_t launch_read_stream(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 
 // Decode-step glue (decode_glue.hip)
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int batch, int d, int n_experts, float* logits,

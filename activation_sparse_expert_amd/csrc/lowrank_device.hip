@@ -233,16 +233,17 @@ std::string lowrank_maps_device(const uint16_t* wch_dev, int n_experts, int d, i
   // experts per batch: at most 1 GiB of fp64 matrices
   const int nb = (int)std::max<size_t>(1, std::min<size_t>((size_t)n_experts, ((size_t)1 << 30) / (nn * 8)));
   DevBuf bA, bp, bw, boff, bbeta, bU, bout;
-  hipError_t e = hipMalloc(&bA.p, (size_t)nb * nn * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&bp.p, (size_t)nb * n * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&bw.p, (size_t)nb * n * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&boff.p, (size_t)nb * n * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&bbeta.p, (size_t)nb * n * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&bU.p, (size_t)nb * n * r * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&bout.p, (size_t)nb * other * r * sizeof(double));
+  auto dmalloc = [](void** q, size_t bytes) { return (hipError_t)checked_device_malloc(q, bytes); };
+  hipError_t e = dmalloc(&bA.p, (size_t)nb * nn * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&bp.p, (size_t)nb * n * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&bw.p, (size_t)nb * n * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&boff.p, (size_t)nb * n * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&bbeta.p, (size_t)nb * n * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&bU.p, (size_t)nb * n * r * sizeof(double));
+  if (e == hipSuccess) e = dmalloc(&bout.p, (size_t)nb * other * r * sizeof(double));
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return std::string("device low-rank workspace: ") + hipGetErrorString(e);
+    return std::string(kNoDeviceMemory) + "low-rank workspace: " + hipGetErrorString(e);
   }
   double* A = (double*)bA.p;
   double* p = (double*)bp.p;

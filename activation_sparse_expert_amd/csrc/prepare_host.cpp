@@ -15,6 +15,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <new>
 #include <thread>
 #include <vector>
 
@@ -439,6 +440,7 @@ void lowrank_map(const uint16_t* wd_bits, int d, int m, int r, uint16_t* p_out, 
 
 std::string prepare_expert(const moe_sel_config& cfg, const uint16_t* w_gate, const uint16_t* w_up,
                            const uint16_t* w_down, const ExpertPrep& out) {
+  if (alloc_fault_hit()) throw std::bad_alloc();  // stands for the scratch vectors below
   const int d = cfg.d, m = cfg.m, r = cfg.rank;
   for (size_t i = 0, n = (size_t)m * d; i < n; ++i)
     if (((w_gate[i] >> 7) & 0xFF) == 0xFF || ((w_up[i] >> 7) & 0xFF) == 0xFF || ((w_down[i] >> 7) & 0xFF) == 0xFF)

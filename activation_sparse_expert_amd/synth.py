@@ -118,17 +118,32 @@ def tokens(wid: int, layer: int, batch: int, d: int, index: int = 0) -> np.ndarr
 
 
 def router_logits(wid: int, layer: int, batch: int, n_experts: int,
-                  kind: str = "normal", index: int = 0) -> np.ndarray:
+                  kind: str = "normal", index: int = 0, group: int = 0, group_size: int = 0) -> np.ndarray:
     """Router logits, float32 ``[B][E]``.
 
     ``normal``: iid N(0, 1).
     ``zipf``: expert popularity p_e proportional to rank^-1.1 over a seeded random
     ranking of the experts; logit = log p_e + Gumbel(0, 1) noise, so taking the
     top experts of a row samples experts without replacement in proportion to p.
+    ``disjoint``: iid N(0, 1), then the experts of group ``group`` (members
+    group * group_size .. + group_size - 1 of a seeded permutation of the
+    experts) are lifted by a common shift that puts them above every other
+    expert. Calls with different groups route to disjoint expert sets; the gate
+    weights (a softmax over the chosen logits) are those of N(0, 1) logits.
     """
     rng = _rng(wid, layer, T_LOGITS, index)
     if kind == "normal":
         return rng.standard_normal((batch, n_experts), dtype=np.float32)
+    if kind == "disjoint":
+        lg = rng.standard_normal((batch, n_experts), dtype=np.float32)
+        perm = _rng(wid, layer, T_PERM, 0).permutation(n_experts)
+        chosen = perm[group * group_size:(group + 1) * group_size]
+        assert chosen.size == group_size > 0, "group out of range"
+        rest = np.setdiff1d(np.arange(n_experts), chosen)
+        for t in range(batch):
+            lift = (lg[t, rest].max() if rest.size else np.float32(0)) - lg[t, chosen].min() + np.float32(1)
+            lg[t, chosen] += np.float32(max(lift, 0))
+        return lg
     if kind == "zipf":
         perm = _rng(wid, layer, T_PERM, 0).permutation(n_experts)
         rank = np.empty(n_experts, np.int64)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_SEL_ABI_VERSION 1
+#define MOE_SEL_ABI_VERSION 2
 
 typedef struct moe_sel_ctx moe_sel_ctx;
 
@@ -224,27 +224,48 @@ moe_sel_status moe_sel_debug_selection(moe_sel_ctx* ctx, int32_t* expert_ids, fl
 
 /*
  * Read back what moe_sel_prepare stored for one expert (synchronous, host
- * buffers, same layouts and nullability as moe_sel_prepare_expert_host).
- * Errors: EINVAL (null ctx, expert out of range), EDEVICE.
+ * buffers, same layouts and nullability as moe_sel_prepare_expert_host): the
+ * ternary sketch ("A reader built from weights alone") with its kept-entry
+ * counts nnz_gate / nnz_up [m] (counted from the stored codes), the channel
+ * statistics and the rank-r maps.
+ * Errors: EINVAL (null ctx, expert out of range), ENOMEM, EDEVICE.
  */
 moe_sel_status moe_sel_export_expert(moe_sel_ctx* ctx, int32_t expert,
                                      int8_t* tern_gate, int8_t* tern_up,
                                      float* alpha_gate, float* alpha_up, float* down_norm,
+                                     int32_t* nnz_gate, int32_t* nnz_up,
                                      uint16_t* p_bf16, uint16_t* q_bf16);
 
 /*
  * Synchronise the device and report whether any enqueued call on this context
- * hit a bounded cross-workgroup wait that expired (single-launch path). Such a
- * call's output is invalid; the context's hand-off state is reset so later
- * calls are unaffected. Errors: EINVAL (null ctx), EDEVICE (time-out or HIP error).
+ * hit a bounded cross-workgroup wait that gave up (single-launch path). Such a
+ * call writes NaN to the outputs of the tokens it could not finish, and from
+ * then on every single-launch call on the context writes NaN to all of its
+ * outputs (a producer that was waited for may still store into the context's
+ * hand-off slots), until this function clears the error and resets the
+ * hand-off state. Callers that run many forward calls back to back (a timed
+ * region, a captured graph) should call it after them.
+ * Errors: EINVAL (null ctx), EDEVICE (a wait gave up, or a HIP error).
  */
 moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx);
 
 /*
+ * Polls a cross-workgroup wait of the single-launch path makes before it gives
+ * up (default 2^21, about a second). polls = 0 makes every wait give up at
+ * once, so that the failure handling can be tested with every kernel still
+ * finishing normally. Errors: EINVAL (null ctx, polls outside [0, 2^30]).
+ */
+moe_sel_status moe_sel_set_wait_limit(moe_sel_ctx* ctx, int32_t polls);
+
+/*
  * Choose the execution path of later forward calls on this context (default
  * MOE_SEL_PATH_AUTO). The single-launch path needs d <= 4096, m <= 4096,
- * top_e * rank <= 256, rank dividing 256 and a multiple of 8, batch <= 8, and all of its workgroups
- * resident at once.
+ * top_e * rank <= 256, rank dividing 256 and a multiple of 8, batch <= 8, and
+ * every workgroup of its grid resident at once (the grid grows with batch *
+ * top_e; the occupancy query decides). For the Qwen3-30B-A3B shape (d = 2048,
+ * 128 experts, top-8, m = 768, r = 32) on a 256-CU MI355X that holds for batch
+ * <= 2; larger batches run the multi-kernel path, and a forced single launch
+ * there fails with EUNSUPPORTED.
  * Errors: EINVAL (null ctx or unknown path).
  */
 moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path);
@@ -356,6 +377,42 @@ moe_sel_status moe_sel_residual_rmsnorm(const uint16_t* x, const uint16_t* y, in
 moe_sel_status moe_sel_residual_rmsnorm_router(const uint16_t* x, const uint16_t* y, const uint16_t* w_router,
                                                int32_t batch, int32_t d, int32_t n_experts, float eps,
                                                uint16_t* x_out, float* logits, void* stream);
+
+/*
+ * Inspection and measurement entry points.
+ *
+ * moe_sel_debug_silu: out[i] = silu_pinned(z[i]), the binary32 silu inside the
+ * channel score (the score formula at the top of this header), evaluated by
+ * the same device function the forward kernels use, so a test can compare it
+ * bit for bit with another implementation.
+ *   z, out  [n] fp32, device, 4-byte aligned; n >= 0.
+ * moe_sel_debug_score: the pinned score of n channels from given exact
+ * integer sketch dots: G = alpha_g * dot_gate * 2^xexp, U = alpha_u * dot_up *
+ * 2^xexp, h_hat = silu_pinned(G) * U, score per `kind` (moe_sel_set_score).
+ *   dot_gate, dot_up, xexp [n] int32; stats [n][4] fp32 {alpha_g, alpha_u,
+ *   ||down column||, unused}, 16-byte aligned; h_hat, score [n] fp32; device.
+ * moe_sel_read_stream: reads every byte of buf once with 16-byte loads and
+ * folds them into *sink (device), so that timing it gives the device's
+ * measured HBM read bandwidth, the ceiling the forward's bytes are set against.
+ *   buf device, 16-byte aligned; bytes a multiple of 16.
+ * All three are asynchronous on stream. Errors: EINVAL (checked before
+ * enqueueing), EDEVICE.
+ */
+moe_sel_status moe_sel_debug_silu(const float* z, float* out, int64_t n, void* stream);
+moe_sel_status moe_sel_debug_score(const int32_t* dot_gate, const int32_t* dot_up, const int32_t* xexp,
+                                   const float* stats, moe_sel_score kind, float* h_hat, float* score,
+                                   int64_t n, void* stream);
+moe_sel_status moe_sel_read_stream(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * Allocation fault injection, for tests of the out-of-memory paths: with
+ * nth >= 1, the nth host or device allocation this library attempts from now
+ * on (in any thread) fails as if memory were exhausted, and the injector
+ * disarms; nth = 0 disarms it. The entry point that hits it returns
+ * MOE_SEL_ENOMEM and frees everything it had allocated.
+ * Errors: EINVAL (nth < 0).
+ */
+moe_sel_status moe_sel_debug_fail_alloc(int32_t nth);
 
 #ifdef __cplusplus
 }

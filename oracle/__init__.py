@@ -15,12 +15,14 @@ from .moe_oracle import (  # noqa: F401
     compensation,
     expert_swiglu_selected,
     f64_to_bf16_bits,
+    preacts_from_dots,
     prepare_expert,
     quantize_token,
     residual_rmsnorm,
     route,
     router_logits,
     score_channels,
+    score_from_preacts,
     select_threshold,
     select_topk,
     silu_pinned,

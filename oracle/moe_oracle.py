@@ -232,8 +232,15 @@ def sketch_preacts(prep: dict, q: np.ndarray, e: int):
     """
     dg = prep["tern_g"].astype(np.int64) @ q
     du = prep["tern_u"].astype(np.int64) @ q
-    g = np.ldexp(prep["alpha_g"].astype(F32) * dg.astype(F32), e).astype(F32)
-    u = np.ldexp(prep["alpha_u"].astype(F32) * du.astype(F32), e).astype(F32)
+    return preacts_from_dots(dg, du, e, prep["alpha_g"], prep["alpha_u"])
+
+
+def preacts_from_dots(dg, du, e, alpha_g, alpha_u):
+    """G_hat = binary32(alpha_g * binary32(dg)) * 2^e and likewise U_hat, from the
+    exact integer sketch dots (the second half of ``sketch_preacts``); ``e`` may be
+    a scalar or one exponent per entry."""
+    g = np.ldexp(np.asarray(alpha_g, F32) * np.asarray(dg).astype(F32), e).astype(F32)
+    u = np.ldexp(np.asarray(alpha_u, F32) * np.asarray(du).astype(F32), e).astype(F32)
     return g, u
 
 
@@ -256,12 +263,21 @@ def score_channels(prep: dict, q: np.ndarray, e: int, kind: str = "full"):
     Returns (h_hat float32 [m], score float32 [m]).
     """
     g, u = sketch_preacts(prep, q, e)
+    return score_from_preacts(g, u, prep["c"], kind)
+
+
+def score_from_preacts(g: np.ndarray, u: np.ndarray, c: np.ndarray, kind: str = "full"):
+    """The score's binary32 arithmetic after the sketch pre-activations (the
+    second half of ``score_channels``): h_hat = silu_pinned(G_hat) * U_hat and the
+    score of the given kind from h_hat and the down-column norms c.
+    Returns (h_hat float32, score float32)."""
     sg = silu_pinned(g)
-    h = (sg * u).astype(F32)
+    h = (sg * np.asarray(u, F32)).astype(F32)
+    c = np.asarray(c, F32)
     if kind in ("full", "x_int16"):
-        score = (np.abs(h) * prep["c"].astype(F32)).astype(F32)
+        score = (np.abs(h) * c).astype(F32)
     elif kind == "gate_only":
-        score = (np.abs(sg) * prep["c"].astype(F32)).astype(F32)
+        score = (np.abs(sg) * c).astype(F32)
     elif kind == "no_down_norm":
         score = np.abs(h).astype(F32)
     else:

@@ -35,7 +35,41 @@ def test_header_declarations_are_exported():
     for name in declared:
         assert hasattr(lib, name), name
     assert declared <= set(b.EXPORTED)
-    assert b.moe_sel_abi_version() == 1
+    assert b.moe_sel_abi_version() == 2
+
+
+def test_allocation_fault_injection_host():
+    """The armed allocation fails with ENOMEM, once; the next call succeeds."""
+    cfg = b.make_config(d=64, n_experts=1, m=64, rank=4, max_top_e=1)
+    rng = np.random.default_rng(3)
+    w = _bits(rng.normal(0, 0.02, (64, 64)))
+    b.moe_sel_debug_fail_alloc(1)
+    with pytest.raises(b.MoeSelError) as ei:
+        b.moe_sel_prepare_expert_host(cfg, w, w, w)
+    assert ei.value.status == b.MOE_SEL_ENOMEM
+    assert "allocation" in b.moe_sel_last_error()
+    out = b.moe_sel_prepare_expert_host(cfg, w, w, w)  # disarmed after firing
+    assert out["nnz_gate"].sum() > 0
+    b.moe_sel_debug_fail_alloc(5)
+    b.moe_sel_debug_fail_alloc(0)  # disarms
+    b.moe_sel_prepare_expert_host(cfg, w, w, w)
+    with pytest.raises(b.MoeSelError) as ei:
+        b.moe_sel_debug_fail_alloc(-1)
+    assert ei.value.status == b.MOE_SEL_EINVAL
+
+
+def test_debug_entry_points_validate_before_enqueueing():
+    """Null, misaligned and negative arguments are refused on the host (no GPU needed)."""
+    lib = b._lib
+    assert lib.moe_sel_debug_silu(None, None, 0, None) == b.MOE_SEL_OK
+    assert lib.moe_sel_debug_silu(None, None, 4, None) == b.MOE_SEL_EINVAL
+    assert lib.moe_sel_debug_silu(16, 32, -1, None) == b.MOE_SEL_EINVAL
+    assert lib.moe_sel_debug_silu(18, 32, 4, None) == b.MOE_SEL_EINVAL  # misaligned
+    assert lib.moe_sel_debug_score(16, 16, 16, 16, 9, 16, 16, 4, None) == b.MOE_SEL_EINVAL  # unknown kind
+    assert lib.moe_sel_debug_score(16, 16, 16, 24, 0, 16, 16, 4, None) == b.MOE_SEL_EINVAL  # stats misaligned
+    assert lib.moe_sel_read_stream(None, 16, 16, None) == b.MOE_SEL_EINVAL
+    assert lib.moe_sel_read_stream(16, 24, 16, None) == b.MOE_SEL_EINVAL  # not a multiple of 16
+    assert lib.moe_sel_set_wait_limit(None, 0) == b.MOE_SEL_EINVAL
 
 
 def test_config_validation():
