@@ -28,6 +28,7 @@ EXPORTED = (
     "moe_sel_set_path", "moe_sel_last_path", "moe_sel_set_score", "moe_sel_router_logits", "moe_sel_residual_rmsnorm",
     "moe_sel_residual_rmsnorm_router", "moe_sel_save", "moe_sel_load", "moe_sel_set_wait_limit",
     "moe_sel_debug_silu", "moe_sel_debug_score", "moe_sel_read_stream", "moe_sel_debug_fail_alloc",
+    "moe_sel_forward_noalloc",
 )
 
 MOE_SEL_PATH_AUTO, MOE_SEL_PATH_MULTI_KERNEL, MOE_SEL_PATH_SINGLE_LAUNCH = range(3)
@@ -74,6 +75,7 @@ def _load():
         "moe_sel_prepare": (ctypes.c_int, [ctypes.POINTER(moe_sel_config), vp, vp, vp, vp,
                                            ctypes.POINTER(vp)]),
         "moe_sel_forward": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_sel_forward_noalloc": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "moe_sel_forward_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp]),
         "moe_sel_forward_threshold": (ctypes.c_int, [vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]),
         "moe_sel_debug_selection": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp]),
@@ -198,6 +200,12 @@ def moe_sel_forward(ctx, x, logits, batch, top_e, k_budget, out, stream=None):
     st = _lib.moe_sel_forward(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e), int(k_budget),
                               _dev_ptr(out), _stream(stream))
     _check(st, "moe_sel_forward")
+
+
+def moe_sel_forward_noalloc(ctx, x, logits, batch, top_e, k_budget, out, stream=None):
+    st = _lib.moe_sel_forward_noalloc(ctx, _dev_ptr(x), _dev_ptr(logits), int(batch), int(top_e), int(k_budget),
+                                      _dev_ptr(out), _stream(stream))
+    _check(st, "moe_sel_forward_noalloc")
 
 
 def moe_sel_forward_threshold(ctx, x, logits, batch, top_e, threshold, out, stream=None):

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -427,6 +428,53 @@ moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
   return st;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of moe_sel_forward_noalloc: one file-scope device array, of which each
+// GPU holds its own copy until the process ends. Sub-arrays at fixed offsets,
+// each sized for the largest call the entry point accepts: the four hand-off
+// slot arrays of the single-launch kernel (kept empty between calls), its error
+// word, and the arrays it fills for inspection. Host code never passes the
+// array's name to a kernel or a copy: set-up looks up each device's copy with
+// hipGetSymbolAddress and keeps that pointer.
+// ---------------------------------------------------------------------------
+constexpr size_t kScrXscore = (size_t)3 << 20;   // (score, h_hat) slots
+constexpr size_t kScrZpart = (size_t)256 << 10;  // score-block shares of Q^T h_hat
+constexpr size_t kScrPartial = (size_t)3 << 20;  // gather-block down partials
+constexpr size_t kScrZcopy = (size_t)256 << 10;  // z for the combine blocks
+constexpr size_t kScrErr = 256;                  // error word
+constexpr size_t kScrInspect = (size_t)1 << 20;  // hhat, score, sel_idx, pair arrays
+constexpr size_t kScrSlots = kScrXscore + kScrZpart + kScrPartial + kScrZcopy;
+constexpr size_t kScratchBytes = kScrSlots + kScrErr + kScrInspect;
+static_assert(kScratchBytes % 256 == 0, "scratch sub-arrays keep 256-byte alignment");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};  // device address of each GPU's copy (null until set up)
+
+// Once per device, with that device current: find this GPU's copy of the
+// scratch array and empty its slots. Called while a context is created.
+moe_sel_status scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return MOE_SEL_OK;  // the no-allocation entry point then refuses
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return MOE_SEL_OK;
+  unsigned char* p = nullptr;
+  hipError_t e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+  if (e == hipSuccess) e = hipMemsetAsync(p, 0xFF, kScrSlots, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(p + kScrSlots, 0, kScrErr, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_fail(e, "scratch set-up");
+  g_scratch_ptr[dev] = p;
+  return MOE_SEL_OK;
+}
+
+unsigned char* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
 // After the prepared arrays are queued on s: empty hand-off slots and the
 // device properties of the single-launch path, then wait for s.
 moe_sel_status finish_layer(moe_sel_ctx* ctx, hipStream_t s) {
@@ -443,7 +491,7 @@ moe_sel_status finish_layer(moe_sel_ctx* ctx, hipStream_t s) {
   }
   he = hipStreamSynchronize(s);
   if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize");
-  return MOE_SEL_OK;
+  return ctx->xscore ? scratch_setup(ctx->device) : MOE_SEL_OK;
 }
 
 // A context for cfg on the current device, with no buffers yet.
@@ -794,6 +842,56 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
   return MOE_SEL_OK;
 }
 
+moe_sel_status moe_sel_forward_noalloc(moe_sel_ctx* ctx, const uint16_t* x, const float* logits, int32_t batch,
+                                       int32_t top_e, int32_t k_budget, uint16_t* out, void* stream) {
+  g_last_error.clear();
+  moe_sel_status st = check_forward(ctx, x, logits, batch, top_e, k_budget, out);
+  if (st != MOE_SEL_OK) return st;
+  DeviceGuard guard(ctx->device);
+  unsigned char* scr = scratch_ptr(ctx->device);
+  if (!scr) return fail(MOE_SEL_EUNSUPPORTED, "no-allocation scratch is not set up on this device (a layer that "
+                                              "cannot run as one launch, or a device index above 63)");
+  const moe_sel::FwdArgs a = make_args(ctx, x, logits, batch, top_e, k_budget, out);
+  moe_sel::FusedArgs f;
+  if (!plan_fused(ctx, a, false, &f))
+    return fail(MOE_SEL_EUNSUPPORTED, "moe_sel_forward_noalloc runs only calls the single launch can take");
+  // the call's share of each scratch sub-array
+  const size_t pairs = (size_t)batch * top_e, m = ctx->cfg.m, d = ctx->cfg.d;
+  const size_t r1 = std::max(ctx->cfg.rank, 1), slices = d / 64;
+  const size_t need_xscore = pairs * f.ncs * m * 8;
+  const size_t need_zpart = pairs * (m / f.score_ch) * r1 * 4;
+  const size_t need_partial = (size_t)batch * slices * top_e * f.nc * 64 * 4;
+  const size_t need_zcopy = (size_t)batch * 2 * slices * top_e * r1 * 4;
+  const size_t need_inspect = 3 * pairs * m * 4 + 3 * pairs * 4 + 3 * 256;
+  if (need_xscore > kScrXscore || need_zpart > kScrZpart || need_partial > kScrPartial || need_zcopy > kScrZcopy ||
+      need_inspect > kScrInspect)
+    return fail(MOE_SEL_EUNSUPPORTED,
+                "call needs more scratch than moe_sel_forward_noalloc holds (" + std::to_string(kScratchBytes >> 20) +
+                    " MiB per device: hand-off slots " + std::to_string(need_xscore + need_zpart + need_partial + need_zcopy) +
+                    " bytes of at most " + std::to_string(kScrSlots) + ")");
+  unsigned char* q = scr;
+  f.xscore = (uint64_t*)q;
+  f.zpart = (float*)(q += kScrXscore);
+  f.partial = (float*)(q += kScrZpart);
+  f.zcopy = (float*)(q += kScrPartial);
+  f.err = (int*)(q += kScrZcopy);
+  q += kScrErr;
+  auto take = [&q](size_t bytes) {
+    unsigned char* r = q;
+    q += (bytes + 255) / 256 * 256;
+    return r;
+  };
+  f.hhat = (float*)take(pairs * m * 4);
+  f.score = (float*)take(pairs * m * 4);
+  f.sel_idx = (int*)take(pairs * m * 4);
+  f.pair_expert = (int*)take(pairs * 4);
+  f.pair_w = (float*)take(pairs * 4);
+  f.sel_count = (int*)take(pairs * 4);
+  const hipError_t e = moe_sel::launch_fused(f, false, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return MOE_SEL_OK;
+}
+
 moe_sel_status moe_sel_forward_threshold(moe_sel_ctx* ctx, const uint16_t* x, const float* logits, int32_t batch,
                                          int32_t top_e, float threshold, uint16_t* out, void* stream) {
   g_last_error.clear();
@@ -920,13 +1018,21 @@ moe_sel_status moe_sel_check_device(moe_sel_ctx* ctx) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   if (!ctx->err) return MOE_SEL_OK;
-  int bits = 0;
+  int bits = 0, sbits = 0;
   if ((e = hipMemcpy(&bits, ctx->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
-  if (bits == 0) return MOE_SEL_OK;
+  unsigned char* scr = scratch_ptr(ctx->device);
+  if (scr && (e = hipMemcpy(&sbits, scr + kScrSlots, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (bits == 0 && sbits == 0) return MOE_SEL_OK;
   // a bounded wait expired: reset the hand-off state so the next call starts clean
-  (void)reset_handoff(ctx, nullptr);
+  if (bits) (void)reset_handoff(ctx, nullptr);
+  if (sbits) {
+    (void)hipMemsetAsync(scr, 0xFF, kScrSlots, nullptr);
+    (void)hipMemsetAsync(scr + kScrSlots, 0, kScrErr, nullptr);
+  }
   (void)hipDeviceSynchronize();
-  return fail(MOE_SEL_EDEVICE, "a cross-block wait timed out (bits " + std::to_string(bits) +
+  return fail(MOE_SEL_EDEVICE, "a cross-block wait timed out (bits " + std::to_string(bits | sbits) +
+                                   (sbits ? ", in the device's no-allocation scratch" : "") +
                                    "); outputs of the affected calls are invalid");
 }
 

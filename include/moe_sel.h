@@ -186,6 +186,28 @@ moe_sel_status moe_sel_forward(moe_sel_ctx* ctx, const uint16_t* x, const float*
                                uint16_t* out, void* stream);
 
 /*
+ * moe_sel_forward without any allocation, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it). Same arguments, results and errors as moe_sel_forward on the
+ * single-launch path (bit-identical outputs); its per-call scratch (hand-off
+ * slots, the error word and the inspection arrays) is a fixed 7.5 MiB device
+ * array that the library holds on each GPU until the process ends, not the
+ * context's workspace. It enqueues one kernel and calls no allocating routine.
+ *   Limits: only calls the single launch can run (see moe_sel_set_path), and
+ *   at most 3 MiB each of gather hand-off and down-partial slots (the
+ *   Qwen3-30B-A3B-shaped layer fits at batch 1); EUNSUPPORTED otherwise,
+ *   before anything is enqueued.
+ *   Every call on a GPU shares that GPU's array: calls that overlap in time on
+ *   one GPU (other streams, other threads) race and must not be issued. A
+ *   wait that gives up poisons later calls of this entry point on the GPU, for
+ *   every context, until moe_sel_check_device on a context of that GPU.
+ *   moe_sel_debug_selection does not see these calls.
+ */
+moe_sel_status moe_sel_forward_noalloc(moe_sel_ctx* ctx, const uint16_t* x, const float* logits,
+                                       int32_t batch, int32_t top_e, int32_t k_budget,
+                                       uint16_t* out, void* stream);
+
+/*
  * The threshold selector the pages contrast with top-k ("KAIST drops
  * calibration from MoE decoding...", section "The threshold promises a budget
  * but does not keep it"): each routed pair keeps every channel whose score
