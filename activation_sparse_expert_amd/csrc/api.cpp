@@ -54,11 +54,12 @@ struct moe_sel_ctx {
   int max_tiles = 0;
   // single-launch path
   uint64_t* xscore = nullptr;
+  int* readers = nullptr;
   float* zpart = nullptr;
   float* partial = nullptr;
   float* zcopy = nullptr;
   int* err = nullptr;
-  size_t xscore_count = 0, zpart_count = 0, partial_count = 0, zcopy_count = 0;
+  size_t xscore_count = 0, readers_count = 0, zpart_count = 0, partial_count = 0, zcopy_count = 0;
   int fused_max_batch = 0;
   int num_cus = 0;
   int fused_bpc_sparse = 0, fused_bpc_dense = 0;
@@ -257,6 +258,7 @@ bool plan_fused(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, moe_se
   moe_sel::FusedArgs f;
   static_cast<moe_sel::FwdArgs&>(f) = base;
   f.xscore = c->xscore;
+  f.readers = c->readers;
   f.zpart = c->zpart;
   f.partial = c->partial;
   f.zcopy = c->zcopy;
@@ -271,18 +273,20 @@ bool plan_fused(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, moe_se
   f.n_combine = base.batch * (base.d / 32);
   const int bpc = dense ? c->fused_bpc_dense : c->fused_bpc_sparse;
   const long capacity = (long)bpc * c->num_cus;
-  // score blocks of 32 channels spread the sketch over more CUs; 64 when that grid would not fit
-  f.score_ch = moe_sel::kFusedScoreChMin;
-  f.n_score = dense ? 0 : pairs * (base.m / f.score_ch);
-  if (!dense && ((long)f.n_score + f.n_gather + f.n_z + f.n_combine > capacity ||
-                 !moe_sel::fused_narrow_score_ok(base.m, base.r))) {
-    f.score_ch = 2 * moe_sel::kFusedScoreChMin;
-    f.n_score = pairs * (base.m / f.score_ch);
+  // score blocks of 32 channels spread the sketch over more CUs; 64 when that
+  // grid would not fit. Every block of the grid must be resident at once (the
+  // score hand-off waits across blocks).
+  for (int sc = moe_sel::kFusedScoreChMin; sc <= 2 * moe_sel::kFusedScoreChMin; sc *= 2) {
+    if (!dense && sc == moe_sel::kFusedScoreChMin && !moe_sel::fused_narrow_score_ok(base.m, base.r)) continue;
+    f.score_ch = sc;
+    f.n_score = dense ? 0 : pairs * (base.m / sc);
+    if ((long)moe_sel::fused_grid(f, dense) <= capacity) {
+      *out = f;
+      return true;
+    }
+    if (dense) break;
   }
-  const long total = (long)f.n_score + f.n_gather + f.n_z + f.n_combine;
-  if (total > capacity) return false;
-  *out = f;
-  return true;
+  return false;
 }
 
 // The single-launch path when its blocks all fit on the device at once, else
@@ -313,6 +317,7 @@ hipError_t reset_handoff(moe_sel_ctx* c, hipStream_t s) {
                {c->zcopy, c->zcopy_count * 4}};
   for (const auto& sl : slots)
     if (he == hipSuccess) he = hipMemsetAsync(sl.p, 0xFF, sl.bytes, s);
+  if (he == hipSuccess) he = hipMemsetAsync(c->readers, 0, c->readers_count * 4, s);
   if (he == hipSuccess) he = hipMemsetAsync(c->err, 0, 4, s);
   return he;
 }
@@ -414,11 +419,13 @@ moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
     const size_t fp = (size_t)ctx->fused_max_batch * c.max_top_e;
     const size_t nc_max = (m + kMinChunk - 1) / kMinChunk;
     const size_t slices = d / 64;
-    ctx->xscore_count = fp * (nc_max + 1) * m;
+    ctx->xscore_count = fp * m;
+    ctx->readers_count = fp;
     ctx->zpart_count = fp * (m / moe_sel::kFusedScoreChMin) * std::max<size_t>(r, 1);
     ctx->partial_count = (size_t)ctx->fused_max_batch * slices * c.max_top_e * nc_max * 64;
     ctx->zcopy_count = (size_t)ctx->fused_max_batch * 2 * slices * c.max_top_e * std::max<size_t>(r, 1);
     ALLOC(xscore, ctx->xscore_count);
+    ALLOC(readers, ctx->readers_count);
     ALLOC(zpart, ctx->zpart_count);
     ALLOC(partial, ctx->partial_count);
     ALLOC(zcopy, ctx->zcopy_count);
@@ -441,7 +448,7 @@ constexpr size_t kScrXscore = (size_t)3 << 20;   // (score, h_hat) slots
 constexpr size_t kScrZpart = (size_t)256 << 10;  // score-block shares of Q^T h_hat
 constexpr size_t kScrPartial = (size_t)3 << 20;  // gather-block down partials
 constexpr size_t kScrZcopy = (size_t)256 << 10;  // z for the combine blocks
-constexpr size_t kScrErr = 256;                  // error word
+constexpr size_t kScrErr = 4096;                 // error word, then the reader counts (zeroed)
 constexpr size_t kScrInspect = (size_t)1 << 20;  // hhat, score, sel_idx, pair arrays
 constexpr size_t kScrSlots = kScrXscore + kScrZpart + kScrPartial + kScrZcopy;
 constexpr size_t kScratchBytes = kScrSlots + kScrErr + kScrInspect;
@@ -858,13 +865,13 @@ moe_sel_status moe_sel_forward_noalloc(moe_sel_ctx* ctx, const uint16_t* x, cons
   // the call's share of each scratch sub-array
   const size_t pairs = (size_t)batch * top_e, m = ctx->cfg.m, d = ctx->cfg.d;
   const size_t r1 = std::max(ctx->cfg.rank, 1), slices = d / 64;
-  const size_t need_xscore = pairs * f.ncs * m * 8;
+  const size_t need_xscore = pairs * m * 8;
   const size_t need_zpart = pairs * (m / f.score_ch) * r1 * 4;
   const size_t need_partial = (size_t)batch * slices * top_e * f.nc * 64 * 4;
   const size_t need_zcopy = (size_t)batch * 2 * slices * top_e * r1 * 4;
   const size_t need_inspect = 3 * pairs * m * 4 + 3 * pairs * 4 + 3 * 256;
   if (need_xscore > kScrXscore || need_zpart > kScrZpart || need_partial > kScrPartial || need_zcopy > kScrZcopy ||
-      need_inspect > kScrInspect)
+      need_inspect > kScrInspect || 4 * (pairs + 64) > kScrErr)
     return fail(MOE_SEL_EUNSUPPORTED,
                 "call needs more scratch than moe_sel_forward_noalloc holds (" + std::to_string(kScratchBytes >> 20) +
                     " MiB per device: hand-off slots " + std::to_string(need_xscore + need_zpart + need_partial + need_zcopy) +
@@ -875,6 +882,7 @@ moe_sel_status moe_sel_forward_noalloc(moe_sel_ctx* ctx, const uint16_t* x, cons
   f.partial = (float*)(q += kScrZpart);
   f.zcopy = (float*)(q += kScrPartial);
   f.err = (int*)(q += kScrZcopy);
+  f.readers = f.err + 64;
   q += kScrErr;
   auto take = [&q](size_t bytes) {
     unsigned char* r = q;

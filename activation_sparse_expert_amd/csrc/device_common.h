@@ -717,5 +717,22 @@ __device__ __forceinline__ int ld_coh(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte device-coherent loads and stores through a buffer resource, with the
+// same device-scope cache policy (sc1) as the agent-scope relaxed atomics above.
+// The 16 bytes are not one atomic access, but each of their dwords is, so a
+// poller checks every dword for the empty sentinel. Offsets are in bytes and
+// checked by the hardware against the resource's size.
+constexpr int kDeviceScope = 16;  // cache-policy bit of the buffer instructions: device scope (sc1)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_coh128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kDeviceScope));
+}
+__device__ __forceinline__ void st_coh128(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, kDeviceScope);
+}
+
 }  // namespace dev
 }  // namespace moe_sel

@@ -54,12 +54,14 @@ using namespace dev;
 constexpr int kMaxChunkSparse = 8;   // channels per gather block, all loaded at once
 constexpr int kMaxChunkDense = 16;
 constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
+constexpr int kDirectRank = 64;      // boundary-bin keys ranked by their owners (more: radix passes)
+static_assert(kWaves == 4, "the select reads its four wave totals as one int4");
 constexpr int kScoreBlk = 16;        // sketch blocks in flight per lane group pair (d = 2048 in one batch)
 constexpr int kZPass = 4;            // compensation row passes loaded together
 constexpr int kZWarm = 16;           // Q pieces per thread in flight while the z block warms L2
 constexpr int kMaxZPart = 4;         // zpart values per thread ((m / 32) * r <= 1024)
 constexpr int kMaxP = 4;             // 16-byte P pieces per combine thread (top_e * r <= 256)
-constexpr int kCombPer = 24;         // partial values per combine thread per poll batch
+constexpr int kCombPer = 8;          // producers whose partials a combine thread polls per batch
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr uint64_t kEmpty64 = 0xFFFFFFFFFFFFFFFFull;
 
@@ -70,8 +72,12 @@ struct Smem {
     int hist[2048];                // radix select
     uint64_t route[3 * kThreads];  // routing scratch
   };
-  int cand[2 * kThreads];          // boundary-bucket candidates of the select
+  alignas(16) int cand[2 * kThreads];  // boundary-bin candidates of the select (order keys)
   int tmp[kWaves + 2];
+  alignas(16) int sel_ws[kWaves];  // wave totals of the select's first scan
+  alignas(16) int sel_ws2[kWaves]; // and of its second
+  alignas(16) int sel_b[4];        // boundary bin, keys above it, keys in it, candidates placed
+  uint64_t sel_t;                  // order key of the last boundary-bin key taken
   float red[kWaves][2 * kMaxChunkDense];
   uint32_t amax[kWaves];
   int qsum[kWaves][4];             // per wave: sum of x_q over each quarter of d (the score role's split)
@@ -100,6 +106,22 @@ __device__ __forceinline__ void gave_up(int* err, int bit) {
   if ((threadIdx.x & 63) == 0) atomicOr(err, bit);
 }
 constexpr float kPoison = __builtin_nanf("");
+
+// Phase marks for measuring the kernel's timeline: MARK(ev) compiles to nothing
+// unless the library is built with MOE_SEL_TIMELINE, which records the wall
+// clock of thread 0 of each block at each mark (events 0..7 per block; their
+// meaning by role: 0 entry, 1 routed, 2 first wait over / dots done, 3 select
+// done / second wait over, 4 SwiGLU done, 5 end).
+#ifdef MOE_SEL_TIMELINE
+constexpr int kMarkEvents = 8, kMarkBlocks = 8192;
+__device__ unsigned long long g_marks[kMarkBlocks * kMarkEvents];
+#define MARK(ev)                                                                        \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < kMarkBlocks) g_marks[blockIdx.x * kMarkEvents + (ev)] = wall_clock64(); \
+  } while (0)
+#else
+#define MARK(ev) ((void)0)
+#endif
 
 template <int SLOTS>
 __device__ __forceinline__ void load_x(const uint16_t* x, int d, uint4 (&xv)[SLOTS]) {
@@ -196,6 +218,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
   uint4 xv[SLOTS];
   load_x<SLOTS>(a.x + (size_t)t * a.d, a.d, xv);  // in flight during the routing
   route(a, t, sm, false);                          // the expert only: no gate weights here
+  MARK(1);
   const int e = sm.ids[slot];
   // every global load of this block: the sketch codes, the SC Q rows, the statistics.
   // Lane = (lane group, channel c); wave = (matrix, half of the d parts). The d
@@ -264,6 +287,7 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
       }
     }
   }
+  MARK(2);
   const int cx = x16 ? 256 * code_acc_total(acc) + code_acc_total(acc_lo) : code_acc_total(acc);
   s_part[wave * 64 + lane] = cx - qs;  // sum (code - 1) * q = sum t * q
 #pragma unroll
@@ -284,53 +308,185 @@ __device__ __forceinline__ void score_role(const FusedArgs& a, int bid, Smem& sm
     s_sc[c] = sc;
   }
   __syncthreads();
-  if (wave == kWaves - 1) {
-    // the last wave: this block's share of Q^T h_hat over its channels, for the z
-    // block, at the same time as the other waves publish the scores
+  if (wave == 0) {
+    // publish (score, h_hat) of the block's channels once, for every reader of the pair
+    if (lane < SC) {
+      const uint64_t v = (uint64_t)__float_as_uint(s_sc[lane]) | ((uint64_t)__float_as_uint(s_h[lane]) << 32);
+      st_coh64(&a.xscore[(size_t)p * a.m + j0 + lane], v);
+      st_coh(&a.hhat[(size_t)p * a.m + j0 + lane], s_h[lane]);  // for inspection only
+      st_coh(&a.score[(size_t)p * a.m + j0 + lane], s_sc[lane]);
+    }
+  } else if (wave == kWaves - 1) {
+    // this block's share of Q^T h_hat over its channels, for the z block
     for (int col = lane; col < r; col += 64) {
       float z = 0.0f;
 #pragma unroll 16
       for (int j = 0; j < SC; ++j) z += s_h[j] * bf16f(s_q[j * r + col]);
       st_coh(&a.zpart[((size_t)p * zg + sb) * r + col], z);
     }
-  } else {
-    // publish (score, h_hat) of the block's channels to each gather block of the pair
-    for (int i = tid; i < a.ncs * SC; i += kThreads - 64) {
-      const int cc = i / SC, l = i % SC;
-      const uint64_t v = (uint64_t)__float_as_uint(s_sc[l]) | ((uint64_t)__float_as_uint(s_h[l]) << 32);
-      st_coh64(&a.xscore[((size_t)p * a.ncs + cc) * a.m + j0 + l], v);
-    }
   }
-  if (tid < SC) {  // for inspection only
-    st_coh(&a.hhat[(size_t)p * a.m + j0 + tid], s_h[tid]);
-    st_coh(&a.score[(size_t)p * a.m + j0 + tid], s_sc[tid]);
-  }
+  MARK(3);
+  MARK(5);
 }
 
 // ---------------------------------------------------------------------------
 // gather role
 // ---------------------------------------------------------------------------
-// Waits for the pair's m (score, h_hat) values in this block's own slots (and,
-// for the z block, the pair's zpart slots), then selects the pair's top-k: the
-// selected channels ascending in s_sel[0..k), the sketch activations in s_hh,
-// the zpart values in s_zp. Chunk 0 also records the selection for inspection.
+// Top-k (1 <= k < m) of the m keys of a pair (binary32 bits of non-negative
+// scores, so their unsigned order is the scores' order) held consecutively, R
+// per thread (thread t: channels t R .. t R + R - 1): writes the selected
+// channels in ascending order to s_sel[0..k). Larger scores first, equal scores
+// to the lower channel index ("Top-k instead of a threshold").
+//   1. a 2048-bin histogram of key bits 30..20 (an eighth of an octave a bin);
+//   2. the bin D holding the k-th largest key, by one scan of the bin counts;
+//   3. the keys in bin D ranked exactly (larger first, lower index first) by one
+//      wave, which publishes the order key of the last one taken (a bin of more
+//      than kDirectRank keys, from ties or clusters, goes to three radix passes
+//      that give the k-th key T, equal keys taken lowest index first);
+//   4. the ascending positions of the taken keys, by one more scan.
+// sm.hist and sm.sel_b[3] must be zero, with a barrier passed since. Barriers
+// inside (all threads call).
+template <int MK>
+__device__ __forceinline__ void select_consecutive(const uint32_t (&key)[MK], int R, int m, int k, Smem& sm,
+                                                   int* s_sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = tid * R;
+#pragma unroll
+  for (int u = 0; u < MK; ++u)
+    if (u < R && j0 + u < m) atomicAdd(&sm.hist[key[u] >> 20], 1);
+  __syncthreads();
+  int h[8];
+  {
+    const int4 lo = *(const int4*)&sm.hist[tid * 8], hi = *(const int4*)&sm.hist[tid * 8 + 4];
+    h[0] = lo.x; h[1] = lo.y; h[2] = lo.z; h[3] = lo.w;
+    h[4] = hi.x; h[5] = hi.y; h[6] = hi.z; h[7] = hi.w;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) cnt += h[b];
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) sm.sel_ws[wave] = incl;
+  __syncthreads();
+  const int4 ws = *(const int4*)sm.sel_ws;
+  const int before = incl - cnt + (wave > 0 ? ws.x : 0) + (wave > 1 ? ws.y : 0) + (wave > 2 ? ws.z : 0);
+  int above = ws.x + ws.y + ws.z + ws.w - before - cnt;  // keys in the bins above this thread's eight
+#pragma unroll
+  for (int b = 7; b >= 0; --b) {
+    if (above < k && k <= above + h[b]) {
+      sm.sel_b[0] = tid * 8 + b;
+      sm.sel_b[1] = above;
+      sm.sel_b[2] = h[b];
+    }
+    above += h[b];
+  }
+  __syncthreads();
+  const int4 sb = *(const int4*)sm.sel_b;
+  const uint32_t D = (uint32_t)sb.x;
+  const int krem = k - sb.y, ncand = sb.z;
+  bool take[MK];
+  if (ncand <= kDirectRank) {
+    // the boundary bin's keys go to a list: each wave takes its slots with one
+    // LDS atomic, its lanes place their keys by ballot offsets
+    uint64_t* s_cand = (uint64_t*)sm.cand;
+    uint64_t bal[MK];
+    int wcount = 0;
+#pragma unroll
+    for (int u = 0; u < MK; ++u) {
+      bal[u] = __ballot(u < R && j0 + u < m && (key[u] >> 20) == D);
+      wcount += __popcll(bal[u]);
+    }
+    if (wcount) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.sel_b[3], wcount);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int u = 0; u < MK; ++u) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u], 0));
+        if ((bal[u] >> lane) & 1) s_cand[base + below] = order_key(key[u], j0 + u);
+        base += __popcll(bal[u]);
+      }
+    }
+    // zero keys pad the list to a multiple of 8 (an order key of 0 is below
+    // every real one, so the padding never counts)
+    if (tid < 8) s_cand[ncand + tid] = 0ull;
+    __syncthreads();
+    // wave 0 ranks the list, one entry per lane (larger first, lower index
+    // first; the order keys are distinct), and publishes the order key of
+    // rank krem - 1: the bin's keys at or above it are taken
+    if (wave == 0) {
+      const uint64_t mine = lane < ncand ? s_cand[lane] : 0ull;
+      const ulonglong2* c2 = (const ulonglong2*)s_cand;
+      int rank = 0;
+      for (int i = 0; i < ncand; i += 8) {
+        const ulonglong2 a0 = c2[i / 2], a1 = c2[i / 2 + 1], a2 = c2[i / 2 + 2], a3 = c2[i / 2 + 3];
+        rank += (a0.x > mine) + (a0.y > mine) + (a1.x > mine) + (a1.y > mine) + (a2.x > mine) + (a2.y > mine) +
+                (a3.x > mine) + (a3.y > mine);
+      }
+      if (lane < ncand && rank == krem - 1) sm.sel_t = mine;
+    }
+    __syncthreads();
+    const uint64_t t_ord = sm.sel_t;
+#pragma unroll
+    for (int u = 0; u < MK; ++u) {
+      const bool valid = u < R && j0 + u < m;
+      const uint32_t dg = key[u] >> 20;
+      take[u] = valid && (dg > D || (dg == D && order_key(key[u], j0 + u) >= t_ord));
+    }
+  } else {
+    uint32_t T;
+    int kr;
+    block_topk_radix<MK>(key, R, m, k, sm.hist, sm.tmp, T, kr);
+    int n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < MK; ++u) n_eq += (u < R && j0 + u < m) && key[u] == T;
+    int eq_total;
+    int eq_before = block_excl_scan(n_eq, sm.tmp, &eq_total);
+#pragma unroll
+    for (int u = 0; u < MK; ++u) {
+      const bool valid = u < R && j0 + u < m;
+      const bool eq = valid && key[u] == T;
+      take[u] = valid && (key[u] > T || (eq && eq_before < kr));
+      eq_before += eq;
+    }
+  }
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < MK; ++u) n += take[u];
+  const int incl2 = wave_incl_scan(n);
+  if (lane == 63) sm.sel_ws2[wave] = incl2;
+  __syncthreads();
+  const int4 ws2 = *(const int4*)sm.sel_ws2;
+  int pos = incl2 - n + (wave > 0 ? ws2.x : 0) + (wave > 1 ? ws2.y : 0) + (wave > 2 ? ws2.z : 0);
+#pragma unroll
+  for (int u = 0; u < MK; ++u)
+    if (take[u]) s_sel[pos++] = j0 + u;
+}
+
+// Waits for the pair's m (score, h_hat) values in the pair's slots (and, for the
+// z block, the pair's zpart slots), then selects the pair's top-k: the selected
+// channels ascending in s_sel[0..k); for the z block also the sketch
+// activations in s_hh and the zpart values in s_zp. Chunk 0 also records the
+// selection for inspection. Every reader calls empty_pair_slots at its end.
 template <int MK>  // key slots per thread: m <= MK * kThreads
 __device__ __forceinline__ bool gather_select_mk(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
-                                                 float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
-                                                 float* s_zp) {
+                                                 float* s_hh, int* s_sel, float* s_zp) {
   const int tid = threadIdx.x, m = a.m, k = a.k, r = a.r;
   const int zg = m / a.score_ch;
-  uint64_t* slots = a.xscore + ((size_t)p * a.ncs + c) * m;
+  const int R = (m + kThreads - 1) / kThreads;  // consecutive channels per thread
+  const uint64_t* slots = a.xscore + (size_t)p * m + (size_t)tid * R;
   const int nzp = with_zpart ? zg * r : 0;
   float* zslots = a.zpart + (size_t)p * zg * r;
-  block_topk_prezero(sm.hist, sm.tmp);  // ordered before the select by the polling barrier
+  // cleared for the select, ordered before it by the polling barrier
+#pragma unroll
+  for (int b = 0; b < 8; ++b) sm.hist[tid * 8 + b] = 0;
+  if (tid == 0) sm.sel_b[3] = 0;
   uint64_t v[MK];
   float zv[kMaxZPart];
   uint32_t pending = 0;  // bit u: key slot u; bit 16 + u: zpart slot u
 #pragma unroll
   for (int u = 0; u < MK; ++u) {
     v[u] = 0ull;
-    if (tid + u * kThreads < m) pending |= 1u << u;
+    if (u < R && tid * R + u < m) pending |= 1u << u;
   }
 #pragma unroll
   for (int u = 0; u < kMaxZPart; ++u) {
@@ -346,7 +502,7 @@ __device__ __forceinline__ bool gather_select_mk(const FusedArgs& a, int p, int 
     }
 #pragma unroll
     for (int u = 0; u < MK; ++u)
-      if ((pending >> u) & 1) v[u] = ld_coh64(slots + tid + u * kThreads);
+      if ((pending >> u) & 1) v[u] = ld_coh64(slots + u);
 #pragma unroll
     for (int u = 0; u < kMaxZPart; ++u)
       if ((pending >> (16 + u)) & 1) zv[u] = ld_coh(zslots + tid + u * kThreads);
@@ -358,6 +514,7 @@ __device__ __forceinline__ bool gather_select_mk(const FusedArgs& a, int p, int 
       if (!empty(zv[u])) pending &= ~(1u << (16 + u));
     if (__syncthreads_and(pending == 0)) break;
   }
+  MARK(2);
   if (bad) {
     // slots still empty after giving up hold no score: rank them as 0 (the
     // sentinel's key bits would index past the select's histogram) with a NaN
@@ -367,54 +524,54 @@ __device__ __forceinline__ bool gather_select_mk(const FusedArgs& a, int p, int 
     for (int u = 0; u < MK; ++u)
       if ((uint32_t)v[u] == kEmpty) v[u] = (uint64_t)__float_as_uint(kPoison) << 32;
   }
+  uint32_t key[MK];
 #pragma unroll
-  for (int u = 0; u < MK; ++u) {
-    const int j = tid + u * kThreads;
-    if (j < m) {
-      s_keys[j] = (uint32_t)v[u];
-      s_hh[j] = __uint_as_float((uint32_t)(v[u] >> 32));
-      st_coh64(slots + j, kEmpty64);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kMaxZPart; ++u) {
-    const int i = tid + u * kThreads;
-    if (i < nzp) {
-      s_zp[i] = zv[u];
-      clear_coh(zslots + i);
-    }
-  }
-  __syncthreads();
-  if (k >= m || k <= 0) {
-    for (int j = tid; j < k; j += kThreads) s_sel[j] = j;
-    __syncthreads();
-  } else {
-    uint32_t key[MK];
-    const int per = (m + kThreads - 1) / kThreads;  // consecutive keys per thread
-#pragma unroll
-    for (int u = 0; u < MK; ++u) {
-      const int j = tid * per + u;
-      key[u] = (u < per && j < m) ? s_keys[j] : 0u;
-    }
-    int sel[MK];
-    block_topk_select_strided<MK, true>(key, per, m, k, sm.hist, sm.cand, s_take, sm.tmp, sel);
+  for (int u = 0; u < MK; ++u) key[u] = (u < R && tid * R + u < m) ? (uint32_t)v[u] : 0u;
+  if (with_zpart) {
 #pragma unroll
     for (int u = 0; u < MK; ++u)
-      if (sel[u] >= 0) s_sel[sel[u]] = tid * per + u;
-    __syncthreads();
+      if (u < R && tid * R + u < m) s_hh[tid * R + u] = __uint_as_float((uint32_t)(v[u] >> 32));
+#pragma unroll
+    for (int u = 0; u < kMaxZPart; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < nzp) {
+        s_zp[i] = zv[u];
+        clear_coh(zslots + i);
+      }
+    }
   }
+  if (k >= m || k <= 0) {
+    for (int j = tid; j < k; j += kThreads) s_sel[j] = j;
+  } else {
+    select_consecutive<MK>(key, R, m, k, sm, s_sel);
+  }
+  __syncthreads();
   if (c == 0)
     for (int i = tid; i < k; i += kThreads) a.sel_idx[(size_t)p * m + i] = s_sel[i];  // for inspection only
+  MARK(3);
   return bad;
 }
 
 // The select with as few key slots per thread as m allows (4 covers m <= 1024).
 // Returns true when the wait for the scores gave up.
 __device__ __forceinline__ bool gather_select(const FusedArgs& a, int p, int c, bool with_zpart, Smem& sm,
-                                              float* s_hh, uint32_t* s_keys, int* s_sel, unsigned char* s_take,
-                                              float* s_zp) {
-  if (a.m <= 4 * kThreads) return gather_select_mk<4>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
-  return gather_select_mk<kMaxKeysPer>(a, p, c, with_zpart, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+                                              float* s_hh, int* s_sel, float* s_zp) {
+  if (a.m <= 4 * kThreads) return gather_select_mk<4>(a, p, c, with_zpart, sm, s_hh, s_sel, s_zp);
+  return gather_select_mk<kMaxKeysPer>(a, p, c, with_zpart, sm, s_hh, s_sel, s_zp);
+}
+
+// Called by every reader of pair p's score slots at its end, when it has read
+// them (all threads): each reader counts itself, and the one that completes the
+// count of a.ncs readers empties the slots and sets the count back to 0, so that
+// the next call starts from empty slots. The count's round trip is waited for
+// here, at the end, off the path to the output.
+__device__ __forceinline__ void empty_pair_slots(const FusedArgs& a, int p, Smem& sm) {
+  if (threadIdx.x == 0) sm.tmp[0] = atomicAdd(&a.readers[p], 1);
+  __syncthreads();
+  if (sm.tmp[0] != a.ncs - 1) return;
+  uint64_t* slots = a.xscore + (size_t)p * a.m;
+  for (int j = threadIdx.x; j < a.m; j += kThreads) st_coh64(slots + j, kEmpty64);
+  if (threadIdx.x == 0) st_coh(&a.readers[p], 0);
 }
 
 template <bool DENSE, int SLOTS>
@@ -428,11 +585,9 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nslots = d / 8;  // 16-byte pieces of a hidden vector
-  float* s_hh = (float*)dyn;                            // m
-  uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
-  int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m: the selection, ascending
-  unsigned char* s_take = dyn + 12 * (size_t)m;         // m
-  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zpart rows: the z block's only
+  float* s_hh = (float*)dyn;                 // m: sketch activations (the z block's only)
+  int* s_sel = (int*)(dyn + 4 * (size_t)m);  // m: the selection, ascending
+  float* s_zp = (float*)(dyn + 8 * (size_t)m);  // zpart rows: the z block's only
 
   uint4 xv[SLOTS];  // eight bf16 of x per slot (zero past d)
   const uint16_t* xrow = a.x + (size_t)t * d;
@@ -442,11 +597,12 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
     xv[u] = s < nslots ? *(const uint4*)(xrow + 8 * s) : make_uint4(0, 0, 0, 0);
   }
   route(a, t, sm);
+  MARK(1);
   const int count = DENSE ? m : a.k;
   const int first = c * C;
   int mine = count - first;
   mine = mine < 0 ? 0 : (mine > C ? C : mine);
-  const bool bad = DENSE ? false : gather_select(a, p, c, false, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const bool bad = DENSE ? false : gather_select(a, p, c, false, sm, s_hh, s_sel, s_zp);
   const int e = sm.ids[slot];
   const float wp = sm.w[slot];
   if (!DENSE && c == 0 && tid == 0) {  // routing and selection of the pair, for inspection
@@ -514,6 +670,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
     }
   }
   __syncthreads();
+  MARK(4);
   float yacc[SLOTS][8];
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u)
@@ -543,20 +700,27 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
     for (int u = 0; u < SLOTS; ++u)
 #pragma unroll
       for (int q = 0; q < 8; ++q) yacc[u][q] = kPoison;
-  // ---- result: down partial (slice-major [t][slice][producer][64])
+  // ---- result: down partial (slice-major [t][slice][producer][64]); a
+  // thread's eight values are 32 contiguous bytes, so a wave's two 16-byte
+  // stores write whole lines
   const int slices = d / 64;
   const int qt = a.top_e * a.nc;
   const int q = slot * a.nc + c;
+  const __amdgpu_buffer_rsrc_t prs = coh_rsrc(a.partial, (uint32_t)((size_t)a.batch * slices * qt * 256));
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     const int s = tid + u * kThreads;
     if (s < nslots) {
       const int sl = s >> 3, off = (s & 7) * 8;
-      float* dst = a.partial + (((size_t)t * slices + sl) * qt + q) * 64 + off;
-#pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) st_coh2(dst + 2 * h2, yacc[u][2 * h2], yacc[u][2 * h2 + 1]);
+      const uint32_t at = (uint32_t)(((((size_t)t * slices + sl) * qt + q) * 64 + off) * 4);
+      st_coh128(prs, at, make_uint4(__float_as_uint(yacc[u][0]), __float_as_uint(yacc[u][1]),
+                                    __float_as_uint(yacc[u][2]), __float_as_uint(yacc[u][3])));
+      st_coh128(prs, at + 16, make_uint4(__float_as_uint(yacc[u][4]), __float_as_uint(yacc[u][5]),
+                                         __float_as_uint(yacc[u][6]), __float_as_uint(yacc[u][7])));
     }
   }
+  if (!DENSE) empty_pair_slots(a, p, sm);
+  MARK(5);
 }
 
 // ---------------------------------------------------------------------------
@@ -570,13 +734,12 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
   const int t = p / a.top_e, slot = p % a.top_e;
   const int tid = threadIdx.x;
   const int zg = m / a.score_ch;                        // zpart rows: one per score block
-  float* s_hh = (float*)dyn;                            // m
-  uint32_t* s_keys = (uint32_t*)(dyn + 4 * (size_t)m);  // m
-  int* s_sel = (int*)(dyn + 8 * (size_t)m);             // m
-  unsigned char* s_take = dyn + 12 * (size_t)m;         // m
-  float* s_zp = (float*)(dyn + 13 * (size_t)m);         // zg * r
+  float* s_hh = (float*)dyn;                    // m
+  int* s_sel = (int*)(dyn + 4 * (size_t)m);     // m
+  float* s_zp = (float*)(dyn + 8 * (size_t)m);  // zg * r
   float* s_zr = s_zp + zg * r;                          // kThreads x 8, then r
   route(a, t, sm);
+  MARK(1);
   const int e = sm.ids[slot];
   {
     // read the expert's whole Q (m x r bf16) once while the scores are still being
@@ -597,7 +760,7 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
     }
     if (a.k < 0 && tid == 0) a.err[0] = (int)acc;
   }
-  const bool bad = gather_select(a, p, a.nc, true, sm, s_hh, s_keys, s_sel, s_take, s_zp);
+  const bool bad = gather_select(a, p, a.nc, true, sm, s_hh, s_sel, s_zp);
   const int count = a.k;
   // thread t owns 8 consecutive columns (group t % (r/8)) of rows t / (r/8) + n * rows_per_pass
   float zacc[8];
@@ -639,6 +802,8 @@ __device__ __forceinline__ void z_role(const FusedArgs& a, int p, Smem& sm, unsi
     const int col = i % r, half_slice = i / r;
     st_coh(&a.zcopy[(((size_t)t * 2 * slices + half_slice) * a.top_e + slot) * r + col], s_zc[col]);
   }
+  empty_pair_slots(a, p, sm);
+  MARK(5);
 }
 
 // ---------------------------------------------------------------------------
@@ -651,18 +816,19 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
   const int t = bid / (2 * slices), hs = bid % (2 * slices);  // hs: half-slice index
   const int sl = hs >> 1, hf = hs & 1;
   const int tid = threadIdx.x;
-  const int el = tid & 31, pg = tid >> 5;  // element, producer lane group (8)
+  const int q4 = tid & 7, pg = tid >> 3;  // elements 4 q4 .. 4 q4 + 3, producer group (32)
   const int qt = a.top_e * a.nc;
   const int r = DENSE ? 0 : a.r;
   const int rdiv = r > 0 ? r : 1;
   float* s_red = (float*)dyn;                 // kThreads x 8
   float* s_z = s_red + kThreads * 8;          // top_e x r
-  float* s_y = s_z + 256;                     // 8 x 32
+  float* s_y = s_z + 256;                     // 32 x 32
 
   // an earlier wait on this context gave up: its late stores may sit in slots
   // that this call reads, so the output is NaN until the host clears the error
   const bool poisoned = ld_coh(a.err) != 0;
   route(a, t, sm);
+  MARK(1);
   // prefetch P[e][c][32 elements] for the token's experts: top_e * r rows of 64 bytes
   const int npieces = a.top_e * r * 4;
   uint4 pv[kMaxP];
@@ -674,7 +840,6 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
     pv[u] = npieces ? *(const uint4*)(a.pmat + ((size_t)sm.ids[s] * r + cc) * d + 64 * sl + 32 * hf + 8 * part)
                     : make_uint4(0, 0, 0, 0);
   }
-  const float* src = a.partial + ((size_t)t * slices + sl) * qt * 64 + 32 * hf + el;
   float* zsrc = a.zcopy + ((size_t)t * 2 * slices + hs) * a.top_e * rdiv;
   const bool zthread = r > 0 && tid < a.top_e * r;
   int spins = 0;
@@ -701,6 +866,7 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
     }
   }
   __syncthreads();
+  MARK(2);
   // P z for these elements: every thread's pieces share part (tid & 3): elements 8*part..+7
   float pz[8];
 #pragma unroll
@@ -717,61 +883,79 @@ __device__ __forceinline__ void combine_role(const FusedArgs& a, int bid, Smem& 
 #pragma unroll
   for (int q = 0; q < 8; ++q) s_red[tid * 8 + q] = pz[q];
   __syncthreads();
-  float yz = 0.0f;
+  // P z of elements 4 q4 .. + 3: element 8 part + qq has pieces from threads
+  // th == part (mod 4); this thread takes th = part + 4 (2 pg) and part + 4 (2 pg + 1)
+  float yz[4];
   {
-    // element el = 8 * part + qq: threads th == part (mod 4); this thread takes th = part + 4 (pg + 8 n)
-    const int part = el >> 3, qq = el & 7;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) yz += s_red[(part + 4 * (pg + 8 * n)) * 8 + qq];
+    const int part = q4 >> 1, qq = (q4 & 1) * 4;
+    const float4 a0 = *(const float4*)&s_red[(part + 8 * pg) * 8 + qq];
+    const float4 a1 = *(const float4*)&s_red[(part + 8 * pg + 4) * 8 + qq];
+    yz[0] = a0.x + a1.x;
+    yz[1] = a0.y + a1.y;
+    yz[2] = a0.z + a1.z;
+    yz[3] = a0.w + a1.w;
   }
-  // every wave polls its own slots: partial values of producers pg + 8 u, in
-  // batches of 8 * kCombPer; values are summed in producer order
-  float y = 0.0f;
-  for (int base = 0; base < qt; base += 8 * kCombPer) {
-    const float* bsrc = src + (size_t)(base + pg) * 64;
-    float v[kCombPer];
+  // every wave polls its own slots with 16-byte loads: elements 4 q4 .. + 3 of
+  // the partials of producers pg + 32 u, in batches of 32 * kCombPer; values are
+  // summed in producer order
+  MARK(4);
+  const __amdgpu_buffer_rsrc_t prs = coh_rsrc(a.partial, (uint32_t)((size_t)a.batch * slices * qt * 256));
+  const uint32_t row0 = (uint32_t)((((size_t)t * slices + sl) * qt) * 256 + (32 * hf + 4 * q4) * 4);
+  float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = 0; base < qt; base += 32 * kCombPer) {
+    uint4 v[kCombPer];
     uint32_t pending = 0;
 #pragma unroll
     for (int u = 0; u < kCombPer; ++u) {
-      v[u] = 0.0f;
-      if (base + pg + 8 * u < qt) pending |= 1u << u;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (base + pg + 32 * u < qt) pending |= 1u << u;
     }
     while (true) {
       if (spent(spins, a.spin_limit)) {
         gave_up(a.err, 2);
-        y = kPoison;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = kPoison;
         break;
       }
 #pragma unroll
       for (int u = 0; u < kCombPer; ++u)
-        if ((pending >> u) & 1) v[u] = ld_coh(bsrc + (size_t)u * 512);
+        if ((pending >> u) & 1) v[u] = ld_coh128(prs, row0 + (uint32_t)(base + pg + 32 * u) * 256);
 #pragma unroll
       for (int u = 0; u < kCombPer; ++u)
-        if (!empty(v[u])) pending &= ~(1u << u);
+        if (v[u].x != kEmpty && v[u].y != kEmpty && v[u].z != kEmpty && v[u].w != kEmpty) pending &= ~(1u << u);
       if (__all(pending == 0)) break;
     }
 #pragma unroll
     for (int u = 0; u < kCombPer; ++u) {
-      if (base + pg + 8 * u < qt) {
-        y += v[u];
-        clear_coh(const_cast<float*>(bsrc) + (size_t)u * 512);
+      if (base + pg + 32 * u < qt) {
+        y[0] += __uint_as_float(v[u].x);
+        y[1] += __uint_as_float(v[u].y);
+        y[2] += __uint_as_float(v[u].z);
+        y[3] += __uint_as_float(v[u].w);
+        st_coh128(prs, row0 + (uint32_t)(base + pg + 32 * u) * 256, make_uint4(kEmpty, kEmpty, kEmpty, kEmpty));
       }
     }
   }
-  s_y[pg * 32 + el] = y + yz;
+  *(float4*)&s_y[pg * 32 + 4 * q4] = make_float4(y[0] + yz[0], y[1] + yz[1], y[2] + yz[2], y[3] + yz[3]);
   __syncthreads();
+  MARK(3);
   if (tid < 32) {
     float o = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) o += s_y[g * 32 + tid];
+#pragma unroll 8
+    for (int g = 0; g < 32; ++g) o += s_y[g * 32 + tid];
     a.out[(size_t)t * d + 64 * sl + 32 * hf + tid] = f32_to_bf16_dev(poisoned ? kPoison : o);
   }
+  MARK(5);
 }
 
 template <bool DENSE, int SLOTS>
 __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ Smem sm;
+  MARK(0);
+  // blocks in role order: every score block first (their code streams start
+  // first), then the gather, z and combine blocks; producers sit below their
+  // consumers
   int bid = blockIdx.x;
   if (!DENSE) {
     if (bid < a.n_score) {
@@ -798,6 +982,13 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
 
 }  // namespace
 
+#ifdef MOE_SEL_TIMELINE
+// copies the phase marks (kMarkBlocks x kMarkEvents wall-clock values) to host
+extern "C" int moe_sel_timeline_read(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_marks), sizeof(g_marks));
+}
+#endif
+
 bool fused_supported(int d, int m, int r, int top_e) {
   return d <= 4096 && m <= kMaxKeysPer * kThreads && top_e * r <= 256 && top_e <= 64 &&
          (m / (2 * kFusedScoreChMin)) * r <= kMaxZPart * kThreads && (r == 0 || (kThreads % r == 0 && r % 8 == 0));
@@ -809,9 +1000,9 @@ bool fused_narrow_score_ok(int m, int r) { return (m / kFusedScoreChMin) * r <= 
 
 size_t fused_lds_bytes(int d, int m, int r) {
   const size_t score = 2 * (size_t)d + 128 * (size_t)r + 512 + 1024;
-  const size_t gather = 13 * (size_t)m + 4 * (size_t)(m / kFusedScoreChMin) * (size_t)std::max(r, 1) + (size_t)kThreads * 8 * 4 +
-                        4 * (size_t)std::max(r, 1);
-  const size_t combine = (size_t)kThreads * 8 * 4 + 256 * 4 + 8 * 32 * 4;
+  const size_t gather = 8 * (size_t)m + 4 * (size_t)(m / kFusedScoreChMin) * (size_t)std::max(r, 1) +
+                        (size_t)kThreads * 8 * 4 + 4 * (size_t)std::max(r, 1);
+  const size_t combine = (size_t)kThreads * 8 * 4 + 256 * 4 + 32 * 32 * 4;
   return std::max(score, std::max(gather, combine));
 }
 
@@ -829,12 +1020,15 @@ int fused_blocks_per_cu(bool dense, int d, int m, int r) {
   return n;
 }
 
+int fused_grid(const FusedArgs& a, bool dense) {
+  return (dense ? 0 : a.n_score + a.n_z) + a.n_gather + a.n_combine;
+}
+
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream) {
   if (dense ? (a.chunk != 8 && a.chunk != kMaxChunkDense) : a.chunk != kMaxChunkSparse) return hipErrorInvalidValue;
-  const int total = (dense ? 0 : a.n_score + a.n_z) + a.n_gather + a.n_combine;
   void* args[] = {(void*)&a};
-  return hipLaunchKernel(fused_kernel(dense, a.d), dim3(total), dim3(kThreads), args, fused_lds_bytes(a.d, a.m, a.r),
-                         stream);
+  return hipLaunchKernel(fused_kernel(dense, a.d), dim3(fused_grid(a, dense)), dim3(kThreads), args,
+                         fused_lds_bytes(a.d, a.m, a.r), stream);
 }
 
 }  // namespace moe_sel

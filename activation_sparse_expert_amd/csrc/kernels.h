@@ -84,8 +84,10 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream);
 
 // Single-launch forward (fused.hip): block roles score / gather / combine.
 struct FusedArgs : FwdArgs {
-  // hand-off slots, each with one consumer, empty = 0xFFFFFFFF
-  uint64_t* xscore;  // [P][ncs][m]       (score, h_hat) for gather block (pair, c) / the z block
+  // hand-off slots, empty = 0xFFFFFFFF
+  uint64_t* xscore;  // [P][m]            (score, h_hat) of each pair, read by the pair's gather blocks and z block
+  int* readers;      // [P]               consumers that have read each pair's xscore slots; the last one empties
+                     //                   them and sets the count back to 0
   float* zpart;      // [P][m/score_ch][r] each score block's share of Q^T h_hat, for the z block
   float* partial;    // [B][d/64][top_e*nc][64] gate-weighted down partials, for combine
   float* zcopy;      // [B][d/32][top_e][r] z of each routed pair, for each combine block
@@ -94,7 +96,7 @@ struct FusedArgs : FwdArgs {
   int spin_limit;    // polls before a cross-block wait gives up (0: every wait gives up at once)
   int n_score, n_gather, n_z, n_combine;
   int nc;            // gather blocks per pair
-  int ncs;           // consumer slots per pair: the gather blocks, then the z block (if any)
+  int ncs;           // readers of a pair's xscore slots: the gather blocks and the z block (if any)
   int chunk;         // channels per gather block
   int score_ch;      // channels per score block: 32, or 64 when the grid of 32 would not fit
 };
@@ -105,6 +107,7 @@ int fused_max_chunk(bool dense);
 bool fused_narrow_score_ok(int m, int r);  // kFusedScoreChMin-channel score blocks fit the z block's slots
 size_t fused_lds_bytes(int d, int m, int r);
 int fused_blocks_per_cu(bool dense, int d, int m, int r);
+int fused_grid(const FusedArgs& a, bool dense);  // blocks of a planned call
 hipError_t launch_fused(const FusedArgs& a, bool dense, hipStream_t stream);
 
 // polls before a cross-block wait of the single-launch kernel gives up, unless the host sets another limit
