@@ -111,7 +111,8 @@ constexpr float kPoison = __builtin_nanf("");
 // unless the library is built with MOE_SEL_TIMELINE, which records the wall
 // clock of thread 0 of each block at each mark (events 0..7 per block; their
 // meaning by role: 0 entry, 1 routed, 2 first wait over / dots done, 3 select
-// done / second wait over, 4 SwiGLU done, 5 end).
+// done / second wait over, 4 SwiGLU done, 5 end; gather only: 6 gate and up
+// rows in, 7 down rows in).
 #ifdef MOE_SEL_TIMELINE
 constexpr int kMarkEvents = 8, kMarkBlocks = 8192;
 __device__ unsigned long long g_marks[kMarkBlocks * kMarkEvents];
@@ -119,8 +120,18 @@ __device__ unsigned long long g_marks[kMarkBlocks * kMarkEvents];
   do {                                                                                  \
     if (threadIdx.x == 0 && blockIdx.x < kMarkBlocks) g_marks[blockIdx.x * kMarkEvents + (ev)] = wall_clock64(); \
   } while (0)
+// where each block runs: XCC_ID (hardware register 20) above HW_ID (register 4:
+// CU, shader array and engine in bits 8..15)
+__device__ unsigned long long g_place[kMarkBlocks];
+#define PLACE()                                                                             \
+  do {                                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < kMarkBlocks)                                       \
+      g_place[blockIdx.x] = ((unsigned long long)__builtin_amdgcn_s_getreg((3 << 11) | 20) << 32) | \
+                            (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4);              \
+  } while (0)
 #else
 #define MARK(ev) ((void)0)
+#define PLACE() ((void)0)
 #endif
 
 template <int SLOTS>
@@ -658,6 +669,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
       }
     }
   }
+  MARK(6);
 #pragma unroll
   for (int i = 0; i < kMaxChunk; ++i) {
     if (i < C) {
@@ -695,6 +707,7 @@ __device__ __forceinline__ void gather_role(const FusedArgs& a, int bid, Smem& s
       for (int s = 0; s < SLOTS; ++s) axpy8_bf16(h, dv[i][s], yacc[s]);
     }
   }
+  MARK(7);
   if (bad)  // the selection came from incomplete scores: publish NaN
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u)
@@ -953,6 +966,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ Smem sm;
   MARK(0);
+  PLACE();
   // blocks in role order: every score block first (their code streams start
   // first), then the gather, z and combine blocks; producers sit below their
   // consumers
@@ -986,6 +1000,10 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
 // copies the phase marks (kMarkBlocks x kMarkEvents wall-clock values) to host
 extern "C" int moe_sel_timeline_read(unsigned long long* host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_marks), sizeof(g_marks));
+}
+// copies the blocks' placements (kMarkBlocks values) to host
+extern "C" int moe_sel_timeline_place(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_place), sizeof(g_place));
 }
 #endif
 
