@@ -252,9 +252,11 @@ bool plan_fused(moe_sel_ctx* c, const moe_sel::FwdArgs& base, bool dense, moe_se
       !moe_sel::fused_supported(base.d, base.m, base.r, base.top_e))
     return false;
   const int count = dense ? base.m : base.k;
+  // 8 channels a gather block, or 12 (dense) when that leaves too many blocks
+  const int max_chunk = moe_sel::fused_max_chunk(dense);
   int chunk = kMinChunk;
-  while (chunk < moe_sel::fused_max_chunk(dense) && (size_t)pairs * ((count + chunk - 1) / chunk) > (size_t)kTargetGather)
-    chunk *= 2;
+  while (chunk < max_chunk && (size_t)pairs * ((count + chunk - 1) / chunk) > (size_t)kTargetGather)
+    chunk = std::min(max_chunk, chunk * 3 / 2);
   moe_sel::FusedArgs f;
   static_cast<moe_sel::FwdArgs&>(f) = base;
   f.xscore = c->xscore;

@@ -52,7 +52,7 @@ namespace {
 using namespace dev;
 
 constexpr int kMaxChunkSparse = 8;   // channels per gather block, all loaded at once
-constexpr int kMaxChunkDense = 16;
+constexpr int kMaxChunkDense = 12;   // (158 VGPRs for d <= 2048: three blocks per CU)
 constexpr int kMaxKeysPer = 16;      // m <= 16 * 256
 constexpr int kDirectRank = 64;      // boundary-bin keys ranked by their owners (more: radix passes)
 static_assert(kWaves == 4, "the select reads its four wave totals as one int4");

@@ -329,11 +329,6 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
   const size_t ebase = (size_t)e * codes_dwords_per_expert(d, m);
   const uint32_t* cg = a.codes + ebase + codes_dword_index(d, m, grp, 0, 0, 16 * wave + li, lg);
   const uint32_t* cu = a.codes + ebase + codes_dword_index(d, m, grp, 1, 0, 16 * wave + li, lg);
-  // Q rows of the group, staged while the codes stream
-  if (r > 0)
-    for (int i = tid; i < 64 * r; i += kThreads)
-      s_q[i] = __uint_as_float((uint32_t)a.qmat[((size_t)e * m + 64 * grp) * r + i] << 16);
-
   // lane holds C[channel 4 lg + v][token li] of each subtile
   const int ch0 = 64 * grp + 16 * wave + 4 * lg;
   float4 st[4];
@@ -364,6 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[u][q] = *(const i32x4*)(x4 + 64 * (b + 4 * u) + 16 * q);
       }
+
 #pragma unroll
       for (int u = 0; u < SB; ++u)
 #pragma unroll
@@ -403,6 +399,30 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
     }
   }
   if (r == 0) return;
+  // Q rows of the group (64 r bf16, r <= 128) into registers, all in flight
+  // with the codes; written to LDS after the main loop
+  constexpr int kQg = 64 * 128 / 8 / kThreads;
+  const int qpieces = 8 * r;
+  const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * m + 64 * grp) * r);
+  uint4 qv[kQg];
+#pragma unroll
+  for (int u = 0; u < kQg; ++u) {
+    const int i = tid + u * kThreads;
+    qv[u] = i < qpieces ? qsrc[i] : make_uint4(0, 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int u = 0; u < kQg; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < qpieces) {
+      const uint32_t w4[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        s_q[8 * i + 2 * h] = bf16lo(w4[h]);
+        s_q[8 * i + 2 * h + 1] = bf16hi(w4[h]);
+      }
+    }
+  }
   __syncthreads();
   // this group's share of Q^T h_hat for every token of the tile
   const int groups_r = groups * r;
@@ -645,6 +665,21 @@ constexpr int kSelMaxWords = 512;  // m <= 16384
 constexpr int kSelThreads = 1024, kSelWaves = kSelThreads / 64;
 constexpr int kSelBins = 4096;     // first pass: bits 30..19
 
+// Phase marks of the select blocks: SEL_MARK(ev) compiles to nothing unless
+// the library is built with MOE_SEL_TIMELINE, which records the wall clock of
+// thread 0 of each of the first 64 blocks (events: 0 entry, 1 histogram
+// built, 2 boundary bin found, 3 candidates placed, 4 candidates ranked, 5
+// bitmap complete, 6 index list written).
+#ifdef MOE_SEL_TIMELINE
+__device__ unsigned long long g_sel_marks[64 * 8];
+#define SEL_MARK(ev)                                                                       \
+  do {                                                                                     \
+    if (threadIdx.x == 0 && blockIdx.x < 64) g_sel_marks[blockIdx.x * 8 + (ev)] = wall_clock64(); \
+  } while (0)
+#else
+#define SEL_MARK(ev) ((void)0)
+#endif
+
 // exclusive scan over the 1024 threads of a select block; s_w: kSelWaves ints
 __device__ __forceinline__ int sel_excl_scan(int v, int* s_w, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -728,6 +763,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   const int nfull = m / kSelThreads;
   const bool topk = k > 0 && k < m;
   const uint32_t* keys = (const uint32_t*)(a.score + (size_t)p * m);
+  SEL_MARK(0);
   uint32_t key[KPT];
   SEL_FOR_KEYS(key[u] = keys[j];)
   if (tid < words) s_bits[tid] = k >= m ? 0xFFFFFFFFu : 0u;
@@ -736,7 +772,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   __syncthreads();
   if (topk) {
     SEL_FOR_KEYS(atomicAdd(&s_hist[key[u] >> 19], 1);)
+    SEL_MARK(1);
     sel_find_bin<kSelBins / kSelThreads>(s_hist, k, s_tmp, s_sc);
+    SEL_MARK(2);
     // candidates: keys with (key >> cshift) == cval
     uint32_t cval = (uint32_t)s_sc[0];
     int cshift = 19;
@@ -804,6 +842,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
         })
       }
       __syncthreads();
+      SEL_MARK(3);
       const int c = tid >> 2, part = tid & 3;
       const bool live = c < ncand;
       const uint64_t kc = live ? ck[c] : 0ull;
@@ -817,6 +856,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
         const int ic = cidx[c];
         atomicOr(&s_bits[ic >> 5], 1u << (ic & 31));
       }
+      SEL_MARK(4);
     } else {
       // the krem lowest-index copies of the k-th key, one word per thread
       __syncthreads();
@@ -842,6 +882,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
     SEL_FOR_KEYS(mark_wave(s_bits, j - lane, key[u] > a.thr_bits);)
   }
   __syncthreads();
+  SEL_MARK(5);
   // ascending index list from the bitmap, one word per thread
   int* idx_out = a.sel_idx + (size_t)p * m;
   const uint32_t wb = tid < words ? s_bits[tid] : 0u;
@@ -862,6 +903,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
     a.sel_count[p] = tot;
     if (ul) a.ucount[p] = tot;
   }
+  SEL_MARK(6);
 }
 #undef SEL_FOR_KEYS
 
@@ -986,6 +1028,24 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     const int pp = a.tpair[first + (j < n ? j : 0)];
     xr[ns] = a.x + (size_t)(pp / a.top_e) * d + 8 * lg;
   }
+  // the compensation share's inputs, in flight with the weights (sparse): the
+  // Q rows of the block's channels (r <= 128 bf16 each: at most one 16-byte
+  // piece a thread), and h_hat of each (channel, token) the token selected
+  // (kCh x kT values: two a thread), zero elsewhere
+  const int qpr = (r & 7) == 0 ? r / 8 : 0;  // 16-byte pieces of a Q row (rows not 16-byte aligned: later)
+  uint4 qp = make_uint4(0, 0, 0, 0);
+  float hzv[kCh * kT / kThreads];
+  if (r > 0) {
+    const int ci = tid / max(qpr, 1), pos = kCh * chunk + ci;
+    if (tid < kCh * qpr && pos < uc)
+      qp = *(const uint4*)(a.qmat + ((size_t)e * m + ul[pos]) * r + 8 * (tid % qpr));
+#pragma unroll
+    for (int u = 0; u < kCh * kT / kThreads; ++u) {
+      const int i = tid + u * kThreads, hc = i / kT, j = i % kT, hp = kCh * chunk + hc;
+      hzv[u] = 0.0f;
+      if (j < n && hp < uc && ((um[hp] >> j) & 1ull)) hzv[u] = a.hhat[(size_t)a.tpair[first + j] * m + ul[hp]];
+    }
+  }
   const int nsteps = d / 32;
   const int kpad = a.kpad;
   constexpr int U = 8;
@@ -1047,17 +1107,26 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   }
   if (r == 0) return;
   // Q^T h_hat over this block's selected channels, per token
-  for (int i = tid; i < kCh * r; i += kThreads) {
-    const int ci = i / r, c = i % r;
-    const int pos = kCh * chunk + ci;
-    s_qr[i] = pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16) : 0.0f;
+  if (qpr) {
+    if (tid < kCh * qpr) {
+      const uint32_t w4[4] = {qp.x, qp.y, qp.z, qp.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        s_qr[8 * tid + 2 * h] = bf16lo(w4[h]);
+        s_qr[8 * tid + 2 * h + 1] = bf16hi(w4[h]);
+      }
+    }
+  } else {
+    for (int i = tid; i < kCh * r; i += kThreads) {
+      const int ci = i / r, c = i % r;
+      const int pos = kCh * chunk + ci;
+      s_qr[i] = pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16) : 0.0f;
+    }
   }
-  for (int i = tid; i < kCh * n; i += kThreads) {
-    const int ci = i / n, j = i % n;
-    const int pos = kCh * chunk + ci;
-    float hz = 0.0f;
-    if (pos < uc && ((um[pos] >> j) & 1ull)) hz = a.hhat[(size_t)a.tpair[first + j] * m + ul[pos]];
-    s_hz[ci][j] = hz;
+#pragma unroll
+  for (int u = 0; u < kCh * kT / kThreads; ++u) {
+    const int i = tid + u * kThreads;
+    s_hz[i / kT][i % kT] = hzv[u];
   }
   __syncthreads();
   for (int i = tid; i < n * r; i += kThreads) {
@@ -1096,6 +1165,7 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
 // ===========================================================================
 
 // nchg: chunks per tile in the grid, enough for the largest union of the call
+static_assert(2 * kB1Waves == kCh, "each wave of the batch-1 gate/up block takes two channels");
 __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense, int nchg) {
   __shared__ float s_hz[kCh];
   __shared__ float s_qr[kCh * 128];
@@ -1115,20 +1185,6 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
   const int r = dense ? 0 : a.r;
   const int pp = a.tpair[first];
   const int npc = d / 8;
-  // the compensation share's inputs, in flight with the weights
-  constexpr int kQPer = kCh * 128 / kB1Threads;  // r <= 128
-  float qv[kQPer];
-  if (r > 0) {
-#pragma unroll
-    for (int u = 0; u < kQPer; ++u) {
-      const int i = tid + u * kB1Threads;
-      const int ci = i / r, c = i % r, pos = kCh * chunk + ci;
-      qv[u] = i < kCh * r && pos < uc ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + ul[pos]) * r + c] << 16)
-                                      : 0.0f;
-    }
-  }
-  float hzv = 0.0f;
-  if (r > 0 && tid < kCh && kCh * chunk + tid < uc) hzv = a.hhat[(size_t)pp * m + ul[kCh * chunk + tid]];
   const uint16_t* xr = a.x + (size_t)(pp / a.top_e) * d;
   const uint16_t* rows[2];
   bool live[2];
@@ -1149,6 +1205,20 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
       uv[ci][i] = ld ? *(const uint4*)(rows[ci] + d + 8 * pc) : make_uint4(0, 0, 0, 0);
     }
   }
+  // the compensation share's inputs (sparse), addressed with this wave's own
+  // channel indices and issued after its rows (no wait before the rows): lane
+  // l < 2 r / 8 loads 16-byte piece l % (r / 8) of channel l / (r / 8)'s Q row,
+  // lanes 0 and 1 h_hat of the two channels; zero for channels past the union.
+  // Ranks that are not a multiple of 8 read Q at the end instead.
+  const int qpr = (r & 7) == 0 ? r / 8 : 0;
+  uint4 qp = make_uint4(0, 0, 0, 0);
+  float hzv = 0.0f;
+  if (r > 0) {
+    const int qc = lane / max(qpr, 1);
+    if (lane < 2 * qpr && live[qc & 1])
+      qp = *(const uint4*)(a.qmat + ((size_t)e * m + ((qc & 1) ? ul1 : ul0)) * r + 8 * (lane % qpr));
+    if (lane < 2 && live[lane]) hzv = a.hhat[(size_t)pp * m + (lane ? ul1 : ul0)];
+  }
   float sg[2] = {0.0f, 0.0f}, su[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kB1Pieces; ++i) {
@@ -1166,12 +1236,25 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
     if (lane == 0 && pos0 + ci < uc) a.hbuf[(size_t)pp * a.kpad + pos0 + ci] = f32_to_bf16_dev(silu_f32(g) * u);
   }
   if (r == 0) return;
+  // this wave's two channels' Q rows and h_hat into the block's arrays
+  if (qpr) {
+    if (lane < 2 * qpr) {
+      const uint32_t w4[4] = {qp.x, qp.y, qp.z, qp.w};
+      float* dst = s_qr + (2 * wave + lane / qpr) * r + 8 * (lane % qpr);
 #pragma unroll
-  for (int u = 0; u < kQPer; ++u) {
-    const int i = tid + u * kB1Threads;
-    if (i < kCh * r) s_qr[i] = qv[u];
+      for (int h = 0; h < 4; ++h) {
+        dst[2 * h] = bf16lo(w4[h]);
+        dst[2 * h + 1] = bf16hi(w4[h]);
+      }
+    }
+  } else {
+    for (int i = lane; i < 2 * r; i += 64) {
+      const int ci = i / r, c = i % r;
+      s_qr[(2 * wave + ci) * r + c] =
+          live[ci] ? __uint_as_float((uint32_t)a.qmat[((size_t)e * m + (ci ? ul1 : ul0)) * r + c] << 16) : 0.0f;
+    }
   }
-  if (tid < kCh) s_hz[tid] = hzv;
+  if (lane < 2) s_hz[2 * wave + lane] = hzv;
   __syncthreads();
   if (tid < r) {
     float z = 0.0f;
@@ -1225,8 +1308,13 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
   const uint16_t* hr = a.hbuf + (size_t)pp * a.kpad;
   const size_t col = (size_t)SW * sl;
   uint4 wv[kB1Rows][NP];
+  uint32_t hv[kB1Rows];  // the rows' activations (bf16 bits; rows past the union take z below)
   // loads of the rows k0 .. k0 + 7 (channel indices from ulv in the first round)
+  // and of their activations, which every lane reads unconditionally (clamped
+  // inside the row) so that the round waits for them once, with the rows
   auto load_round = [&](int k0, bool first_round) {
+#pragma unroll
+    for (int i = 0; i < kB1Rows; ++i) hv[i] = hr[min(k0 + i, a.kpad - 1)];
 #pragma unroll
     for (int i = 0; i < kB1Rows; ++i) {
       const int k = k0 + i;
@@ -1280,7 +1368,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
     for (int i = 0; i < kB1Rows; ++i) {
       const int k = k0 + i;
       if (k < ke) {
-        const float h = k < uc ? bf16f(hr[k]) : s_z[k - uc];
+        const float h = k < uc ? __uint_as_float(hv[i] << 16) : s_z[k - uc];
 #pragma unroll
         for (int q = 0; q < NP; ++q) axpy8_bf16(h, wv[i][q], acc[q]);
       }
@@ -1392,18 +1480,26 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   const int og = tid % OG, cg = tid / OG;
   const size_t col = (size_t)SW * sl + 8 * og;
   // rows k in [kb, kb + kn) of this block, read once here instead of on each
-  // stage's load path (an index load ahead of every weight load)
+  // stage's load path (an index load ahead of every weight load); the split
+  // keeps kn <= kDownChCap (checked at launch), so the weight loads' addresses
+  // come from LDS alone and every stage's loads stay in flight together
   const int kb = KS * st0, kn = min(K, KS * st1) - kb;
-  const bool staged = kn <= kDownChCap;
-  if (staged)
-    for (int i = tid; i < kn; i += kThreads) {
-      const int k = kb + i;
-      s_ch[i] = k < uc ? ul[k] : -1 - (k - uc);
+  for (int i = tid; i < kn; i += kThreads) {
+    const int k = kb + i;
+    s_ch[i] = k < uc ? ul[k] : -1 - (k - uc);
+  }
+  // the output rows' pairs, in flight with the weights
+  int prow[kMSub][4];
+#pragma unroll
+  for (int ms = 0; ms < kMSub; ++ms)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * ms + 4 * lg + v;
+      prow[ms][v] = a.tpair[first + (j < n ? j : 0)];
     }
   __syncthreads();
   auto brow = [&](int k) -> const uint16_t* {
-    k = min(k, K - 1);
-    const int c = staged ? s_ch[k - kb] : (k < uc ? ul[k] : -1 - (k - uc));
+    const int c = s_ch[min(k, K - 1) - kb];
     if (c >= 0) return a.wch + (((size_t)e * m + c) * 3 + 2) * d + col;
     return a.pmat + ((size_t)e * a.r + (-1 - c)) * d + col;
   };
@@ -1418,13 +1514,19 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   for (int ms = 0; ms < kMSub; ++ms)
 #pragma unroll
     for (int nw = 0; nw < NW; ++nw) acc[ms][nw] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 cur[RPT];
-  if (st0 < st1) {
+  // one stage: its activations first, unconditionally (clamped inside the row),
+  // then the rows of the stage after it into the other buffer, so that the
+  // waits for the activations and for this stage's rows (issued one stage
+  // earlier) leave the next rows in flight; two buffers alternate (the loop is
+  // unrolled by two), so no register copy waits for a load
+  auto stage = [&](int st, const u32x4 (&cur)[RPT], u32x4 (&nxt)[RPT]) {
+    u32x4 va[KS / 32][kMSub];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) cur[i] = *(const u32x4*)brow(KS * st0 + RPT * cg + i);
-  }
-  for (int st = st0; st < st1; ++st) {
-    u32x4 nxt[RPT];
+    for (int ks = 0; ks < KS / 32; ++ks)
+#pragma unroll
+      for (int ms = 0; ms < kMSub; ++ms) va[ks][ms] = *(const u32x4*)(hrow[ms] + min(KS * st + 32 * ks, kpad - 32));
+    // (the last stage loads its own rows again: a branch here would leave the
+    // waits below unable to count the loads in flight)
     const int stn = st + 1 < st1 ? st + 1 : st;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) nxt[i] = *(const u32x4*)brow(KS * stn + RPT * cg + i);
@@ -1442,23 +1544,27 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     for (int ks = 0; ks < KS / 32; ++ks) {
       const int k0 = KS * st + 32 * ks;
       if (k0 < K) {
-        u32x4 va[kMSub];
-#pragma unroll
-        for (int ms = 0; ms < kMSub; ++ms)
-          if (ms < msub) va[ms] = *(const u32x4*)(hrow[ms] + k0);
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
           const u32x4 bv = *(const u32x4*)(s_b + (16 * NW * wave + 16 * nw + li) * PITCH + 32 * ks + 8 * lg);
 #pragma unroll
           for (int ms = 0; ms < kMSub; ++ms)
             if (ms < msub)
-              acc[ms][nw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ms]), as_bf16x8(bv), acc[ms][nw], 0, 0, 0);
+              acc[ms][nw] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[ks][ms]), as_bf16x8(bv), acc[ms][nw], 0, 0, 0);
         }
       }
     }
     __syncthreads();
+  };
+  u32x4 buf0[RPT], buf1[RPT];
+  if (st0 < st1) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < RPT; ++i) buf0[i] = *(const u32x4*)brow(KS * st0 + RPT * cg + i);
+  }
+  for (int st = st0; st < st1; st += 2) {
+    stage(st, buf0, buf1);
+    if (st + 1 < st1) stage(st + 1, buf1, buf0);
   }
   // lane holds C[token 16 ms + 4 lg + v][output 16 NW wave + 16 nw + li]
   float* yp = a.ypart + (size_t)kci * a.batch * a.top_e * d;
@@ -1468,7 +1574,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     for (int v = 0; v < 4; ++v) {
       const int j = 16 * ms + 4 * lg + v;
       if (ms < msub && j < n) {
-        float* yrow = yp + (size_t)a.tpair[first + j] * d + (size_t)SW * sl + 16 * NW * wave + li;
+        float* yrow = yp + (size_t)prow[ms][v] * d + (size_t)SW * sl + 16 * NW * wave + li;
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) yrow[16 * nw] = acc[ms][nw][v];
       }
@@ -1483,6 +1589,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
 __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   constexpr int N = 16;  // partial values in flight per thread
   __shared__ float s_y[kWaves][64];
+  __shared__ float s_pw[64];  // the token's gate weights (top_e <= 64)
   const int per_tok = a.d / 64;
   const int t = blockIdx.x / per_tok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1492,6 +1599,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   const float* w = a.pair_w + (size_t)t * a.top_e;
   const int total = a.top_e * kc;
   const int v_lo = total * wave / kWaves, v_hi = total * (wave + 1) / kWaves;
+  // the gate weights, read once into LDS (one round trip, instead of one per
+  // partial added)
+  if (threadIdx.x < a.top_e) s_pw[threadIdx.x] = w[threadIdx.x];
+  __syncthreads();
   float y = 0.0f;
   for (int v0 = v_lo; v0 < v_hi; v0 += N) {
     float part[N];
@@ -1508,7 +1619,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
     lq = v0 % kc;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      if (v0 + u < v_hi) y += w[ls] * part[u];
+      if (v0 + u < v_hi) y += s_pw[ls] * part[u];
       if (++lq == kc) {
         lq = 0;
         ++ls;
@@ -1549,6 +1660,13 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
   kc = std::max(kc, (nst_max + kDownMaxStages - 1) / kDownMaxStages);
   return kc < 1 ? 1 : (kc > kMaxDownSplit ? kMaxDownSplit : kc);
 }
+
+#ifdef MOE_SEL_TIMELINE
+// copies the select blocks' phase marks (64 blocks x 8 wall-clock values) to host
+extern "C" int moe_sel_timeline_select(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_sel_marks), sizeof(g_sel_marks));
+}
+#endif
 
 hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int pairs = a.batch * a.top_e;
@@ -1610,6 +1728,12 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     return hipGetLastError();
   }
   const int kc = grouped_down_split(a.max_tiles, a.d, kmax, dense ? 0 : a.r);
+  {
+    // every block's rows fit its LDS index list (the split guarantees it)
+    const int ks = sw == 256 ? 32 : 128;
+    const int nst_max = (kmax + (dense ? 0 : a.r) + ks - 1) / ks;
+    if ((nst_max + kc - 1) / kc * ks > kDownChCap) return hipErrorInvalidValue;
+  }
   if (sw == 256)
     hipLaunchKernelGGL(k_down_g<4>, dim3(a.max_tiles * (a.d / 256) * kc), dim3(kThreads), 0, stream, a, dense ? 1 : 0, kc);
   else
