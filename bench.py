@@ -60,6 +60,11 @@ def algorithmic_bytes(d, m, n_exp, top_e, r, k, batch, dense=False):
     return pairs * (m * d // 2 + 12 * m + 6 * d * k + 2 * (m + d) * r) + per_tok
 
 
+def progress(msg):
+    """One line on stderr as each stage ends (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def sources_digest(paths=FUSED_SOURCES):
     h = hashlib.sha256()
     for p in paths:
@@ -388,6 +393,7 @@ def main():
     stream = torch.cuda.Stream()
     blk = Block(b, synth, torch, w, args.copies, args.tokens, stream, args.big_batch)
     setup_s = time.time() - t0
+    progress(f"{args.copies} layers prepared in {setup_s:.1f} s")
 
     spread = {}
     ms = time_block(torch, blk, k, args.steps, args.warmup, args.eager, batch, spread=spread)
@@ -396,6 +402,7 @@ def main():
     if not args.no_dense:
         single_call["dense"] = single_call_latency(torch, blk, None, batch)
     single = path == b.MOE_SEL_PATH_SINGLE_LAUNCH
+    progress(f"batch {batch}, k={k}: {ms * 1e3:.2f} us per call")
     extra_k = {}
     if not args.no_extra_budgets:
         for k2 in w["ks"]:
@@ -406,6 +413,7 @@ def main():
                                     "achieved_GBs": round(algorithmic_bytes(d, m, n_exp, top_e, r, k2, batch)
                                                           / (ms2 * 1e-3) / 1e9, 1)}
     ms_dense = None if args.no_dense else time_block(torch, blk, None, args.steps, args.warmup, args.eager, batch)
+    progress("other budgets and the dense block timed")
     big = None
     if args.big_batch:
         bb = args.big_batch
@@ -421,6 +429,7 @@ def main():
             big["speedup_vs_dense"] = round(ms_bd / ms_b, 3)
     if big is not None:
         big.update(batch_bytes(b, torch, blk, k, args.big_batch, ms_b, ms_bd))
+        progress(f"batch {args.big_batch} timed")
     ceiling = read_ceiling(b, torch, stream)
     if args.traffic_probe:
         src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(2.0)
@@ -497,17 +506,22 @@ def main():
     if args.expert_sweep:
         result["expert_count_sweep"] = expert_sweep(b, synth, torch, blk, args.steps // 2, args.warmup // 2)
         result["score_ablation"] = score_ablation(b, torch, blk, w["ks"])
+        progress("expert-count sweep and score ablation done")
     if args.threshold and args.big_batch == 64:
         result["threshold_vs_topk"] = threshold_experiment(b, synth, torch, blk, k, args.steps, args.warmup)
+        progress("threshold experiment done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(blk.host_layer0, w, k, args.cpu_seconds)
+        progress("CPU baseline done")
     blk.destroy()
     del blk
     if args.mixtral:
         result["mixtral"] = time_mixtral(b, synth, torch, stream, args.mixtral_steps, args.eager,
                                          ablation=not args.no_ablation)
+        progress("Mixtral-shaped block timed")
     if args.decode48:
         result["decode48"] = time_decode48(b, synth, torch, stream, args.decode_layers, args.decode_steps)
+        progress("48-layer decode timed")
 
     print(json.dumps(result), flush=True)
 
