@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
     i32x4 accg = i32x4{0, 0, 0, 0}, accu = i32x4{0, 0, 0, 0};
     const int8_t* x4 = xr[ns] - 16 * lg + 64 * lg;  // token row + block offset lg
     int b = 0;
-    constexpr int SB = 4;  // groups of four code blocks per iteration
+    constexpr int SB = 2;  // groups of four code blocks per iteration
     for (; b + 4 * SB <= nb; b += 4 * SB) {
       u32x4 wg[SB], wu[SB];
       i32x4 xv[SB][4];
@@ -359,6 +359,8 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[u][q] = *(const i32x4*)(x4 + 64 * (b + 4 * u) + 16 * q);
       }
+      // every load of the batch issued before the first product (110 VGPRs)
+      __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
       for (int u = 0; u < SB; ++u)
@@ -1048,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   }
   const int nsteps = d / 32;
   const int kpad = a.kpad;
-  constexpr int U = 8;
+  constexpr int U = 4;
   // token subtiles one after another (weights re-read from L2 after the first)
   for (int ns = 0; ns < nsub; ++ns) {
     f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1062,6 +1064,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
         uv[u] = *(const u32x4*)(urow + k0);
         xv[u] = *(const u32x4*)(xr[ns] + k0);
       }
+      // every load of the batch issued before the first product (the scheduler
+      // would otherwise interleave them with the MFMAs and keep few in flight);
+      // four steps a batch keep the kernel at 90 VGPRs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv[u]), as_bf16x8(xv[u]), accg, 0, 0, 0);
