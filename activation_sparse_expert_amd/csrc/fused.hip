@@ -380,15 +380,24 @@ __device__ __forceinline__ void select_consecutive(const uint32_t (&key)[MK], in
   __syncthreads();
   const int4 ws = *(const int4*)sm.sel_ws;
   const int before = incl - cnt + (wave > 0 ? ws.x : 0) + (wave > 1 ? ws.y : 0) + (wave > 2 ? ws.z : 0);
-  int above = ws.x + ws.y + ws.z + ws.w - before - cnt;  // keys in the bins above this thread's eight
+  const int above = ws.x + ws.y + ws.z + ws.w - before - cnt;  // keys in the bins above this thread's eight
+  if (above < k && k <= above + cnt) {
+    // the one thread whose bins hold the k-th largest key walks them, without
+    // branches (the other waves go straight to the barrier)
+    int acc = above, bd = 0, ad = 0, nd = 0;
+    bool found = false;
 #pragma unroll
-  for (int b = 7; b >= 0; --b) {
-    if (above < k && k <= above + h[b]) {
-      sm.sel_b[0] = tid * 8 + b;
-      sm.sel_b[1] = above;
-      sm.sel_b[2] = h[b];
+    for (int b = 7; b >= 0; --b) {
+      const bool here = !found && k <= acc + h[b];
+      bd = here ? b : bd;
+      ad = here ? acc : ad;
+      nd = here ? h[b] : nd;
+      found = found || here;
+      acc += h[b];
     }
-    above += h[b];
+    sm.sel_b[0] = tid * 8 + bd;
+    sm.sel_b[1] = ad;
+    sm.sel_b[2] = nd;
   }
   __syncthreads();
   const int4 sb = *(const int4*)sm.sel_b;
