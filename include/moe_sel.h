@@ -286,9 +286,10 @@ moe_sel_status moe_sel_set_wait_limit(moe_sel_ctx* ctx, int32_t polls);
  * every workgroup of its grid resident at once (the grid grows with batch *
  * top_e; the occupancy query decides). For the Qwen3-30B-A3B shape (d = 2048,
  * 128 experts, top-8, m = 768, r = 32) on a 256-CU MI355X that holds for batch
- * 1 only: its grid is 408 workgroups at k = 138, and batch 2 needs 816, more
- * than the 768 that fit at three per CU. Larger batches run the multi-kernel
- * path, and a forced single launch there fails with EUNSUPPORTED.
+ * <= 2 (768 workgroups fit at three per CU; at k = 138 batch 1 takes 408 and
+ * batch 2 takes 624 with 64-channel score blocks, batch 3 would take 936).
+ * Larger batches run the multi-kernel path, and a forced single launch there
+ * fails with EUNSUPPORTED.
  * Errors: EINVAL (null ctx or unknown path).
  */
 moe_sel_status moe_sel_set_path(moe_sel_ctx* ctx, moe_sel_path path);

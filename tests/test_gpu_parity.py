@@ -252,6 +252,34 @@ def test_qwen3_shape_parity(b, torch, qwen, k):
     assert abs(k / qwen.m - {100: 0.13, 138: 0.18}[k]) <= 1 / (2 * qwen.m)
 
 
+@pytest.mark.parametrize("k", [100, 138])
+def test_qwen3_batch2_single_launch(b, torch, qwen_layer, k):
+    """Two tokens of the Qwen3 shape fit the single launch at three blocks per
+    CU (64-channel score blocks at k = 138: 192 + 288 + 16 + 128 = 624 of 768);
+    selections bit-exact and outputs within tolerance. Three tokens do not fit:
+    a forced single launch is refused before anything runs."""
+    lay = qwen_layer
+    b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_SINGLE_LAUNCH)
+    lay.path = "single_launch"
+    try:
+        w = synth.WORKLOADS["qwen3"]
+        x = synth.tokens(w["wid"], 0, 3, lay.d, index=60)
+        logits = synth.router_logits(w["wid"], 0, 3, lay.E, index=60)
+        out = _run(b, torch, lay, x[:2], logits[:2], k)
+        assert b.moe_sel_last_path(lay.ctx) == b.MOE_SEL_PATH_SINGLE_LAUNCH
+        ref = lay.oracle.forward(x[:2], logits[:2], lay.top_e, k)
+        _check_selection(b, lay, ref, 2, lay.top_e, k)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+        xd, lgd = to_dev_u16(torch, x), to_dev_f32(torch, logits)
+        out3 = torch.zeros((3, lay.d), dtype=torch.int16, device="cuda")
+        with pytest.raises(b.MoeSelError) as ei:
+            b.moe_sel_forward(lay.ctx, xd, lgd, 3, lay.top_e, k, out3)
+        assert ei.value.status == b.MOE_SEL_EUNSUPPORTED
+    finally:
+        b.moe_sel_set_path(lay.ctx, b.MOE_SEL_PATH_AUTO)
+        lay.path = None
+
+
 @pytest.mark.parametrize("top_e,k", [(8, 138), (6, 100)])
 def test_qwen3_small_batch_parity(b, torch, qwen_layer, top_e, k):
     """Four tokens on the expert-grouped path: 32 or 24 routed pairs over 128
