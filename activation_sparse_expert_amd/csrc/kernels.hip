@@ -766,8 +766,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   const bool topk = k > 0 && k < m;
   const uint32_t* keys = (const uint32_t*)(a.score + (size_t)p * m);
   SEL_MARK(0);
+  // every key slot loads unconditionally (slots past m read key m - 1 and are
+  // never used), so all of a thread's loads are in flight at once; under the
+  // slots' guards each load waited for the one before
   uint32_t key[KPT];
-  SEL_FOR_KEYS(key[u] = keys[j];)
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) key[u] = keys[min(tid + u * kSelThreads, m - 1)];
   if (tid < words) s_bits[tid] = k >= m ? 0xFFFFFFFFu : 0u;
   if (topk) *(int4*)(s_hist + 4 * tid) = make_int4(0, 0, 0, 0);
   if (tid == 0) s_sc[3] = 0;  // candidate slots taken in the first pass
