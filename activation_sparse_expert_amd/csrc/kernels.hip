@@ -56,6 +56,20 @@ constexpr int kCh = 16;          // union channels per gate/up block
 constexpr int kPlanThreads = 1024;
 constexpr int kDownPitch = 40;   // halfwords per LDS row of the transposed down tile (80 bytes)
 
+// Phase marks of the one-pair-tile kernels: ROW_MARK(kern, ev) compiles to
+// nothing unless the library is built with MOE_SEL_TIMELINE, which records the
+// wall clock of thread 0 of each of the first 512 blocks (kern: 0 score, 1
+// gate/up, 2 down, 3 combine; the events are listed at each kernel).
+#ifdef MOE_SEL_TIMELINE
+__device__ unsigned long long g_row_marks[4 * 512 * 8];
+#define ROW_MARK(kern, ev)                                                                       \
+  do {                                                                                           \
+    if (threadIdx.x == 0 && blockIdx.x < 512) g_row_marks[((kern) * 512 + blockIdx.x) * 8 + (ev)] = wall_clock64(); \
+  } while (0)
+#else
+#define ROW_MARK(kern, ev) ((void)0)
+#endif
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // four byte-wide codes (t + 1) per dword, in hidden-element order (see the code layout)
@@ -504,6 +518,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   const bool x16 = a.score_kind == 3;  // int16 activations (score ablation; self-routing calls only)
   int e, pp;
   uint4 xv = make_uint4(0, 0, 0, 0);
+  ROW_MARK(0, 0);  // marks: 0 entry, 1 routed, 2 x_q and Q rows in LDS, 3 dots summed, 4 end
   if (self_route) {
     if (tile >= a.batch * a.top_e) return;  // one single-token tile per routed pair
     const int tt = tile / a.top_e;
@@ -511,6 +526,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     route_b1(a.logits + (size_t)tt * a.n_experts, a.n_experts, a.top_e, s_ids, s_w, s_rkey, s_rval);
     pp = tile;
     e = s_ids[tile % a.top_e];
+    ROW_MARK(0, 1);
   } else {
     const int ntl = *a.n_tiles;
     e = a.tile_expert[tile];
@@ -602,6 +618,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     }
   }
   __syncthreads();  // x_q and the Q rows in LDS
+  ROW_MARK(0, 2);
   CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
   for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
     if (c0 != b0) {
@@ -629,6 +646,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   // sum of (t + 1) x_q over the quarter
   s_part[wave][lane] = x16 ? 256 * code_acc_total(acc) + code_acc_total(acc_lo) : code_acc_total(acc);
   __syncthreads();
+  ROW_MARK(0, 3);
   if (wave == 0) {
     const int dg = s_part[0][lane] + s_part[2][lane] + s_part[4][lane] + s_part[6][lane];
     const int du = s_part[1][lane] + s_part[3][lane] + s_part[5][lane] + s_part[7][lane];
@@ -647,6 +665,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     for (int ch = 0; ch < 64; ++ch) z += s_h[ch] * s_q[ch * r + tid];
     a.gzpart[((size_t)pp * groups + grp) * r + tid] = z;
   }
+  ROW_MARK(0, 4);
 }
 
 // ===========================================================================
@@ -1170,8 +1189,10 @@ __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int 
 // 15 columns empty. Wave w takes channels 2w and 2w + 1 of the block; lane l
 // holds the 16-byte pieces l + 64 i of x and of both rows, so each load
 // instruction reads 1 KiB of a row in one run. fp32 products summed per lane,
-// then over the wave. Sparse blocks also leave their channels' share of
-// Q^T h_hat, as above.
+// then over the wave. Sparse blocks also leave a part of z = Q^T h_hat over
+// the skipped channels: the score blocks' shares of an even slice of the
+// groups minus the block's own channels' share, so that z is the sum of the
+// pair's gate/up blocks' parts.
 // ===========================================================================
 
 // nchg: chunks per tile in the grid, enough for the largest union of the call
@@ -1185,6 +1206,7 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // this wave's two channel indices, read with the tile's entries before the union size is known
   const int pos0 = kCh * chunk + 2 * wave;
+  ROW_MARK(1, 0);  // marks: 0 entry, 1 tile known, 2 rows in and dotted, 3 activations written, 4 end
   const int* ul = a.ulist + (size_t)tile * m;
   const int ul0 = ul[min(pos0, m - 1)], ul1 = ul[min(pos0 + 1, m - 1)];
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
@@ -1192,6 +1214,7 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
   if (tile >= ntl) return;
   const int nch = max(1, (uc + kCh - 1) / kCh);
   if (chunk >= nch) return;
+  ROW_MARK(1, 1);
   const int r = dense ? 0 : a.r;
   const int pp = a.tpair[first];
   const int npc = d / 8;
@@ -1223,11 +1246,22 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
   const int qpr = (r & 7) == 0 ? r / 8 : 0;
   uint4 qp = make_uint4(0, 0, 0, 0);
   float hzv = 0.0f;
+  // The block also adds up groups [g0, g1) of the score blocks' per-group
+  // shares of Q^T h_hat (the groups spread evenly over the pair's nch blocks),
+  // so that the down kernel sums one vector per gate/up block. Thread t < r
+  // takes column t; the first two groups load with the rows (every thread,
+  // clamped, so no load waits on a branch), any further ones at the end.
+  const int groups = m / kGroup;
+  const int g0 = groups * chunk / nch, g1 = groups * (chunk + 1) / nch;
+  const float* gzc = a.gzpart + (size_t)pp * groups * r + min(tid, max(r - 1, 0));
+  float gzv[2] = {0.0f, 0.0f};
   if (r > 0) {
     const int qc = lane / max(qpr, 1);
     if (lane < 2 * qpr && live[qc & 1])
       qp = *(const uint4*)(a.qmat + ((size_t)e * m + ((qc & 1) ? ul1 : ul0)) * r + 8 * (lane % qpr));
     if (lane < 2 && live[lane]) hzv = a.hhat[(size_t)pp * m + (lane ? ul1 : ul0)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) gzv[u] = gzc[(size_t)min(g0 + u, groups - 1) * r];
   }
   float sg[2] = {0.0f, 0.0f}, su[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -1240,11 +1274,13 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
       }
     }
   }
+  ROW_MARK(1, 2);
 #pragma unroll
   for (int ci = 0; ci < 2; ++ci) {
     const float g = wave_sum(sg[ci]), u = wave_sum(su[ci]);
     if (lane == 0 && pos0 + ci < uc) a.hbuf[(size_t)pp * a.kpad + pos0 + ci] = f32_to_bf16_dev(silu_f32(g) * u);
   }
+  ROW_MARK(1, 3);
   if (r == 0) return;
   // this wave's two channels' Q rows and h_hat into the block's arrays
   if (qpr) {
@@ -1270,8 +1306,13 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
     float z = 0.0f;
 #pragma unroll
     for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci] * s_qr[ci * r + tid];
-    a.zsel[((size_t)pp * maxch + chunk) * r + tid] = z;
+    // this block's groups (in order) minus its selected channels' share
+    float gs = g0 < g1 ? gzv[0] : 0.0f;
+    if (g0 + 1 < g1) gs += gzv[1];
+    for (int g = g0 + 2; g < g1; ++g) gs += gzc[(size_t)g * r];
+    a.zsel[((size_t)pp * maxch + chunk) * r + tid] = gs - z;
   }
+  ROW_MARK(1, 4);
 }
 
 // ===========================================================================
@@ -1282,8 +1323,9 @@ __global__ __launch_bounds__(kB1Threads) void k_gate_up_b1(FwdArgs a, int dense,
 // load reads 1 KiB of a row in one run. Wave sums meet in LDS in a fixed
 // order; every block writes its partial, zero when its range is empty. A block
 // whose range reaches the P^T rows first finishes their activations z = Q^T
-// h_hat over the skipped channels: the score blocks' per-group shares minus
-// the gate/up blocks' selected-channel shares, in fp32.
+// h_hat over the skipped channels, in fp32: the sum of the gate/up blocks'
+// parts, loaded before the block's first rows so that it is ready while
+// they stream in.
 // ===========================================================================
 constexpr int kB1Rows = 8;  // rows per wave per round
 
@@ -1304,6 +1346,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
   // largest K); the first round's channel indices are read with the tile's
   // entries, before the union size is known
   const int kb = kci * rpb;
+  ROW_MARK(2, 0);  // marks: 0 entry, 1 tile known, 2 z ready, 3 rows summed, 4 end
   const int* ul = a.ulist + (size_t)tile * m;
   int ulv[kB1Rows];
 #pragma unroll
@@ -1311,6 +1354,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile];
   if (tile >= ntl) return;
+  ROW_MARK(2, 1);
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
   const int ke = min(K, kb + rpb);
@@ -1338,21 +1382,38 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
     }
   };
   int k0 = kb + kB1Rows * wave;
+  // this block's rows reach P^T: z = Q^T h_hat over the skipped channels, the
+  // sum of the nch gate/up blocks' parts (wave w adds parts c0 .. c1 - 1 of
+  // columns lane + 64 i); the first kZv parts of the first 64 columns load
+  // before the rows, clamped, the rest after them
+  constexpr int kZv = 16;
+  const bool zblock = r > 0 && ke > max(uc, kb);
+  const int maxch = m / kCh;
+  const int nch = max(1, (uc + kCh - 1) / kCh);
+  const int c0 = nch * wave / kB1Waves, c1 = nch * (wave + 1) / kB1Waves;
+  const float* zs = a.zsel + (size_t)pp * maxch * r;
+  float zv[kZv];
+  if (zblock) {
+    const float* zc = zs + min(lane, r - 1);
+#pragma unroll
+    for (int u = 0; u < kZv; ++u) zv[u] = zc[(size_t)min(c0 + u, maxch - 1) * r];
+  }
   if (k0 < ke) load_round(k0, true);
-  if (r > 0 && ke > max(uc, kb)) {
-    // this block's rows reach P^T: z = Q^T h_hat over the skipped channels
-    const int groups = m / kGroup, maxch = m / kCh;
-    const int nch = max(1, (uc + kCh - 1) / kCh);
+  if (zblock) {
     const bool all_kept = a.k >= m;
-    const int g0 = groups * wave / kB1Waves, g1 = groups * (wave + 1) / kB1Waves;
-    const int c0 = nch * wave / kB1Waves, c1 = nch * (wave + 1) / kB1Waves;
-    const float* gz = a.gzpart + (size_t)pp * groups * r;
-    const float* zs = a.zsel + (size_t)pp * maxch * r;
     for (int cb = 0; cb < r; cb += 64) {
       const int c = cb + lane;
       float z = 0.0f;
-      if (c < r && !all_kept)
-        z = sum_strided<16>(gz + (size_t)g0 * r + c, r, g1 - g0) - sum_strided<16>(zs + (size_t)c0 * r + c, r, c1 - c0);
+      if (c < r && !all_kept) {
+        if (cb == 0) {
+#pragma unroll
+          for (int u = 0; u < kZv; ++u)
+            if (c0 + u < c1) z += zv[u];
+          z += sum_strided<16>(zs + (size_t)(c0 + kZv) * r + c, r, c1 - c0 - kZv);
+        } else {
+          z = sum_strided<16>(zs + (size_t)c0 * r + c, r, c1 - c0);
+        }
+      }
       s_zp[wave][lane] = z;
       __syncthreads();
       if (wave == 0 && c < r) {
@@ -1368,6 +1429,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
       __syncthreads();
     }
   }
+  ROW_MARK(2, 2);
   float acc[NP][8];
 #pragma unroll
   for (int q = 0; q < NP; ++q)
@@ -1385,6 +1447,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
     }
     if (k0 + kRound < ke) load_round(k0 + kRound, false);
   }
+  ROW_MARK(2, 3);
 #pragma unroll
   for (int q = 0; q < NP; ++q)
 #pragma unroll
@@ -1397,6 +1460,7 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
     for (int w = 0; w < kB1Waves; ++w) y += s_red[w][o];
     yp[o] = y;
   }
+  ROW_MARK(2, 4);
 }
 
 // ===========================================================================
@@ -1609,6 +1673,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   const float* w = a.pair_w + (size_t)t * a.top_e;
   const int total = a.top_e * kc;
   const int v_lo = total * wave / kWaves, v_hi = total * (wave + 1) / kWaves;
+  ROW_MARK(3, 0);  // marks: 0 entry, 1 partials summed, 2 end
   // the gate weights, read once into LDS (one round trip, instead of one per
   // partial added)
   if (threadIdx.x < a.top_e) s_pw[threadIdx.x] = w[threadIdx.x];
@@ -1638,12 +1703,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(FwdArgs a, int kc) {
   }
   s_y[wave][lane] = y;
   __syncthreads();
+  ROW_MARK(3, 1);
   if (wave == 0) {
     float o = 0.0f;
 #pragma unroll
     for (int g = 0; g < kWaves; ++g) o += s_y[g][lane];
     a.out[(size_t)t * a.d + i] = f32_to_bf16_dev(o);
   }
+  ROW_MARK(3, 2);
 }
 
 }  // namespace
@@ -1675,6 +1742,10 @@ int grouped_down_split(int max_tiles, int d, int kmax, int r) {
 // copies the select blocks' phase marks (64 blocks x 8 wall-clock values) to host
 extern "C" int moe_sel_timeline_select(unsigned long long* host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_sel_marks), sizeof(g_sel_marks));
+}
+// copies the one-pair-tile kernels' phase marks (4 kernels x 512 blocks x 8 values) to host
+extern "C" int moe_sel_timeline_rows(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_row_marks), sizeof(g_row_marks));
 }
 #endif
 
