@@ -454,13 +454,14 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 
 // ===========================================================================
 // Sketch scores for one-pair tiles (batch 1 and small sparse batches), one
-// block per (pair, 64-channel group) with 8 waves = (matrix, quarter of the
-// hidden dimension). Lane l is
-// channel l of the group and reads its 16-byte code piece of each 64-element
-// block, so one load instruction reads a block's 1 KiB of the group at once;
-// the token's x_q sits in LDS. The exact integer dots of the quarters are
-// added in LDS, then scores and h_hat as above, and the group's share of
-// Q^T h_hat.
+// block per (pair, 64-channel group) with 8 waves, each an eighth of the
+// hidden dimension for both matrices. Lane l is channel l of the group and
+// reads its 16-byte code piece of each 64-element block, so one load
+// instruction reads a block's 1 KiB of the group at once; the token's x_q sits
+// in LDS, and each read of it serves the gate and the up codes (the LDS
+// broadcast, not the dot products, limits this loop). The exact integer dots
+// of the eighths are added in LDS, then scores and h_hat as above, and the
+// group's share of Q^T h_hat.
 // ===========================================================================
 // kernels for one-pair tiles (batch 1, small sparse batches): 8 waves per block
 constexpr int kB1Threads = 512, kB1Waves = kB1Threads / 64;
@@ -500,9 +501,12 @@ __device__ __forceinline__ void route_b1(const float* logits, int n_experts, int
 // routes its token and quantises its x itself, as the routing kernel would, and
 // the blocks of group 0 write their pair's routing and one-token tile for the
 // later kernels.
+// X16: int16 activations (the score ablation; self-routing calls only), an
+// instance of its own so that its registers do not cost the int8 one occupancy
+template <bool X16>
 __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_route) {
   extern __shared__ float s_dyn_sb1[];  // x_q [2d] bytes (int8, or int16 high then low bytes), then Q rows [64][r]
-  __shared__ int s_part[kB1Waves][64];
+  __shared__ int s_part[kB1Waves][64], s_part2[kB1Waves][64];
   __shared__ float s_h[64];
   __shared__ uint64_t s_rkey[256];
   __shared__ float s_rval[256];
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   const int npc = d / 8;
   int8_t* s_xq = (int8_t*)s_dyn_sb1;
   float* s_q = s_dyn_sb1 + d / 2;
-  const bool x16 = a.score_kind == 3;  // int16 activations (score ablation; self-routing calls only)
+  constexpr bool x16 = X16;
   int e, pp;
   uint4 xv = make_uint4(0, 0, 0, 0);
   ROW_MARK(0, 0);  // marks: 0 entry, 1 routed, 2 x_q and Q rows in LDS, 3 dots summed, 4 end
@@ -535,15 +539,23 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
     pp = a.tpair[first];
   }
   const int t = pp / a.top_e;
-  const int mat = wave & 1, quarter = wave >> 1;
+  // wave w takes the code blocks [b0, b1) of both matrices (an eighth of the
+  // hidden dimension; d >= 512 gives every wave a block), so each x_q read
+  // from LDS feeds the gate and the up dot
   const int nb = d / kBlock;
-  const int b0 = nb * quarter / 4, b1 = nb * (quarter + 1) / 4;
-  const uint4* cp = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(d, m) +
-                                   codes_dword_index(d, m, grp, mat, 0, lane, 0));
+  const int b0 = nb * wave / kB1Waves, b1 = nb * (wave + 1) / kB1Waves;
+  const uint4* cpg = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(d, m) +
+                                    codes_dword_index(d, m, grp, 0, 0, lane, 0));
+  const uint4* cpu = (const uint4*)(a.codes + (size_t)e * codes_dwords_per_expert(d, m) +
+                                    codes_dword_index(d, m, grp, 1, 0, lane, 0));
   // every global load first: codes, Q rows, statistics, and x_q when it comes from the routing kernel
-  uint4 cb[kSB1Blk];
+  constexpr int kSB1Pair = kSB1Blk / 2;  // blocks of both matrices in flight
+  uint4 cbg[kSB1Pair], cbu[kSB1Pair];
 #pragma unroll
-  for (int i = 0; i < kSB1Blk; ++i) cb[i] = cp[(size_t)min(b0 + i, b1 - 1) * 64];
+  for (int i = 0; i < kSB1Pair; ++i) {
+    cbg[i] = cpg[(size_t)min(b0 + i, b1 - 1) * 64];
+    cbu[i] = cpu[(size_t)min(b0 + i, b1 - 1) * 64];
+  }
   constexpr int kQv = 64 * 128 * 2 / 16 / kB1Threads;  // 16-byte Q pieces per thread, r <= 128
   const int qpieces = 8 * r;
   const uint4* qsrc = (const uint4*)(a.qmat + ((size_t)e * m + 64 * grp) * r);
@@ -619,37 +631,55 @@ __global__ __launch_bounds__(kB1Threads) void k_score_b1(FwdArgs a, int self_rou
   }
   __syncthreads();  // x_q and the Q rows in LDS
   ROW_MARK(0, 2);
-  CodeAcc acc, acc_lo;  // acc_lo: the low bytes of int16 activations
-  for (int c0 = b0; c0 < b1; c0 += kSB1Blk) {
+  CodeAcc accg, accu, accg_lo, accu_lo;  // *_lo: the low bytes of int16 activations
+  for (int c0 = b0; c0 < b1; c0 += kSB1Pair) {
     if (c0 != b0) {
 #pragma unroll
-      for (int i = 0; i < kSB1Blk; ++i) cb[i] = cp[(size_t)min(c0 + i, b1 - 1) * 64];
+      for (int i = 0; i < kSB1Pair; ++i) {
+        cbg[i] = cpg[(size_t)min(c0 + i, b1 - 1) * 64];
+        cbu[i] = cpu[(size_t)min(c0 + i, b1 - 1) * 64];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < kSB1Blk; ++i) {
+    for (int i = 0; i < kSB1Pair; ++i) {
       if (c0 + i < b1) {
         const int4* xb = (const int4*)(s_xq + 64 * (c0 + i));
-        dot_codes16(cb[i].x, xb[0], acc);
-        dot_codes16(cb[i].y, xb[1], acc);
-        dot_codes16(cb[i].z, xb[2], acc);
-        dot_codes16(cb[i].w, xb[3], acc);
+        const int4 x0 = xb[0], x1 = xb[1], x2 = xb[2], x3 = xb[3];
+        dot_codes16(cbg[i].x, x0, accg);
+        dot_codes16(cbg[i].y, x1, accg);
+        dot_codes16(cbg[i].z, x2, accg);
+        dot_codes16(cbg[i].w, x3, accg);
+        dot_codes16(cbu[i].x, x0, accu);
+        dot_codes16(cbu[i].y, x1, accu);
+        dot_codes16(cbu[i].z, x2, accu);
+        dot_codes16(cbu[i].w, x3, accu);
         if (x16) {
           const int4* xl = (const int4*)(s_xq + d + 64 * (c0 + i));
-          dot_codes16_u(cb[i].x, xl[0], acc_lo);
-          dot_codes16_u(cb[i].y, xl[1], acc_lo);
-          dot_codes16_u(cb[i].z, xl[2], acc_lo);
-          dot_codes16_u(cb[i].w, xl[3], acc_lo);
+          const int4 l0 = xl[0], l1 = xl[1], l2 = xl[2], l3 = xl[3];
+          dot_codes16_u(cbg[i].x, l0, accg_lo);
+          dot_codes16_u(cbg[i].y, l1, accg_lo);
+          dot_codes16_u(cbg[i].z, l2, accg_lo);
+          dot_codes16_u(cbg[i].w, l3, accg_lo);
+          dot_codes16_u(cbu[i].x, l0, accu_lo);
+          dot_codes16_u(cbu[i].y, l1, accu_lo);
+          dot_codes16_u(cbu[i].z, l2, accu_lo);
+          dot_codes16_u(cbu[i].w, l3, accu_lo);
         }
       }
     }
   }
-  // sum of (t + 1) x_q over the quarter
-  s_part[wave][lane] = x16 ? 256 * code_acc_total(acc) + code_acc_total(acc_lo) : code_acc_total(acc);
+  // sums of (t + 1) x_q over the wave's blocks, gate then up
+  s_part[wave][lane] = x16 ? 256 * code_acc_total(accg) + code_acc_total(accg_lo) : code_acc_total(accg);
+  s_part2[wave][lane] = x16 ? 256 * code_acc_total(accu) + code_acc_total(accu_lo) : code_acc_total(accu);
   __syncthreads();
   ROW_MARK(0, 3);
   if (wave == 0) {
-    const int dg = s_part[0][lane] + s_part[2][lane] + s_part[4][lane] + s_part[6][lane];
-    const int du = s_part[1][lane] + s_part[3][lane] + s_part[5][lane] + s_part[7][lane];
+    int dg = 0, du = 0;
+#pragma unroll
+    for (int w = 0; w < kB1Waves; ++w) {
+      dg += s_part[w][lane];
+      du += s_part2[w][lane];
+    }
     float h, sc;
     pinned_score(dg - qs, du - qs, xe, st, h, sc, a.score_kind);
     const int j = 64 * grp + lane;
@@ -725,16 +755,22 @@ __device__ __forceinline__ int sel_excl_scan(int v, int* s_w, int* total) {
 template <int BPT>
 __device__ __forceinline__ void sel_find_bin(const int* s_hist, int kr, int* s_tmp, int* s_sc) {
   __syncthreads();
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int h[BPT], c = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     h[i] = s_hist[BPT * tid + i];
     c += h[i];
   }
-  int total;
-  const int before = sel_excl_scan(c, s_tmp, &total);
-  int above = total - before - c;  // keys in bins above this thread's
+  // keys in bins above this thread's: those of the later waves, then of the
+  // later lanes of this wave (s_tmp is not written again before the barrier
+  // that ends this call)
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int above = __builtin_amdgcn_readlane(incl, 63) - incl;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) above += w > wave ? s_tmp[w] : 0;
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (above < kr && kr <= above + h[i]) {
@@ -747,41 +783,36 @@ __device__ __forceinline__ void sel_find_bin(const int* s_hist, int kr, int* s_t
   __syncthreads();
 }
 
-// A wave's predicate as bitmap words: the wave's lanes hold the 64 indices
-// j0 .. j0 + 63 (j0 a multiple of 64), so the two words are this wave's alone
-// in a pass. mark_wave ORs them in; store_wave writes them whole (words not
-// yet written). All lanes of the wave call.
+// A wave's predicate ORed into the bitmap: the wave's lanes hold the 64
+// indices j0 .. j0 + 63 (j0 a multiple of 64), so the two words are this
+// wave's alone in a pass. All lanes of the wave call.
 __device__ __forceinline__ void mark_wave(uint32_t* bits, int j0, bool pred) {
   const uint64_t b = __ballot(pred);
   const int lane = threadIdx.x & 63;
   if (lane == 0 && (uint32_t)b) bits[j0 >> 5] |= (uint32_t)b;
   if (lane == 32 && (uint32_t)(b >> 32)) bits[(j0 >> 5) + 1] |= (uint32_t)(b >> 32);
 }
-__device__ __forceinline__ void store_wave(uint32_t* bits, int j0, bool pred) {
-  const uint64_t b = __ballot(pred);
-  if ((threadIdx.x & 63) == 0) *(uint64_t*)(bits + (j0 >> 5)) = b;
-}
 
-// Key slot u of a thread is j = tid + 1024 u. Slots below nfull = m / 1024 are
-// valid in every thread, slot nfull only where j < m: the guard is a uniform
-// branch for the full slots, so the unrolled loops carry no per-key exec masks.
-// As m is a multiple of 64, a wave's slot is valid in all lanes or none.
+// Key slot u of a thread is j = tid + 1024 u. As m is a multiple of 64, a
+// wave's slot is valid in all lanes or none: the guard compares the wave's
+// first index (a scalar) with m, a scalar branch with no per-key exec masks.
 #define SEL_FOR_KEYS(BODY)                                     \
   _Pragma("unroll") for (int u = 0; u < KPT; ++u) {            \
     const int j = tid + u * kSelThreads;                       \
-    if (u < nfull || (u == nfull && j < m)) { BODY }           \
+    if (jw0 + u * kSelThreads < m) { BODY }                    \
   }
 
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tiles) {
+  static_assert(KPT <= 64, "lane u keeps key slot u's ballot");
   __shared__ __align__(16) int s_hist[kSelBins];  // histograms, then candidates
   __shared__ __align__(8) uint32_t s_bits[kSelMaxWords];
-  __shared__ int s_tmp[kSelWaves + 2];
+  __shared__ __align__(16) int s_tmp[kSelWaves + 2];
   __shared__ int s_sc[4];
   const int p = blockIdx.x;
   const int m = a.m, k = a.k, words = m / 32;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nfull = m / kSelThreads;
+  const int jw0 = __builtin_amdgcn_readfirstlane(tid - lane);  // the wave's first key index
   const bool topk = k > 0 && k < m;
   const uint32_t* keys = (const uint32_t*)(a.score + (size_t)p * m);
   SEL_MARK(0);
@@ -810,13 +841,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
     uint64_t* ck = (uint64_t*)s_hist;  // kSelCand order keys (the histogram is consumed)
     int* cidx = s_hist + 2 * kSelCand;
     if (ncand <= kSelCand) {
-      // keys above the boundary bin into the bitmap; the bin's keys take slots
-      // one by one (there are few) instead of from a block scan
-      SEL_FOR_KEYS(const uint32_t dg = key[u] >> 19; store_wave(s_bits, j - lane, dg > cval); if (dg == cval) {
-        const int slot = atomicAdd(&s_sc[3], 1);
-        ck[slot] = order_key(key[u], j);
-        cidx[slot] = j;
-      })
+      // keys above the boundary bin into the bitmap: lane u of a wave keeps
+      // the wave's slot-u ballot (two words, whole: no other wave writes them)
+      // and all slots are stored at once after the pass; the bin's keys take
+      // slots one by one (there are few) instead of from a block scan
+      uint32_t above_lo = 0, above_hi = 0;
+      SEL_FOR_KEYS(const uint32_t dg = key[u] >> 19; const uint64_t ab = __ballot(dg > cval);
+                   above_lo = lane == u ? (uint32_t)ab : above_lo;
+                   above_hi = lane == u ? (uint32_t)(ab >> 32) : above_hi; if (dg == cval) {
+                     const int slot = atomicAdd(&s_sc[3], 1);
+                     ck[slot] = order_key(key[u], j);
+                     cidx[slot] = j;
+                   })
+      if (lane < KPT && jw0 + lane * kSelThreads < m)
+        *(uint64_t*)(s_bits + ((jw0 + lane * kSelThreads) >> 5)) = ((uint64_t)above_hi << 32) | above_lo;
       placed = true;
     } else {
       // ties or clusters: radix passes over the bits 31..20, 19..9 and 8..0 of the
@@ -908,23 +946,55 @@ __global__ __launch_bounds__(kSelThreads) void k_select(FwdArgs a, int pair_tile
   }
   __syncthreads();
   SEL_MARK(5);
-  // ascending index list from the bitmap, one word per thread
+  // Ascending index list from the bitmap: wave 0 turns the words' bit counts
+  // into exclusive prefix sums (8 words per lane; the histogram's LDS is free
+  // by now), then each wave places its own key slots: the 64 channels of a
+  // wave's slot are two bitmap words, so a selected lane's rank is the prefix
+  // before them plus the selected lanes below it, and the wave's stores cover
+  // consecutive list entries.
+  int* s_pre = s_hist;  // [kSelMaxWords + 1]
+  if (tid < 64) {
+    constexpr int kWpl = kSelMaxWords / 64;
+    int c[kWpl], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kWpl; ++i) {
+      const int q = kWpl * lane + i;
+      c[i] = q < words ? __popc(s_bits[q]) : 0;
+      sum += c[i];
+    }
+    const int incl = wave_incl_scan(sum);
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < kWpl; ++i) {
+      s_pre[kWpl * lane + i] = run;
+      run += c[i];
+    }
+    if (lane == 63) s_pre[kSelMaxWords] = incl;
+  }
+  __syncthreads();
   int* idx_out = a.sel_idx + (size_t)p * m;
-  const uint32_t wb = tid < words ? s_bits[tid] : 0u;
-  int tot;
-  int pos = sel_excl_scan(__popc(wb), s_tmp, &tot);
-  uint32_t rest = wb;
   // one pair per tile: tile p is pair p alone, and its union is the selection
   // itself (the row kernels that read it need no token masks)
   int* ul = pair_tiles ? a.ulist + (size_t)p * m : nullptr;
-  while (rest) {
-    const int jj = 32 * tid + __ffs(rest) - 1;
-    if (ul) ul[pos] = jj;
-    idx_out[pos++] = jj;
-    rest &= rest - 1u;
+  // every slot's two words and prefix are read first (clamped inside the
+  // arrays; slots past m are not used), so the reads wait once, not per slot
+  uint64_t wbits[KPT];
+  int pre[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int q = min((jw0 + u * kSelThreads) >> 5, kSelMaxWords - 2);
+    wbits[u] = *(const uint64_t*)(s_bits + q);
+    pre[u] = s_pre[q];
   }
-  if (tid < words) a.selbits[(size_t)p * words + tid] = wb;
+  SEL_FOR_KEYS(if ((wbits[u] >> lane) & 1u) {
+    const int pos = pre[u] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(wbits[u] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)wbits[u], 0u));
+    idx_out[pos] = j;
+    if (ul) ul[pos] = j;
+  })
+  if (tid < words) a.selbits[(size_t)p * words + tid] = s_bits[tid];
   if (tid == 0) {
+    const int tot = s_pre[kSelMaxWords];
     a.sel_count[p] = tot;
     if (ul) a.ucount[p] = tot;
   }
@@ -1764,9 +1834,12 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a, pair_tiles ? 1 : 0);
   if (!pair_tiles) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   if (!dense) {
-    if (b1)
-      hipLaunchKernelGGL(k_score_b1, dim3(a.max_tiles * groups), dim3(kB1Threads), 2 * (size_t)a.d + 256 * (size_t)a.r,
-                         stream, a, self_route ? 1 : 0);
+    if (b1 && a.score_kind == 3)
+      hipLaunchKernelGGL(k_score_b1<true>, dim3(a.max_tiles * groups), dim3(kB1Threads),
+                         2 * (size_t)a.d + 256 * (size_t)a.r, stream, a, self_route ? 1 : 0);
+    else if (b1)
+      hipLaunchKernelGGL(k_score_b1<false>, dim3(a.max_tiles * groups), dim3(kB1Threads),
+                         2 * (size_t)a.d + 256 * (size_t)a.r, stream, a, self_route ? 1 : 0);
     else
       hipLaunchKernelGGL(k_score_g, dim3(a.max_tiles * groups), dim3(kThreads),
                          ((size_t)kT * 64 + (size_t)64 * a.r) * 4, stream, a);
