@@ -70,6 +70,20 @@ __device__ unsigned long long g_row_marks[4 * 512 * 8];
 #define ROW_MARK(kern, ev) ((void)0)
 #endif
 
+// Phase marks of the expert-tile gate/up (kern 0) and down (kern 1) kernels,
+// the same way: thread 0 of each of the first 8192 blocks; events 0 entry, 1
+// tile known, 2 weights consumed, 3 end (a block with no work: 0 and 3 only).
+#ifdef MOE_SEL_TIMELINE
+__device__ unsigned long long g_tile_marks[2 * 8192 * 4];
+#define TILE_MARK_AT(kern, idx, ev)                                                          \
+  do {                                                                                       \
+    if (threadIdx.x == 0 && (idx) < 8192) g_tile_marks[((kern) * 8192 + (idx)) * 4 + (ev)] = wall_clock64(); \
+  } while (0)
+#else
+#define TILE_MARK_AT(kern, idx, ev) ((void)0)
+#endif
+#define TILE_MARK(kern, ev) TILE_MARK_AT(kern, blockIdx.x, ev)
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // four byte-wide codes (t + 1) per dword, in hidden-element order (see the code layout)
@@ -1091,19 +1105,24 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
 // four waves. Activations of tokens that did not select a channel are zero.
 // Blocks of a sparse call also leave their channels' share of Q^T h_hat per
 // token, from which k_zfin finishes the compensation coordinates.
+//
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
-  __shared__ f32x4 s_acc[kWaves][2][64];  // 8 KiB
-  __shared__ float s_hz[kCh][kT];
-  __shared__ float s_qr[kCh * 128];
+struct GateUpSmem {
+  f32x4 acc[kWaves][2][64];  // 8 KiB
+  float hz[kCh][kT];
+  float qr[kCh * 128];
+};
+
+__device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int tile, int chunk, int item,
+                                             GateUpSmem& sm) {
+  auto& s_acc = sm.acc;
+  auto& s_hz = sm.hz;
+  float* s_qr = sm.qr;
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
-  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
-  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
-  if (tile >= ntl) return;
-  const int nch = max(1, (uc + kCh - 1) / kCh);
-  if (chunk >= nch) return;
+  TILE_MARK_AT(0, item, 1);
   const int nsub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -1126,20 +1145,30 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   // the compensation share's inputs, in flight with the weights (sparse): the
   // Q rows of the block's channels (r <= 128 bf16 each: at most one 16-byte
   // piece a thread), and h_hat of each (channel, token) the token selected
-  // (kCh x kT values: two a thread), zero elsewhere
+  // (kCh x kT values: two a thread), zero elsewhere. Lane c < kCh of every
+  // wave holds the block's channel c (the A rows), so the channel indices come
+  // from a lane shuffle, not a load; the token masks and pairs load with the
+  // channel indices, and every load is unconditional at a clamped address and
+  // masked afterwards, so none of them waits on a branch or adds a round trip
+  // before the weights.
+  // (the raw values are masked where the tail uses them: a select here would
+  // wait for its load).
   const int qpr = (r & 7) == 0 ? r / 8 : 0;  // 16-byte pieces of a Q row (rows not 16-byte aligned: later)
+  constexpr int kHz = kCh * kT / kThreads;
   uint4 qp = make_uint4(0, 0, 0, 0);
-  float hzv[kCh * kT / kThreads];
+  float hzv[kHz];
+  uint64_t umv[kHz];
   if (r > 0) {
-    const int ci = tid / max(qpr, 1), pos = kCh * chunk + ci;
-    if (tid < kCh * qpr && pos < uc)
-      qp = *(const uint4*)(a.qmat + ((size_t)e * m + ul[pos]) * r + 8 * (tid % qpr));
+    int tpv[kHz];
 #pragma unroll
-    for (int u = 0; u < kCh * kT / kThreads; ++u) {
-      const int i = tid + u * kThreads, hc = i / kT, j = i % kT, hp = kCh * chunk + hc;
-      hzv[u] = 0.0f;
-      if (j < n && hp < uc && ((um[hp] >> j) & 1ull)) hzv[u] = a.hhat[(size_t)a.tpair[first + j] * m + ul[hp]];
+    for (int u = 0; u < kHz; ++u) {
+      const int i = tid + u * kThreads, hc = i / kT, j = i % kT;
+      umv[u] = um[min(kCh * chunk + hc, max(uc - 1, 0))];
+      tpv[u] = a.tpair[first + min(j, n - 1)];
     }
+    if (qpr) qp = *(const uint4*)(a.qmat + ((size_t)e * m + __shfl(ja, min(tid / qpr, kCh - 1), 64)) * r + 8 * (tid % qpr));
+#pragma unroll
+    for (int u = 0; u < kHz; ++u) hzv[u] = a.hhat[(size_t)tpv[u] * m + __shfl(ja, (tid + u * kThreads) / kT, 64)];
   }
   const int nsteps = d / 32;
   const int kpad = a.kpad;
@@ -1176,6 +1205,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     }
     s_acc[wave][0][lane] = accg;
     s_acc[wave][1][lane] = accu;
+    TILE_MARK_AT(0, item, 2);
     __syncthreads();
     // wave 0 finishes the subtile: lane holds channels 4 lg + v, token 16 ns + li
     if (wave == 0) {
@@ -1204,11 +1234,15 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     }
     __syncthreads();
   }
-  if (r == 0) return;
+  if (r == 0) {
+    TILE_MARK_AT(0, item, 3);
+    return;
+  }
   // Q^T h_hat over this block's selected channels, per token
   if (qpr) {
     if (tid < kCh * qpr) {
-      const uint32_t w4[4] = {qp.x, qp.y, qp.z, qp.w};
+      const bool live = kCh * chunk + tid / qpr < uc;
+      const uint32_t w4[4] = {live ? qp.x : 0u, live ? qp.y : 0u, live ? qp.z : 0u, live ? qp.w : 0u};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         s_qr[8 * tid + 2 * h] = bf16lo(w4[h]);
@@ -1223,9 +1257,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < kCh * kT / kThreads; ++u) {
-    const int i = tid + u * kThreads;
-    s_hz[i / kT][i % kT] = hzv[u];
+  for (int u = 0; u < kHz; ++u) {
+    const int i = tid + u * kThreads, hc = i / kT, j = i % kT;
+    s_hz[hc][j] = j < n && kCh * chunk + hc < uc && ((umv[u] >> j) & 1ull) ? hzv[u] : 0.0f;
   }
   __syncthreads();
   for (int i = tid; i < n * r; i += kThreads) {
@@ -1235,6 +1269,20 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
     for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci][j] * s_qr[ci * r + c];
     a.zsel[((size_t)a.tpair[first + j] * maxch + chunk) * r + c] = z;
   }
+  TILE_MARK_AT(0, item, 3);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
+  __shared__ GateUpSmem sm;
+  const int maxch = a.m / kCh;
+  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
+  TILE_MARK(0, 0);
+  const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  if (tile >= ntl || chunk >= max(1, (uc + kCh - 1) / kCh)) {
+    TILE_MARK(0, 3);
+    return;
+  }
+  gate_up_item(a, dense, tile, chunk, blockIdx.x, sm);
 }
 
 // sum of p[q * stride] for q < count in index order, N loads in flight at a time
@@ -1608,9 +1656,13 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   const int per_tile = slices * kc;
   const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
   const int sl = rem % slices, kci = rem / slices;
+  TILE_MARK(1, 0);
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
-  if (tile >= ntl) return;
+  if (tile >= ntl) {
+    TILE_MARK(1, 3);
+    return;
+  }
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
   const int nst = (K + KS - 1) / KS;
@@ -1658,20 +1710,23 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   for (int ms = 0; ms < kMSub; ++ms)
 #pragma unroll
     for (int nw = 0; nw < NW; ++nw) acc[ms][nw] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // one stage: its activations first, unconditionally (clamped inside the row),
-  // then the rows of the stage after it into the other buffer, so that the
-  // waits for the activations and for this stage's rows (issued one stage
-  // earlier) leave the next rows in flight; two buffers alternate (the loop is
-  // unrolled by two), so no register copy waits for a load
-  auto stage = [&](int st, const u32x4 (&cur)[RPT], u32x4 (&nxt)[RPT]) {
-    u32x4 va[KS / 32][kMSub];
+  // one stage: the activations and rows of the stage after it go into the
+  // other buffers first (activations clamped inside the row), then this
+  // stage's, issued one stage earlier, are waited for, which leaves the next
+  // stage's loads in flight; two buffer sets alternate (the loop is unrolled by
+  // two), so no register copy waits for a load
+  typedef u32x4 ActBuf[KS / 32][kMSub];
+  auto load_act = [&](int st, ActBuf& va) {
 #pragma unroll
     for (int ks = 0; ks < KS / 32; ++ks)
 #pragma unroll
       for (int ms = 0; ms < kMSub; ++ms) va[ks][ms] = *(const u32x4*)(hrow[ms] + min(KS * st + 32 * ks, kpad - 32));
+  };
+  auto stage = [&](int st, const u32x4 (&cur)[RPT], const ActBuf& va, u32x4 (&nxt)[RPT], ActBuf& nva) {
     // (the last stage loads its own rows again: a branch here would leave the
     // waits below unable to count the loads in flight)
     const int stn = st + 1 < st1 ? st + 1 : st;
+    load_act(stn, nva);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) nxt[i] = *(const u32x4*)brow(KS * stn + RPT * cg + i);
     // 4 x 8 transpose: output o gets channels RPT cg .. RPT cg + 3
@@ -1702,14 +1757,18 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
     __syncthreads();
   };
   u32x4 buf0[RPT], buf1[RPT];
+  ActBuf va0, va1;
   if (st0 < st1) {
+    load_act(st0, va0);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) buf0[i] = *(const u32x4*)brow(KS * st0 + RPT * cg + i);
   }
+  TILE_MARK(1, 1);
   for (int st = st0; st < st1; st += 2) {
-    stage(st, buf0, buf1);
-    if (st + 1 < st1) stage(st + 1, buf1, buf0);
+    stage(st, buf0, va0, buf1, va1);
+    if (st + 1 < st1) stage(st + 1, buf1, va1, buf0, va0);
   }
+  TILE_MARK(1, 2);
   // lane holds C[token 16 ms + 4 lg + v][output 16 NW wave + 16 nw + li]
   float* yp = a.ypart + (size_t)kci * a.batch * a.top_e * d;
 #pragma unroll
@@ -1723,6 +1782,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
         for (int nw = 0; nw < NW; ++nw) yrow[16 * nw] = acc[ms][nw][v];
       }
     }
+  TILE_MARK(1, 3);
 }
 
 // Per token and 64 outputs (one block): the four waves take contiguous quarters
@@ -1816,6 +1876,10 @@ extern "C" int moe_sel_timeline_select(unsigned long long* host) {
 // copies the one-pair-tile kernels' phase marks (4 kernels x 512 blocks x 8 values) to host
 extern "C" int moe_sel_timeline_rows(unsigned long long* host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_row_marks), sizeof(g_row_marks));
+}
+// copies the expert-tile kernels' phase marks (2 kernels x 8192 blocks x 4 values) to host
+extern "C" int moe_sel_timeline_tiles(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tile_marks), sizeof(g_tile_marks));
 }
 #endif
 
