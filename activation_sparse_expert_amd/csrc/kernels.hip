@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -370,49 +371,8 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
   const size_t blk4 = (size_t)64;  // u32x4 per (group, matrix, block)
   const u32x4* cg4 = (const u32x4*)(a.codes + ebase + codes_dword_index(d, m, grp, 0, lg, 16 * wave + li, 0));
   const u32x4* cu4 = (const u32x4*)(a.codes + ebase + codes_dword_index(d, m, grp, 1, lg, 16 * wave + li, 0));
-  // token subtiles one after another: the codes stream from HBM once and are
-  // re-read from L2 for the later subtiles of a large tile
-  for (int ns = 0; ns < nsub; ++ns) {
-    i32x4 accg = i32x4{0, 0, 0, 0}, accu = i32x4{0, 0, 0, 0};
-    const int8_t* x4 = xr[ns] - 16 * lg + 64 * lg;  // token row + block offset lg
-    int b = 0;
-    constexpr int SB = 2;  // groups of four code blocks per iteration
-    for (; b + 4 * SB <= nb; b += 4 * SB) {
-      u32x4 wg[SB], wu[SB];
-      i32x4 xv[SB][4];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        wg[u] = cg4[(size_t)(b + 4 * u) * blk4];
-        wu[u] = cu4[(size_t)(b + 4 * u) * blk4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[u][q] = *(const i32x4*)(x4 + 64 * (b + 4 * u) + 16 * q);
-      }
-      // every load of the batch issued before the first product (110 VGPRs)
-      __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-      for (int u = 0; u < SB; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[u][q]), xv[u][q], accg, 0, 0, 0);
-          accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[u][q]), xv[u][q], accu, 0, 0, 0);
-        }
-    }
-    for (; b + 4 <= nb; b += 4) {
-      const u32x4 wg = cg4[(size_t)b * blk4], wu = cu4[(size_t)b * blk4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const i32x4 xv = *(const i32x4*)(x4 + 64 * b + 16 * q);
-        accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wg[q]), xv, accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(wu[q]), xv, accu, 0, 0, 0);
-      }
-    }
-    // remaining blocks one at a time: lane (i + 16 g) takes dword g of block b
-    for (; b < nb; ++b) {
-      const i32x4 xv = *(const i32x4*)(xr[ns] + 64 * b);
-      accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(cg[(size_t)b * 256]), xv, accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_codes(cu[(size_t)b * 256]), xv, accu, 0, 0, 0);
-    }
+  // scores and h_hat of token subtile ns from its exact integer sums
+  auto finish = [&](int ns, const i32x4& accg, const i32x4& accu) {
     const int j = 16 * ns + li;
     if (j < n) {
       const int pp = a.tpair[first + j];
@@ -427,7 +387,77 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) s_h[j * 64 + 16 * wave + 4 * lg + v] = h[v];
     }
-  }
+  };
+  // Every code load feeds all NS token subtiles of the tile, so a tile of more
+  // than 16 tokens streams its codes once instead of once per subtile.
+  static_assert(kMSub == 2, "one or two token subtiles per tile");
+  auto run = [&](auto ns_count) {
+    constexpr int NS = decltype(ns_count)::value;
+    constexpr int SB = NS == 1 ? 2 : 1;  // groups of four code blocks per iteration
+    i32x4 accg[NS], accu[NS];
+    const int8_t* x4[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      accg[ns] = accu[ns] = i32x4{0, 0, 0, 0};
+      x4[ns] = xr[ns] - 16 * lg + 64 * lg;  // token row + block offset lg
+    }
+    int b = 0;
+    for (; b + 4 * SB <= nb; b += 4 * SB) {
+      u32x4 wg[SB], wu[SB];
+      i32x4 xv[SB][4][NS];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        wg[u] = cg4[(size_t)(b + 4 * u) * blk4];
+        wu[u] = cu4[(size_t)(b + 4 * u) * blk4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) xv[u][q][ns] = *(const i32x4*)(x4[ns] + 64 * (b + 4 * u) + 16 * q);
+      }
+      // every load of the batch issued before the first product
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x4 eg = expand_codes(wg[u][q]), eu = expand_codes(wu[u][q]);
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) {
+            accg[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eg, xv[u][q][ns], accg[ns], 0, 0, 0);
+            accu[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eu, xv[u][q][ns], accu[ns], 0, 0, 0);
+          }
+        }
+    }
+    for (; b + 4 <= nb; b += 4) {
+      const u32x4 wg = cg4[(size_t)b * blk4], wu = cu4[(size_t)b * blk4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x4 eg = expand_codes(wg[q]), eu = expand_codes(wu[q]);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const i32x4 xv = *(const i32x4*)(x4[ns] + 64 * b + 16 * q);
+          accg[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eg, xv, accg[ns], 0, 0, 0);
+          accu[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eu, xv, accu[ns], 0, 0, 0);
+        }
+      }
+    }
+    // remaining blocks one at a time: lane (i + 16 g) takes dword g of block b
+    for (; b < nb; ++b) {
+      const i32x4 eg = expand_codes(cg[(size_t)b * 256]), eu = expand_codes(cu[(size_t)b * 256]);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const i32x4 xv = *(const i32x4*)(xr[ns] + 64 * b);
+        accg[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eg, xv, accg[ns], 0, 0, 0);
+        accu[ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(eu, xv, accu[ns], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) finish(ns, accg[ns], accu[ns]);
+  };
+  if (nsub > 1)
+    run(std::integral_constant<int, 2>{});
+  else
+    run(std::integral_constant<int, 1>{});
   if (r == 0) return;
   // Q rows of the group (64 r bf16, r <= 128) into registers, all in flight
   // with the codes; written to LDS after the main loop
@@ -1172,42 +1202,13 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
   }
   const int nsteps = d / 32;
   const int kpad = a.kpad;
-  constexpr int U = 4;
-  // token subtiles one after another (weights re-read from L2 after the first)
-  for (int ns = 0; ns < nsub; ++ns) {
-    f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
-    int s = wave;
-    for (; s + kWaves * (U - 1) < nsteps; s += kWaves * U) {
-      u32x4 gv[U], uv[U], xv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k0 = 32 * (s + kWaves * u);
-        gv[u] = *(const u32x4*)(grow + k0);
-        uv[u] = *(const u32x4*)(urow + k0);
-        xv[u] = *(const u32x4*)(xr[ns] + k0);
-      }
-      // every load of the batch issued before the first product (the scheduler
-      // would otherwise interleave them with the MFMAs and keep few in flight);
-      // four steps a batch keep the kernel at 90 VGPRs
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv[u]), as_bf16x8(xv[u]), accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv[u]), as_bf16x8(xv[u]), accu, 0, 0, 0);
-      }
-    }
-    for (; s < nsteps; s += kWaves) {
-      const int k0 = 32 * s;
-      const u32x4 gv = *(const u32x4*)(grow + k0), uv = *(const u32x4*)(urow + k0);
-      const u32x4 xv = *(const u32x4*)(xr[ns] + k0);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv), as_bf16x8(xv), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv), as_bf16x8(xv), accu, 0, 0, 0);
-    }
+  // wave 0 finishes token subtile ns from the four waves' sums: lane holds
+  // channels 4 lg + v, token 16 ns + li
+  auto finish = [&](int ns, const f32x4& accg, const f32x4& accu) {
     s_acc[wave][0][lane] = accg;
     s_acc[wave][1][lane] = accu;
     TILE_MARK_AT(0, item, 2);
     __syncthreads();
-    // wave 0 finishes the subtile: lane holds channels 4 lg + v, token 16 ns + li
     if (wave == 0) {
       const int j = 16 * ns + li;
       f32x4 g = s_acc[0][0][lane], u = s_acc[0][1][lane];
@@ -1233,7 +1234,60 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
       }
     }
     __syncthreads();
-  }
+  };
+  // Wave w takes the contiguous quarter [s_beg, s_end) of the hidden
+  // dimension's 32-element steps, so a batch of U steps reads U x 64
+  // consecutive bytes of each of the 16 rows (quarters interleaved step by
+  // step left each batch's pieces 256 bytes apart). Every weight load feeds
+  // all NS token subtiles of the tile, so a tile of more than 16 tokens reads
+  // its rows once instead of once per subtile.
+  const int s_beg = nsteps * wave / kWaves, s_end = nsteps * (wave + 1) / kWaves;
+  static_assert(kMSub == 2, "one or two token subtiles per tile");
+  auto run = [&](auto ns_count) {
+    constexpr int NS = decltype(ns_count)::value;
+    constexpr int U = 4;
+    f32x4 accg[NS], accu[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) accg[ns] = accu[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int s = s_beg;
+    for (; s + U <= s_end; s += U) {
+      u32x4 gv[U], uv[U], xv[U][NS];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k0 = 32 * (s + u);
+        gv[u] = *(const u32x4*)(grow + k0);
+        uv[u] = *(const u32x4*)(urow + k0);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) xv[u][ns] = *(const u32x4*)(xr[ns] + k0);
+      }
+      // every load of the batch issued before the first product (the scheduler
+      // would otherwise interleave them with the MFMAs and keep few in flight)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          accg[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv[u]), as_bf16x8(xv[u][ns]), accg[ns], 0, 0, 0);
+          accu[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv[u]), as_bf16x8(xv[u][ns]), accu[ns], 0, 0, 0);
+        }
+    }
+    for (; s < s_end; ++s) {
+      const int k0 = 32 * s;
+      const u32x4 gv = *(const u32x4*)(grow + k0), uv = *(const u32x4*)(urow + k0);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const u32x4 xv = *(const u32x4*)(xr[ns] + k0);
+        accg[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(gv), as_bf16x8(xv), accg[ns], 0, 0, 0);
+        accu[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uv), as_bf16x8(xv), accu[ns], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) finish(ns, accg[ns], accu[ns]);
+  };
+  if (nsub > 1)
+    run(std::integral_constant<int, 2>{});
+  else
+    run(std::integral_constant<int, 1>{});
   if (r == 0) {
     TILE_MARK_AT(0, item, 3);
     return;
