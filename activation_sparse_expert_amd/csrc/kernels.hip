@@ -1711,6 +1711,21 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   const int tile = blockIdx.x / per_tile, rem = blockIdx.x % per_tile;
   const int sl = rem % slices, kci = rem / slices;
   TILE_MARK(1, 0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int* ul = a.ulist + (size_t)tile * m;
+  // The block takes the tile's stages kci, kci + kc, kci + 2 kc, ... (KS rows
+  // each), so which union positions it reads does not depend on the union's
+  // size: their channel indices load here, with the tile's entries, in one
+  // round trip (thread t: stage t / KS of the block, row t % KS; clamped into
+  // the tile's list, and positions past the union are not used as indices).
+  constexpr int kIdxPer = kDownChCap / kThreads;
+  int uidx[kIdxPer];
+#pragma unroll
+  for (int q = 0; q < kIdxPer; ++q) {
+    const int t = tid + q * kThreads;
+    uidx[q] = ul[min(KS * (kci + kc * (t / KS)) + t % KS, m - 1)];
+  }
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
   const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   if (tile >= ntl) {
@@ -1720,23 +1735,20 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   const int r = dense ? 0 : a.r;
   const int K = uc + r;
   const int nst = (K + KS - 1) / KS;
-  const int spc = (nst + kc - 1) / kc;
-  const int st0 = kci * spc, st1 = min(nst, st0 + spc);
+  const int spc = nst > kci ? (nst - kci + kc - 1) / kc : 0;  // this block's stages
   const int msub = (n + 15) >> 4;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const int* ul = a.ulist + (size_t)tile * m;
   const int kpad = a.kpad;
   const int og = tid % OG, cg = tid / OG;
   const size_t col = (size_t)SW * sl + 8 * og;
-  // rows k in [kb, kb + kn) of this block, read once here instead of on each
-  // stage's load path (an index load ahead of every weight load); the split
-  // keeps kn <= kDownChCap (checked at launch), so the weight loads' addresses
-  // come from LDS alone and every stage's loads stay in flight together
-  const int kb = KS * st0, kn = min(K, KS * st1) - kb;
-  for (int i = tid; i < kn; i += kThreads) {
-    const int k = kb + i;
-    s_ch[i] = k < uc ? ul[k] : -1 - (k - uc);
+  // the block's rows, read from LDS on each stage's load path: a union
+  // position's channel, or -1 - (row of P^T); rows past K (the last stage's
+  // tail, whose activations are zero) take any channel of the expert. The
+  // split keeps spc KS <= kDownChCap (checked at launch).
+#pragma unroll
+  for (int q = 0; q < kIdxPer; ++q) {
+    const int t = tid + q * kThreads;
+    const int k = KS * (kci + kc * (t / KS)) + t % KS;
+    if (t < spc * KS) s_ch[t] = k < uc || k >= K ? min(max(uidx[q], 0), m - 1) : -1 - (k - uc);
   }
   // the output rows' pairs, in flight with the weights
   int prow[kMSub][4];
@@ -1748,8 +1760,9 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
       prow[ms][v] = a.tpair[first + (j < n ? j : 0)];
     }
   __syncthreads();
-  auto brow = [&](int k) -> const uint16_t* {
-    const int c = s_ch[min(k, K - 1) - kb];
+  // row `row` of the block's stage i
+  auto brow = [&](int i, int row) -> const uint16_t* {
+    const int c = s_ch[KS * i + row];
     if (c >= 0) return a.wch + (((size_t)e * m + c) * 3 + 2) * d + col;
     return a.pmat + ((size_t)e * a.r + (-1 - c)) * d + col;
   };
@@ -1776,13 +1789,15 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
 #pragma unroll
       for (int ms = 0; ms < kMSub; ++ms) va[ks][ms] = *(const u32x4*)(hrow[ms] + min(KS * st + 32 * ks, kpad - 32));
   };
-  auto stage = [&](int st, const u32x4 (&cur)[RPT], const ActBuf& va, u32x4 (&nxt)[RPT], ActBuf& nva) {
+  // stage i of the block is the tile's stage kci + kc i
+  auto stage = [&](int i, const u32x4 (&cur)[RPT], const ActBuf& va, u32x4 (&nxt)[RPT], ActBuf& nva) {
     // (the last stage loads its own rows again: a branch here would leave the
     // waits below unable to count the loads in flight)
-    const int stn = st + 1 < st1 ? st + 1 : st;
-    load_act(stn, nva);
+    const int in = i + 1 < spc ? i + 1 : i;
+    const int st = kci + kc * i;
+    load_act(kci + kc * in, nva);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) nxt[i] = *(const u32x4*)brow(KS * stn + RPT * cg + i);
+    for (int q = 0; q < RPT; ++q) nxt[q] = *(const u32x4*)brow(in, RPT * cg + q);
     // 4 x 8 transpose: output o gets channels RPT cg .. RPT cg + 3
 #pragma unroll
     for (int o = 0; o < 8; ++o) {
@@ -1812,15 +1827,15 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
   };
   u32x4 buf0[RPT], buf1[RPT];
   ActBuf va0, va1;
-  if (st0 < st1) {
-    load_act(st0, va0);
+  if (spc > 0) {
+    load_act(kci, va0);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) buf0[i] = *(const u32x4*)brow(KS * st0 + RPT * cg + i);
+    for (int q = 0; q < RPT; ++q) buf0[q] = *(const u32x4*)brow(0, RPT * cg + q);
   }
   TILE_MARK(1, 1);
-  for (int st = st0; st < st1; st += 2) {
-    stage(st, buf0, va0, buf1, va1);
-    if (st + 1 < st1) stage(st + 1, buf1, va1, buf0, va0);
+  for (int i = 0; i < spc; i += 2) {
+    stage(i, buf0, va0, buf1, va1);
+    if (i + 1 < spc) stage(i + 1, buf1, va1, buf0, va0);
   }
   TILE_MARK(1, 2);
   // lane holds C[token 16 ms + 4 lg + v][output 16 NW wave + 16 nw + li]
