@@ -1133,6 +1133,9 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
 // SwiGLU of 16 union channels for every token of a tile: bf16 MFMA 16x16x32
 // (M = channels, N = tokens, K = hidden), the hidden dimension split over the
 // four waves. Activations of tokens that did not select a channel are zero.
+// Expert-tile activations (here, k_zfin, k_down_g) sit in the activation
+// buffer's row of the token's tile slot (tile_first + token), so the down
+// kernel addresses them without the slot's pair index.
 // Blocks of a sparse call also leave their channels' share of Q^T h_hat per
 // token, from which k_zfin finishes the compensation coordinates.
 //
@@ -1226,11 +1229,10 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
         hb[v] = f32_to_bf16_dev(h);
       }
       if (j < n) {
-        const int pp = a.tpair[first + j];
         uint2 w2;
         w2.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
         w2.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-        *(uint2*)(a.hbuf + (size_t)pp * kpad + kCh * chunk + 4 * lg) = w2;
+        *(uint2*)(a.hbuf + (size_t)(first + j) * kpad + kCh * chunk + 4 * lg) = w2;
       }
     }
     __syncthreads();
@@ -1677,7 +1679,7 @@ __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
       for (int h = kZWaves / 2; h > 0; h >>= 1)
 #pragma unroll
         for (int w = 0; w < h; ++w) zt[w] += zt[w + h];
-      a.hbuf[(size_t)pp * kpad + uc + c] = f32_to_bf16_dev(zt[0]);
+      a.hbuf[(size_t)(tf + j) * kpad + uc + c] = f32_to_bf16_dev(zt[0]);
     }
     __syncthreads();
   }
@@ -1770,7 +1772,7 @@ __global__ __launch_bounds__(kThreads) void k_down_g(FwdArgs a, int dense, int k
 #pragma unroll
   for (int ms = 0; ms < kMSub; ++ms) {
     const int j = 16 * ms + li;
-    hrow[ms] = a.hbuf + (size_t)a.tpair[first + (j < n ? j : 0)] * kpad + 8 * lg;
+    hrow[ms] = a.hbuf + (size_t)(first + (j < n ? j : 0)) * kpad + 8 * lg;
   }
   f32x4 acc[kMSub][NW];
 #pragma unroll
