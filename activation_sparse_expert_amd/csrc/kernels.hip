@@ -491,8 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_score_g(FwdArgs a) {
     float z = 0.0f;
 #pragma unroll 8
     for (int ch = 0; ch < 64; ++ch) z += s_h[j * 64 + ch] * s_q[ch * r + c];
-    const int pp = a.tpair[first + j];
-    a.gzpart[(size_t)pp * groups_r + grp * r + c] = z;
+    a.gzpart[(size_t)(first + j) * groups_r + grp * r + c] = z;  // by tile slot
   }
 }
 
@@ -1146,15 +1145,16 @@ struct GateUpSmem {
   float qr[kCh * 128];
 };
 
+// uc, e, first, n: the tile's union size, expert, first slot and tokens; ja:
+// the block's union channel for lane li (read with them, clamped into the
+// expert: positions past the union are masked where they are used)
 __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int tile, int chunk, int item,
-                                             GateUpSmem& sm) {
+                                             GateUpSmem& sm, int uc, int e, int first, int n, int ja) {
   auto& s_acc = sm.acc;
   auto& s_hz = sm.hz;
   float* s_qr = sm.qr;
   const int d = a.d, m = a.m;
   const int maxch = m / kCh;
-  const int uc = a.ucount[tile];
-  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   TILE_MARK_AT(0, item, 1);
   const int nsub = (n + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1163,9 +1163,7 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
   const int* ul = a.ulist + (size_t)tile * m;
   const uint64_t* um = a.umask + (size_t)tile * m;
 
-  // A rows: union channel 16 chunk + li (clamped); B columns: token 16 ns + li (clamped)
-  const int pos_a = min(kCh * chunk + li, max(uc - 1, 0));
-  const int ja = uc > 0 ? ul[pos_a] : 0;
+  // A rows: union channel 16 chunk + li; B columns: token 16 ns + li (clamped)
   const uint16_t* grow = a.wch + ((size_t)e * m + ja) * 3 * d + 8 * lg;
   const uint16_t* urow = grow + d;
   const uint16_t* xr[kMSub];
@@ -1254,14 +1252,17 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
     int s = s_beg;
     for (; s + U <= s_end; s += U) {
       u32x4 gv[U], uv[U], xv[U][NS];
+      // the weights first: the first batch's are issued while the token rows'
+      // pair indices are still on their way
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int k0 = 32 * (s + u);
-        gv[u] = *(const u32x4*)(grow + k0);
-        uv[u] = *(const u32x4*)(urow + k0);
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) xv[u][ns] = *(const u32x4*)(xr[ns] + k0);
+        gv[u] = *(const u32x4*)(grow + 32 * (s + u));
+        uv[u] = *(const u32x4*)(urow + 32 * (s + u));
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) xv[u][ns] = *(const u32x4*)(xr[ns] + 32 * (s + u));
       // every load of the batch issued before the first product (the scheduler
       // would otherwise interleave them with the MFMAs and keep few in flight)
       __builtin_amdgcn_sched_barrier(0);
@@ -1323,7 +1324,7 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
     float z = 0.0f;
 #pragma unroll
     for (int ci = 0; ci < kCh; ++ci) z += s_hz[ci][j] * s_qr[ci * r + c];
-    a.zsel[((size_t)a.tpair[first + j] * maxch + chunk) * r + c] = z;
+    a.zsel[((size_t)(first + j) * maxch + chunk) * r + c] = z;  // by tile slot
   }
   TILE_MARK_AT(0, item, 3);
 }
@@ -1333,12 +1334,17 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   const int maxch = a.m / kCh;
   const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
   TILE_MARK(0, 0);
+  // the tile's entries and this block's channel indices in one round trip
+  // (a union position is read before the union's size is known)
+  const int li = threadIdx.x & 15;
+  const int ul_raw = a.ulist[(size_t)tile * a.m + min(kCh * chunk + li, a.m - 1)];
   const int ntl = *a.n_tiles, uc = a.ucount[tile];
+  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
   if (tile >= ntl || chunk >= max(1, (uc + kCh - 1) / kCh)) {
     TILE_MARK(0, 3);
     return;
   }
-  gate_up_item(a, dense, tile, chunk, blockIdx.x, sm);
+  gate_up_item(a, dense, tile, chunk, blockIdx.x, sm, uc, e, first, n, min(max(ul_raw, 0), a.m - 1));
 }
 
 // sum of p[q * stride] for q < count in index order, N loads in flight at a time
@@ -1656,13 +1662,13 @@ __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
   const int nch = max(1, (uc + kCh - 1) / kCh);
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
-  const int pp = a.tpair[tf + j];
+  const int slot = tf + j;  // the shares and the activations are kept by tile slot
   // wave q sums its quarter of the groups and of the gate/up blocks
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g0 = groups * q / kZWaves, g1 = groups * (q + 1) / kZWaves;
   const int c0 = nch * q / kZWaves, c1 = nch * (q + 1) / kZWaves;
-  const float* gz = a.gzpart + (size_t)pp * groups * r;
-  const float* zs = a.zsel + (size_t)pp * maxch * r;
+  const float* gz = a.gzpart + (size_t)slot * groups * r;
+  const float* zs = a.zsel + (size_t)slot * maxch * r;
   for (int cb = 0; cb < kend - uc; cb += 64) {
     const int c = cb + lane;
     float z = 0.0f;
@@ -1679,7 +1685,7 @@ __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
       for (int h = kZWaves / 2; h > 0; h >>= 1)
 #pragma unroll
         for (int w = 0; w < h; ++w) zt[w] += zt[w + h];
-      a.hbuf[(size_t)(tf + j) * kpad + uc + c] = f32_to_bf16_dev(zt[0]);
+      a.hbuf[(size_t)slot * kpad + uc + c] = f32_to_bf16_dev(zt[0]);
     }
     __syncthreads();
   }
