@@ -55,7 +55,6 @@ constexpr int kT = kTileTokens;  // tokens per tile
 constexpr int kMSub = kT / 16;   // MFMA subtiles of 16 tokens
 constexpr int kCh = 16;          // union channels per gate/up block
 constexpr int kPlanThreads = 1024;
-constexpr int kDownPitch = 40;   // halfwords per LDS row of the transposed down tile (80 bytes)
 
 // Phase marks of the one-pair-tile kernels: ROW_MARK(kern, ev) compiles to
 // nothing unless the library is built with MOE_SEL_TIMELINE, which records the
@@ -91,16 +90,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ i32x4 expand_codes(uint32_t w) {
   return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
                (int)((w >> 6) & 0x03030303u)};
-}
-
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  v |= (uint32_t)dpp_i<kQuadXor1>((int)v);
-  v |= (uint32_t)dpp_i<kQuadXor2>((int)v);
-  v |= (uint32_t)dpp_i<kRowHalfMirror>((int)v);
-  v |= (uint32_t)dpp_i<kRowMirror>((int)v);
-  v |= (uint32_t)dpp_i<kRowBcast15, 0xA>((int)v);
-  v |= (uint32_t)dpp_i<kRowBcast31, 0xC>((int)v);
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // ===========================================================================
@@ -841,7 +830,7 @@ __device__ __forceinline__ void mark_wave(uint32_t* bits, int j0, bool pred) {
 // first index (a scalar) with m, a scalar branch with no per-key exec masks.
 #define SEL_FOR_KEYS(BODY)                                     \
   _Pragma("unroll") for (int u = 0; u < KPT; ++u) {            \
-    const int j = tid + u * kSelThreads;                       \
+    [[maybe_unused]] const int j = tid + u * kSelThreads;      \
     if (jw0 + u * kSelThreads < m) { BODY }                    \
   }
 
@@ -1073,7 +1062,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
   const int ntl = *a.n_tiles, first = a.tile_first[tile], n = a.tile_n[tile];
   if (tile >= ntl) return;
   const int m = a.m, words = m / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   int* ul = a.ulist + (size_t)tile * m;
   uint64_t* um = a.umask + (size_t)tile * m;
   if (dense) {
