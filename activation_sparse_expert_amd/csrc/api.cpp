@@ -49,6 +49,7 @@ struct moe_sel_ctx {
   int* ulist = nullptr;
   uint64_t* umask = nullptr;
   int* ucount = nullptr;
+  int* slot_ucount = nullptr;
   uint16_t* hbuf = nullptr;
   float* zsel = nullptr;
   int max_tiles = 0;
@@ -236,6 +237,7 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.ulist = c->ulist;
   a.umask = c->umask;
   a.ucount = c->ucount;
+  a.slot_ucount = c->slot_ucount;
   a.hbuf = c->hbuf;
   a.zsel = c->zsel;
   a.max_tiles = moe_sel::grouped_max_tiles(batch * top_e, c->cfg.n_experts);
@@ -411,6 +413,7 @@ moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
   ALLOC(ulist, mt * m);
   ALLOC(umask, mt * m);
   ALLOC(ucount, mt);
+  ALLOC(slot_ucount, pairs);
   ALLOC(hbuf, pairs * moe_sel::grouped_kpad(c.m, c.rank));
   ALLOC(zsel, pairs * (m / 16) * std::max<size_t>(r, 1));
 

@@ -47,7 +47,9 @@ struct FwdArgs {
   int* ulist;              // [max_tiles][m] union channels of a tile, ascending
   uint64_t* umask;         // [max_tiles][m] which tile tokens selected each union channel
   int* ucount;             // [max_tiles]
-  uint16_t* hbuf;          // [P][kpad] bf16 activations by union position, then z
+  int* slot_ucount;        // [P] union size of the tile of each tile slot (expert tiles)
+  uint16_t* hbuf;          // [P][kpad] bf16 activations by union position, then z (rows: pairs for one-pair
+                           // tiles, tile slots (tile_first + token) for expert tiles)
   float* zsel;             // [P][m/16][r] Q^T h_hat over one gate/up block's selected channels
   int max_tiles, kpad;
 };

@@ -1072,6 +1072,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
       um[j] = all;
     }
     if (tid == 0) a.ucount[tile] = m;
+    if (tid < n) a.slot_ucount[first + tid] = m;
     return;
   }
   if (n == 1) {
@@ -1082,6 +1083,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
       um[j] = 1ull;
     }
     if (tid == 0) a.ucount[tile] = cnt;
+    if (tid == 0) a.slot_ucount[first] = cnt;
     return;
   }
   // one thread per bitmap word: the tokens' words, their union, then the listed
@@ -1115,6 +1117,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     run += tot;
   }
   if (tid == 0) a.ucount[tile] = run;
+  if (tid < n) a.slot_ucount[first + tid] = run;  // for k_zfin, which runs per slot
 }
 
 // ===========================================================================
@@ -1633,25 +1636,25 @@ __global__ __launch_bounds__(kB1Threads) void k_down_b1(FwdArgs a, int dense, in
 }
 
 // ===========================================================================
-// After gate/up, one block per (tile, token): z = Q^T h_hat over the
-// token's skipped channels, i.e. the score blocks' per-group shares (all
-// channels) minus the gate/up blocks' selected-channel shares, each summed in
-// block order, written to the activation columns after the union; then zeros
-// up to the next multiple of 32 columns.
+// After gate/up, one block per tile slot (a token of a tile): z = Q^T h_hat
+// over the token's skipped channels, i.e. the score blocks' per-group shares
+// (all channels) minus the gate/up blocks' selected-channel shares, each
+// summed in block order, written to the activation columns after the union;
+// then zeros up to the next multiple of 32 columns. The grid is the call's
+// pairs (every slot holds one), and the slot's union size is its only entry,
+// so no block waits for tile entries or exits without work.
 // ===========================================================================
 
 constexpr int kZThreads = 256, kZWaves = kZThreads / 64;
 
 __global__ __launch_bounds__(kZThreads) void k_zfin(FwdArgs a) {
   __shared__ float s_part[kZWaves][64];
-  const int tile = blockIdx.x / kT, j = blockIdx.x % kT;
-  const int ntl = *a.n_tiles, tn = a.tile_n[tile], uc = a.ucount[tile], tf = a.tile_first[tile];
-  if (tile >= ntl || j >= tn) return;
+  const int slot = blockIdx.x;  // the shares and the activations are kept by tile slot
+  const int uc = a.slot_ucount[slot];
   const int m = a.m, r = a.r, maxch = m / kCh, kpad = a.kpad, groups = m / kGroup;
   const int nch = max(1, (uc + kCh - 1) / kCh);
   const int kend = (uc + r + 31) / 32 * 32;
   const bool all_kept = a.k >= m;
-  const int slot = tf + j;  // the shares and the activations are kept by tile slot
   // wave q sums its quarter of the groups and of the gate/up blocks
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g0 = groups * q / kZWaves, g1 = groups * (q + 1) / kZWaves;
@@ -1994,7 +1997,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
     hipLaunchKernelGGL(k_gate_up_g, dim3(a.max_tiles * (a.m / kCh)), dim3(kThreads), 0, stream, a, dense ? 1 : 0);
   }
   // the row down kernel finishes the compensation coordinates itself
-  if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.max_tiles * kT), dim3(kZThreads), 0, stream, a);
+  if (!dense && !b1) hipLaunchKernelGGL(k_zfin, dim3(a.batch * a.top_e), dim3(kZThreads), 0, stream, a);
   const int sw = grouped_down_width(a.d);
   if (b1) {
     const int kc1 = grouped_down_split_b1(kmax, dense ? 0 : a.r);
