@@ -50,6 +50,9 @@ struct moe_sel_ctx {
   uint64_t* umask = nullptr;
   int* ucount = nullptr;
   int* slot_ucount = nullptr;
+  int* tile_choff = nullptr;
+  int* n_items = nullptr;
+  int* gu_items = nullptr;
   uint16_t* hbuf = nullptr;
   float* zsel = nullptr;
   int max_tiles = 0;
@@ -238,6 +241,9 @@ moe_sel::FwdArgs make_args(moe_sel_ctx* c, const uint16_t* x, const float* logit
   a.umask = c->umask;
   a.ucount = c->ucount;
   a.slot_ucount = c->slot_ucount;
+  a.tile_choff = c->tile_choff;
+  a.n_items = c->n_items;
+  a.gu_items = c->gu_items;
   a.hbuf = c->hbuf;
   a.zsel = c->zsel;
   a.max_tiles = moe_sel::grouped_max_tiles(batch * top_e, c->cfg.n_experts);
@@ -414,6 +420,9 @@ moe_sel_status alloc_layer(moe_sel_ctx* ctx) {
   ALLOC(umask, mt * m);
   ALLOC(ucount, mt);
   ALLOC(slot_ucount, pairs);
+  ALLOC(tile_choff, mt);
+  ALLOC(n_items, 1);
+  ALLOC(gu_items, mt * (m / 16) * moe_sel::kGuItemInts);
   ALLOC(hbuf, pairs * moe_sel::grouped_kpad(c.m, c.rank));
   ALLOC(zsel, pairs * (m / 16) * std::max<size_t>(r, 1));
 

@@ -48,6 +48,10 @@ struct FwdArgs {
   uint64_t* umask;         // [max_tiles][m] which tile tokens selected each union channel
   int* ucount;             // [max_tiles]
   int* slot_ucount;        // [P] union size of the tile of each tile slot (expert tiles)
+  int* tile_choff;         // [max_tiles] first gate/up work item of each tile
+  int* n_items;            // [1] gate/up work items of the call
+  int* gu_items;           // [max_tiles * m/16][kGuItemInts] gate/up work items, tile by tile: tile, chunk,
+                           // expert, first slot, tokens, union size, 2 unused, the chunk's 16 union channels
   uint16_t* hbuf;          // [P][kpad] bf16 activations by union position, then z (rows: pairs for one-pair
                            // tiles, tile slots (tile_first + token) for expert tiles)
   float* zsel;             // [P][m/16][r] Q^T h_hat over one gate/up block's selected channels
@@ -56,6 +60,7 @@ struct FwdArgs {
 
 // expert tiles hold up to this many tokens
 constexpr int kTileTokens = 32;
+constexpr int kGuItemInts = 24;  // ints per gate/up work item
 inline int grouped_max_tiles(int pairs, int n_experts) {
   const int bound = pairs / kTileTokens + (pairs < n_experts ? pairs : n_experts);
   return pairs < bound ? pairs : bound;

@@ -245,17 +245,30 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(FwdArgs a, int pair_ti
 }
 
 // ===========================================================================
+// Gate/up work items a tile of n tokens is given, one per chunk of kCh union
+// channels: as many as its largest union can fill (n k channels, all m for
+// dense and threshold calls), at least one (a k = 0 call still writes its
+// compensation share). The plan lays them out tile by tile; the union kernel
+// fills them; the gate/up kernel runs one block per item, so its live blocks
+// come first in the grid instead of interleaved with chunks past the unions.
+__device__ __forceinline__ int gu_chunk_bound(const FwdArgs& a, int n, int dense) {
+  const int maxch = a.m / kCh;
+  if (dense || a.thr_mode) return maxch;
+  const long u = min((long)a.m, (long)n * a.k);
+  return max(1, (int)((u + kCh - 1) / kCh));
+}
+
 // Plan: pairs sorted by (expert, token) and cut into tiles of up to kT tokens.
 // One block. Pairs of a token have distinct experts, so within an expert the
 // order by token is the order by pair index, and a token's rank among an
 // expert's tokens is a popcount over per-expert token bitmaps of a chunk.
 // ===========================================================================
-__global__ __launch_bounds__(kPlanThreads) void k_plan(FwdArgs a) {
+__global__ __launch_bounds__(kPlanThreads) void k_plan(FwdArgs a, int dense) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1024];
   __shared__ int s_run[1024];
   __shared__ uint32_t s_bm[1024 * 4];  // per expert: bitmap of the chunk's tokens (<= 128)
-  __shared__ int s_wc[16], s_wt[16];
+  __shared__ int s_wc[16], s_wt[16], s_wk[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.n_experts, P = a.batch * a.top_e;
   if (tid < E) {
@@ -268,28 +281,40 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(FwdArgs a) {
   // exclusive scans over experts of the pair counts and of the tile counts
   const int c = tid < E ? s_cnt[tid] : 0;
   const int nt = (c + kT - 1) / kT;
-  const int ic = wave_incl_scan(c), it = wave_incl_scan(nt);
+  int nk = 0;  // gate/up work items of this expert's tiles
+  for (int i = 0; i < nt; ++i) nk += gu_chunk_bound(a, min(kT, c - i * kT), dense);
+  const int ic = wave_incl_scan(c), it = wave_incl_scan(nt), ik = wave_incl_scan(nk);
   if (lane == 63) {
     s_wc[wave] = ic;
     s_wt[wave] = it;
+    s_wk[wave] = ik;
   }
   __syncthreads();
-  int bc = 0, bt = 0, tot_t = 0;
+  int bc = 0, bt = 0, bk = 0, tot_t = 0, tot_k = 0;
   for (int w = 0; w < kPlanThreads / 64; ++w) {
     bc += w < wave ? s_wc[w] : 0;
     bt += w < wave ? s_wt[w] : 0;
+    bk += w < wave ? s_wk[w] : 0;
     tot_t += s_wt[w];
+    tot_k += s_wk[w];
   }
   const int off = bc + ic - c, toff = bt + it - nt;
   if (tid < E) {
     s_off[tid] = off;
+    int ko = bk + ik - nk;
     for (int i = 0; i < nt; ++i) {
+      const int tn = min(kT, c - i * kT);
       a.tile_expert[toff + i] = tid;
       a.tile_first[toff + i] = off + i * kT;
-      a.tile_n[toff + i] = min(kT, c - i * kT);
+      a.tile_n[toff + i] = tn;
+      a.tile_choff[toff + i] = ko;
+      ko += gu_chunk_bound(a, tn, dense);
     }
   }
-  if (tid == 0) *a.n_tiles = tot_t;
+  if (tid == 0) {
+    *a.n_tiles = tot_t;
+    *a.n_items = tot_k;
+  }
   // stable placement, chunks of ct tokens (ct * top_e <= 1024 pairs, ct <= 128)
   const int ct = max(1, min(128, kPlanThreads / a.top_e));
   for (int t0 = 0; t0 < a.batch; t0 += ct) {
@@ -1060,12 +1085,30 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
   __shared__ int s_tmp[kWaves];
   const int tile = blockIdx.x;
   const int ntl = *a.n_tiles, first = a.tile_first[tile], n = a.tile_n[tile];
+  const int e = a.tile_expert[tile], choff = a.tile_choff[tile];
   if (tile >= ntl) return;
   const int m = a.m, words = m / 32;
   const int tid = threadIdx.x;
   int* ul = a.ulist + (size_t)tile * m;
   uint64_t* um = a.umask + (size_t)tile * m;
-  if (dense) {
+  // the tile's gate/up work items: channel of union position pos, and (once the
+  // union's size is known) the headers and the positions past the union
+  const int nb = gu_chunk_bound(a, n, dense);
+  int* items = a.gu_items + (size_t)choff * kGuItemInts;
+  auto item_ch = [&](int pos, int ch) { items[(pos / kCh) * kGuItemInts + 8 + pos % kCh] = ch; };
+  auto finish_items = [&](int uc) {
+    for (int pos = uc + tid; pos < nb * kCh; pos += kThreads) item_ch(pos, 0);
+    if (tid < nb) {
+      int* h = items + tid * kGuItemInts;
+      h[0] = tile;
+      h[1] = tid;
+      h[2] = e;
+      h[3] = first;
+      h[4] = n;
+      h[5] = uc;
+    }
+  };
+  if (dense) {  // (dense gate/up blocks map themselves to every chunk: no items)
     const uint64_t all = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
     for (int j = tid; j < m; j += kThreads) {
       ul[j] = j;
@@ -1079,11 +1122,14 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
     const int pp = a.tpair[first];
     const int cnt = a.sel_count[pp];
     for (int j = tid; j < cnt; j += kThreads) {
-      ul[j] = a.sel_idx[(size_t)pp * m + j];
+      const int ch = a.sel_idx[(size_t)pp * m + j];
+      ul[j] = ch;
       um[j] = 1ull;
+      item_ch(j, ch);
     }
     if (tid == 0) a.ucount[tile] = cnt;
     if (tid == 0) a.slot_ucount[first] = cnt;
+    finish_items(cnt);
     return;
   }
   // one thread per bitmap word: the tokens' words, their union, then the listed
@@ -1111,6 +1157,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
       if ((u >> bit) & 1u) {
         ul[pos] = 32 * w + bit;
         um[pos] = (uint64_t)v[bit];
+        item_ch(pos, 32 * w + bit);
         ++pos;
       }
     }
@@ -1118,6 +1165,7 @@ __global__ __launch_bounds__(kThreads) void k_union(FwdArgs a, int dense) {
   }
   if (tid == 0) a.ucount[tile] = run;
   if (tid < n) a.slot_ucount[first + tid] = run;  // for k_zfin, which runs per slot
+  finish_items(run);
 }
 
 // ===========================================================================
@@ -1323,20 +1371,43 @@ __device__ __forceinline__ void gate_up_item(const FwdArgs& a, int dense, int ti
 
 __global__ __launch_bounds__(kThreads) void k_gate_up_g(FwdArgs a, int dense) {
   __shared__ GateUpSmem sm;
-  const int maxch = a.m / kCh;
-  const int tile = blockIdx.x / maxch, chunk = blockIdx.x % maxch;
   TILE_MARK(0, 0);
-  // the tile's entries and this block's channel indices in one round trip
-  // (a union position is read before the union's size is known)
   const int li = threadIdx.x & 15;
-  const int ul_raw = a.ulist[(size_t)tile * a.m + min(kCh * chunk + li, a.m - 1)];
-  const int ntl = *a.n_tiles, uc = a.ucount[tile];
-  const int e = a.tile_expert[tile], first = a.tile_first[tile], n = a.tile_n[tile];
-  if (tile >= ntl || chunk >= max(1, (uc + kCh - 1) / kCh)) {
+  int tile, chunk, e, first, n, uc, ch;
+  bool live;
+  if (dense) {
+    // every chunk of every tile: union position p is channel p
+    const int maxch = a.m / kCh;
+    tile = blockIdx.x / maxch;
+    chunk = blockIdx.x % maxch;
+    const int ntl = *a.n_tiles;
+    e = a.tile_expert[tile];
+    first = a.tile_first[tile];
+    n = a.tile_n[tile];
+    uc = a.m;
+    ch = kCh * chunk + li;
+    live = tile < ntl;
+  } else {
+    // block b runs work item b of the call (items of a tile are consecutive;
+    // the blocks past the last item exit): the item's tile entries and its 16
+    // channels come in one round trip. An item past its tile's union (the
+    // items are laid out for the largest union) exits too.
+    const int* item = a.gu_items + (size_t)blockIdx.x * kGuItemInts;
+    const int nit = *a.n_items;
+    tile = item[0];
+    chunk = item[1];
+    e = item[2];
+    first = item[3];
+    n = item[4];
+    uc = item[5];
+    ch = item[8 + li];
+    live = (int)blockIdx.x < nit && chunk < max(1, (uc + kCh - 1) / kCh);
+  }
+  if (!live) {
     TILE_MARK(0, 3);
     return;
   }
-  gate_up_item(a, dense, tile, chunk, blockIdx.x, sm, uc, e, first, n, min(max(ul_raw, 0), a.m - 1));
+  gate_up_item(a, dense, tile, chunk, blockIdx.x, sm, uc, e, first, n, min(max(ch, 0), a.m - 1));
 }
 
 // sum of p[q * stride] for q < count in index order, N loads in flight at a time
@@ -1965,7 +2036,7 @@ hipError_t launch_forward(const FwdArgs& a, bool dense, hipStream_t stream) {
   const int groups = a.m / kGroup;
   if (!self_route)
     hipLaunchKernelGGL(k_route_quant, dim3(a.batch), dim3(kThreads), 0, stream, a, pair_tiles ? 1 : 0);
-  if (!pair_tiles) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  if (!pair_tiles) hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, a, dense ? 1 : 0);
   if (!dense) {
     if (b1 && a.score_kind == 3)
       hipLaunchKernelGGL(k_score_b1<true>, dim3(a.max_tiles * groups), dim3(kB1Threads),
