@@ -503,6 +503,31 @@ def test_tiles_split_across_many_tokens_per_expert(b, torch):
         lay.close()
 
 
+@pytest.mark.parametrize("k", [1, 5, 40])
+def test_expert_tile_work_items_small_budgets(b, torch, k):
+    """Expert tiles of 1 to 32 tokens with budgets that leave most of each
+    tile's m/16 channel chunks empty: the gate/up work items are laid out for
+    at most n k union channels per tile (n tokens), so small budgets give tiles
+    fewer items than chunks, and a tile of many tokens more items than its union
+    fills. Selections and outputs match the oracle."""
+    lay = Layer(b, "tiny", max_batch=96)
+    try:
+        rng = np.random.default_rng(29 + k)
+        bsz = 96
+        x = synth.f32_to_bf16_bits(rng.standard_normal((bsz, lay.d)).astype(np.float32))
+        logits = rng.standard_normal((bsz, lay.E)).astype(np.float32)
+        logits[:, 5] += 1.5  # one expert takes about three tiles of tokens, another few
+        logits[:, 6] -= 2.0
+        lay.path = "multi_kernel"
+        out = _run(b, torch, lay, x, logits, k)
+        ref = lay.oracle.forward(x, logits, lay.top_e, k)
+        assert (ref["expert_ids"] == 5).sum() > 64
+        _check_selection(b, lay, ref, bsz, lay.top_e, k)
+        assert rel_err(out_to_f64(torch, out), ref["y"]) <= TOL
+    finally:
+        lay.close()
+
+
 def test_qwen3_batch64_zipf_parity(b, torch):
     """Qwen3-shaped block at 64 decode tokens with Zipf(1.1)-skewed routing: the
     per-expert union path selects each token's own channels bit for bit and every
