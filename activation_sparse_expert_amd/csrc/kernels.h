@@ -69,7 +69,7 @@ inline int grouped_kpad(int m, int r) { return (m + r + 31) / 32 * 32; }
 bool grouped_supported(int d, int m);
 // down projection: outputs per block, and the split of its K range over blocks
 constexpr int kDownTargetBlocks = 1024;
-constexpr int kDownMaxStages = 8;
+constexpr int kDownMaxStages = 6;
 constexpr int kMaxDownSplit = 64;
 int grouped_down_width(int d);
 // kmax: the largest union of channels a tile of the call can hold
